@@ -1,0 +1,22 @@
+"""Build the fp64 oracle library (test infrastructure) with the host g++."""
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "dma_oracle.cpp")
+# DMA_ORACLE_LIB lets a test run load a differently built copy of the oracle.
+LIB_PATH = os.environ.get("DMA_ORACLE_LIB", os.path.join(HERE, "libdma_oracle.so"))
+
+
+def build(verbose=False, src=SRC, out=None):
+    out = out or LIB_PATH
+    cmd = ["g++", "-O2", "-std=c++17", "-fopenmp", "-fPIC", "-shared", src, "-o", out + ".tmp"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))
