@@ -1,0 +1,168 @@
+"""Benchmark of the DMA forward on one MI355X.
+
+A step is one whole forward over one batch of seeded synthetic input already
+resident in HBM: dynamic weights, causal top-w keep mask with skip lists, and
+the masked attention.  The default workload is the 16K-token GQA prefill
+(B=1, Hq=32, Hkv=8, S=16384, D=128, w=2048, bf16).
+
+Prints one JSON line:
+  value          effective TFLOP/s of the whole forward, counting 4*D flops per
+                 kept (query head, query row, key) triple
+  ms_per_step    wall time per forward (synchronised on both sides of K steps)
+  roofline       the attention kernel (dominant) against the bf16 dense MFMA peak;
+                 its duration comes from HIP events on the launch stream
+  cpu_baseline   the fp64 oracle on a bounded sample of the same workload
+  stages_ms      event-timed weights / mask / attention per step
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "effective TFLOP/s (kept pairs) + ms/fwd, 16K-token DMA prefill, 1 MI355X"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill_16k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="CPU time budget of the oracle sample")
+    return ap.parse_args()
+
+
+def cpu_baseline(x, wl, budget_s):
+    """The fp64 oracle on a bounded sample: delta for every key plus the keep
+    set and attention of randomly drawn query rows; the delta time is prorated
+    to the sampled share of rows."""
+    import numpy as np
+    import oracle
+
+    t0 = time.perf_counter()
+    d64 = oracle.weights(x["V"], x["Delta"], x["A"])
+    t_w = time.perf_counter() - t0
+    Qc, Kc, Vc = (x[k].float().cpu() for k in ("Q", "K", "V"))
+    rng = np.random.default_rng(wl.seed)
+    total_rows = wl.B * wl.Hq * wl.Sq
+
+    def draw(n):
+        return np.stack([rng.integers(0, wl.B, n), rng.integers(0, wl.Hq, n),
+                         rng.integers(0, wl.Sq, n)], 1).astype(np.int64)
+
+    probe = draw(256)
+    t0 = time.perf_counter()
+    oracle.attn_rows(Qc, Kc, Vc, d64, wl.q_offset, wl.w, probe)
+    per_row = (time.perf_counter() - t0) / len(probe)
+    n = int(min(total_rows, max(256, (budget_s - t_w) / max(per_row, 1e-9))))
+    rows = draw(n)
+    t0 = time.perf_counter()
+    oracle.attn_rows(Qc, Kc, Vc, d64, wl.q_offset, wl.w, rows)
+    t_rows = time.perf_counter() - t0
+    kept = np.minimum(wl.q_offset + rows[:, 2] + 1, wl.w).sum()
+    t = t_rows + t_w * n / total_rows
+    return {"value": float(4 * wl.D * kept / t / 1e12), "unit": "TFLOP/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"fp64 oracle: delta of all {wl.B * wl.Hkv * wl.Sk} keys ({t_w:.2f} s, "
+                      f"prorated) + keep set and attention of {n} random query rows of "
+                      f"{total_rows} ({t_rows:.2f} s)",
+            "seconds": round(t_w + t_rows, 2)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the DMA forward "
+              "here is the single-GPU hot path, see DESIGN.md for how it would shard.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import trainable_dynamic_mask_amd as dma
+    from trainable_dynamic_mask_amd.configs import WORKLOADS
+    from trainable_dynamic_mask_amd.inputs import make_inputs
+
+    wl = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lib = dma.load()
+    x = make_inputs(wl, device=dev)
+    delta = torch.empty(wl.B, wl.Hkv, wl.Sk, dtype=torch.float32, device=dev)
+    mask = dma.alloc_mask(wl.B, wl.Hkv, wl.Sq, wl.Sk, wl.q_offset, wl.w, dev)
+    ws_t = torch.empty(max(16, lib.dma_topk_workspace_bytes(wl.B, wl.Hkv, wl.Sq, wl.Sk)),
+                       dtype=torch.uint8, device=dev)
+    O = torch.empty_like(x["Q"])
+    nbytes_a = lib.dma_attn_workspace_bytes(wl.B, wl.Hq, wl.Sq, wl.D, wl.w)
+    ws_a = torch.empty(max(16, nbytes_a), dtype=torch.uint8, device=dev)
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+
+    def step(e=None):
+        if e:
+            e[0].record()
+        dma.weights(x["V"], x["Delta"], x["A"], out=delta)
+        if e:
+            e[1].record()
+        dma.topk_mask(delta, wl.Sq, wl.q_offset, wl.w, mask=mask, workspace=ws_t)
+        if e:
+            e[2].record()
+        dma.attn_fwd(x["Q"], x["K"], x["V"], delta, mask, out=O, workspace=ws_a)
+        if e:
+            e[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(ev[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    st = {"weights": 0.0, "mask": 0.0, "attention": 0.0}
+    for e in ev:
+        st["weights"] += e[0].elapsed_time(e[1]) / args.steps
+        st["mask"] += e[1].elapsed_time(e[2]) / args.steps
+        st["attention"] += e[2].elapsed_time(e[3]) / args.steps
+    assert torch.isfinite(O.float()).all(), "non-finite output"
+
+    flops = wl.effective_flops()
+    value = flops / (ms_step * 1e-3) / 1e12
+    attn_tflops = flops / (st["attention"] * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "Hq": wl.Hq, "Hkv": wl.Hkv, "Sq": wl.Sq,
+                   "Sk": wl.Sk, "D": wl.D, "w": wl.w, "kept_pairs": wl.kept_pairs(),
+                   "effective_flop": flops},
+        "roofline": {"bound": "mfma", "kernel": "attn_prefill_bf16_kernel" if wl.Sq > 1
+                     else "decode_split_kernel",
+                     "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+        "stages_ms": {k: round(v, 4) for k, v in st.items()},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(x, wl, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,175 @@
+/*
+ * dma.h - C ABI of the MI355X (gfx950) Dynamic Mask Attention forward.
+ *
+ * The method is the one of the Hugging Face blog "Trainable Dynamic Mask
+ * Sparse Attention" (cited here as "the DMA blog"):
+ *   1. dynamic weights  delta = exp(tau(v Delta) x A), tau = softplus
+ *      (section "Dynamic Sparse Mask Generation", delta equation);
+ *   2. keep mask        m_t = f(top_w(delta + m_c^t)): query position p keeps
+ *      the w causally valid keys j <= p with the largest delta, equal delta
+ *      going to the lower key index, and f puts -inf on every other key
+ *      (section "Mask Combination with Causal Constraints");
+ *   3. attention        o_t = softmax(q_t k^T / sqrt(d_h) o m_t) v, read as
+ *      adding delta to the scaled scores of kept keys; masked keys get weight
+ *      exactly 0, so their work is skipped (section "Efficient Sparse
+ *      Attention Computation" and its "Forward Pass Safety" item).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are device memory owned by the caller.  The library
+ *     allocates nothing and keeps no state besides its loaded code objects.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
+ *     work on it; outputs are ready once the stream reaches them.
+ *   - Every argument is validated on the host before anything is enqueued.
+ *     On any error nothing is launched or written and a status is returned.
+ *     A launch failure reported by the runtime maps to DMA_ERR_HIP.
+ *   - Sizes and strides are in elements.  Empty work (B == 0, or no query
+ *     rows, or no keys for dma_weights) returns DMA_OK without launching.
+ *   - Shapes use B batch, Hq query heads, Hkv key/value heads (Hq % Hkv == 0,
+ *     query head hq reads kv head hq / (Hq/Hkv)), Sq query rows, Sk key rows,
+ *     D head size (64 or 128), w keys kept per query row (w >= 1); query row
+ *     i sits at absolute position p = q_offset + i, with q_offset + Sq <= Sk.
+ *   - Calls are reentrant; calls on one stream run in order.
+ */
+#ifndef DMA_H
+#define DMA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DMA_OK = 0,
+  DMA_ERR_INVALID_ARG = 1, /* null pointer, bad size, bad stride or alignment */
+  DMA_ERR_UNSUPPORTED = 2, /* a legal shape this build does not handle */
+  DMA_ERR_WORKSPACE = 3,   /* workspace or list capacity too small */
+  DMA_ERR_HIP = 4          /* the HIP runtime reported an error */
+} dma_status;
+
+typedef enum { DMA_F32 = 0, DMA_BF16 = 1 } dma_dtype;
+
+/* Build limits. */
+#define DMA_MAX_SK (1 << 20) /* keys per sequence */
+#define DMA_BLOCK_Q 64       /* query rows per tile (Bq) */
+#define DMA_BLOCK_K 64       /* keys per key tile (Bk) */
+
+/* Human-readable name of a status code (static storage). */
+const char* dma_status_string(dma_status s);
+
+/* ABI version; bumped whenever a signature or a layout below changes. */
+int dma_abi_version(void);
+
+/* Tile sizes fixed by this build: Bq query rows per tile, Bk keys per key tile. */
+void dma_tile_sizes(int32_t* Bq, int32_t* Bk);
+
+/*
+ * Mask produced by dma_topk_mask and consumed by dma_attn_fwd.  Sizes come
+ * from dma_mask_dims.  Query rows are cut into n_tiles = ceil(Sq / Bq) tiles
+ * per (b, kv head); tile index g = (b*Hkv + h)*n_tiles + t covers query rows
+ * [t*Bq, min(Sq, (t+1)*Bq)).
+ *
+ *   evict  int32 [B*Hkv*Sk]  eviction row of each key (written when Sq > 1):
+ *          key j is kept by exactly the query positions p with j <= p < evict[j]
+ *          (positions over the whole sequence 0..Sk-1; evict[j] == j for a key
+ *          no position keeps, evict[j] == Sk for a key kept to the end).  This interval form is exact because delta has
+ *          no query index, so a key once dropped never returns.
+ *   u_idx  int32 [n_tiles_total * u_stride]  the union U_g of the keep sets of
+ *          the tile's rows, as two ascending runs: first the u_nfull[g] keys
+ *          every row of the tile keeps, then the keys only some rows keep.
+ *   u_cnt, u_nfull  int32 [n_tiles_total]   |U_g| and the length of the first run.
+ *   u_dmax float [n_tiles_total]   largest delta over U_g.
+ *   kt_idx int32 [n_tiles_total * kt_stride]  ascending key-tile indices kt with
+ *          [kt*Bk, (kt+1)*Bk) holding at least one key of U_g (the block-skip
+ *          list: every other key tile is skipped).  May be NULL (not written).
+ *   kt_cnt int32 [n_tiles_total]   length of that list (NULL iff kt_idx is NULL).
+ * With Sq == 1 (one decode row) evict is not read or written and may be NULL.
+ */
+typedef struct {
+  int32_t* evict;
+  int32_t* u_idx;
+  int32_t* u_cnt;
+  int32_t* u_nfull;
+  float* u_dmax;
+  int32_t* kt_idx;
+  int32_t* kt_cnt;
+} dma_mask;
+
+typedef struct {
+  int64_t n_tiles;       /* tiles per (b, kv head): ceil(Sq / Bq) */
+  int64_t n_tiles_total; /* B * Hkv * n_tiles */
+  int64_t u_stride;      /* min(Sk, w + Bq - 1): largest possible |U_g| */
+  int64_t kt_stride;     /* ceil(Sk / Bk) */
+  int64_t evict_elems;   /* B*Hkv*Sk, or 0 when Sq == 1 */
+  int64_t u_elems;       /* n_tiles_total * u_stride */
+  int64_t kt_elems;      /* n_tiles_total * kt_stride */
+} dma_mask_dims;
+
+/* Sizes of the mask arrays for a call of dma_topk_mask with these arguments. */
+dma_status dma_mask_dims_for(int64_t B, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t q_offset,
+                             int64_t w, dma_mask_dims* out);
+
+/* Workspace bytes dma_topk_mask needs (0 when Sq <= 1). */
+size_t dma_topk_workspace_bytes(int64_t B, int64_t Hkv, int64_t Sq, int64_t Sk);
+
+/* Workspace bytes dma_attn_fwd needs (split partials of the one-row path; 0
+ * when Sq > 1). */
+size_t dma_attn_workspace_bytes(int64_t B, int64_t Hq, int64_t Sq, int64_t D, int64_t w);
+
+/*
+ * Step 1: dynamic weights (DMA blog, delta equation).
+ *   pre[b,j,h]   = sum_{c < Hkv*D} V[b,j,c] * Delta[c,h]   (c = kv_head*D + channel)
+ *   delta[b,h,j] = exp(softplus(pre[b,j,h]) * A[h])
+ * V       [B, Sk, Hkv, D] of type vt (F32 or BF16); element (b,j,c) at
+ *         b*v_stride_b + j*v_stride_s + c, i.e. each key's Hkv*D values are
+ *         contiguous.  16-byte aligned base and strides.
+ * Delta   float [Hkv*D, Hkv] row-major.   A float [Hkv].
+ * delta   float [B, Hkv, Sk] contiguous (output).
+ * Arithmetic: fp32 accumulation, fp32 softplus/exp.  Limits: Hkv*D <= 2048.
+ */
+dma_status dma_weights(const void* V, dma_dtype vt, int64_t B, int64_t Sk, int64_t Hkv, int64_t D,
+                       int64_t v_stride_b, int64_t v_stride_s, const float* Delta, const float* A,
+                       float* delta, void* stream);
+
+/*
+ * Step 2: causal top-w keep mask and block-skip lists (DMA blog, m_t
+ * equation), for query positions q_offset .. q_offset+Sq-1 over keys 0..Sk-1.
+ * delta  float [B, Hkv, Sk] (from dma_weights or any other source; NaN is
+ *        not allowed).  Ordering is exact: larger delta wins, equal delta
+ *        goes to the lower key index.
+ * out    arrays sized by dma_mask_dims_for (kt_idx/kt_cnt may be NULL).
+ * ws     dma_topk_workspace_bytes(...) bytes of device scratch (16-byte aligned),
+ *        may be NULL when that is 0.  Its contents are undefined afterwards.
+ * Results are integer and deterministic: bit-identical on every run.
+ */
+dma_status dma_topk_mask(const float* delta, int64_t B, int64_t Hkv, int64_t Sq, int64_t Sk,
+                         int64_t q_offset, int64_t w, const dma_mask* out, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/*
+ * Step 3: masked attention (DMA blog, o_t equation with additive mask).
+ *   For query row i of head hq (position p = q_offset + i, kv head h):
+ *   s_j = scale * (q . k_j) + delta[b,h,j] over the keys j row p keeps,
+ *   O[b,i,hq,:] = sum_j softmax(s)_j v_j,   lse[b,hq,i] = log sum_j exp(s_j).
+ * Q [B,Sq,Hq,D], K and V [B,Sk,Hkv,D] of type t; q_strides / kv_strides give
+ * the element strides of the b, s and head dimensions (the D values of a
+ * head are contiguous; K and V share strides); 16-byte aligned.
+ * delta, mask: from steps 1 and 2 for the same (B, Hkv, Sq, Sk, q_offset, w).
+ * scale  <= 0 selects 1/sqrt(D).
+ * O      [B,Sq,Hq,D] contiguous, type t (output).   lse float [B,Hq,Sq] or NULL.
+ * ws     dma_attn_workspace_bytes(...) bytes (NULL allowed when 0).
+ * Arithmetic: BF16 inputs use bf16 MFMA products with fp32 accumulation and
+ * an fp32 online softmax; F32 inputs are computed in fp32 throughout.
+ */
+dma_status dma_attn_fwd(const void* Q, const void* K, const void* V, dma_dtype t, int64_t B,
+                        int64_t Sq, int64_t Sk, int64_t Hq, int64_t Hkv, int64_t D,
+                        const int64_t q_strides[3], const int64_t kv_strides[3], int64_t q_offset,
+                        int64_t w, const float* delta, const dma_mask* mask, float scale, void* O,
+                        float* lse, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DMA_H */

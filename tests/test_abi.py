@@ -1,0 +1,140 @@
+"""CPU checks of the C ABI library: it loads, exports every function that
+include/dma.h declares, and rejects bad arguments on the host before any
+launch (no GPU needed for these paths)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from trainable_dynamic_mask_amd import _lib
+from trainable_dynamic_mask_amd._lib import DmaMask, DmaMaskDims
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+FAKE = ctypes.c_void_p(0x10000)      # 16-byte aligned, never dereferenced
+MISALIGNED = ctypes.c_void_p(0x10004)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "dma.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dma_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_versions(lib):
+    assert lib.dma_status_string(0) == b"ok"
+    assert lib.dma_status_string(3) == b"workspace too small"
+    assert lib.dma_abi_version() == 1
+    bq, bk = ctypes.c_int32(), ctypes.c_int32()
+    lib.dma_tile_sizes(ctypes.byref(bq), ctypes.byref(bk))
+    assert (bq.value, bk.value) == (64, 64)
+
+
+def _dims(lib, *args):
+    d = DmaMaskDims()
+    return lib.dma_mask_dims_for(*args, ctypes.byref(d)), d
+
+
+def test_mask_dims(lib):
+    rc, d = _dims(lib, 1, 8, 16384, 16384, 0, 2048)
+    assert rc == OK
+    assert (d.n_tiles, d.n_tiles_total, d.u_stride, d.kt_stride) == (256, 2048, 2111, 256)
+    assert d.evict_elems == 8 * 16384 and d.u_elems == 2048 * 2111
+    rc, d = _dims(lib, 64, 8, 1, 32768, 32767, 2048)      # one decode row
+    assert rc == OK and d.u_stride == 2048 and d.evict_elems == 0
+    rc, d = _dims(lib, 1, 1, 10, 10, 0, 50)                # w larger than the sequence
+    assert rc == OK and d.u_stride == 10
+    assert _dims(lib, 1, 1, 10, 9, 0, 5)[0] == INVALID     # rows past the keys
+    assert _dims(lib, 1, 1, 5, 10, 6, 5)[0] == INVALID     # q_offset + Sq > Sk
+    assert _dims(lib, 1, 1, 10, 10, 0, 0)[0] == INVALID    # w < 1
+    assert _dims(lib, 1, 0, 10, 10, 0, 3)[0] == INVALID    # no heads
+    assert _dims(lib, 1, 1, 2, (1 << 20) + 1, 0, 3)[0] == UNSUPPORTED
+    assert _dims(lib, 1, 1, 1, 40000, 39999, 3)[0] == UNSUPPORTED  # decode row past 32768 keys
+    assert _dims(lib, 70000, 1, 2, 2, 0, 1)[0] == UNSUPPORTED
+
+
+def test_workspace_sizes(lib):
+    assert lib.dma_topk_workspace_bytes(1, 8, 16384, 16384) >= 8 * 16384 * 20
+    assert lib.dma_topk_workspace_bytes(1, 8, 1, 16384) == 0
+    assert lib.dma_attn_workspace_bytes(2, 32, 4096, 128, 2048) == 0
+    assert lib.dma_attn_workspace_bytes(64, 32, 1, 128, 2048) == 64 * 32 * 8 * 130 * 4
+
+
+def _weights(lib, V=FAKE, vt=1, B=1, Sk=16, Hkv=2, D=64, sb=None, ss=None, Dl=FAKE, A=FAKE,
+             out=FAKE):
+    ss = Hkv * D if ss is None else ss
+    sb = ss * Sk if sb is None else sb
+    return lib.dma_weights(V, vt, B, Sk, Hkv, D, sb, ss, Dl, A, out, None)
+
+
+def test_weights_validation(lib):
+    assert _weights(lib, D=96) == UNSUPPORTED
+    assert _weights(lib, Hkv=32, D=128) == UNSUPPORTED       # value row over 2048
+    assert _weights(lib, Hkv=0) == INVALID
+    assert _weights(lib, vt=7) == INVALID
+    assert _weights(lib, V=None) == INVALID
+    assert _weights(lib, out=None) == INVALID
+    assert _weights(lib, V=MISALIGNED) == INVALID
+    assert _weights(lib, ss=100) == INVALID                  # row stride below Hkv*D
+    assert _weights(lib, ss=132) == INVALID                  # 264-byte rows: not 16-aligned
+    assert _weights(lib, B=0, V=None) == OK                  # empty: nothing launched
+    assert _weights(lib, Sk=0, V=None) == OK
+
+
+def _topk(lib, B=1, Hkv=2, Sq=16, Sk=16, q0=0, w=4, mask=True, ws=FAKE, ws_bytes=1 << 30):
+    m = DmaMask(FAKE, FAKE, FAKE, FAKE, FAKE, None, None)
+    return lib.dma_topk_mask(FAKE, B, Hkv, Sq, Sk, q0, w, ctypes.byref(m) if mask else None,
+                             ws, ws_bytes, None)
+
+
+def test_topk_validation(lib):
+    assert _topk(lib, q0=1) == INVALID
+    assert _topk(lib, w=0) == INVALID
+    assert _topk(lib, mask=False) == INVALID
+    assert _topk(lib, ws=None, ws_bytes=0) == WORKSPACE
+    assert _topk(lib, ws_bytes=10) == WORKSPACE
+    assert _topk(lib, ws=MISALIGNED) == INVALID
+    assert _topk(lib, Sq=0, Sk=16, q0=16) == OK
+    assert _topk(lib, B=0) == OK
+    m = DmaMask(None, FAKE, FAKE, FAKE, FAKE, None, None)       # evict missing for Sq > 1
+    assert lib.dma_topk_mask(FAKE, 1, 2, 16, 16, 0, 4, ctypes.byref(m), FAKE, 1 << 30, None) == INVALID
+    m = DmaMask(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)       # kt_idx without kt_cnt
+    assert lib.dma_topk_mask(FAKE, 1, 2, 16, 16, 0, 4, ctypes.byref(m), FAKE, 1 << 30, None) == INVALID
+
+
+def _attn(lib, t=1, B=1, Sq=16, Sk=16, Hq=4, Hkv=2, D=128, qs=None, ks=None, q0=0, w=4,
+          scale=0.0, Q=FAKE, O=FAKE, ws=None, ws_bytes=0):
+    qs = qs or (Sq * Hq * D, Hq * D, D)
+    ks = ks or (Sk * Hkv * D, Hkv * D, D)
+    m = DmaMask(FAKE, FAKE, FAKE, FAKE, FAKE, None, None)
+    return lib.dma_attn_fwd(Q, FAKE, FAKE, t, B, Sq, Sk, Hq, Hkv, D, (ctypes.c_int64 * 3)(*qs),
+                            (ctypes.c_int64 * 3)(*ks), q0, w, FAKE, ctypes.byref(m), scale, O,
+                            None, ws, ws_bytes, None)
+
+
+def test_attn_validation(lib):
+    assert _attn(lib, Hq=3) == INVALID                       # Hq not a multiple of Hkv
+    assert _attn(lib, D=96) == UNSUPPORTED
+    assert _attn(lib, D=64) == UNSUPPORTED                   # bf16 prefill is built for D=128
+    assert _attn(lib, scale=math.nan) == INVALID
+    assert _attn(lib, Q=MISALIGNED) == INVALID
+    assert _attn(lib, O=None) == INVALID
+    assert _attn(lib, qs=(16 * 4 * 128, 4 * 128, 100)) == INVALID   # head stride below D
+    assert _attn(lib, ks=(16 * 2 * 128, 2 * 128 + 3, 128)) == INVALID  # odd row stride
+    assert _attn(lib, Sq=1, Sk=16, q0=15) == WORKSPACE       # decode row needs split partials
+    assert _attn(lib, Sq=0, q0=16) == OK
+    assert _attn(lib, B=0) == OK

@@ -1,0 +1,167 @@
+"""GPU masked attention (Hugging Face blog "Trainable Dynamic Mask Sparse
+Attention", section "Efficient Sparse Attention Computation") against the
+fp64 oracle, through the C ABI.
+
+Stage-wise: the oracle gets the GPU's delta, so it selects exactly the keys
+the mask step selected (the mask itself is pinned bit-exactly elsewhere).
+End-to-end: the oracle's own fp64 delta; rows whose keep set differs from the
+GPU's (fp32 vs fp64 near-ties) are counted, explained and left out.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import trainable_dynamic_mask_amd as dma
+from trainable_dynamic_mask_amd.configs import WORKLOADS
+from trainable_dynamic_mask_amd.inputs import make_inputs, make_small
+from tests.dma_check import compare_rows, sample_rows, to64
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(x, wl, scale=None):
+    d = dma.weights(x["V"], x["Delta"], x["A"])
+    gm = dma.topk_mask(d, wl.Sq, wl.q_offset, wl.w)
+    O, lse = dma.attn_fwd(x["Q"], x["K"], x["V"], d, gm, scale=scale, return_lse=True)
+    torch.cuda.synchronize()
+    return d, gm, O, lse
+
+
+def _oracle_rows(x, d, wl, rows, scale=None):
+    return oracle.attn_rows(x["Q"], x["K"], x["V"], to64(d), wl.q_offset, wl.w, rows, scale)
+
+
+def _all_rows(wl):
+    b, h, i = np.meshgrid(np.arange(wl.B), np.arange(wl.Hq), np.arange(wl.Sq), indexing="ij")
+    return np.stack([b.ravel(), h.ravel(), i.ravel()], 1)
+
+
+def test_tiny_f32_every_row(gpu_lib):
+    wl = WORKLOADS["tiny_f32"]
+    x = make_inputs(wl, device="cuda")
+    d, gm, O, lse = _run(x, wl)
+    rows = _all_rows(wl)
+    Or, Lr = _oracle_rows(x, d, wl, rows)
+    m, r = compare_rows(O, lse, Or, Lr, rows, "f32", "tiny_f32")
+    print(f"tiny_f32: max abs {m:.2e} rel L2 {r:.2e}")
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,S,w,dtype,D", [
+    (1, 4, 1, 64, 16, "bf16", 128),      # one tile, MQA group of 4
+    (2, 8, 2, 200, 37, "bf16", 128),     # ragged last tile
+    (1, 2, 2, 129, 129, "bf16", 128),    # w >= S: plain causal
+    (1, 8, 8, 300, 1, "bf16", 128),      # w = 1, G = 1
+    (1, 16, 2, 260, 70, "bf16", 128),    # G = 8: two head groups per kv head
+    (2, 6, 2, 190, 50, "bf16", 128),     # G = 3
+    (1, 4, 2, 333, 100, "f32", 64),
+    (1, 4, 4, 150, 20, "f32", 128),
+])
+def test_small_every_row(gpu_lib, B, Hq, Hkv, S, w, dtype, D):
+    wl, x = make_small(B, Hq, Hkv, S, S, D, w, dtype=dtype, delta_std=0.05, seed=S + w,
+                       device="cuda")
+    d, gm, O, lse = _run(x, wl)
+    rows = _all_rows(wl)
+    Or, Lr = _oracle_rows(x, d, wl, rows)
+    compare_rows(O, lse, Or, Lr, rows, dtype, f"{(B, Hq, Hkv, S, w, dtype, D)}")
+
+
+def test_window_one_copies_value_rows_exactly(gpu_lib):
+    wl, x = make_small(1, 4, 2, 200, 200, 128, 1, dtype="bf16", seed=5, device="cuda")
+    d, gm, O, lse = _run(x, wl)
+    d64 = to64(d)
+    for hq in range(4):
+        h = hq // 2
+        best = np.array([int(np.argmax(d64[0, h, : i + 1])) for i in range(200)])
+        assert torch.equal(O[0, :, hq], x["V"][0, torch.as_tensor(best, device="cuda"), h])
+
+
+def test_custom_scale_and_strided_inputs(gpu_lib):
+    # Q, K, V as views into packed per-token buffers
+    B, S, Hq, Hkv, D, w = 2, 150, 8, 2, 128, 40
+    wl, x = make_small(B, Hq, Hkv, S, S, D, w, dtype="bf16", seed=11, device="cuda")
+    qkv = torch.zeros(B, S, Hq + 2 * Hkv + 1, D, dtype=torch.bfloat16, device="cuda")
+    qkv[:, :, :Hq] = x["Q"]
+    qkv[:, :, Hq:Hq + Hkv] = x["K"]
+    qkv[:, :, Hq + Hkv:Hq + 2 * Hkv] = x["V"]
+    Q, K, V = qkv[:, :, :Hq], qkv[:, :, Hq:Hq + Hkv], qkv[:, :, Hq + Hkv:Hq + 2 * Hkv]
+    kv = torch.zeros(B, S, 2 * Hkv, D, dtype=torch.bfloat16, device="cuda")
+    kv[:, :, :Hkv] = K
+    kv[:, :, Hkv:] = V
+    d = dma.weights(x["V"], x["Delta"], x["A"])
+    gm = dma.topk_mask(d, S, 0, w)
+    O, lse = dma.attn_fwd(Q, kv[:, :, :Hkv], kv[:, :, Hkv:], d, gm, scale=0.05, return_lse=True)
+    rows = _all_rows(wl)
+    Or, Lr = oracle.attn_rows(x["Q"], x["K"], x["V"], to64(d), 0, w, rows, scale=0.05)
+    compare_rows(O, lse, Or, Lr, rows, "bf16", "strided")
+
+
+@pytest.mark.parametrize("q0,Sq,Sk,w", [(100, 70, 170, 30), (500, 129, 629, 200),
+                                        (64, 64, 128, 64)])
+def test_chunked_prefill_query_offset(gpu_lib, q0, Sq, Sk, w):
+    wl, x = make_small(1, 8, 2, Sq, Sk, 128, w, dtype="bf16", q_offset=q0, seed=q0, device="cuda")
+    d, gm, O, lse = _run(x, wl)
+    rows = _all_rows(wl)
+    Or, Lr = _oracle_rows(x, d, wl, rows)
+    compare_rows(O, lse, Or, Lr, rows, "bf16", "chunked")
+
+
+def test_heavy_tailed_delta(gpu_lib):
+    # Delta std 0.5: delta spans many orders of magnitude within a tile
+    wl, x = make_small(1, 4, 1, 500, 500, 128, 60, dtype="bf16", delta_std=0.5, seed=2,
+                       device="cuda")
+    d, gm, O, lse = _run(x, wl)
+    assert float(d.max()) > 1e3
+    rows = _all_rows(wl)
+    Or, Lr = _oracle_rows(x, d, wl, rows)
+    compare_rows(O, lse, Or, Lr, rows, "bf16", "heavy tail")
+
+
+@pytest.mark.parametrize("name,n_random", [("prefill_4k", 300), ("prefill_16k", 300),
+                                           ("prefill_64k", 200)])
+def test_workload_sampled_rows(gpu_lib, name, n_random):
+    wl = WORKLOADS[name]
+    x = make_inputs(wl, device="cuda")
+    d, gm, O, lse = _run(x, wl)
+    assert torch.isfinite(O.float()).all()
+    rows = sample_rows(wl.B, wl.Hq, wl.Sq, wl.w, n_random, seed=wl.seed)
+    Or, Lr = _oracle_rows(x, d, wl, rows)
+    m, r = compare_rows(O, lse, Or, Lr, rows, wl.dtype, name)
+    print(f"{name}: {len(rows)} rows, max abs {m:.2e} rel L2 {r:.2e}")
+
+
+@pytest.mark.parametrize("name", ["prefill_4k", "prefill_16k"])
+def test_end_to_end_with_oracle_delta(gpu_lib, name):
+    wl = WORKLOADS[name]
+    x = make_inputs(wl, device="cuda")
+    d, gm, O, lse = _run(x, wl)
+    d64 = oracle.weights(x["V"], x["Delta"], x["A"])       # the oracle's own delta
+    e_gpu = gm.evict.cpu().numpy().reshape(wl.B, wl.Hkv, wl.Sk)
+    rows = sample_rows(wl.B, wl.Hq, wl.Sq, wl.w, 200, seed=wl.seed + 1)
+    keep, differ = [], 0
+    for (b, hq, i) in rows:
+        h = hq // wl.G
+        ref = oracle.keep_row(d64[b, h], i, wl.w)
+        j = np.arange(i + 1)
+        gpu = j[(j <= i) & (e_gpu[b, h, : i + 1] > i)]
+        if np.array_equal(ref, gpu):
+            keep.append((b, hq, i))
+        else:
+            differ += 1
+            # a differing keep set must come from a near tie of fp64 delta
+            sd = sorted(set(ref) ^ set(gpu))
+            vals = d64[b, h, sd]
+            assert vals.max() - vals.min() <= 1e-4 * vals.max(), (b, hq, i, sd, vals)
+    rows = np.array(keep, np.int64)
+    Or, Lr = oracle.attn_rows(x["Q"], x["K"], x["V"], d64, wl.q_offset, wl.w, rows)
+    m, r = compare_rows(O, lse, Or, Lr, rows, wl.dtype, name + " end-to-end")
+    print(f"{name} end-to-end: {len(rows)} rows compared, {differ} left out (near ties); "
+          f"max abs {m:.2e} rel L2 {r:.2e}")
+
+
+def test_empty_query_rows(gpu_lib):
+    wl, x = make_small(1, 4, 2, 10, 10, 128, 3, device="cuda")
+    d = dma.weights(x["V"], x["Delta"], x["A"])
+    gm = dma.topk_mask(d, 0, 10, 3)
+    O = dma.attn_fwd(x["Q"][:, :0], x["K"], x["V"], d, gm)
+    assert O.shape == (1, 0, 4, 128)

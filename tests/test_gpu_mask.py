@@ -1,0 +1,111 @@
+"""GPU keep masks and block-skip lists (Hugging Face blog "Trainable Dynamic
+Mask Sparse Attention", section "Mask Combination with Causal Constraints")
+against the oracle's literal per-row top-w sets, bit-exact on a shared delta,
+through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import trainable_dynamic_mask_amd as dma
+from trainable_dynamic_mask_amd.configs import WORKLOADS
+from trainable_dynamic_mask_amd.inputs import make_inputs
+from tests.dma_check import check_mask, to64
+
+pytestmark = pytest.mark.gpu
+
+
+def _delta(kind, B, H, S, seed):
+    g = torch.Generator().manual_seed(seed)
+    if kind == "ties":       # few distinct values: exact ties everywhere
+        d = torch.randint(0, 5, (B, H, S), generator=g).float() + 1.0
+    elif kind == "allequal":
+        d = torch.full((B, H, S), 2.0)
+    elif kind == "increasing":  # newest key always best: a sliding window
+        d = torch.arange(S, dtype=torch.float32).expand(B, H, S).contiguous() + 1.0
+    elif kind == "decreasing":  # oldest keys always best: the first w keys
+        d = (S - torch.arange(S, dtype=torch.float32)).expand(B, H, S).contiguous()
+    else:
+        d = torch.exp(torch.randn(B, H, S, generator=g))
+    return d.cuda()
+
+
+@pytest.mark.parametrize("kind", ["random", "ties", "allequal", "increasing", "decreasing"])
+@pytest.mark.parametrize("S,w", [(1, 1), (2, 1), (63, 5), (64, 64), (65, 7), (200, 37),
+                                 (300, 300), (333, 1000), (1000, 130)])
+def test_mask_small(gpu_lib, kind, S, w):
+    d = _delta(kind, 2, 3, S, seed=S * 7 + w)
+    gm = dma.topk_mask(d, S, 0, w)
+    torch.cuda.synchronize()
+    check_mask(gm, d)
+
+
+@pytest.mark.parametrize("S,w", [(4097, 100), (8192, 3000), (12345, 2048)])
+def test_mask_multi_chunk_sort(gpu_lib, S, w):
+    # several 4096-key sort chunks, ragged tail, merge passes
+    d = _delta("ties", 1, 2, S, seed=S)
+    gm = dma.topk_mask(d, S, 0, w)
+    check_mask(gm, d)
+
+
+@pytest.mark.parametrize("q0,Sq,Sk,w", [(10, 50, 60, 7), (100, 130, 300, 40), (0, 70, 200, 9),
+                                        (4000, 200, 4200, 512)])
+def test_mask_query_offset(gpu_lib, q0, Sq, Sk, w):
+    d = _delta("ties", 1, 2, Sk, seed=q0 + Sq)
+    gm = dma.topk_mask(d, Sq, q0, w)
+    check_mask(gm, d)
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "prefill_4k", "prefill_16k", "prefill_64k"])
+def test_mask_workloads(gpu_lib, name):
+    wl = WORKLOADS[name]
+    x = make_inputs(wl, device="cuda")
+    d = dma.weights(x["V"], x["Delta"], x["A"])
+    gm = dma.topk_mask(d, wl.Sq, wl.q_offset, wl.w)
+    torch.cuda.synchronize()
+    check_mask(gm, d)
+
+
+def test_mask_deterministic(gpu_lib):
+    d = _delta("ties", 2, 4, 9000, seed=3)
+    a = dma.topk_mask(d, 9000, 0, 700)
+    b = dma.topk_mask(d, 9000, 0, 700)
+    for f in ("evict", "u_idx", "u_cnt", "u_nfull", "u_dmax", "kt_idx", "kt_cnt"):
+        ta, tb = getattr(a, f), getattr(b, f)
+        n = a.dims["u_elems"] if f == "u_idx" else a.dims["kt_elems"] if f == "kt_idx" else ta.numel()
+        assert torch.equal(ta[:n], tb[:n]), f
+
+
+@pytest.mark.parametrize("kind", ["random", "ties", "allequal"])
+@pytest.mark.parametrize("p,w", [(0, 1), (5, 10), (4095, 2048), (32767, 2048), (20000, 1)])
+def test_decode_select(gpu_lib, kind, p, w):
+    Sk = p + 1 + 3  # cache longer than the row's prefix
+    d = _delta(kind, 3, 2, Sk, seed=p + w)
+    gm = dma.topk_mask(d, 1, p, w)
+    torch.cuda.synchronize()
+    check_mask(gm, d)
+
+
+def test_decode_workload(gpu_lib):
+    wl = WORKLOADS["decode_32k"]
+    x = make_inputs(wl, device="cuda")
+    d = dma.weights(x["V"], x["Delta"], x["A"])
+    gm = dma.topk_mask(d, 1, wl.q_offset, wl.w)
+    torch.cuda.synchronize()
+    u = gm.u_idx.cpu().numpy().reshape(wl.B, wl.Hkv, -1)
+    cnt = gm.u_cnt.cpu().numpy().reshape(wl.B, wl.Hkv)
+    d64 = to64(d)
+    assert (cnt == wl.w).all()
+    for b in range(wl.B):
+        for h in range(wl.Hkv):
+            np.testing.assert_array_equal(u[b, h, : cnt[b, h]],
+                                          oracle.keep_row(d64[b, h], wl.q_offset, wl.w))
+
+
+def test_mask_empty(gpu_lib):
+    d = torch.ones(0, 2, 10, device="cuda")
+    gm = dma.topk_mask(d, 10, 0, 3)
+    assert gm.dims["n_tiles_total"] == 0
+    d = torch.ones(1, 2, 10, device="cuda")
+    gm = dma.topk_mask(d, 0, 10, 3)
+    assert gm.dims["n_tiles_total"] == 0

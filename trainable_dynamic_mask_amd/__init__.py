@@ -1,0 +1,170 @@
+"""Dynamic Mask Attention (DMA) forward for MI355X (gfx950).
+
+The method is the one of the Hugging Face blog "Trainable Dynamic Mask
+Sparse Attention": per-key dynamic weights delta = exp(softplus(v Delta) A)
+from the value states, a causal top-w keep mask per query, and attention
+softmax(q k^T / sqrt(d) + delta) v over only the kept keys.  Every step runs
+in hand-written HIP kernels behind a C ABI (include/dma.h); this module only
+marshals torch tensors (device memory and the current stream) into it.
+
+    delta = weights(V, Delta, A)
+    mask  = topk_mask(delta, Sq, q_offset, w)
+    O     = attn_fwd(Q, K, V, delta, mask, q_offset, w)
+or  O = forward(Q, K, V, Delta, A, w)
+"""
+import ctypes
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import DmaMask, DmaMaskDims, check, load
+
+__all__ = ["weights", "topk_mask", "attn_fwd", "forward", "mask_dims", "Mask", "tile_sizes",
+           "load"]
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return _lib.DMA_BF16
+    if t == torch.float32:
+        return _lib.DMA_F32
+    raise TypeError(f"unsupported dtype {t}")
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return ctypes.c_void_p(t.data_ptr() if t is not None and t.numel() else 0)
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("DMA tensors must live on the GPU")
+
+
+def tile_sizes():
+    bq, bk = ctypes.c_int32(), ctypes.c_int32()
+    load().dma_tile_sizes(ctypes.byref(bq), ctypes.byref(bk))
+    return bq.value, bk.value
+
+
+def mask_dims(B, Hkv, Sq, Sk, q_offset, w):
+    d = DmaMaskDims()
+    check("dma_mask_dims_for", load().dma_mask_dims_for(B, Hkv, Sq, Sk, q_offset, w,
+                                                          ctypes.byref(d)))
+    return {f: getattr(d, f) for f, _ in DmaMaskDims._fields_}
+
+
+@dataclass
+class Mask:
+    """Device arrays of one mask (layouts in include/dma.h)."""
+    B: int
+    Hkv: int
+    Sq: int
+    Sk: int
+    q_offset: int
+    w: int
+    dims: dict
+    evict: Optional[torch.Tensor]
+    u_idx: torch.Tensor
+    u_cnt: torch.Tensor
+    u_nfull: torch.Tensor
+    u_dmax: torch.Tensor
+    kt_idx: Optional[torch.Tensor]
+    kt_cnt: Optional[torch.Tensor]
+
+    def cstruct(self):
+        return DmaMask(_ptr(self.evict), _ptr(self.u_idx), _ptr(self.u_cnt), _ptr(self.u_nfull),
+                       _ptr(self.u_dmax), _ptr(self.kt_idx), _ptr(self.kt_cnt))
+
+
+def alloc_mask(B, Hkv, Sq, Sk, q_offset, w, device, kt_lists=True) -> Mask:
+    d = mask_dims(B, Hkv, Sq, Sk, q_offset, w)
+    i32 = dict(dtype=torch.int32, device=device)
+    n = d["n_tiles_total"]
+    return Mask(B, Hkv, Sq, Sk, q_offset, w, d,
+                evict=torch.empty(d["evict_elems"], **i32) if d["evict_elems"] else None,
+                u_idx=torch.empty(max(1, d["u_elems"]), **i32),
+                u_cnt=torch.empty(max(1, n), **i32),
+                u_nfull=torch.empty(max(1, n), **i32),
+                u_dmax=torch.empty(max(1, n), dtype=torch.float32, device=device),
+                kt_idx=torch.empty(max(1, d["kt_elems"]), **i32) if kt_lists else None,
+                kt_cnt=torch.empty(max(1, n), **i32) if kt_lists else None)
+
+
+def weights(V: torch.Tensor, Delta: torch.Tensor, A: torch.Tensor,
+            out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """delta[b,h,j] = exp(softplus(V[b,j,:] . Delta[:,h]) * A[h]);  V [B,Sk,Hkv,D]."""
+    _need_cuda(V, Delta, A)
+    B, Sk, Hkv, D = V.shape
+    if V.stride(3) != 1 or V.stride(2) != D:
+        raise ValueError("V rows must be contiguous over (kv head, channel)")
+    Delta = Delta.contiguous().float()
+    A = A.contiguous().float()
+    if out is None:
+        out = torch.empty(B, Hkv, Sk, dtype=torch.float32, device=V.device)
+    check("dma_weights", load().dma_weights(_ptr(V), _dtype_code(V.dtype), B, Sk, Hkv, D,
+                                            V.stride(0), V.stride(1), _ptr(Delta), _ptr(A),
+                                            _ptr(out), _stream(V.device)))
+    return out
+
+
+def topk_mask(delta: torch.Tensor, Sq: int, q_offset: int, w: int, kt_lists: bool = True,
+              mask: Optional[Mask] = None, workspace: Optional[torch.Tensor] = None) -> Mask:
+    """Causal top-w keep mask of query positions q_offset..q_offset+Sq-1."""
+    _need_cuda(delta)
+    delta = delta.contiguous()
+    B, Hkv, Sk = delta.shape
+    lib = load()
+    if mask is None:
+        mask = alloc_mask(B, Hkv, Sq, Sk, q_offset, w, delta.device, kt_lists)
+    nbytes = lib.dma_topk_workspace_bytes(B, Hkv, Sq, Sk)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(16, nbytes), dtype=torch.uint8, device=delta.device)
+    ms = mask.cstruct()
+    check("dma_topk_mask", lib.dma_topk_mask(_ptr(delta), B, Hkv, Sq, Sk, q_offset, w,
+                                             ctypes.byref(ms), _ptr(workspace), nbytes,
+                                             _stream(delta.device)))
+    return mask
+
+
+def attn_fwd(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, delta: torch.Tensor, mask: Mask,
+             scale: Optional[float] = None, return_lse: bool = False,
+             out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Masked attention; Q [B,Sq,Hq,D], K/V [B,Sk,Hkv,D] (any b/s/h strides)."""
+    _need_cuda(Q, K, V, delta)
+    B, Sq, Hq, D = Q.shape
+    _, Sk, Hkv, _ = K.shape
+    if K.stride() != V.stride() or Q.stride(3) != 1 or K.stride(3) != 1:
+        raise ValueError("K and V must share strides; the D values must be contiguous")
+    lib = load()
+    if out is None:
+        out = torch.empty(B, Sq, Hq, D, dtype=Q.dtype, device=Q.device)
+    lse = torch.empty(B, Hq, Sq, dtype=torch.float32, device=Q.device) if return_lse else None
+    nbytes = lib.dma_attn_workspace_bytes(B, Hq, Sq, D, mask.w)
+    if nbytes and (workspace is None or workspace.numel() < nbytes):
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=Q.device)
+    qs = (ctypes.c_int64 * 3)(Q.stride(0), Q.stride(1), Q.stride(2))
+    ks = (ctypes.c_int64 * 3)(K.stride(0), K.stride(1), K.stride(2))
+    ms = mask.cstruct()
+    check("dma_attn_fwd", lib.dma_attn_fwd(
+        _ptr(Q), _ptr(K), _ptr(V), _dtype_code(Q.dtype), B, Sq, Sk, Hq, Hkv, D, qs, ks,
+        mask.q_offset, mask.w, _ptr(delta.contiguous()), ctypes.byref(ms),
+        float(scale) if scale is not None else 0.0, _ptr(out), _ptr(lse),
+        _ptr(workspace) if nbytes else ctypes.c_void_p(0), nbytes, _stream(Q.device)))
+    return (out, lse) if return_lse else out
+
+
+def forward(Q, K, V, Delta, A, w, q_offset=0, scale=None, return_all=False):
+    """The whole DMA forward: weights, keep mask, attention."""
+    delta = weights(V, Delta, A)
+    mask = topk_mask(delta, Q.shape[1], q_offset, w)
+    O = attn_fwd(Q, K, V, delta, mask, scale=scale)
+    if return_all:
+        return O, delta, mask
+    return O

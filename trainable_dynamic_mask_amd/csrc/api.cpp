@@ -1,0 +1,219 @@
+// C ABI of the DMA forward (declared in include/dma.h): host-side argument
+// validation, size queries and dispatch to the gfx950 kernels.  Nothing is
+// enqueued unless every argument checks out.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/dma.h"
+#include "common.h"
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct Dims {
+  int64_t n_tiles, u_stride, kt_stride;
+};
+
+// Shapes shared by the mask and attention calls.
+dma_status check_mask_shape(int64_t B, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t q0,
+                            int64_t w) {
+  if (B < 0 || Hkv < 1 || Sq < 0 || Sk < 0 || q0 < 0 || w < 1) return DMA_ERR_INVALID_ARG;
+  if (q0 + Sq > Sk) return DMA_ERR_INVALID_ARG;
+  if (Sk > DMA_MAX_SK) return DMA_ERR_UNSUPPORTED;
+  if (Sq == 1 && q0 + 1 > 32768) return DMA_ERR_UNSUPPORTED;  // one-row select keeps keys in registers
+  if (B * Hkv > 65535) return DMA_ERR_UNSUPPORTED;  // (batch, kv head) is a grid dimension
+  return DMA_OK;
+}
+
+Dims dims_of(int64_t Sq, int64_t Sk, int64_t w) {
+  Dims d;
+  d.n_tiles = cdiv(Sq, DMA_BLOCK_Q);
+  d.u_stride = Sq == 1 ? (w < Sk ? w : Sk) : (w + DMA_BLOCK_Q - 1 < Sk ? w + DMA_BLOCK_Q - 1 : Sk);
+  if (d.u_stride < 1) d.u_stride = 1;
+  d.kt_stride = cdiv(Sk, DMA_BLOCK_K);
+  if (d.kt_stride < 1) d.kt_stride = 1;
+  return d;
+}
+
+dma_status hip_status(hipError_t e) { return e == hipSuccess ? DMA_OK : DMA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* dma_status_string(dma_status s) {
+  switch (s) {
+    case DMA_OK: return "ok";
+    case DMA_ERR_INVALID_ARG: return "invalid argument";
+    case DMA_ERR_UNSUPPORTED: return "unsupported shape";
+    case DMA_ERR_WORKSPACE: return "workspace too small";
+    case DMA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int dma_abi_version(void) { return kAbiVersion; }
+
+void dma_tile_sizes(int32_t* Bq, int32_t* Bk) {
+  if (Bq) *Bq = DMA_BLOCK_Q;
+  if (Bk) *Bk = DMA_BLOCK_K;
+}
+
+dma_status dma_mask_dims_for(int64_t B, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t q_offset,
+                             int64_t w, dma_mask_dims* out) {
+  if (!out) return DMA_ERR_INVALID_ARG;
+  const dma_status st = check_mask_shape(B, Hkv, Sq, Sk, q_offset, w);
+  if (st != DMA_OK) return st;
+  const Dims d = dims_of(Sq, Sk, w);
+  out->n_tiles = d.n_tiles;
+  out->n_tiles_total = B * Hkv * d.n_tiles;
+  out->u_stride = d.u_stride;
+  out->kt_stride = d.kt_stride;
+  out->evict_elems = Sq == 1 ? 0 : B * Hkv * Sk;
+  out->u_elems = out->n_tiles_total * d.u_stride;
+  out->kt_elems = out->n_tiles_total * d.kt_stride;
+  return DMA_OK;
+}
+
+size_t dma_topk_workspace_bytes(int64_t B, int64_t Hkv, int64_t Sq, int64_t Sk) {
+  if (B <= 0 || Hkv <= 0 || Sq <= 1 || Sk <= 0) return 0;
+  return dma_topk_ws_bytes(B * Hkv, Sk);
+}
+
+size_t dma_attn_workspace_bytes(int64_t B, int64_t Hq, int64_t Sq, int64_t D, int64_t w) {
+  if (B <= 0 || Hq <= 0 || Sq != 1 || D <= 0 || w <= 0) return 0;
+  return dma_attn_decode_ws_bytes(B, Hq, D, w);
+}
+
+dma_status dma_weights(const void* V, dma_dtype vt, int64_t B, int64_t Sk, int64_t Hkv, int64_t D,
+                       int64_t v_stride_b, int64_t v_stride_s, const float* Delta, const float* A,
+                       float* delta, void* stream) {
+  if (vt != DMA_F32 && vt != DMA_BF16) return DMA_ERR_INVALID_ARG;
+  if (B < 0 || Sk < 0 || Hkv < 1 || D < 1) return DMA_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return DMA_ERR_UNSUPPORTED;
+  if (Hkv * D > 2048) return DMA_ERR_UNSUPPORTED;
+  if (Sk > ((int64_t)1 << 31) - 64 || B > 65535) return DMA_ERR_UNSUPPORTED;
+  if (B == 0 || Sk == 0) return DMA_OK;
+  if (!V || !Delta || !A || !delta) return DMA_ERR_INVALID_ARG;
+  const int64_t esz = vt == DMA_BF16 ? 2 : 4;
+  if (v_stride_s < Hkv * D || v_stride_b < 0 || (B > 1 && v_stride_b < v_stride_s * Sk))
+    return DMA_ERR_INVALID_ARG;
+  if (!aligned16(V) || (v_stride_s * esz) % 16 != 0 || (v_stride_b * esz) % 16 != 0)
+    return DMA_ERR_INVALID_ARG;
+  return hip_status(dma_launch_weights(V, vt == DMA_BF16, B, Sk, Hkv, D, v_stride_b, v_stride_s,
+                                       Delta, A, delta, static_cast<hipStream_t>(stream)));
+}
+
+dma_status dma_topk_mask(const float* delta, int64_t B, int64_t Hkv, int64_t Sq, int64_t Sk,
+                         int64_t q_offset, int64_t w, const dma_mask* out, void* ws,
+                         size_t ws_bytes, void* stream) {
+  const dma_status st = check_mask_shape(B, Hkv, Sq, Sk, q_offset, w);
+  if (st != DMA_OK) return st;
+  if (!out) return DMA_ERR_INVALID_ARG;
+  if (B == 0 || Sq == 0) return DMA_OK;
+  if (!delta || !out->u_idx || !out->u_cnt || !out->u_nfull || !out->u_dmax)
+    return DMA_ERR_INVALID_ARG;
+  if ((out->kt_idx == nullptr) != (out->kt_cnt == nullptr)) return DMA_ERR_INVALID_ARG;
+  if (Sq > 1 && !out->evict) return DMA_ERR_INVALID_ARG;
+  const Dims d = dims_of(Sq, Sk, w);
+  DmaTopkArgs a;
+  a.delta = delta;
+  a.B = B;
+  a.Hkv = Hkv;
+  a.Sq = Sq;
+  a.Sk = Sk;
+  a.q0 = q_offset;
+  a.w = w;
+  a.n_tiles = d.n_tiles;
+  a.u_stride = d.u_stride;
+  a.kt_stride = d.kt_stride;
+  a.evict = out->evict;
+  a.u_idx = out->u_idx;
+  a.u_cnt = out->u_cnt;
+  a.u_nfull = out->u_nfull;
+  a.u_dmax = out->u_dmax;
+  a.kt_idx = out->kt_idx;
+  a.kt_cnt = out->kt_cnt;
+  a.ws = ws;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (Sq == 1) return hip_status(dma_launch_topk_decode(a, s));
+  const size_t need = dma_topk_workspace_bytes(B, Hkv, Sq, Sk);
+  if (ws_bytes < need || !ws) return DMA_ERR_WORKSPACE;
+  if (!aligned16(ws)) return DMA_ERR_INVALID_ARG;
+  return hip_status(dma_launch_topk_prefill(a, s));
+}
+
+dma_status dma_attn_fwd(const void* Q, const void* K, const void* V, dma_dtype t, int64_t B,
+                        int64_t Sq, int64_t Sk, int64_t Hq, int64_t Hkv, int64_t D,
+                        const int64_t q_strides[3], const int64_t kv_strides[3], int64_t q_offset,
+                        int64_t w, const float* delta, const dma_mask* mask, float scale, void* O,
+                        float* lse, void* ws, size_t ws_bytes, void* stream) {
+  if (t != DMA_F32 && t != DMA_BF16) return DMA_ERR_INVALID_ARG;
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || D < 1) return DMA_ERR_INVALID_ARG;
+  const dma_status st = check_mask_shape(B, Hkv, Sq, Sk, q_offset, w);
+  if (st != DMA_OK) return st;
+  if (D != 64 && D != 128) return DMA_ERR_UNSUPPORTED;
+  if (t == DMA_BF16 && Sq > 1 && D != 128) return DMA_ERR_UNSUPPORTED;
+  if (std::isnan(scale)) return DMA_ERR_INVALID_ARG;
+  if (B == 0 || Sq == 0) return DMA_OK;
+  if (!Q || !K || !V || !delta || !mask || !O || !q_strides || !kv_strides)
+    return DMA_ERR_INVALID_ARG;
+  if (!mask->u_idx || !mask->u_cnt || !mask->u_nfull || !mask->u_dmax) return DMA_ERR_INVALID_ARG;
+  if (Sq > 1 && !mask->evict) return DMA_ERR_INVALID_ARG;
+  const int64_t esz = t == DMA_BF16 ? 2 : 4;
+  for (int i = 0; i < 3; ++i)
+    if (q_strides[i] < 0 || kv_strides[i] < 0 || (q_strides[i] * esz) % 16 != 0 ||
+        (kv_strides[i] * esz) % 16 != 0)
+      return DMA_ERR_INVALID_ARG;
+  if ((Hq > 1 && q_strides[2] < D) || (Hkv > 1 && kv_strides[2] < D)) return DMA_ERR_INVALID_ARG;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O)) return DMA_ERR_INVALID_ARG;
+  const Dims d = dims_of(Sq, Sk, w);
+  DmaAttnArgs a;
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.B = B;
+  a.Sq = Sq;
+  a.Sk = Sk;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.D = D;
+  a.qsb = q_strides[0];
+  a.qss = q_strides[1];
+  a.qsh = q_strides[2];
+  a.ksb = kv_strides[0];
+  a.kss = kv_strides[1];
+  a.ksh = kv_strides[2];
+  a.q0 = q_offset;
+  a.w = w;
+  a.delta = delta;
+  a.evict = mask->evict;
+  a.u_idx = mask->u_idx;
+  a.u_cnt = mask->u_cnt;
+  a.u_nfull = mask->u_nfull;
+  a.u_dmax = mask->u_dmax;
+  a.n_tiles = d.n_tiles;
+  a.u_stride = d.u_stride;
+  a.scale = scale > 0.f ? scale : 1.f / std::sqrt((float)D);
+  a.O = O;
+  a.lse = lse;
+  a.ws = ws;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (Sq == 1) {
+    const size_t need = dma_attn_decode_ws_bytes(B, Hq, D, d.u_stride);
+    if (ws_bytes < need || !ws) return DMA_ERR_WORKSPACE;
+    if (!aligned16(ws)) return DMA_ERR_INVALID_ARG;
+    return hip_status(dma_launch_attn_decode(a, t == DMA_BF16, s));
+  }
+  if (t == DMA_BF16) return hip_status(dma_launch_attn_prefill_bf16(a, s));
+  return hip_status(dma_launch_attn_prefill_f32(a, s));
+}
+
+}  // extern "C"

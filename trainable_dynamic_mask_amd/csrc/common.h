@@ -1,0 +1,111 @@
+// Device helpers and launch declarations shared by the gfx950 kernels of the
+// DMA forward.  Wavefronts are 64 lanes wide throughout.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define DMA_WAVE 64
+
+namespace dma {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Order-preserving map of an fp32 value onto uint32: a < b  <=>  ord(a) < ord(b)
+// (for non-NaN values; -0 and +0 map to neighbouring codes).
+__device__ __forceinline__ uint32_t ord32(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Composite sort key of key j: larger key beats.  The index part makes all keys
+// of one sequence distinct, equal weights going to the lower index.
+__device__ __forceinline__ uint64_t key_of(float d, uint32_t j) {
+  return ((uint64_t)ord32(d) << 32) | (uint64_t)(0xffffffffu - j);
+}
+__device__ __forceinline__ uint32_t index_of(uint64_t k) { return 0xffffffffu - (uint32_t)k; }
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+// number of set bits of m below this lane
+__device__ __forceinline__ int rank_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+}
+
+}  // namespace dma
+
+// ---- host-side launchers (defined next to their kernels) -------------------
+// Each returns hipGetLastError() after enqueueing.
+hipError_t dma_launch_weights(const void* V, int is_bf16, int64_t B, int64_t Sk, int64_t Hkv,
+                              int64_t D, int64_t sb, int64_t ss, const float* Delta,
+                              const float* A, float* delta, hipStream_t st);
+
+struct DmaTopkArgs {
+  const float* delta;
+  int64_t B, Hkv, Sq, Sk, q0, w;
+  int64_t n_tiles, u_stride, kt_stride;
+  int32_t* evict;
+  int32_t* u_idx;
+  int32_t* u_cnt;
+  int32_t* u_nfull;
+  float* u_dmax;
+  int32_t* kt_idx;
+  int32_t* kt_cnt;
+  void* ws;
+};
+hipError_t dma_launch_topk_prefill(const DmaTopkArgs& a, hipStream_t st);
+hipError_t dma_launch_topk_decode(const DmaTopkArgs& a, hipStream_t st);
+size_t dma_topk_ws_bytes(int64_t BH, int64_t Sk);
+
+struct DmaAttnArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  int64_t B, Sq, Sk, Hq, Hkv, D;
+  int64_t qsb, qss, qsh;  // Q strides (b, s, h)
+  int64_t ksb, kss, ksh;  // K/V strides (b, s, h)
+  int64_t q0, w;
+  const float* delta;
+  const int32_t* evict;
+  const int32_t* u_idx;
+  const int32_t* u_cnt;
+  const int32_t* u_nfull;
+  const float* u_dmax;
+  int64_t n_tiles, u_stride;
+  float scale;
+  void* O;
+  float* lse;
+  void* ws;
+};
+hipError_t dma_launch_attn_prefill_bf16(const DmaAttnArgs& a, hipStream_t st);
+hipError_t dma_launch_attn_prefill_f32(const DmaAttnArgs& a, hipStream_t st);
+hipError_t dma_launch_attn_decode(const DmaAttnArgs& a, int is_bf16, hipStream_t st);
+size_t dma_attn_decode_ws_bytes(int64_t B, int64_t Hq, int64_t D, int64_t u_stride);

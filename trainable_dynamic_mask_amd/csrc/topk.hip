@@ -1,0 +1,495 @@
+// Causal top-w keep mask of the DMA forward (Hugging Face blog "Trainable
+// Dynamic Mask Sparse Attention", section "Mask Combination with Causal
+// Constraints", m_t = f(top_w(delta + m_c^t))): query position p keeps the w
+// keys j <= p with the largest delta, equal delta going to the lower index.
+//
+// Because delta carries no query index, the keep sets nest: keep(p) is a
+// subset of keep(p-1) plus {p}.  So key j is kept on exactly one run of
+// positions [j, e_j), where e_j = max(j, b_j) and b_j is the w-th smallest
+// index among the keys that beat j (Sk when fewer than w beat it).  The mask
+// is built from that form in four steps per (batch, kv head) sequence:
+//   T1  sort the keys by the 64-bit composite (delta order, reversed index):
+//       bitonic sort of 4096-key chunks in LDS, then merge-path merges;
+//   T1b rank[j] = position of key j in that order;
+//   T2  eviction rows: ranks are cut into blocks; a block builds the bitmap of
+//       the indices of all better-ranked keys, selects its w-th smallest set
+//       bit b, then walks its own ranks in order with one wave: each key gets
+//       e = max(j, b) and, when j < b, b steps down to the previous set bit.
+//       The wave keeps a 2048-bit window of the bitmap in registers;
+//   T3  per 64-row query tile: the union of the rows' keep sets (keys with
+//       e_j > max(j, tile start) and j <= tile end), the keys every row keeps
+//       first, the natural key tiles touched, and the largest delta.
+// A single query row (decode) skips T1-T3: one workgroup per sequence finds
+// the w-th largest delta by a bitwise search over the order-preserving
+// 32-bit codes and compacts the kept keys in index order.
+#include "common.h"
+
+#include <climits>
+
+namespace {
+
+constexpr int kSortChunk = 4096;
+constexpr int kSortThreads = 1024;
+constexpr int kMergeItems = 8;
+constexpr int kListRows = 64;   // query rows per tile (Bq)
+constexpr int kPartialCap = 128;  // keys only some rows of a tile keep: at most 2*Bq-1
+
+// ---------------------------------------------------------------- T1: chunk sort
+__global__ __launch_bounds__(kSortThreads) void sort_chunk_kernel(const float* __restrict__ delta,
+                                                                  int Sk,
+                                                                  uint64_t* __restrict__ out) {
+  __shared__ uint64_t s[kSortChunk];
+  const int seg = blockIdx.y;
+  const int c0 = blockIdx.x * kSortChunk;
+  const float* d = delta + (int64_t)seg * Sk;
+  for (int i = threadIdx.x; i < kSortChunk; i += kSortThreads) {
+    const int j = c0 + i;
+    s[i] = (j < Sk) ? dma::key_of(d[j], (uint32_t)j) : 0ull;  // 0 sorts after every real key
+  }
+  __syncthreads();
+  for (int k = 2; k <= kSortChunk; k <<= 1) {
+    for (int jj = k >> 1; jj > 0; jj >>= 1) {
+      for (int p = threadIdx.x; p < kSortChunk / 2; p += kSortThreads) {
+        const int i = ((p & ~(jj - 1)) << 1) | (p & (jj - 1));
+        const int l = i + jj;
+        const bool desc = (i & k) == 0;
+        const uint64_t a = s[i], b = s[l];
+        if ((a < b) == desc) {
+          s[i] = b;
+          s[l] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  uint64_t* o = out + (int64_t)seg * Sk;
+  for (int i = threadIdx.x; i < kSortChunk; i += kSortThreads)
+    if (c0 + i < Sk) o[c0 + i] = s[i];
+}
+
+// ---------------------------------------------------------------- T1: merge
+// Merge neighbouring descending runs of length L into runs of 2L.
+__global__ __launch_bounds__(256) void merge_kernel(const uint64_t* __restrict__ src,
+                                                    uint64_t* __restrict__ dst, int Sk, int L) {
+  const int seg = blockIdx.y;
+  const int64_t o_glob = ((int64_t)blockIdx.x * 256 + threadIdx.x) * kMergeItems;
+  if (o_glob >= Sk) return;
+  const int base = (int)(o_glob / (2 * L)) * (2 * L);
+  const int o = (int)o_glob - base;
+  const int la = min(L, Sk - base);
+  const int lb = max(0, min(L, Sk - base - L));
+  const uint64_t* A = src + (int64_t)seg * Sk + base;
+  const uint64_t* B = A + L;
+  // co-rank: number of A elements among the first o outputs
+  int lo = max(0, o - lb), hi = min(o, la);
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (A[mid] > B[o - mid - 1]) lo = mid + 1;
+    else hi = mid;
+  }
+  int ia = lo, ib = o - lo;
+  uint64_t* D = dst + (int64_t)seg * Sk + base + o;
+  const int n = min(kMergeItems, la + lb - o);
+  for (int k = 0; k < n; ++k) {
+    const bool takeA = (ib >= lb) || (ia < la && A[ia] > B[ib]);
+    D[k] = takeA ? A[ia++] : B[ib++];
+  }
+}
+
+// ---------------------------------------------------------------- T1b: ranks
+__global__ __launch_bounds__(256) void rank_kernel(const uint64_t* __restrict__ sorted, int Sk,
+                                                   int32_t* __restrict__ rank) {
+  const int seg = blockIdx.y;
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r >= Sk) return;
+  const uint32_t j = dma::index_of(sorted[(int64_t)seg * Sk + r]);
+  rank[(int64_t)seg * Sk + j] = r;
+}
+
+// Exclusive prefix sum over a block of NT threads (NT/64 waves); also returns the total.
+template <int NT>
+__device__ __forceinline__ int block_excl_scan(int v, int* s_w, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) s_w[wave] = x;
+  __syncthreads();
+  int before = 0;
+  total = 0;
+#pragma unroll
+  for (int k = 0; k < NT / 64; ++k) {
+    const int t = s_w[k];
+    if (k < wave) before += t;
+    total += t;
+  }
+  __syncthreads();
+  return before + x - v;
+}
+
+// ---------------------------------------------------------------- T2: eviction rows
+__global__ __launch_bounds__(256) void evict_kernel(const uint64_t* __restrict__ sorted,
+                                                    const int32_t* __restrict__ rank, int Sk, int w,
+                                                    int R, int32_t* __restrict__ evict) {
+  extern __shared__ uint32_t bm[];  // bitmap of indices, ceil(Sk/32) words
+  __shared__ int s_w[4];
+  __shared__ int s_f;
+  const int seg = blockIdx.y;
+  const uint64_t* K = sorted + (int64_t)seg * Sk;
+  const int32_t* rk = rank + (int64_t)seg * Sk;
+  int32_t* E = evict + (int64_t)seg * Sk;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r0 = blockIdx.x * R, r1 = min(Sk, r0 + R);
+  // the w best keys are never beaten by w others: kept to the end
+  for (int r = r0 + (int)threadIdx.x; r < min(r1, w); r += 256) E[dma::index_of(K[r])] = Sk;
+  const int rs = max(r0, w);
+  if (rs >= r1) return;
+  const int nw = (Sk + 31) >> 5;
+
+  // bitmap of { j : rank[j] < rs }, 64 indices per ballot
+  for (int jb = wave * 256; jb < Sk; jb += 1024) {
+    uint64_t m[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int j = jb + c * 64 + lane;
+      m[c] = dma::ballot(j < Sk && rk[j] < rs);
+    }
+    if (lane < 8) {
+      const int c = lane >> 1;
+      const int wi = ((jb + c * 64) >> 5) + (lane & 1);
+      if (wi < nw) bm[wi] = (lane & 1) ? (uint32_t)(m[c] >> 32) : (uint32_t)m[c];
+    }
+  }
+  __syncthreads();
+
+  // select the w-th smallest set bit
+  if (threadIdx.x == 0) s_f = 0;  // overwritten below: at least w bits are set
+  const int per = (nw + 255) / 256;
+  const int wlo = threadIdx.x * per, whi = min(nw, wlo + per);
+  int cnt = 0;
+  for (int k = wlo; k < whi; ++k) cnt += __popc(bm[k]);
+  int total;
+  const int before = block_excl_scan<256>(cnt, s_w, total);
+  if (before < w && before + cnt >= w) {
+    int need = w - before;
+    for (int k = wlo; k < whi; ++k) {
+      uint32_t x = bm[k];
+      const int c = __popc(x);
+      if (need <= c) {
+        for (int q = 1; q < need; ++q) x &= x - 1;
+        s_f = k * 32 + __builtin_ctz(x);
+        break;
+      }
+      need -= c;
+    }
+  }
+  __syncthreads();
+  if (wave != 0) return;
+
+  // walk the block's ranks in order on one wave
+  int f = s_f;
+  int wb = max(0, (f >> 5) - 63);  // window: words [wb, wb+64), lane l holds word wb+l
+  uint32_t win = (wb + lane < nw) ? bm[wb + lane] : 0u;
+  for (int g0 = rs; g0 < r1; g0 += 64) {
+    const int r = g0 + lane;
+    const int xl = (r < r1) ? (int)dma::index_of(K[r]) : 0;
+    int el = 0;
+    const int steps = min(64, r1 - g0);
+    for (int s = 0; s < steps; ++s) {
+      const int x = __builtin_amdgcn_readlane(xl, s);
+      if (lane == s) el = x < f ? f : x;
+      if (x < f) {
+        const int xw = x >> 5;
+        if (xw >= wb) {
+          if (lane == xw - wb) win |= 1u << (x & 31);
+        } else if (lane == 0) {
+          bm[xw] |= 1u << (x & 31);
+        }
+        // f <- largest set index below f (x itself qualifies)
+        for (;;) {
+          const int fl = f - wb * 32;
+          const int fw = fl >> 5, fb = fl & 31;
+          const uint32_t mw =
+              lane < fw ? win : (lane == fw ? (win & ((1u << fb) - 1u)) : 0u);
+          const uint64_t bal = dma::ballot(mw != 0u);
+          if (bal) {
+            const int hl = 63 - __builtin_clzll(bal);
+            const uint32_t word = __builtin_amdgcn_readlane(mw, hl);
+            f = (wb + hl) * 32 + 31 - __builtin_clz(word);
+            break;
+          }
+          if (wb == 0) {  // unreachable: at least w set indices lie below f
+            f = -1;
+            break;
+          }
+          wb = max(0, wb - 64);
+          win = (wb + lane < nw) ? bm[wb + lane] : 0u;
+        }
+      }
+    }
+    if (r < r1) E[xl] = el;
+  }
+}
+
+// ---------------------------------------------------------------- T3: tile lists
+__global__ __launch_bounds__(256) void lists_kernel(
+    const float* __restrict__ delta, const int32_t* __restrict__ evict, int Sk, int Sq, int q0,
+    int n_tiles, int u_stride, int kt_stride, int32_t* __restrict__ u_idx,
+    int32_t* __restrict__ u_cnt, int32_t* __restrict__ u_nfull, float* __restrict__ u_dmax,
+    int32_t* __restrict__ kt_idx, int32_t* __restrict__ kt_cnt) {
+  __shared__ int s_part[kPartialCap];
+  __shared__ int s_w[3][4];
+  __shared__ float s_m[4];
+  const int seg = blockIdx.y, t = blockIdx.x;
+  const int64_t g = (int64_t)seg * n_tiles + t;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int p_lo = q0 + t * kListRows;
+  const int p_hi = q0 + min(Sq, t * kListRows + kListRows) - 1;
+  const int32_t* E = evict + (int64_t)seg * Sk;
+  const float* Dl = delta + (int64_t)seg * Sk;
+  int32_t* out = u_idx + g * u_stride;
+  int32_t* kout = kt_idx ? kt_idx + g * kt_stride : nullptr;
+  int nfull = 0, npart = 0, nkt = 0;
+  float dmax = -INFINITY;
+  for (int base = 0; base <= p_hi; base += 1024) {
+    uint64_t mf[4], mp[4];
+    int nf = 0, np = 0, nk = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int j = base + wave * 256 + c * 64 + lane;
+      const bool valid = j <= p_hi;
+      const int e = valid ? E[j] : 0;
+      const bool member = valid && e > max(j, p_lo);
+      const bool full = member && j <= p_lo && e > p_hi;
+      if (member) dmax = fmaxf(dmax, Dl[j]);
+      mf[c] = dma::ballot(full);
+      mp[c] = dma::ballot(member && !full);
+      nf += __popcll(mf[c]);
+      np += __popcll(mp[c]);
+      nk += ((mf[c] | mp[c]) != 0ull) ? 1 : 0;
+    }
+    if (lane == 0) {
+      s_w[0][wave] = nf;
+      s_w[1][wave] = np;
+      s_w[2][wave] = nk;
+    }
+    __syncthreads();
+    int of = nfull, op = npart, ok = nkt, tf = 0, tp = 0, tk = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (k < wave) {
+        of += s_w[0][k];
+        op += s_w[1][k];
+        ok += s_w[2][k];
+      }
+      tf += s_w[0][k];
+      tp += s_w[1][k];
+      tk += s_w[2][k];
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int j = base + wave * 256 + c * 64 + lane;
+      if ((mf[c] >> lane) & 1ull) {
+        const int pos = of + dma::rank_below(mf[c]);
+        if (pos < u_stride) out[pos] = j;
+      }
+      if ((mp[c] >> lane) & 1ull) {
+        const int pos = op + dma::rank_below(mp[c]);
+        if (pos < kPartialCap) s_part[pos] = j;
+      }
+      of += __popcll(mf[c]);
+      op += __popcll(mp[c]);
+      if ((mf[c] | mp[c]) != 0ull) {
+        if (lane == 0 && kout && ok < kt_stride) kout[ok] = (base + wave * 256 + c * 64) / 64;
+        ++ok;
+      }
+    }
+    nfull += tf;
+    npart += tp;
+    nkt += tk;
+    __syncthreads();
+  }
+  const int np = min(npart, kPartialCap);
+  for (int k = threadIdx.x; k < np; k += 256)
+    if (nfull + k < u_stride) out[nfull + k] = s_part[k];
+  dmax = dma::wave_max(dmax);
+  if (lane == 0) s_m[wave] = dmax;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    u_cnt[g] = min(nfull + npart, u_stride);
+    u_nfull[g] = min(nfull, u_stride);
+    u_dmax[g] = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+    if (kt_cnt) kt_cnt[g] = min(nkt, kt_stride);
+  }
+}
+
+// ---------------------------------------------------------------- decode: one row
+// Keys 0..p of one sequence; keeps the w best.  KPT codes per thread stay in
+// registers; the threshold is found bit by bit from the top: the largest code
+// T with #{code >= T} >= w.
+constexpr int kDecThreads = 1024;
+constexpr int kDecKPT = 32;  // rows up to 32768 keys
+
+__global__ __launch_bounds__(kDecThreads) void decode_select_kernel(
+    const float* __restrict__ delta, int Sk, int p, int w, int u_stride, int kt_stride,
+    int32_t* __restrict__ u_idx, int32_t* __restrict__ u_cnt, int32_t* __restrict__ u_nfull,
+    float* __restrict__ u_dmax, int32_t* __restrict__ kt_idx, int32_t* __restrict__ kt_cnt) {
+  __shared__ int s_w[kDecThreads / 64];
+  __shared__ float s_m[kDecThreads / 64];
+  __shared__ uint32_t s_kt[(1 << 20) / 64 / 32];  // key-tile flags as bits
+  const int seg = blockIdx.x;
+  const int n = p + 1;
+  const float* Dl = delta + (int64_t)seg * Sk;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int j0 = tid * kDecKPT;
+  uint32_t code[kDecKPT];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < kDecKPT; ++k) {
+    const int j = j0 + k;
+    const float v = (j < n) ? Dl[j] : 0.f;
+    code[k] = (j < n) ? dma::ord32(v) : 0u;
+    if (j < n) mx = fmaxf(mx, v);
+  }
+  mx = dma::wave_max(mx);
+  if (lane == 0) s_m[wave] = mx;
+  int32_t* out = u_idx + (int64_t)seg * u_stride;
+  const int nkt = (n + 63) / 64;
+  for (int k = tid; k < (nkt + 31) / 32; k += kDecThreads) s_kt[k] = 0u;
+
+  uint32_t T = 0;  // codes >= T: at least w of them (0 counts every real key)
+  int need_eq = 0, tot;
+  if (n > w) {
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = T | (1u << bit);
+      int c = 0;
+#pragma unroll
+      for (int k = 0; k < kDecKPT; ++k) c += (code[k] >= cand && j0 + k < n) ? 1 : 0;
+      block_excl_scan<kDecThreads>(c, s_w, tot);
+      if (tot >= w) T = cand;
+    }
+    int gt = 0;
+#pragma unroll
+    for (int k = 0; k < kDecKPT; ++k) gt += (code[k] > T && j0 + k < n) ? 1 : 0;
+    block_excl_scan<kDecThreads>(gt, s_w, tot);
+    need_eq = w - tot;  // how many of the keys whose code equals T are kept (lowest index first)
+  }
+  // ordered compaction
+  int eq = 0, keep = 0;
+#pragma unroll
+  for (int k = 0; k < kDecKPT; ++k) {
+    const bool in = j0 + k < n;
+    eq += (in && n > w && code[k] == T) ? 1 : 0;
+  }
+  const int eq_before = block_excl_scan<kDecThreads>(eq, s_w, tot);
+  int eq_left = max(0, need_eq - eq_before);
+#pragma unroll
+  for (int k = 0; k < kDecKPT; ++k) {
+    const bool in = j0 + k < n;
+    bool kept = in && (n <= w || code[k] > T);
+    if (in && n > w && code[k] == T && eq_left > 0) {
+      kept = true;
+      --eq_left;
+    }
+    keep += kept ? 1 : 0;
+  }
+  const int pos0 = block_excl_scan<kDecThreads>(keep, s_w, tot);
+  eq_left = max(0, need_eq - eq_before);
+  int pos = pos0;
+#pragma unroll
+  for (int k = 0; k < kDecKPT; ++k) {
+    const int j = j0 + k;
+    const bool in = j < n;
+    bool kept = in && (n <= w || code[k] > T);
+    if (in && n > w && code[k] == T && eq_left > 0) {
+      kept = true;
+      --eq_left;
+    }
+    if (kept) {
+      if (pos < u_stride) out[pos] = j;
+      ++pos;
+      atomicOr(&s_kt[j >> 11], 1u << ((j >> 6) & 31));
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float m = s_m[0];
+    for (int k = 1; k < kDecThreads / 64; ++k) m = fmaxf(m, s_m[k]);
+    u_cnt[seg] = min(tot, u_stride);
+    u_nfull[seg] = min(tot, u_stride);
+    u_dmax[seg] = m;
+  }
+  if (kt_idx) {
+    // ordered compaction of the key-tile flags
+    int c = 0;
+    const int kw = (nkt + 31) / 32;
+    const int per = (kw + kDecThreads - 1) / kDecThreads;
+    for (int k = tid * per; k < min(kw, tid * per + per); ++k) c += __popc(s_kt[k]);
+    int ktot;
+    int at = block_excl_scan<kDecThreads>(c, s_w, ktot);
+    for (int k = tid * per; k < min(kw, tid * per + per); ++k) {
+      uint32_t x = s_kt[k];
+      while (x) {
+        const int b = __builtin_ctz(x);
+        x &= x - 1;
+        if (at < kt_stride) kt_idx[(int64_t)seg * kt_stride + at] = k * 32 + b;
+        ++at;
+      }
+    }
+    if (tid == 0) kt_cnt[seg] = min(ktot, kt_stride);
+  }
+}
+
+}  // namespace
+
+size_t dma_topk_ws_bytes(int64_t BH, int64_t Sk) {
+  // two key buffers (ping-pong merges) + ranks
+  const size_t n = (size_t)BH * (size_t)Sk;
+  return n * (2 * sizeof(uint64_t) + sizeof(int32_t)) + 256;
+}
+
+hipError_t dma_launch_topk_prefill(const DmaTopkArgs& a, hipStream_t st) {
+  const int64_t BH = a.B * a.Hkv;
+  const int Sk = (int)a.Sk;
+  const size_t n = (size_t)BH * (size_t)Sk;
+  uint64_t* kA = static_cast<uint64_t*>(a.ws);
+  uint64_t* kB = kA + n;
+  int32_t* rank = reinterpret_cast<int32_t*>(kB + n);
+
+  const int nch = (Sk + kSortChunk - 1) / kSortChunk;
+  hipLaunchKernelGGL(sort_chunk_kernel, dim3(nch, BH), dim3(kSortThreads), 0, st, a.delta, Sk,
+                     kA);
+  uint64_t* src = kA;
+  uint64_t* dst = kB;
+  for (int L = kSortChunk; L < Sk; L <<= 1) {
+    const int nthr = (Sk + kMergeItems - 1) / kMergeItems;
+    hipLaunchKernelGGL(merge_kernel, dim3((nthr + 255) / 256, BH), dim3(256), 0, st, src, dst, Sk,
+                       L);
+    uint64_t* t = src;
+    src = dst;
+    dst = t;
+  }
+  hipLaunchKernelGGL(rank_kernel, dim3((Sk + 255) / 256, BH), dim3(256), 0, st, src, Sk, rank);
+  const int R = Sk > 16384 ? 512 : 256;
+  const int nwords = (Sk + 31) / 32;
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&evict_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)(nwords * sizeof(uint32_t)));
+  hipLaunchKernelGGL(evict_kernel, dim3((Sk + R - 1) / R, BH), dim3(256),
+                     (size_t)nwords * sizeof(uint32_t), st, src, rank, Sk, (int)a.w, R, a.evict);
+  hipLaunchKernelGGL(lists_kernel, dim3((unsigned)a.n_tiles, BH), dim3(256), 0, st, a.delta,
+                     a.evict, Sk, (int)a.Sq, (int)a.q0, (int)a.n_tiles, (int)a.u_stride,
+                     (int)a.kt_stride, a.u_idx, a.u_cnt, a.u_nfull, a.u_dmax, a.kt_idx, a.kt_cnt);
+  return hipGetLastError();
+}
+
+hipError_t dma_launch_topk_decode(const DmaTopkArgs& a, hipStream_t st) {
+  const int64_t BH = a.B * a.Hkv;
+  hipLaunchKernelGGL(decode_select_kernel, dim3(BH), dim3(kDecThreads), 0, st, a.delta, (int)a.Sk,
+                     (int)a.q0, (int)a.w, (int)a.u_stride, (int)a.kt_stride, a.u_idx, a.u_cnt,
+                     a.u_nfull, a.u_dmax, a.kt_idx, a.kt_cnt);
+  return hipGetLastError();
+}
