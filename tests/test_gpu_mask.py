@@ -70,10 +70,16 @@ def test_mask_deterministic(gpu_lib):
     d = _delta("ties", 2, 4, 9000, seed=3)
     a = dma.topk_mask(d, 9000, 0, 700)
     b = dma.topk_mask(d, 9000, 0, 700)
-    for f in ("evict", "u_idx", "u_cnt", "u_nfull", "u_dmax", "kt_idx", "kt_cnt"):
-        ta, tb = getattr(a, f), getattr(b, f)
-        n = a.dims["u_elems"] if f == "u_idx" else a.dims["kt_elems"] if f == "kt_idx" else ta.numel()
-        assert torch.equal(ta[:n], tb[:n]), f
+    for f in ("evict", "u_cnt", "u_nfull", "u_dmax", "kt_cnt"):
+        assert torch.equal(getattr(a, f), getattr(b, f)), f
+    # list entries past each tile's count are never written: compare the counted ones
+    nt = a.dims["n_tiles_total"]
+    for f, cnt, stride in (("u_idx", a.u_cnt, a.dims["u_stride"]),
+                           ("kt_idx", a.kt_cnt, a.dims["kt_stride"])):
+        ta = getattr(a, f)[: nt * stride].view(nt, stride).cpu()
+        tb = getattr(b, f)[: nt * stride].view(nt, stride).cpu()
+        for g, c in enumerate(cnt.cpu().tolist()):
+            assert torch.equal(ta[g, :c], tb[g, :c]), (f, g)
 
 
 @pytest.mark.parametrize("kind", ["random", "ties", "allequal"])
