@@ -98,12 +98,12 @@ __global__ __launch_bounds__(256) void merge_kernel(const uint64_t* __restrict__
 
 // ---------------------------------------------------------------- T1b: ranks
 __global__ __launch_bounds__(256) void rank_kernel(const uint64_t* __restrict__ sorted, int Sk,
-                                                   int32_t* __restrict__ rank) {
+                                                   int rstride, int32_t* __restrict__ rank) {
   const int seg = blockIdx.y;
   const int r = blockIdx.x * 256 + threadIdx.x;
   if (r >= Sk) return;
   const uint32_t j = dma::index_of(sorted[(int64_t)seg * Sk + r]);
-  rank[(int64_t)seg * Sk + j] = r;
+  rank[(int64_t)seg * rstride + j] = r;
 }
 
 // Exclusive prefix sum over a block of NT threads (NT/64 waves); also returns the total.
@@ -132,14 +132,18 @@ __device__ __forceinline__ int block_excl_scan(int v, int* s_w, int& total) {
 
 // ---------------------------------------------------------------- T2: eviction rows
 __global__ __launch_bounds__(256) void evict_kernel(const uint64_t* __restrict__ sorted,
-                                                    const int32_t* __restrict__ rank, int Sk, int w,
-                                                    int R, int32_t* __restrict__ evict) {
-  extern __shared__ uint32_t bm[];  // bitmap of indices, ceil(Sk/32) words
-  __shared__ int s_w[4];
-  __shared__ int s_f;
+                                                    const int32_t* __restrict__ rank, int Sk,
+                                                    int rstride, int w, int R,
+                                                    int32_t* __restrict__ evict) {
+  // Dynamic LDS only, so the bitmap starts at byte 0 (8-byte aligned for the
+  // 64-bit word reads): bitmap of indices in whole 64-bit words, then s_w, s_f.
+  extern __shared__ __align__(16) uint32_t bm[];
+  const int nw64 = (Sk + 63) >> 6;
+  int* s_w = reinterpret_cast<int*>(bm + 2 * nw64);
+  int& s_f = s_w[4];
   const int seg = blockIdx.y;
   const uint64_t* K = sorted + (int64_t)seg * Sk;
-  const int32_t* rk = rank + (int64_t)seg * Sk;
+  const int32_t* rk = rank + (int64_t)seg * rstride;
   int32_t* E = evict + (int64_t)seg * Sk;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r0 = blockIdx.x * R, r1 = min(Sk, r0 + R);
@@ -148,31 +152,48 @@ __global__ __launch_bounds__(256) void evict_kernel(const uint64_t* __restrict__
   const int rs = max(r0, w);
   if (rs >= r1) return;
   const int nw = (Sk + 31) >> 5;
+  if (threadIdx.x == 0 && (nw & 1)) bm[nw] = 0u;  // pad to whole 64-bit words
 
-  // bitmap of { j : rank[j] < rs }, 64 indices per ballot
-  for (int jb = wave * 256; jb < Sk; jb += 1024) {
-    uint64_t m[4];
+  // Bitmap of { j : rank[j] < rs }: thread t builds words [t*per, (t+1)*per) from
+  // its contiguous ranks with 16-byte loads, then selects the w-th smallest set
+  // bit from per-thread popcounts and one block scan.
+  const int per = (nw + 255) / 256;
+  const int wlo = min(nw, (int)threadIdx.x * per), whi = min(nw, wlo + per);
+  int cnt = 0;
+  for (int wi = wlo; wi < whi; wi += 2) {
+    uint32_t word[2] = {0u, 0u};
+    int4 v[2][8];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int j = jb + c * 64 + lane;
-      m[c] = dma::ballot(j < Sk && rk[j] < rs);
-    }
-    if (lane < 8) {
-      const int c = lane >> 1;
-      const int wi = ((jb + c * 64) >> 5) + (lane & 1);
-      if (wi < nw) bm[wi] = (lane & 1) ? (uint32_t)(m[c] >> 32) : (uint32_t)m[c];
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int j = (wi + u) * 32 + q * 4;
+        v[u][q] = (wi + u < whi && j + 3 < Sk) ? *reinterpret_cast<const int4*>(rk + j)
+                                               : make_int4(INT_MAX, INT_MAX, INT_MAX, INT_MAX);
+        if (wi + u < whi && j + 3 >= Sk) {  // ragged tail of the last word
+          v[u][q].x = j < Sk ? rk[j] : INT_MAX;
+          v[u][q].y = j + 1 < Sk ? rk[j + 1] : INT_MAX;
+          v[u][q].z = j + 2 < Sk ? rk[j + 2] : INT_MAX;
+        }
+      }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        word[u] |= (v[u][q].x < rs ? 1u : 0u) << (q * 4);
+        word[u] |= (v[u][q].y < rs ? 1u : 0u) << (q * 4 + 1);
+        word[u] |= (v[u][q].z < rs ? 1u : 0u) << (q * 4 + 2);
+        word[u] |= (v[u][q].w < rs ? 1u : 0u) << (q * 4 + 3);
+      }
+      if (wi + u < whi) {
+        bm[wi + u] = word[u];
+        cnt += __popc(word[u]);
+      }
     }
   }
-  __syncthreads();
-
-  // select the w-th smallest set bit
-  if (threadIdx.x == 0) s_f = 0;  // overwritten below: at least w bits are set
-  const int per = (nw + 255) / 256;
-  const int wlo = threadIdx.x * per, whi = min(nw, wlo + per);
-  int cnt = 0;
-  for (int k = wlo; k < whi; ++k) cnt += __popc(bm[k]);
   int total;
-  const int before = block_excl_scan<256>(cnt, s_w, total);
+  const int before = block_excl_scan<256>(cnt, s_w, total);  // its barriers publish bm
+  if (threadIdx.x == 0 && total < w) s_f = -1;  // unreachable: rs >= w ranks are set
   if (before < w && before + cnt >= w) {
     int need = w - before;
     for (int k = wlo; k < whi; ++k) {
@@ -189,60 +210,65 @@ __global__ __launch_bounds__(256) void evict_kernel(const uint64_t* __restrict__
   __syncthreads();
   if (wave != 0) return;
 
-  // walk the block's ranks in order on one wave
+  // Walk the block's ranks in order on one wave.  Everything the walk carries
+  // is wave-uniform (scalar registers): f, the 64-bit bitmap word holding f
+  // (with this walk's own insertions), and its index.  Insertions below that
+  // word go to LDS; f only ever moves down, so words above it are never read
+  // again.  Each lane records the key and eviction row of one step; they are
+  // stored 64 at a time.
+  uint64_t* bm64 = reinterpret_cast<uint64_t*>(bm);
   int f = s_f;
-  int wb = max(0, (f >> 5) - 63);  // window: words [wb, wb+64), lane l holds word wb+l
-  uint32_t win = (wb + lane < nw) ? bm[wb + lane] : 0u;
+  if (f < 0) return;  // unreachable (see above)
+  int cwi = f >> 6;
+  uint64_t cw = bm64[cwi];
   for (int g0 = rs; g0 < r1; g0 += 64) {
-    const int r = g0 + lane;
-    const int xl = (r < r1) ? (int)dma::index_of(K[r]) : 0;
-    int el = 0;
     const int steps = min(64, r1 - g0);
+    const int xl = lane < steps ? (int)dma::index_of(K[g0 + lane]) : 0;  // one key per lane
+    int el = 0;
     for (int s = 0; s < steps; ++s) {
       const int x = __builtin_amdgcn_readlane(xl, s);
-      if (lane == s) el = x < f ? f : x;
+      const int e = x < f ? f : x;
+      if (lane == s) el = e;
       if (x < f) {
-        const int xw = x >> 5;
-        if (xw >= wb) {
-          if (lane == xw - wb) win |= 1u << (x & 31);
+        const int xw = x >> 6;
+        if (xw == cwi) {
+          cw |= 1ull << (x & 63);
         } else if (lane == 0) {
-          bm[xw] |= 1u << (x & 31);
+          atomicOr(&bm[x >> 5], 1u << (x & 31));  // ds_or_b32: no return, no wait
         }
         // f <- largest set index below f (x itself qualifies)
-        for (;;) {
-          const int fl = f - wb * 32;
-          const int fw = fl >> 5, fb = fl & 31;
-          const uint32_t mw =
-              lane < fw ? win : (lane == fw ? (win & ((1u << fb) - 1u)) : 0u);
-          const uint64_t bal = dma::ballot(mw != 0u);
-          if (bal) {
-            const int hl = 63 - __builtin_clzll(bal);
-            const uint32_t word = __builtin_amdgcn_readlane(mw, hl);
-            f = (wb + hl) * 32 + 31 - __builtin_clz(word);
-            break;
-          }
-          if (wb == 0) {  // unreachable: at least w set indices lie below f
-            f = -1;
-            break;
-          }
-          wb = max(0, wb - 64);
-          win = (wb + lane < nw) ? bm[wb + lane] : 0u;
+        uint64_t m = cw & ((1ull << (f & 63)) - 1ull);
+        while (m == 0ull && cwi > 0) {
+          --cwi;
+          cw = bm64[cwi];
+          m = cw;
         }
+        f = m ? (cwi << 6) + 63 - __builtin_clzll(m) : -1;  // -1: unreachable (w bits below f)
       }
     }
-    if (r < r1) E[xl] = el;
+    if (lane < steps) E[xl] = el;
   }
 }
 
 // ---------------------------------------------------------------- T3: tile lists
-__global__ __launch_bounds__(256) void lists_kernel(
+// Wave w scans keys [w*L, (w+1)*L) of 0..p_hi (L a multiple of 64, so each
+// 64-key tile of the block-skip list belongs to one wave), 8 x 64 keys per
+// step with all loads issued first.  Pass 1 counts, one barrier turns counts
+// into offsets, pass 2 writes: no barrier per step.
+// The largest delta over U equals the largest delta over keys 0..p_hi: that
+// key is kept by row p_hi, and any key beating a member of U is itself kept by
+// row p_hi.
+constexpr int kListWaves = 8;
+constexpr int kListUnroll = 8;
+
+__global__ __launch_bounds__(kListWaves * 64) void lists_kernel(
     const float* __restrict__ delta, const int32_t* __restrict__ evict, int Sk, int Sq, int q0,
     int n_tiles, int u_stride, int kt_stride, int32_t* __restrict__ u_idx,
     int32_t* __restrict__ u_cnt, int32_t* __restrict__ u_nfull, float* __restrict__ u_dmax,
     int32_t* __restrict__ kt_idx, int32_t* __restrict__ kt_cnt) {
   __shared__ int s_part[kPartialCap];
-  __shared__ int s_w[3][4];
-  __shared__ float s_m[4];
+  __shared__ int s_c[3][kListWaves];
+  __shared__ float s_m[kListWaves];
   const int seg = blockIdx.y, t = blockIdx.x;
   const int64_t g = (int64_t)seg * n_tiles + t;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -250,79 +276,94 @@ __global__ __launch_bounds__(256) void lists_kernel(
   const int p_hi = q0 + min(Sq, t * kListRows + kListRows) - 1;
   const int32_t* E = evict + (int64_t)seg * Sk;
   const float* Dl = delta + (int64_t)seg * Sk;
+  const int n = p_hi + 1;
+  const int L = ((n + 64 * kListWaves - 1) / (64 * kListWaves)) * 64;
+  const int j0 = min(n, wave * L), j1 = min(n, j0 + L);
+
+  int nf = 0, np = 0, nk = 0;
+  float dm = -INFINITY;
+  for (int jb = j0; jb < j1; jb += 64 * kListUnroll) {
+    int e[kListUnroll];
+    float d[kListUnroll];
+#pragma unroll
+    for (int u = 0; u < kListUnroll; ++u) {
+      const int j = jb + u * 64 + lane;
+      e[u] = j < j1 ? E[j] : 0;
+      d[u] = j < j1 ? Dl[j] : -INFINITY;
+    }
+#pragma unroll
+    for (int u = 0; u < kListUnroll; ++u) {
+      const int j = jb + u * 64 + lane;
+      dm = fmaxf(dm, d[u]);
+      const bool member = j < j1 && e[u] > max(j, p_lo);
+      const bool full = member && j <= p_lo && e[u] > p_hi;
+      const uint64_t bf = dma::ballot(full), bp = dma::ballot(member && !full);
+      nf += __popcll(bf);
+      np += __popcll(bp);
+      nk += (bf | bp) ? 1 : 0;
+    }
+  }
+  dm = dma::wave_max(dm);
+  if (lane == 0) {
+    s_c[0][wave] = nf;
+    s_c[1][wave] = np;
+    s_c[2][wave] = nk;
+    s_m[wave] = dm;
+  }
+  __syncthreads();
+  int of = 0, op = 0, ok = 0, tf = 0, tp = 0, tk = 0;
+  float dmax = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < kListWaves; ++k) {
+    if (k < wave) {
+      of += s_c[0][k];
+      op += s_c[1][k];
+      ok += s_c[2][k];
+    }
+    tf += s_c[0][k];
+    tp += s_c[1][k];
+    tk += s_c[2][k];
+    dmax = fmaxf(dmax, s_m[k]);
+  }
   int32_t* out = u_idx + g * u_stride;
   int32_t* kout = kt_idx ? kt_idx + g * kt_stride : nullptr;
-  int nfull = 0, npart = 0, nkt = 0;
-  float dmax = -INFINITY;
-  for (int base = 0; base <= p_hi; base += 1024) {
-    uint64_t mf[4], mp[4];
-    int nf = 0, np = 0, nk = 0;
+  for (int jb = j0; jb < j1; jb += 64 * kListUnroll) {
+    int e[kListUnroll];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int j = base + wave * 256 + c * 64 + lane;
-      const bool valid = j <= p_hi;
-      const int e = valid ? E[j] : 0;
-      const bool member = valid && e > max(j, p_lo);
-      const bool full = member && j <= p_lo && e > p_hi;
-      if (member) dmax = fmaxf(dmax, Dl[j]);
-      mf[c] = dma::ballot(full);
-      mp[c] = dma::ballot(member && !full);
-      nf += __popcll(mf[c]);
-      np += __popcll(mp[c]);
-      nk += ((mf[c] | mp[c]) != 0ull) ? 1 : 0;
-    }
-    if (lane == 0) {
-      s_w[0][wave] = nf;
-      s_w[1][wave] = np;
-      s_w[2][wave] = nk;
-    }
-    __syncthreads();
-    int of = nfull, op = npart, ok = nkt, tf = 0, tp = 0, tk = 0;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      if (k < wave) {
-        of += s_w[0][k];
-        op += s_w[1][k];
-        ok += s_w[2][k];
-      }
-      tf += s_w[0][k];
-      tp += s_w[1][k];
-      tk += s_w[2][k];
+    for (int u = 0; u < kListUnroll; ++u) {
+      const int j = jb + u * 64 + lane;
+      e[u] = j < j1 ? E[j] : 0;
     }
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int j = base + wave * 256 + c * 64 + lane;
-      if ((mf[c] >> lane) & 1ull) {
-        const int pos = of + dma::rank_below(mf[c]);
+    for (int u = 0; u < kListUnroll; ++u) {
+      const int j = jb + u * 64 + lane;
+      const bool member = j < j1 && e[u] > max(j, p_lo);
+      const bool full = member && j <= p_lo && e[u] > p_hi;
+      const uint64_t bf = dma::ballot(full), bp = dma::ballot(member && !full);
+      if (full) {
+        const int pos = of + dma::rank_below(bf);
         if (pos < u_stride) out[pos] = j;
-      }
-      if ((mp[c] >> lane) & 1ull) {
-        const int pos = op + dma::rank_below(mp[c]);
+      } else if (member) {
+        const int pos = op + dma::rank_below(bp);
         if (pos < kPartialCap) s_part[pos] = j;
       }
-      of += __popcll(mf[c]);
-      op += __popcll(mp[c]);
-      if ((mf[c] | mp[c]) != 0ull) {
-        if (lane == 0 && kout && ok < kt_stride) kout[ok] = (base + wave * 256 + c * 64) / 64;
+      of += __popcll(bf);
+      op += __popcll(bp);
+      if (bf | bp) {
+        if (lane == 0 && kout && ok < kt_stride) kout[ok] = (jb >> 6) + u;
         ++ok;
       }
     }
-    nfull += tf;
-    npart += tp;
-    nkt += tk;
-    __syncthreads();
   }
-  const int np = min(npart, kPartialCap);
-  for (int k = threadIdx.x; k < np; k += 256)
-    if (nfull + k < u_stride) out[nfull + k] = s_part[k];
-  dmax = dma::wave_max(dmax);
-  if (lane == 0) s_m[wave] = dmax;
   __syncthreads();
+  const int npart = min(tp, kPartialCap);
+  for (int k = threadIdx.x; k < npart; k += kListWaves * 64)
+    if (tf + k < u_stride) out[tf + k] = s_part[k];
   if (threadIdx.x == 0) {
-    u_cnt[g] = min(nfull + npart, u_stride);
-    u_nfull[g] = min(nfull, u_stride);
-    u_dmax[g] = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
-    if (kt_cnt) kt_cnt[g] = min(nkt, kt_stride);
+    u_cnt[g] = min(tf + tp, u_stride);
+    u_nfull[g] = min(tf, u_stride);
+    u_dmax[g] = dmax;
+    if (kt_cnt) kt_cnt[g] = min(tk, kt_stride);
   }
 }
 
@@ -445,10 +486,13 @@ __global__ __launch_bounds__(kDecThreads) void decode_select_kernel(
 
 }  // namespace
 
+// rank rows are padded to a multiple of 4 keys so each row starts 16-byte aligned
+static int64_t rank_stride(int64_t Sk) { return (Sk + 3) & ~int64_t(3); }
+
 size_t dma_topk_ws_bytes(int64_t BH, int64_t Sk) {
   // two key buffers (ping-pong merges) + ranks
   const size_t n = (size_t)BH * (size_t)Sk;
-  return n * (2 * sizeof(uint64_t) + sizeof(int32_t)) + 256;
+  return n * 2 * sizeof(uint64_t) + (size_t)BH * rank_stride(Sk) * sizeof(int32_t) + 256;
 }
 
 hipError_t dma_launch_topk_prefill(const DmaTopkArgs& a, hipStream_t st) {
@@ -472,15 +516,16 @@ hipError_t dma_launch_topk_prefill(const DmaTopkArgs& a, hipStream_t st) {
     src = dst;
     dst = t;
   }
-  hipLaunchKernelGGL(rank_kernel, dim3((Sk + 255) / 256, BH), dim3(256), 0, st, src, Sk, rank);
+  const int rs = (int)rank_stride(Sk);
+  hipLaunchKernelGGL(rank_kernel, dim3((Sk + 255) / 256, BH), dim3(256), 0, st, src, Sk, rs, rank);
   const int R = Sk > 16384 ? 512 : 256;
-  const int nwords = (Sk + 31) / 32;
+  const int nwords = ((Sk + 63) / 64) * 2 + 8;  // bitmap + s_w[4], s_f (padded)
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&evict_kernel),
                             hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)(nwords * sizeof(uint32_t)));
   hipLaunchKernelGGL(evict_kernel, dim3((Sk + R - 1) / R, BH), dim3(256),
-                     (size_t)nwords * sizeof(uint32_t), st, src, rank, Sk, (int)a.w, R, a.evict);
-  hipLaunchKernelGGL(lists_kernel, dim3((unsigned)a.n_tiles, BH), dim3(256), 0, st, a.delta,
+                     (size_t)nwords * sizeof(uint32_t), st, src, rank, Sk, rs, (int)a.w, R, a.evict);
+  hipLaunchKernelGGL(lists_kernel, dim3((unsigned)a.n_tiles, BH), dim3(kListWaves * 64), 0, st, a.delta,
                      a.evict, Sk, (int)a.Sq, (int)a.q0, (int)a.n_tiles, (int)a.u_stride,
                      (int)a.kt_stride, a.u_idx, a.u_cnt, a.u_nfull, a.u_dmax, a.kt_idx, a.kt_cnt);
   return hipGetLastError();

@@ -69,19 +69,21 @@ __global__ __launch_bounds__(256) void weights_kernel(const T* __restrict__ V, i
                                                       const float* __restrict__ A,
                                                       float* __restrict__ delta) {
   extern __shared__ float smem[];
-  float* Ds = smem;                 // [C][HB]
+  // Delta slice laid out [h][e][k] (c = k*EPC + e): lanes own consecutive chunks k,
+  // so for a fixed (h, e) a wave reads 64 consecutive words, free of bank conflicts.
+  constexpr int EPC = Chunk<T>::kElems;
+  const int NC = C / EPC;
+  float* Ds = smem;                 // [HB][EPC][NC]
   float* sout = smem + C * HB;      // [HB][kRowsPerBlock]
   const int b = blockIdx.y;
   const int j0 = blockIdx.x * kRowsPerBlock;
   for (int i = threadIdx.x; i < C * HB; i += blockDim.x) {
     const int c = i / HB, h = i % HB;
-    Ds[i] = (h0 + h < Hkv) ? Delta[(int64_t)c * Hkv + h0 + h] : 0.f;
+    Ds[(h * EPC + c % EPC) * NC + c / EPC] = (h0 + h < Hkv) ? Delta[(int64_t)c * Hkv + h0 + h] : 0.f;
   }
   __syncthreads();
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  constexpr int EPC = Chunk<T>::kElems;
-  const int NC = C / EPC;
   const T* Vb = V + (int64_t)b * sb;
   for (int g = 0; g < 2; ++g) {
     const int jb = j0 + wave * 8 + g * kRowsPerGroup;
@@ -100,10 +102,9 @@ __global__ __launch_bounds__(256) void weights_kernel(const T* __restrict__ V, i
       }
 #pragma unroll
       for (int e = 0; e < EPC; ++e) {
-        const float* dc = Ds + (k * EPC + e) * HB;
         float dh[HB];
 #pragma unroll
-        for (int h = 0; h < HB; ++h) dh[h] = dc[h];
+        for (int h = 0; h < HB; ++h) dh[h] = Ds[(h * EPC + e) * NC + k];
 #pragma unroll
         for (int r = 0; r < kRowsPerGroup; ++r) {
           const float x = Chunk<T>::get(raw[r], e);
