@@ -31,19 +31,25 @@ constexpr int kBq = 64;
 constexpr int kBk = 64;
 constexpr int kD = 128;
 constexpr int kKRow = kD + 8;   // K tile row, bf16 elements (272 bytes: spreads LDS banks)
-constexpr int kVRow = kBk + 4;  // V^T tile row, bf16 elements (136 bytes)
+// V tile row: 320 bytes, so the 8 rows x 64 bytes of one transposing read fall
+// on distinct banks (64- or 32-bank LDS) and the 16-byte row stores stay
+// conflict free.
+constexpr int kVRow = kD + 32;
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.f;  // base-2 headroom before O is rescaled (weights stay <= 2^8)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 // K/V tiles are double-buffered (chunk c in buffer c%2); key metadata uses
 // three slots (chunk c in slot c%3) because it is written two chunks ahead.
 struct Smem {
   uint16_t k[2][kBk * kKRow];
-  uint16_t vt[2][kD * kVRow];
+  uint16_t v[2][kBk * kVRow];   // V rows as gathered (read transposed, see PV below)
   int j[3][kBk];       // key index per chunk slot (gather addresses)
   int e[3][kBk];       // eviction row per slot
   int pj[3][kBk];      // key index per slot for the mask (INT_MAX for padding)
@@ -67,8 +73,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 // Register staging of one gathered chunk.  Thread tid owns units
 // u = tid + k*NT of (key pair, 16-byte d-chunk); 16 consecutive threads read
-// one 256-byte key row.  K rows are stored as read; V is stored transposed
-// ([d][key]) two keys at a time.
+// one 256-byte key row.  K and V rows are stored as read.
 template <int NT>
 struct Stage {
   static constexpr int kUnits = (kBk / 2) * (kD / 8) / NT;
@@ -89,21 +94,15 @@ struct Stage {
     }
   }
 
-  __device__ __forceinline__ void store(uint16_t* ks, uint16_t* vt, int tid) const {
+  __device__ __forceinline__ void store(uint16_t* ks, uint16_t* vs, int tid) const {
 #pragma unroll
     for (int u = 0; u < kUnits; ++u) {
       const int pr = tid + u * NT;
       const int kp = pr >> 4, ch = pr & 15;
       *reinterpret_cast<u32x4*>(&ks[(kp * 2) * kKRow + ch * 8]) = k[u][0];
       *reinterpret_cast<u32x4*>(&ks[(kp * 2 + 1) * kKRow + ch * 8]) = k[u][1];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t a0 = v[u][0][q], a1 = v[u][1][q];  // d = ch*8+2q (lo), 2q+1 (hi)
-        *reinterpret_cast<uint32_t*>(&vt[(ch * 8 + 2 * q) * kVRow + kp * 2]) =
-            (a0 & 0xffffu) | (a1 << 16);
-        *reinterpret_cast<uint32_t*>(&vt[(ch * 8 + 2 * q + 1) * kVRow + kp * 2]) =
-            (a0 >> 16) | (a1 & 0xffff0000u);
-      }
+      *reinterpret_cast<u32x4*>(&vs[(kp * 2) * kVRow + ch * 8]) = v[u][0];
+      *reinterpret_cast<u32x4*>(&vs[(kp * 2 + 1) * kVRow + ch * 8]) = v[u][1];
     }
   }
 };
@@ -198,19 +197,31 @@ __device__ __forceinline__ void attend_chunk(Acc& acc, const dma::bf16x8 (&qf)[8
     }
   acc.l += rs;
 
-  // O^T += V^T P^T; A operand slots (hi, t) hold keys base + 4*hi + t (t < 4)
-  // and base + 8 + 4*hi + (t - 4), matching the rows of P^T's registers.
+  // O^T += V^T P^T.  A operand of k-step (mb, hf) for lane (l32, hi): V^T rows
+  // d = db*32 + l32, keys mb*32 + 16*hf + 4*hi + [0,4) and mb*32 + 16*hf + 8 +
+  // 4*hi + [0,4), matching the keys of P^T's registers.  V stays row-major in
+  // LDS; each transposing read serves a 16-lane group g = lane/16: lane r of
+  // the group addresses key row kbase + r/4, columns dbase + 16*(g%2) +
+  // 4*(r%4), and lane i then receives that group's 4 keys at d = dbase +
+  // 16*(g%2) + i.
+  const int g = lane >> 4, r = lane & 15;
+  // address-space cast of the LDS tile pointer (the instruction takes a local address)
+  const __attribute__((address_space(3))) uint16_t* vbase =
+      (const __attribute__((address_space(3))) uint16_t*)sm.v[buf];
 #pragma unroll
   for (int db = 0; db < 4; ++db) {
-    const uint16_t* vrow = &sm.vt[buf][(db * 32 + l32) * kVRow];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        const int kb = mb * 32 + hf * 16 + 4 * hi;
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + kb);
-        const u32x2 up = *reinterpret_cast<const u32x2*>(vrow + kb + 8);
-        const u32x4 vv = {lo[0], lo[1], up[0], up[1]};
+        const int k0 = mb * 32 + 16 * hf + 4 * (g >> 1) + (r >> 2);
+        const int d0 = db * 32 + 16 * (g & 1) + 4 * (r & 3);
+        const i16x4 lo =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + k0 * kVRow + d0));
+        const i16x4 up =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + (k0 + 8) * kVRow + d0));
+        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), up2 = __builtin_bit_cast(u32x2, up);
+        const u32x4 vv = {lo2[0], lo2[1], up2[0], up2[1]};
         acc.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             __builtin_bit_cast(dma::bf16x8, vv), pb[mb][hf], acc.o[db], 0, 0, 0);
       }
@@ -303,7 +314,7 @@ __global__ __launch_bounds__(NH * 128, 1) void attn_prefill_bf16_kernel(DmaAttnA
   __syncthreads();
   if (nch > 0) {
     stg.gather(sm.j[0], Kg, Vg, a.kss, tid);
-    stg.store(sm.k[0], sm.vt[0], tid);
+    stg.store(sm.k[0], sm.v[0], tid);
   }
   __syncthreads();
 
@@ -327,7 +338,7 @@ __global__ __launch_bounds__(NH * 128, 1) void attn_prefill_bf16_kernel(DmaAttnA
     attend_chunk<MASKED>(acc, qf, sm, buf, c % 3, lane, pos, scale2);                 \
     /* publish chunk c+1; metadata of chunk c+2 goes to slot (c+2)%3, whose chunk     \
        c-1 was last read before the previous barrier */                               \
-    if (c + 1 < nch) stg.store(sm.k[buf ^ 1], sm.vt[buf ^ 1], tid);                   \
+    if (c + 1 < nch) stg.store(sm.k[buf ^ 1], sm.v[buf ^ 1], tid);                   \
     if (wave == 0 && c + 2 < nch) {                                                   \
       DMA_STORE_META((c + 2) % 3);                                                    \
       if (c + 3 < nch) DMA_LOAD_IDX(c + 3);                                           \
