@@ -15,6 +15,7 @@ Prints one JSON line:
   stages_ms      event-timed weights / mask / attention per step
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -26,6 +27,12 @@ sys.path.insert(0, ROOT)
 METRIC = "effective TFLOP/s (kept pairs) + ms/fwd, 16K-token DMA prefill, 1 MI355X"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
+# HBM bytes per launch of the attention kernel, from two counter passes (FETCH_SIZE and
+# WRITE_SIZE) scaled by the same counters on a plain copy of known size.  The file carries
+# the hash of the kernel sources it was taken on; a stale file reports null.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_prefill_bf16_kernel.prefill_16k.traffic.txt")
+ATTN_SOURCES = ("trainable_dynamic_mask_amd/csrc/attn_prefill.hip",
+                "trainable_dynamic_mask_amd/csrc/common.h")
 
 
 def parse():
@@ -37,7 +44,49 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU time budget of the oracle sample")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB five times (the reference "
+                         "reading of the FETCH_SIZE / WRITE_SIZE counters) and exit")
     return ap.parse_args()
+
+
+def attn_source_hash():
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """Counter-measured HBM bytes per attention launch, or None when no reading was
+    taken on this workload with the current kernel sources."""
+    if workload != "prefill_16k" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith((" ", "#")):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != attn_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(mib):
+    import torch
+    n = mib << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
+                      "launches": 5}), flush=True)
 
 
 def cpu_baseline(x, wl, budget_s):
@@ -84,6 +133,9 @@ def main():
               "here is the single-GPU hot path, see DESIGN.md for how it would shard.",
               file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     import torch
     import trainable_dynamic_mask_amd as dma
     from trainable_dynamic_mask_amd.configs import WORKLOADS
@@ -156,7 +208,7 @@ def main():
                      else "decode_split_kernel",
                      "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": measured_traffic(wl.name) if wl.Sq > 1 else None},
         "stages_ms": {k: round(v, 4) for k, v in st.items()},
     }
     if not args.no_cpu_baseline:
