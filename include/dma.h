@@ -161,6 +161,9 @@ dma_status dma_topk_mask(const float* delta, int64_t B, int64_t Hkv, int64_t Sq,
  * ws     dma_attn_workspace_bytes(...) bytes (NULL allowed when 0).
  * Arithmetic: BF16 inputs use bf16 MFMA products with fp32 accumulation and
  * an fp32 online softmax; F32 inputs are computed in fp32 throughout.
+ * Limits: BF16 with Sq > 1 needs D == 128 and the rows of one (batch, kv
+ * head) within 4 GiB: (Sk-1)*kv_strides[1]*2 + 256 <= 2^32; otherwise
+ * DMA_ERR_UNSUPPORTED.
  */
 dma_status dma_attn_fwd(const void* Q, const void* K, const void* V, dma_dtype t, int64_t B,
                         int64_t Sq, int64_t Sk, int64_t Hq, int64_t Hkv, int64_t D,

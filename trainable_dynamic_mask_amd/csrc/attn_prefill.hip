@@ -4,25 +4,41 @@
 // the row keeps.  A masked key has weight exactly 0 ("Forward Pass Safety"),
 // so its work is skipped entirely: a workgroup never visits key tiles, it
 // walks the compacted list U of the keys that some row of its 64-row query
-// tile keeps (built by the mask step), 64 gathered keys at a time.
+// tile keeps (built by the mask step), 64 gathered keys (one chunk) at a time.
 //
 // Work split: one workgroup per (query tile, kv head, batch, head group).
-// Its NW waves are NW query heads of the same kv head (GQA), so each gathered
-// K/V chunk in LDS serves NW*64 query rows.  Per chunk and wave:
+// Its NW = 2*NH waves are the NH query heads of one kv head (GQA) times two
+// 32-row halves of the tile, so each gathered K/V chunk in LDS serves NH*64
+// query rows.  Per chunk and wave:
 //   S^T = K Q^T        (keys x queries) on v_mfma_f32_32x32x16_bf16, K from
 //                      LDS, Q^T held in registers for the whole kernel;
-//   online softmax     in the base-2 domain, per query = per lane column;
+//   softmax            online, base 2, per query = per lane column;
 //   O^T += V^T P^T     the S^T accumulator layout is already the B operand
-//                      layout, so P never moves; V is stored transposed in
-//                      LDS ([d][key]) so the A operand is two 8-byte reads.
-// Chunks are double-buffered: the gather of chunk c+1 and the key metadata
-// of chunk c+2 are in flight while chunk c is computed.
+//                      layout, so P never moves; V is read from LDS with the
+//                      transposing ds_read_b64_tr_b16.
+//
+// Ping-pong: the waves form two groups, A (waves 0..NW/2-1) and B (the rest),
+// one wave of each per SIMD.  Each wave alternates an MFMA phase
+//   G_c = { O += V(c-1) P(c-1)^T ;  S(c) = K(c) Q^T }
+// and a VALU phase
+//   S_c = { softmax of S(c) -> P(c) },
+// with a workgroup barrier after every phase.  Group B starts one phase late,
+// so between two barriers one wave of every SIMD runs MFMAs while the other
+// runs the softmax.  Interval 2c holds G_c of group A and S_(c-1) of group B;
+// in it every wave issues its share of the direct global-to-LDS gathers of
+// K(c+1) and V(c), which have all landed by the end of interval 2c+1 and are
+// first read in interval 2c+2.
+//
+// Workgroups are mapped so that each XCD (with its own L2) serves few kv
+// heads, longest query tiles first.
 //
 // Numerics: scores are s = scale*(q.k) + delta.  delta can reach 1e4, where
 // fp32 spacing is ~1e-3, so the bias enters as (delta - dmax) * log2(e) with
 // dmax the largest delta of the tile's list: the subtraction is exact for
 // every key within a factor 2 of dmax (the only keys with weight), and the
-// constant cancels in the softmax and is added back to the log-sum-exp.
+// constant cancels in the softmax and is added back to the log-sum-exp.  The
+// bias, divided by the score scale, is the initial value of the score
+// accumulator, so the MFMAs add q.k to it.
 #include "common.h"
 
 namespace {
@@ -30,11 +46,15 @@ namespace {
 constexpr int kBq = 64;
 constexpr int kBk = 64;
 constexpr int kD = 128;
-constexpr int kKRow = kD + 8;   // K tile row, bf16 elements (272 bytes: spreads LDS banks)
-// V tile row: 320 bytes, so the 8 rows x 64 bytes of one transposing read fall
-// on distinct banks (64- or 32-bank LDS) and the 16-byte row stores stay
-// conflict free.
-constexpr int kVRow = kD + 32;
+// K and V tiles: 64 rows of 256 bytes, no padding.  Each row's sixteen
+// 16-byte chunks are stored permuted so that the reads below hit distinct LDS
+// banks: K chunk c of row r at c ^ (r % 16) (the 16 rows of one 16-byte read
+// land on 16 distinct chunks), V chunk c at c ^ 4*(r % 4) (the 4 rows of one
+// transposing read land on 4 disjoint 64-byte spans).
+constexpr int kRowB = kD * 2;
+constexpr int kTileB = kBk * kRowB;
+constexpr int kSlots = 4;       // metadata of chunk c in slot c % 4
+constexpr int kXcds = 8;        // accelerator complex dies, each with its own L2
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -44,16 +64,16 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
-// K/V tiles are double-buffered (chunk c in buffer c%2); key metadata uses
-// three slots (chunk c in slot c%3) because it is written two chunks ahead.
-struct Smem {
-  uint16_t k[2][kBk * kKRow];
-  uint16_t v[2][kBk * kVRow];   // V rows as gathered (read transposed, see PV below)
-  int j[3][kBk];       // key index per chunk slot (gather addresses)
-  int e[3][kBk];       // eviction row per slot
-  int pj[3][kBk];      // key index per slot for the mask (INT_MAX for padding)
-  float bias[3][kBk];  // (delta - dmax) * log2(e), -inf for padding
+// Key metadata of chunk c lives in slot c % 4; K(c) and V(c) live in LDS
+// buffer c % 2.  The K/V buffers and the metadata are separate __shared__
+// objects, so the compiler can tell the direct-to-LDS gathers apart from
+// the metadata reads and does not make those wait for the gathers.
+struct Meta {
+  int e[kSlots][kBk];       // eviction row per slot
+  int pj[kSlots][kBk];      // key index per slot for the mask (INT_MAX for padding)
+  float bias[kSlots][kBk];  // (delta - dmax) * log2(e) / score scale, -inf for padding
 };
 
 __device__ __forceinline__ dma::bf16x8 to_bf16x8(const float (&p)[8]) {
@@ -71,41 +91,52 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
-// Register staging of one gathered chunk.  Thread tid owns units
-// u = tid + k*NT of (key pair, 16-byte d-chunk); 16 consecutive threads read
-// one 256-byte key row.  K and V rows are stored as read.
-template <int NT>
-struct Stage {
-  static constexpr int kUnits = (kBk / 2) * (kD / 8) / NT;
-  u32x4 k[kUnits][2], v[kUnits][2];
-
-  __device__ __forceinline__ void gather(const int* js, const uint16_t* Kg, const uint16_t* Vg,
-                                         int64_t kss, int tid) {
+// Gather the 64 rows of one K or V chunk straight into LDS with 16-byte
+// direct loads.  The tile is 16 pieces of 1 KB = 4 rows; wave w loads pieces
+// w, w+NW, ...: lane L fills row 4*piece + L/16, stored chunk L%16, which
+// holds logical chunk (L%16) ^ swz(row).  idx[t] is the key index of the
+// lane's row in piece w + t*NW (see gather_rows).
+template <int NW, bool IS_V>
+__device__ __forceinline__ void gather_tile(unsigned char* tile, const int (&idx)[16 / NW],
+                                            const unsigned char* g, uint32_t rowb, int wave,
+                                            int lane) {
+  const int rsub = lane >> 4, pc = lane & 15;
 #pragma unroll
-    for (int u = 0; u < kUnits; ++u) {
-      const int pr = tid + u * NT;
-      const int kp = pr >> 4, ch = pr & 15;
-      const int2 jj = *reinterpret_cast<const int2*>(&js[kp * 2]);
-      const int64_t o0 = (int64_t)jj.x * kss + ch * 8, o1 = (int64_t)jj.y * kss + ch * 8;
-      k[u][0] = *reinterpret_cast<const u32x4*>(Kg + o0);
-      k[u][1] = *reinterpret_cast<const u32x4*>(Kg + o1);
-      v[u][0] = *reinterpret_cast<const u32x4*>(Vg + o0);
-      v[u][1] = *reinterpret_cast<const u32x4*>(Vg + o1);
-    }
+  for (int t = 0; t < 16 / NW; ++t) {
+    const int piece = wave + t * NW;
+    const int row = piece * 4 + rsub;
+    const int lc = pc ^ (IS_V ? ((row & 3) << 2) : (row & 15));
+    __builtin_amdgcn_global_load_lds(g + (uint32_t)idx[t] * rowb + lc * 16,
+                                     (lds_void*)(tile + piece * 1024), 16, 0, 0);
   }
+}
 
-  __device__ __forceinline__ void store(uint16_t* ks, uint16_t* vs, int tid) const {
+// Key indices of the rows this lane gathers for chunk ch, read straight from
+// the tile's key list a step ahead of the gather (positions past the list
+// repeat its last key; their scores are masked).
+template <int NW>
+__device__ __forceinline__ void gather_rows(int (&idx)[16 / NW], const int32_t* list, int cnt,
+                                            int ch, int wave, int lane) {
 #pragma unroll
-    for (int u = 0; u < kUnits; ++u) {
-      const int pr = tid + u * NT;
-      const int kp = pr >> 4, ch = pr & 15;
-      *reinterpret_cast<u32x4*>(&ks[(kp * 2) * kKRow + ch * 8]) = k[u][0];
-      *reinterpret_cast<u32x4*>(&ks[(kp * 2 + 1) * kKRow + ch * 8]) = k[u][1];
-      *reinterpret_cast<u32x4*>(&vs[(kp * 2) * kVRow + ch * 8]) = v[u][0];
-      *reinterpret_cast<u32x4*>(&vs[(kp * 2 + 1) * kVRow + ch * 8]) = v[u][1];
-    }
-  }
-};
+  for (int t = 0; t < 16 / NW; ++t)
+    idx[t] = list[min(ch * kBk + 4 * (wave + t * NW) + (lane >> 4), cnt - 1)];
+}
+
+// Workgroup barrier at the end of a phase.  WAIT_VM: this wave's direct
+// global-to-LDS loads have landed first (they are read by other waves after
+// the barrier); LDS writes always complete first.  The empty asm statements
+// keep the compiler from moving memory accesses across the barrier; no fence
+// is used, as a fence would wait for every load in flight.
+template <bool WAIT_VM>
+__device__ __forceinline__ void phase_barrier() {
+  asm volatile("" ::: "memory");
+  if constexpr (WAIT_VM)
+    __builtin_amdgcn_s_waitcnt(7 << 4);  // vmcnt(0) expcnt(7) lgkmcnt(0)
+  else
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // lgkmcnt(0) only
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // Running softmax state of one wave: 32 query rows.
 struct Acc {
@@ -113,43 +144,126 @@ struct Acc {
   float m, l;        // base-2 reference and this lane's partial row sum
 };
 
-// One gathered chunk of 64 keys for the wave's 32 query rows.  MASKED chunks
-// hold keys that only some rows of the tile keep and apply j <= p < e_j per
-// element; the others hold keys every row keeps.
-template <bool MASKED>
-__device__ __forceinline__ void attend_chunk(Acc& acc, const dma::bf16x8 (&qf)[8],
-                                             const Smem& sm, int buf, int slot, int lane, int pos,
-                                             float scale2) {
+// V^T operands of PV k-step ks = (mb, hf) = (ks/2, ks%2) for the four d
+// blocks: V^T rows d = db*32 + l32, keys mb*32 + 16*hf + 4*hi + [0,4) and
+// mb*32 + 16*hf + 8 + 4*hi + [0,4), matching the keys of P^T's registers.
+// V stays row-major in LDS; each transposing read serves a 16-lane group
+// g = lane/16: lane r of the group addresses key row kbase + r/4, columns
+// dbase + 16*(g%2) + 4*(r%4), and lane i then receives that group's 4 keys
+// at d = dbase + 16*(g%2) + i.
+__device__ __forceinline__ void v_operands(dma::bf16x8 (&vop)[4], const unsigned char* vt,
+                                           int ks, int lane) {
+  const int g = lane >> 4, r = lane & 15;
+  // address-space cast of the LDS tile pointer (the instruction takes a local address)
+  const __attribute__((address_space(3))) unsigned char* vbase =
+      (const __attribute__((address_space(3))) unsigned char*)vt;
+  // key rows k0 and k0 + 8 share k0 % 4, hence the chunk permutation
+  const int k0 = (ks >> 1) * 32 + 16 * (ks & 1) + 4 * (g >> 1) + (r >> 2);
+  const int swz = (k0 & 3) << 2;
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    // element d0 = db*32 + 16*(g%2) + 4*(r%4): logical chunk d0/8, byte (d0%8)*2
+    const int lc = db * 4 + 2 * (g & 1) + ((r & 3) >> 1);
+    const int off = ((lc ^ swz) << 4) + (r & 1) * 8;
+    const i16x4 lo =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + k0 * kRowB + off));
+    const i16x4 up =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + (k0 + 8) * kRowB + off));
+    const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), up2 = __builtin_bit_cast(u32x2, up);
+    const u32x4 vv = {lo2[0], lo2[1], up2[0], up2[1]};
+    vop[db] = __builtin_bit_cast(dma::bf16x8, vv);
+  }
+}
+
+// MFMA phase G_c: S^T(c) = K(c) Q^T (rows = the chunk's 64 keys in two
+// blocks of 32, cols = the wave's 32 queries; lane (l32, hi) reads K row
+// mb*32 + l32, d = kk*16 + 8*hi + [0, 8)), then O^T += V(c-1)^T P(c-1)^T.
+// LDS operand reads run ahead of their MFMAs: K reads four operands ahead,
+// V one PV k-step ahead, so the matrix cores do not wait on single LDS
+// reads.  The sched_group_barrier sequence pins that order (0x100 = LDS
+// read, 0x008 = MFMA) and bounds the registers held by operands in flight.
+__device__ __forceinline__ void g_phase(Acc& acc, const dma::bf16x8 (&pb)[2][2],
+                                        dma::f32x16 (&s)[2], const dma::bf16x8 (&qf)[8],
+                                        const unsigned char* kt, const unsigned char* vt,
+                                        const float* bias_row, int lane) {
   const int l32 = lane & 31, hi = lane >> 5;
-  // S^T = K Q^T: rows = the chunk's 64 keys (two blocks of 32), cols = 32 queries
-  dma::f32x16 s[2];
+  // the scores start from the keys' bias divided by the score scale, so the
+  // MFMAs add q.k to it (register i of block mb holds key mb*32 + 8*(i/4) +
+  // 4*hi + i%4; bias_row points at key 4*hi of the chunk)
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) s[mb][i] = 0.f;
-#pragma unroll
-  for (int kk = 0; kk < 8; ++kk) {
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      const dma::bf16x8 kop = *reinterpret_cast<const dma::bf16x8*>(
-          &sm.k[buf][(mb * 32 + l32) * kKRow + kk * 16 + hi * 8]);
-      s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qf[kk], s[mb], 0, 0, 0);
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const float4 bv = *reinterpret_cast<const float4*>(bias_row + mb * 32 + 8 * q4);
+      s[mb][4 * q4 + 0] = bv.x;
+      s[mb][4 * q4 + 1] = bv.y;
+      s[mb][4 * q4 + 2] = bv.z;
+      s[mb][4 * q4 + 3] = bv.w;
     }
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int kk = q >> 1, mb = q & 1;
+    const int row = mb * 32 + l32;
+    const dma::bf16x8 kop = *reinterpret_cast<const dma::bf16x8*>(
+        kt + row * kRowB + (((kk * 2 + hi) ^ (row & 15)) << 4));
+    s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qf[kk], s[mb], 0, 0, 0);
   }
+  dma::bf16x8 va[4], vb[4];
+  v_operands(va, vt, 0, lane);
+  v_operands(vb, vt, 1, lane);
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+    acc.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db], pb[0][0], acc.o[db], 0, 0, 0);
+  v_operands(va, vt, 2, lane);
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+    acc.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[db], pb[0][1], acc.o[db], 0, 0, 0);
+  v_operands(vb, vt, 3, lane);
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+    acc.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db], pb[1][0], acc.o[db], 0, 0, 0);
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+    acc.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[db], pb[1][1], acc.o[db], 0, 0, 0);
+  // order: bias reads, K reads 4 ahead of the 16 score MFMAs, V k-step 0
+  // read during the last 4 of them, then each PV k-step after the reads of
+  // the next one
+  __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+#pragma unroll
+  for (int q = 0; q < 12; ++q) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+#pragma unroll
+  for (int ks = 0; ks < 3; ++ks) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+}
 
-  // online softmax over the lane's 32 keys: key(mb, i) = mb*32 + 8*(i/4) + 4*hi + i%4;
-  // the other 32 keys of the same query sit in lane ^ 32.
-  const float* biasp = &sm.bias[slot][4 * hi];
+// Softmax of one chunk: logits in the base-2 domain, lazy rescale of O, and
+// P = exp2(s - m) as the bf16 B operands of the PV product.  MASKED chunks
+// hold keys that only some rows of the tile keep and apply j <= p < e_j per
+// element; the others hold keys every row keeps.  Lane (l32, hi) holds
+// key(mb, i) = mb*32 + 8*(i/4) + 4*hi + i%4 of query l32; the other 32 keys
+// of the same query sit in lane ^ 32.
+template <bool MASKED>
+__device__ __forceinline__ void softmax_phase(Acc& acc, dma::f32x16 (&s)[2],
+                                              dma::bf16x8 (&pb)[2][2], const Meta& sm, int slot,
+                                              int hi, int pos, float scale2) {
   const int* pjp = &sm.pj[slot][4 * hi];
   const int* pep = &sm.e[slot][4 * hi];
-  float mx = -INFINITY;
+  // four partial maxima and four partial sums keep the dependency chains
+  // short: a wave runs this phase alone on its SIMD's vector unit
+  float mxp[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const int kb = mb * 32 + 8 * q4;
-      const float4 bv = *reinterpret_cast<const float4*>(biasp + kb);
-      const float bias[4] = {bv.x, bv.y, bv.z, bv.w};
       int4 jv = {0, 0, 0, 0}, evv = {0, 0, 0, 0};
       if constexpr (MASKED) {
         jv = *reinterpret_cast<const int4*>(pjp + kb);
@@ -160,17 +274,22 @@ __device__ __forceinline__ void attend_chunk(Acc& acc, const dma::bf16x8 (&qf)[8
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = q4 * 4 + r;
-        float v = fmaf(s[mb][i], scale2, bias[r]);
+        float v = s[mb][i] * scale2;  // scale2 * (q.k + bias / scale2)
         // kept iff pj <= pos < pe, one unsigned compare (pe <= pj: never)
         if constexpr (MASKED)
           v = ((uint32_t)(pos - pj[r]) < (uint32_t)(pe[r] - pj[r])) ? v : -INFINITY;
         s[mb][i] = v;
-        mx = fmaxf(mx, v);
+        mxp[q4] = fmaxf(mxp[q4], v);
       }
     }
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  // Each lane tests its own 32 keys against the query's shared reference m;
+  // only when some lane needs a new reference does the wave combine the two
+  // halves of each query (lane l and l ^ 32), so the common path has no
+  // cross-lane exchange.
+  float mx = fmaxf(fmaxf(mxp[0], mxp[1]), fmaxf(mxp[2], mxp[3]));
   if (__ballot(mx > acc.m + kLazy) != 0ull) {
     // rare: a logit above the reference by more than the headroom
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(acc.m, mx);
     const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(acc.m - m_new);
     acc.l *= alpha;
@@ -181,8 +300,7 @@ __device__ __forceinline__ void attend_chunk(Acc& acc, const dma::bf16x8 (&qf)[8
     acc.m = m_new;
   }
   const float m_use = (acc.m == -INFINITY) ? 0.f : acc.m;
-  dma::bf16x8 pb[2][2];  // [mb][half]: B operands of the PV product
-  float rs = 0.f;
+  float rsp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -191,58 +309,45 @@ __device__ __forceinline__ void attend_chunk(Acc& acc, const dma::bf16x8 (&qf)[8
 #pragma unroll
       for (int t8 = 0; t8 < 8; ++t8) {
         p[t8] = __builtin_amdgcn_exp2f(s[mb][hf * 8 + t8] - m_use);
-        rs += p[t8];
+        rsp[t8 & 3] += p[t8];
       }
       pb[mb][hf] = to_bf16x8(p);
     }
-  acc.l += rs;
-
-  // O^T += V^T P^T.  A operand of k-step (mb, hf) for lane (l32, hi): V^T rows
-  // d = db*32 + l32, keys mb*32 + 16*hf + 4*hi + [0,4) and mb*32 + 16*hf + 8 +
-  // 4*hi + [0,4), matching the keys of P^T's registers.  V stays row-major in
-  // LDS; each transposing read serves a 16-lane group g = lane/16: lane r of
-  // the group addresses key row kbase + r/4, columns dbase + 16*(g%2) +
-  // 4*(r%4), and lane i then receives that group's 4 keys at d = dbase +
-  // 16*(g%2) + i.
-  const int g = lane >> 4, r = lane & 15;
-  // address-space cast of the LDS tile pointer (the instruction takes a local address)
-  const __attribute__((address_space(3))) uint16_t* vbase =
-      (const __attribute__((address_space(3))) uint16_t*)sm.v[buf];
-#pragma unroll
-  for (int db = 0; db < 4; ++db) {
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const int k0 = mb * 32 + 16 * hf + 4 * (g >> 1) + (r >> 2);
-        const int d0 = db * 32 + 16 * (g & 1) + 4 * (r & 3);
-        const i16x4 lo =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + k0 * kVRow + d0));
-        const i16x4 up =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + (k0 + 8) * kVRow + d0));
-        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), up2 = __builtin_bit_cast(u32x2, up);
-        const u32x4 vv = {lo2[0], lo2[1], up2[0], up2[1]};
-        acc.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(dma::bf16x8, vv), pb[mb][hf], acc.o[db], 0, 0, 0);
-      }
-  }
+  acc.l += (rsp[0] + rsp[1]) + (rsp[2] + rsp[3]);
 }
 
-// Workgroup = NH query heads of one kv head x two 32-row halves of a 64-row
-// query tile: wave w takes head w/2 and rows (w%2)*32 .. +32.
 template <int NH>
 __global__ __launch_bounds__(NH * 128, 1) void attn_prefill_bf16_kernel(DmaAttnArgs a) {
-  constexpr int NT = NH * 128;
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
+  constexpr int NW = NH * 2;
+  __shared__ __align__(16) unsigned char k0[kTileB], k1[kTileB];
+  __shared__ __align__(16) unsigned char v0[kTileB], v1[kTileB];  // rows as gathered
+  __shared__ __align__(16) Meta sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
   const int G = (int)(a.Hq / a.Hkv);
   const int ngrp = G / NH;
-  const int t = blockIdx.x, h = blockIdx.y;
-  const int b = blockIdx.z / ngrp, hgrp = blockIdx.z % ngrp;
+  // Workgroups are dealt to the 8 XCDs round-robin by linear id.  When the
+  // (batch, kv head, head group) combinations split evenly over the XCDs,
+  // XCD x takes combinations x, x+8, ... whole, so each L2 holds the K/V rows
+  // of few heads; within a combination the longest tiles (last) go first.
+  const int ntile = (int)a.n_tiles;
+  const int ncomb = (int)(a.B * a.Hkv) * ngrp;
+  const int lid = blockIdx.x;
+  int t, comb;
+  if (ncomb % kXcds == 0) {
+    const int xcd = lid % kXcds, slot = lid / kXcds;
+    comb = (slot / ntile) * kXcds + xcd;
+    t = ntile - 1 - slot % ntile;
+  } else {
+    comb = lid / ntile;
+    t = ntile - 1 - lid % ntile;
+  }
+  const int hgrp = comb % ngrp;
+  const int h = (comb / ngrp) % (int)a.Hkv;
+  const int b = comb / (ngrp * (int)a.Hkv);
   const int hq = h * G + hgrp * NH + (wave >> 1);
   const int half = wave & 1;
+  const bool grp_a = wave < NW / 2;
   const int64_t seg = (int64_t)b * a.Hkv + h;
   const int64_t g = seg * a.n_tiles + t;
   const int r_lo = t * kBq;
@@ -256,9 +361,13 @@ __global__ __launch_bounds__(NH * 128, 1) void attn_prefill_bf16_kernel(DmaAttnA
   const int32_t* ev = a.evict + seg * a.Sk;
   const int nch = (cnt + kBk - 1) / kBk;
   const int nplain = nfull / kBk;  // leading chunks that every row keeps whole
-  const uint16_t* Kg = static_cast<const uint16_t*>(a.K) + b * a.ksb + h * a.ksh;
-  const uint16_t* Vg = static_cast<const uint16_t*>(a.V) + b * a.ksb + h * a.ksh;
+  const unsigned char* Kg =
+      static_cast<const unsigned char*>(a.K) + (b * a.ksb + h * a.ksh) * 2;
+  const unsigned char* Vg =
+      static_cast<const unsigned char*>(a.V) + (b * a.ksb + h * a.ksh) * 2;
+  const uint32_t rowb = (uint32_t)(a.kss * 2);  // row stride in bytes; offsets fit 32 bits
   const float scale2 = a.scale * kLog2e;
+  const float bias_div = kLog2e / scale2;  // bias enters the scores before the scale
 
   // Q^T operand: lane holds query n = half*32 + l32, d = kk*16 + 8*hi + [0, 8)
   const int n = half * 32 + l32;
@@ -269,54 +378,56 @@ __global__ __launch_bounds__(NH * 128, 1) void attn_prefill_bf16_kernel(DmaAttnA
                            (int64_t)(r_lo + (n < rows ? n : 0)) * a.qss;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      u32x4 v = *reinterpret_cast<const u32x4*>(qrow + kk * 16 + hi * 8);
-      if (n >= rows) v = u32x4{0u, 0u, 0u, 0u};
+      // rows past the tile's end repeat its first row; their output is not written
+      const u32x4 v = *reinterpret_cast<const u32x4*>(qrow + kk * 16 + hi * 8);
       qf[kk] = __builtin_bit_cast(dma::bf16x8, v);
     }
   }
 
-  Stage<NT> stg;
-  // key metadata of the chunk being described (wave 0, one key per lane)
-  int jn = -1, en = 0;
-  float dn = 0.f;
-#define DMA_LOAD_IDX(c_)                   \
-  do {                                     \
-    const int kk_ = (c_) * kBk + lane;     \
-    jn = (kk_ < cnt) ? list[kk_] : -1;     \
-  } while (0)
-#define DMA_FETCH_META()                   \
-  do {                                     \
-    const int jj_ = jn < 0 ? 0 : jn;       \
-    dn = dl[jj_];                          \
-    en = ev[jj_];                          \
-  } while (0)
-#define DMA_STORE_META(slot_)                                         \
-  do {                                                                \
-    const bool pad_ = jn < 0;                                         \
-    sm.j[slot_][lane] = pad_ ? 0 : jn;                                \
-    sm.pj[slot_][lane] = pad_ ? 0x7fffffff : jn;                      \
-    sm.e[slot_][lane] = pad_ ? 0 : en;                                \
-    sm.bias[slot_][lane] = pad_ ? -INFINITY : (dn - dmax) * kLog2e;   \
+  // Key metadata runs one stage per step ahead of its use, so each global
+  // load it issues has a whole step to land: in step c, wave 0 stores the
+  // metadata of chunk c+3 (loaded during step c-1); every wave loads delta
+  // and the eviction row of chunk c+4 (index loaded during step c-1) and the
+  // index of chunk c+5.  One key per lane.  The index loads are
+  // unconditional (clamped to the list) and padding past the list is applied
+  // when the metadata is stored: a conditional load would make the compiler
+  // wait for it on the spot.
+  int jB = 0, jC = 0, eC = 0;
+  float dC = 0.f;
+#define DMA_LOAD_IDX(c_) (list[min((c_) * kBk + lane, cnt - 1)])
+#define DMA_STORE_META(slot_, c_, j_, d_, e_)                           \
+  do {                                                                  \
+    const bool pad_ = (c_) * kBk + lane >= cnt;                         \
+    sm.pj[slot_][lane] = pad_ ? 0x7fffffff : (j_);                      \
+    sm.e[slot_][lane] = pad_ ? 0 : (e_);                                \
+    sm.bias[slot_][lane] = pad_ ? -INFINITY : ((d_) - dmax) * bias_div; \
   } while (0)
 
-  // prologue: metadata of chunks 0 and 1, K/V of chunk 0, indices of chunk 2
-  if (wave == 0 && nch > 0) {
-    DMA_LOAD_IDX(0);
-    DMA_FETCH_META();
-    DMA_STORE_META(0);
-    if (nch > 1) {
-      DMA_LOAD_IDX(1);
-      DMA_FETCH_META();
-      DMA_STORE_META(1);
+  // prologue: metadata of chunks 0..2, then K(0)
+  if (wave == 0) {
+#pragma unroll
+    for (int c = 0; c < 3; ++c) {
+      const int jn = DMA_LOAD_IDX(c);
+      DMA_STORE_META(c, c, jn, dl[jn], ev[jn]);
     }
-    if (nch > 2) DMA_LOAD_IDX(2);
   }
+  // every wave runs the load side of the pipeline (branch-free, so the loop
+  // carries the loaded registers without waiting for them); wave 0 stores
+  jC = DMA_LOAD_IDX(3);
+  dC = dl[jC];
+  eC = ev[jC];
+  jB = DMA_LOAD_IDX(4);
+  for (int i = tid; i < kTileB / 16; i += NW * 64)
+    reinterpret_cast<u32x4*>(v1)[i] = u32x4{0u, 0u, 0u, 0u};
+  // gather rows: kr = the chunk of this step's K gather, vr = of its V gather
+  // (the previous K chunk), nr = the next step's K chunk, loaded a step ahead
+  int kr[16 / NW], vr[16 / NW], nr[16 / NW];
+  gather_rows<NW>(vr, list, cnt, 0, wave, lane);
+  gather_rows<NW>(kr, list, cnt, 1, wave, lane);
+  gather_rows<NW>(nr, list, cnt, 2, wave, lane);
   __syncthreads();
-  if (nch > 0) {
-    stg.gather(sm.j[0], Kg, Vg, a.kss, tid);
-    stg.store(sm.k[0], sm.v[0], tid);
-  }
-  __syncthreads();
+  gather_tile<NW, false>(k0, vr, Kg, rowb, wave, lane);
+  phase_barrier<true>();
 
   Acc acc;
 #pragma unroll
@@ -325,32 +436,87 @@ __global__ __launch_bounds__(NH * 128, 1) void attn_prefill_bf16_kernel(DmaAttnA
     for (int i = 0; i < 16; ++i) acc.o[db][i] = 0.f;
   acc.m = -INFINITY;
   acc.l = 0.f;
+  dma::f32x16 s[2];
+  // P(-1) = 0 against a zeroed V buffer: the PV half of G_0 adds nothing
+  dma::bf16x8 pb[2][2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int t8 = 0; t8 < 8; ++t8) pb[mb][hf][t8] = (__bf16)0.f;
+
+  // gathers of the K chunk in kr into buffer KB_ and the V chunk in vr into
+  // buffer VB_, then the rows move on by one chunk
+#define DMA_GATHER(KB_, VB_)                                                             \
+  do {                                                                                   \
+    gather_tile<NW, false>(KB_, kr, Kg, rowb, wave, lane);                               \
+    gather_tile<NW, true>(VB_, vr, Vg, rowb, wave, lane);                                \
+    _Pragma("unroll") for (int t_ = 0; t_ < 16 / NW; ++t_) {                             \
+      vr[t_] = kr[t_];                                                                   \
+      kr[t_] = nr[t_];                                                                   \
+    }                                                                                    \
+  } while (0)
+
+  // group B idles through interval 0, issuing its share of that interval's
+  // gathers: K(1) and V(0)
+  if (!grp_a) {
+    DMA_GATHER(k1, v0);
+    gather_rows<NW>(nr, list, cnt, 3, wave, lane);  // group B's step 0 gathers K(2), V(1)
+    phase_barrier<false>();
+  }
+
+  // Step c (buffers: KC = K(c), KN = K(c+1), VC = V(c), VP = V(c-1)): G_c,
+  // barrier, S_c, barrier.  Interval 2c (G_c of group A, S_(c-1) of group B)
+  // gathers K(c+1) into KN and V(c) into VC: group A issues them at the end
+  // of G_c, after its own reads of K(c) and V(c-1); group B at the start of
+  // S_(c-1), i.e. its S phase gathers K(c+2) into KC and V(c+1) into VP,
+  // whose chunks it read in G_c.  No wave reads a K/V buffer between issuing
+  // gathers and waiting for them (group A waits after S_c, group B at the
+  // start of G_(c+1) and again after it), so the compiler's conservative
+  // waits for LDS-bound loads never stall a read early.  G_0 and G_nch run
+  // both MFMA halves: G_0's PV multiplies zeros, G_nch's scores (padding
+  // keys) are unused.  Wave 0 stores the metadata of chunk c+3 in S_c
+  // (interval 2c+1): its slot last held chunk c-1, read by group B in
+  // interval 2c.
+#define DMA_STEP(MASKED)                                                                 \
+  do {                                                                                   \
+    unsigned char* KC = (c & 1) ? k1 : k0;                                               \
+    unsigned char* KN = (c & 1) ? k0 : k1;                                               \
+    unsigned char* VC = (c & 1) ? v1 : v0;                                               \
+    unsigned char* VP = (c & 1) ? v0 : v1;                                               \
+    g_phase(acc, pb, s, qf, KC, VP, &sm.bias[c % kSlots][4 * hi], lane);                 \
+    if (grp_a) {                                                                         \
+      DMA_GATHER(KN, VC);                                                                \
+      phase_barrier<false>();                                                            \
+    } else {                                                                             \
+      phase_barrier<true>();                                                             \
+      DMA_GATHER(KC, VP);                                                                \
+    }                                                                                    \
+    gather_rows<NW>(nr, list, cnt, c + (grp_a ? 3 : 4), wave, lane);                     \
+    if (wave == 0) DMA_STORE_META((c + 3) % kSlots, c + 3, jC, dC, eC);                  \
+    jC = jB;                                                                             \
+    dC = dl[jB];                                                                         \
+    eC = ev[jB];                                                                         \
+    jB = DMA_LOAD_IDX(c + 5);                                                            \
+    if (c < nch) softmax_phase<MASKED>(acc, s, pb, sm, c % kSlots, hi, pos, scale2);     \
+    if (grp_a)                                                                           \
+      phase_barrier<true>();                                                             \
+    else                                                                                 \
+      phase_barrier<false>();                                                            \
+  } while (0)
 
   // Chunks [0, nplain) hold only keys every row keeps; the rest need the
-  // per-element mask.  Two loops keep the two bodies' registers apart.
-#define DMA_CHUNK_LOOP(MASKED, c_from, c_to)                                          \
-  for (int c = (c_from); c < (c_to); ++c) {                                           \
-    const int buf = c & 1;                                                            \
-    /* gather chunk c+1 (indices in slot (c+1)%3) while chunk c is computed;          \
-       fetch delta and eviction rows of chunk c+2 (indices loaded last step) */       \
-    if (c + 1 < nch) stg.gather(sm.j[(c + 1) % 3], Kg, Vg, a.kss, tid);              \
-    if (wave == 0 && c + 2 < nch) DMA_FETCH_META();                                   \
-    attend_chunk<MASKED>(acc, qf, sm, buf, c % 3, lane, pos, scale2);                 \
-    /* publish chunk c+1; metadata of chunk c+2 goes to slot (c+2)%3, whose chunk     \
-       c-1 was last read before the previous barrier */                               \
-    if (c + 1 < nch) stg.store(sm.k[buf ^ 1], sm.v[buf ^ 1], tid);                   \
-    if (wave == 0 && c + 2 < nch) {                                                   \
-      DMA_STORE_META((c + 2) % 3);                                                    \
-      if (c + 3 < nch) DMA_LOAD_IDX(c + 3);                                           \
-    }                                                                                 \
-    __syncthreads();                                                                  \
-  }
-  DMA_CHUNK_LOOP(false, 0, nplain)
-  DMA_CHUNK_LOOP(true, nplain, nch)
-#undef DMA_CHUNK_LOOP
-#undef DMA_LOAD_IDX
-#undef DMA_FETCH_META
+  // per-element mask; two loops keep the two bodies' registers apart.  The
+  // last step (c == nch) only finishes the PV product of chunk nch-1.
+  for (int c = 0; c < nplain; ++c) DMA_STEP(false);
+  for (int c = nplain; c <= nch; ++c) DMA_STEP(true);
+  // group A closes with one more barrier so both groups meet equally often
+  if (grp_a) phase_barrier<false>();
+#undef DMA_STEP
+#undef DMA_GATHER
 #undef DMA_STORE_META
+#undef DMA_LOAD_IDX
 
   // epilogue: normalise and write O (and the log-sum-exp)
   const float lt = acc.l + __shfl_xor(acc.l, 32);
@@ -375,11 +541,8 @@ __global__ __launch_bounds__(NH * 128, 1) void attn_prefill_bf16_kernel(DmaAttnA
 template <int NH>
 hipError_t launch(const DmaAttnArgs& a, hipStream_t st) {
   const int G = (int)(a.Hq / a.Hkv);
-  dim3 grid((unsigned)a.n_tiles, (unsigned)a.Hkv, (unsigned)(a.B * (G / NH)));
-  const size_t lds = sizeof(Smem);
-  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_prefill_bf16_kernel<NH>),
-                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  hipLaunchKernelGGL(attn_prefill_bf16_kernel<NH>, grid, dim3(NH * 128), lds, st, a);
+  dim3 grid((unsigned)(a.n_tiles * a.Hkv * a.B * (G / NH)));
+  hipLaunchKernelGGL(attn_prefill_bf16_kernel<NH>, grid, dim3(NH * 128), 0, st, a);
   return hipGetLastError();
 }
 
