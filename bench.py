@@ -38,8 +38,9 @@ ATTN_SOURCES = ("trainable_dynamic_mask_amd/csrc/attn_prefill.hip",
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=100,
+                    help="untimed forwards first: the shader clock needs ~0.1 s of load to reach its sustained level")
     ap.add_argument("--workload", default="prefill_16k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,

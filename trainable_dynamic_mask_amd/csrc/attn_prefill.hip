@@ -24,10 +24,18 @@
 //   S_c = { softmax of S(c) -> P(c) },
 // with a workgroup barrier after every phase.  Group B starts one phase late,
 // so between two barriers one wave of every SIMD runs MFMAs while the other
-// runs the softmax.  Interval 2c holds G_c of group A and S_(c-1) of group B;
-// in it every wave issues its share of the direct global-to-LDS gathers of
-// K(c+1) and V(c), which have all landed by the end of interval 2c+1 and are
-// first read in interval 2c+2.
+// runs the softmax.
+//
+// Memory pipeline: K/V tiles are triple-buffered and gathered straight from
+// HBM into LDS (direct loads, no registers), half by each group, four
+// phases before they are read; the loads of one batch are spread over the
+// issuing phase so that the address unit is never flooded.  The key
+// metadata (list entries, delta, eviction rows) moves the same way, five
+// and three steps ahead, and is turned into the mask and bias of a chunk one
+// step ahead.  The direct loads are inline asm, invisible to the compiler:
+// every wait for them is an explicit vmcnt count at a phase barrier, and no
+// wave ever consumes a register loaded from global memory inside the loop,
+// so the compiler inserts no waits of its own that would stall on them.
 //
 // Workgroups are mapped so that each XCD (with its own L2) serves few kv
 // heads, longest query tiles first.
@@ -53,7 +61,9 @@ constexpr int kD = 128;
 // transposing read land on 4 disjoint 64-byte spans).
 constexpr int kRowB = kD * 2;
 constexpr int kTileB = kBk * kRowB;
-constexpr int kSlots = 4;       // metadata of chunk c in slot c % 4
+constexpr int kBufs = 3;   // K/V tile buffers: chunk c in buffer c % 3
+constexpr int kRaw = 8;    // raw key metadata (index, delta, eviction row): chunk c in slot c % 8
+constexpr int kFin = 4;    // prepared key metadata (mask, bias): chunk c in slot c % 4
 constexpr int kXcds = 8;        // accelerator complex dies, each with its own L2
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -66,14 +76,16 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Key metadata of chunk c lives in slot c % 4; K(c) and V(c) live in LDS
-// buffer c % 2.  The K/V buffers and the metadata are separate __shared__
-// objects, so the compiler can tell the direct-to-LDS gathers apart from
-// the metadata reads and does not make those wait for the gathers.
-struct Meta {
-  int e[kSlots][kBk];       // eviction row per slot
-  int pj[kSlots][kBk];      // key index per slot for the mask (INT_MAX for padding)
-  float bias[kSlots][kBk];  // (delta - dmax) * log2(e) / score scale, -inf for padding
+// Everything the workgroup keeps in LDS (105 KB).
+struct Smem {
+  unsigned char k[kBufs][kTileB];  // K tiles, rows as gathered (swizzled)
+  unsigned char v[kBufs][kTileB];  // V tiles
+  int jraw[kRaw][kBk];             // list entries, clamped to the list: the gather rows
+  float draw[kRaw][kBk];           // delta of those keys
+  int eraw[kRaw][kBk];             // their eviction rows
+  int pj[kFin][kBk];               // key index for the mask (INT_MAX for padding)
+  int e[kFin][kBk];                // eviction row (0 for padding)
+  float bias[kFin][kBk];           // (delta - dmax) * log2(e) / score scale, -inf for padding
 };
 
 __device__ __forceinline__ dma::bf16x8 to_bf16x8(const float (&p)[8]) {
@@ -91,13 +103,44 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
-// Gather the 64 rows of one K or V chunk straight into LDS with 16-byte
-// direct loads.  The tile is 16 pieces of 1 KB = 4 rows; wave w loads pieces
-// w, w+NW, ...: lane L fills row 4*piece + L/16, stored chunk L%16, which
-// holds logical chunk (L%16) ^ swz(row).  idx[t] is the key index of the
-// lane's row in piece w + t*NW (see gather_rows).
+// Direct global-to-LDS loads, written as inline asm so that the compiler
+// neither tracks them nor inserts waits for them: every wait for them is an
+// explicit s_waitcnt vmcnt below.  Lane L's data lands at the LDS byte
+// address m0 + size*L; the instruction after an m0 write needs one wait
+// state.  They have no register results, and their address registers are
+// read when they issue.
+__device__ __forceinline__ void dma_b128(const void* src, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(src), "s"(lds)
+      : "m0");
+}
+__device__ __forceinline__ void dma_b32(const void* src, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %0, off"
+      :
+      : "v"(src), "s"(lds)
+      : "m0");
+}
+
+// LDS byte address of a location in the workgroup's shared memory
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(lds_void*)p;
+}
+
+// Gather the 64 rows of one K or V chunk into the tile at LDS address tile,
+// 16 bytes per lane.  The tile is 16 pieces of 1 KB = 4 rows; wave w loads
+// pieces w, w+NW, ...: lane L fills row 4*piece + L/16, stored chunk L%16,
+// which holds logical chunk (L%16) ^ swz(row).  idx[t] is the key index of
+// the lane's row in piece w + t*NW (see gather_rows).  2 * 16/NW loads per
+// wave for a K and a V tile.
 template <int NW, bool IS_V>
-__device__ __forceinline__ void gather_tile(unsigned char* tile, const int (&idx)[16 / NW],
+__device__ __forceinline__ void gather_tile(uint32_t tile, const int (&idx)[16 / NW],
                                             const unsigned char* g, uint32_t rowb, int wave,
                                             int lane) {
   const int rsub = lane >> 4, pc = lane & 15;
@@ -106,32 +149,50 @@ __device__ __forceinline__ void gather_tile(unsigned char* tile, const int (&idx
     const int piece = wave + t * NW;
     const int row = piece * 4 + rsub;
     const int lc = pc ^ (IS_V ? ((row & 3) << 2) : (row & 15));
-    __builtin_amdgcn_global_load_lds(g + (uint32_t)idx[t] * rowb + lc * 16,
-                                     (lds_void*)(tile + piece * 1024), 16, 0, 0);
+    dma_b128(g + (uint32_t)idx[t] * rowb + lc * 16, tile + piece * 1024);
   }
 }
 
-// Key indices of the rows this lane gathers for chunk ch, read straight from
-// the tile's key list a step ahead of the gather (positions past the list
-// repeat its last key; their scores are masked).
+// The i-th of the 2 * 16/NW direct loads of one batch: K pieces first, then V.
 template <int NW>
-__device__ __forceinline__ void gather_rows(int (&idx)[16 / NW], const int32_t* list, int cnt,
-                                            int ch, int wave, int lane) {
-#pragma unroll
-  for (int t = 0; t < 16 / NW; ++t)
-    idx[t] = list[min(ch * kBk + 4 * (wave + t * NW) + (lane >> 4), cnt - 1)];
+__device__ __forceinline__ void gather_piece(int i, uint32_t ktile, uint32_t vtile,
+                                             const int (&kidx)[16 / NW], const int (&vidx)[16 / NW],
+                                             const unsigned char* kg, const unsigned char* vg,
+                                             uint32_t rowb, int wave, int lane) {
+  constexpr int P = 16 / NW;
+  const bool is_v = i >= P;
+  const int t = is_v ? i - P : i;
+  const int piece = wave + t * NW;
+  const int row = piece * 4 + (lane >> 4);
+  const int lc = (lane & 15) ^ (is_v ? ((row & 3) << 2) : (row & 15));
+  const int idx = is_v ? vidx[t] : kidx[t];
+  dma_b128((is_v ? vg : kg) + (uint32_t)idx * rowb + lc * 16,
+           (is_v ? vtile : ktile) + piece * 1024);
 }
 
-// Workgroup barrier at the end of a phase.  WAIT_VM: this wave's direct
-// global-to-LDS loads have landed first (they are read by other waves after
-// the barrier); LDS writes always complete first.  The empty asm statements
-// keep the compiler from moving memory accesses across the barrier; no fence
-// is used, as a fence would wait for every load in flight.
-template <bool WAIT_VM>
+// Key indices of the rows this lane gathers for chunk ch (see gather_tile):
+// positions past the list repeat its last key, whose scores are masked.
+template <int NW>
+__device__ __forceinline__ void gather_rows(int (&idx)[16 / NW], const Smem& sm, int ch,
+                                            int wave, int lane) {
+#pragma unroll
+  for (int t = 0; t < 16 / NW; ++t)
+    idx[t] = sm.jraw[ch % kRaw][4 * (wave + t * NW) + (lane >> 4)];
+}
+
+// Workgroup barrier at the end of a phase.  This wave's LDS accesses
+// complete first; with VM >= 0, so do all but its VM most recent direct
+// loads (those of its current batch), so every gather issued in the
+// previous batch has landed before the barrier releases the waves that read
+// it.  The empty asm statements keep the compiler from moving memory
+// accesses across the barrier; no fence is used, as a fence would wait for
+// every load in flight.
+template <int VM>
 __device__ __forceinline__ void phase_barrier() {
+  static_assert(VM < 64, "vmcnt holds 6 bits");
   asm volatile("" ::: "memory");
-  if constexpr (WAIT_VM)
-    __builtin_amdgcn_s_waitcnt(7 << 4);  // vmcnt(0) expcnt(7) lgkmcnt(0)
+  if constexpr (VM >= 0)
+    __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4));  // vmcnt(VM) lgkmcnt(0)
   else
     __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // lgkmcnt(0) only
   __builtin_amdgcn_s_barrier();
@@ -182,10 +243,11 @@ __device__ __forceinline__ void v_operands(dma::bf16x8 (&vop)[4], const unsigned
 // V one PV k-step ahead, so the matrix cores do not wait on single LDS
 // reads.  The sched_group_barrier sequence pins that order (0x100 = LDS
 // read, 0x008 = MFMA) and bounds the registers held by operands in flight.
+template <int NDMA, typename F>
 __device__ __forceinline__ void g_phase(Acc& acc, const dma::bf16x8 (&pb)[2][2],
                                         dma::f32x16 (&s)[2], const dma::bf16x8 (&qf)[8],
                                         const unsigned char* kt, const unsigned char* vt,
-                                        const float* bias_row, int lane) {
+                                        const float* bias_row, int lane, F&& dma_issue) {
   const int l32 = lane & 31, hi = lane >> 5;
   // the scores start from the keys' bias divided by the score scale, so the
   // MFMAs add q.k to it (register i of block mb holds key mb*32 + 8*(i/4) +
@@ -202,6 +264,16 @@ __device__ __forceinline__ void g_phase(Acc& acc, const dma::bf16x8 (&pb)[2][2],
     }
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
+    // the direct loads handed to this phase go out evenly between the score
+    // MFMAs, so the address unit is never flooded and the wave never stalls
+    // on a full load queue
+    if constexpr (NDMA > 0) {
+      constexpr int kEvery = NDMA >= 16 ? 1 : 16 / NDMA;
+      if (q % kEvery == 0) {
+#pragma unroll
+        for (int i = 0; i < (NDMA + 15) / 16; ++i) dma_issue((q / kEvery) * ((NDMA + 15) / 16) + i);
+      }
+    }
     const int kk = q >> 1, mb = q & 1;
     const int row = mb * 32 + l32;
     const dma::bf16x8 kop = *reinterpret_cast<const dma::bf16x8*>(
@@ -250,10 +322,10 @@ __device__ __forceinline__ void g_phase(Acc& acc, const dma::bf16x8 (&pb)[2][2],
 // element; the others hold keys every row keeps.  Lane (l32, hi) holds
 // key(mb, i) = mb*32 + 8*(i/4) + 4*hi + i%4 of query l32; the other 32 keys
 // of the same query sit in lane ^ 32.
-template <bool MASKED>
+template <bool MASKED, int NDMA, typename F>
 __device__ __forceinline__ void softmax_phase(Acc& acc, dma::f32x16 (&s)[2],
-                                              dma::bf16x8 (&pb)[2][2], const Meta& sm, int slot,
-                                              int hi, int pos, float scale2) {
+                                              dma::bf16x8 (&pb)[2][2], const Smem& sm, int slot,
+                                              int hi, int pos, float scale2, F&& dma_issue) {
   const int* pjp = &sm.pj[slot][4 * hi];
   const int* pep = &sm.e[slot][4 * hi];
   // four partial maxima and four partial sums keep the dependency chains
@@ -305,6 +377,10 @@ __device__ __forceinline__ void softmax_phase(Acc& acc, dma::f32x16 (&s)[2],
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
+      if constexpr (NDMA > 0) {
+#pragma unroll
+        for (int i = 0; i < NDMA / 4; ++i) dma_issue((mb * 2 + hf) * (NDMA / 4) + i);
+      }
       float p[8];
 #pragma unroll
       for (int t8 = 0; t8 < 8; ++t8) {
@@ -319,10 +395,10 @@ __device__ __forceinline__ void softmax_phase(Acc& acc, dma::f32x16 (&s)[2],
 template <int NH>
 __global__ __launch_bounds__(NH * 128, 1) void attn_prefill_bf16_kernel(DmaAttnArgs a) {
   constexpr int NW = NH * 2;
-  __shared__ __align__(16) unsigned char k0[kTileB], k1[kTileB];
-  __shared__ __align__(16) unsigned char v0[kTileB], v1[kTileB];  // rows as gathered
-  __shared__ __align__(16) Meta sm;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int NG = 2 * (16 / NW);  // direct loads per wave for one K and one V tile
+  __shared__ __align__(16) Smem sm;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   const int G = (int)(a.Hq / a.Hkv);
   const int ngrp = G / NH;
@@ -368,6 +444,10 @@ __global__ __launch_bounds__(NH * 128, 1) void attn_prefill_bf16_kernel(DmaAttnA
   const uint32_t rowb = (uint32_t)(a.kss * 2);  // row stride in bytes; offsets fit 32 bits
   const float scale2 = a.scale * kLog2e;
   const float bias_div = kLog2e / scale2;  // bias enters the scores before the scale
+  const uint32_t lds_k = lds_addr(&sm.k[0][0]), lds_v = lds_addr(&sm.v[0][0]);
+  const uint32_t lds_j = lds_addr(&sm.jraw[0][0]), lds_d = lds_addr(&sm.draw[0][0]),
+                 lds_e = lds_addr(&sm.eraw[0][0]);
+  const int clast = max(cnt - 1, 0);
 
   // Q^T operand: lane holds query n = half*32 + l32, d = kk*16 + 8*hi + [0, 8)
   const int n = half * 32 + l32;
@@ -384,50 +464,53 @@ __global__ __launch_bounds__(NH * 128, 1) void attn_prefill_bf16_kernel(DmaAttnA
     }
   }
 
-  // Key metadata runs one stage per step ahead of its use, so each global
-  // load it issues has a whole step to land: in step c, wave 0 stores the
-  // metadata of chunk c+3 (loaded during step c-1); every wave loads delta
-  // and the eviction row of chunk c+4 (index loaded during step c-1) and the
-  // index of chunk c+5.  One key per lane.  The index loads are
-  // unconditional (clamped to the list) and padding past the list is applied
-  // when the metadata is stored: a conditional load would make the compiler
-  // wait for it on the spot.
-  int jB = 0, jC = 0, eC = 0;
-  float dC = 0.f;
-#define DMA_LOAD_IDX(c_) (list[min((c_) * kBk + lane, cnt - 1)])
-#define DMA_STORE_META(slot_, c_, j_, d_, e_)                           \
-  do {                                                                  \
-    const bool pad_ = (c_) * kBk + lane >= cnt;                         \
-    sm.pj[slot_][lane] = pad_ ? 0x7fffffff : (j_);                      \
-    sm.e[slot_][lane] = pad_ ? 0 : (e_);                                \
-    sm.bias[slot_][lane] = pad_ ? -INFINITY : ((d_) - dmax) * bias_div; \
+  // Key metadata, all by wave 0: the list entries of chunk x are loaded
+  // straight into slot x % 8 of jraw five steps before chunk x is first
+  // multiplied, delta and the eviction rows of those keys three steps
+  // before (addressed by the landed list entries), and in the softmax phase
+  // of the step before, wave 0 turns them into the mask and bias of slot
+  // x % 4, padding the positions past the list.
+#define DMA_LIST(x_) dma_b32(list + min((x_) * kBk + lane, clast), lds_j + ((x_) % kRaw) * 256)
+#define DMA_DELTA(x_, j_)                                   \
+  do {                                                      \
+    dma_b32(dl + (j_), lds_d + ((x_) % kRaw) * 256);        \
+    dma_b32(ev + (j_), lds_e + ((x_) % kRaw) * 256);        \
+  } while (0)
+#define DMA_PREPARE(x_)                                                         \
+  do {                                                                          \
+    const int sr_ = (x_) % kRaw, sf_ = (x_) % kFin;                             \
+    const bool pad_ = (x_) * kBk + lane >= cnt;                                 \
+    const int jj_ = sm.jraw[sr_][lane];                                         \
+    sm.pj[sf_][lane] = pad_ ? 0x7fffffff : jj_;                                 \
+    sm.e[sf_][lane] = pad_ ? 0 : sm.eraw[sr_][lane];                            \
+    sm.bias[sf_][lane] = pad_ ? -INFINITY : (sm.draw[sr_][lane] - dmax) * bias_div; \
   } while (0)
 
-  // prologue: metadata of chunks 0..2, then K(0)
+  // prologue: list entries of chunks 0..4, delta of chunks 0..2, K(0), the
+  // mask and bias of chunk 0; every load of it has landed when it ends
   if (wave == 0) {
 #pragma unroll
-    for (int c = 0; c < 3; ++c) {
-      const int jn = DMA_LOAD_IDX(c);
-      DMA_STORE_META(c, c, jn, dl[jn], ev[jn]);
+    for (int x = 0; x < 5; ++x) DMA_LIST(x);
+  }
+  for (int i = tid; i < kTileB / 16; i += NW * 64)  // V(-1) = 0 (buffer 2)
+    reinterpret_cast<u32x4*>(sm.v[2])[i] = u32x4{0u, 0u, 0u, 0u};
+  if (wave == 0) {
+    __builtin_amdgcn_s_waitcnt(7 << 4);  // vmcnt(0): the list entries have landed
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int x = 0; x < 3; ++x) {
+      const int jj = sm.jraw[x][lane];
+      DMA_DELTA(x, jj);
     }
   }
-  // every wave runs the load side of the pipeline (branch-free, so the loop
-  // carries the loaded registers without waiting for them); wave 0 stores
-  jC = DMA_LOAD_IDX(3);
-  dC = dl[jC];
-  eC = ev[jC];
-  jB = DMA_LOAD_IDX(4);
-  for (int i = tid; i < kTileB / 16; i += NW * 64)
-    reinterpret_cast<u32x4*>(v1)[i] = u32x4{0u, 0u, 0u, 0u};
-  // gather rows: kr = the chunk of this step's K gather, vr = of its V gather
-  // (the previous K chunk), nr = the next step's K chunk, loaded a step ahead
-  int kr[16 / NW], vr[16 / NW], nr[16 / NW];
-  gather_rows<NW>(vr, list, cnt, 0, wave, lane);
-  gather_rows<NW>(kr, list, cnt, 1, wave, lane);
-  gather_rows<NW>(nr, list, cnt, 2, wave, lane);
-  __syncthreads();
-  gather_tile<NW, false>(k0, vr, Kg, rowb, wave, lane);
-  phase_barrier<true>();
+  phase_barrier<0>();
+  int kr[16 / NW], vr[16 / NW];
+  gather_rows<NW>(kr, sm, 0, wave, lane);
+  gather_tile<NW, false>(lds_k, kr, Kg, rowb, wave, lane);
+  __builtin_amdgcn_s_waitcnt(7 << 4);  // vmcnt(0)
+  asm volatile("" ::: "memory");
+  if (wave == 0) DMA_PREPARE(0);
+  phase_barrier<0>();
 
   Acc acc;
 #pragma unroll
@@ -446,77 +529,110 @@ __global__ __launch_bounds__(NH * 128, 1) void attn_prefill_bf16_kernel(DmaAttnA
 #pragma unroll
       for (int t8 = 0; t8 < 8; ++t8) pb[mb][hf][t8] = (__bf16)0.f;
 
-  // gathers of the K chunk in kr into buffer KB_ and the V chunk in vr into
-  // buffer VB_, then the rows move on by one chunk
-#define DMA_GATHER(KB_, VB_)                                                             \
-  do {                                                                                   \
-    gather_tile<NW, false>(KB_, kr, Kg, rowb, wave, lane);                               \
-    gather_tile<NW, true>(VB_, vr, Vg, rowb, wave, lane);                                \
-    _Pragma("unroll") for (int t_ = 0; t_ < 16 / NW; ++t_) {                             \
-      vr[t_] = kr[t_];                                                                   \
-      kr[t_] = nr[t_];                                                                   \
-    }                                                                                    \
+  // Step c is G_c, barrier, S_c, barrier; group A runs G_c in interval 2c,
+  // group B in interval 2c+1.  G_c reads K(c) from buffer c%3 and V(c-1)
+  // from buffer (c+2)%3.  Each K/V tile is gathered half by each group, in
+  // batches, four intervals before it is read:
+  //   group A, batch c (start of G_c):   K(c+2) -> c+2, V(c+1) -> c+1
+  //   group B, batch c (start of S_c):   K(c+3) -> c,   V(c+2) -> c+2
+  // (buffer numbers mod 3), each into a buffer whose last reader ran in the
+  // interval before.  A wave's barrier after its S (group A) or G (group B)
+  // phase waits for all but its latest batch, so batch c has landed by the
+  // end of interval 2c+3 (A) or 2c+5 (B), before K(c+2)/K(c+3) are read.
+  // Wave 0 adds three metadata loads to each group-A batch.  G_0 and G_nch
+  // run both MFMA halves: G_0's PV multiplies zeros, G_nch's scores
+  // (padding keys) are unused.
+#define DMA_TILES(c_)                                                 \
+  const int b0_ = (c_) % kBufs;                                       \
+  const int b2_ = b0_ == 0 ? 2 : b0_ - 1; /* (c+2) % 3 */              \
+  const int b1_ = b0_ == 2 ? 0 : b0_ + 1; /* (c+1) % 3 */              \
+  const unsigned char* KC = sm.k[b0_];                                \
+  const unsigned char* VP = sm.v[b2_]
+#define DMA_STEP_A(MASKED)                                                              \
+  do {                                                                                  \
+    DMA_TILES(c);                                                                       \
+    int jd = 0;                                                                         \
+    if (wave == 0) jd = sm.jraw[(c + 3) % kRaw][lane];                                  \
+    const uint32_t kt_ = lds_k + b2_ * kTileB, vt_ = lds_v + b1_ * kTileB;              \
+    g_phase<NG>(acc, pb, s, qf, KC, VP, &sm.bias[c % kFin][4 * hi], lane, [&](int i_) { \
+      gather_piece<NW>(i_, kt_, vt_, kr, vr, Kg, Vg, rowb, wave, lane);                 \
+    });                                                                                 \
+    if (wave == 0) {                                                                    \
+      DMA_LIST(c + 5);                                                                  \
+      DMA_DELTA(c + 3, jd);                                                             \
+    }                                                                                   \
+    phase_barrier<-1>();                                                                \
+    if (wave == 0) DMA_PREPARE(c + 1);                                                  \
+    if (c < nch)                                                                        \
+      softmax_phase<MASKED, 0>(acc, s, pb, sm, c % kFin, hi, pos, scale2, [](int) {});  \
+    gather_rows<NW>(kr, sm, c + 3, wave, lane);                                         \
+    gather_rows<NW>(vr, sm, c + 2, wave, lane);                                         \
+    if (wave == 0)                                                                      \
+      phase_barrier<NG + 3>();                                                          \
+    else                                                                                \
+      phase_barrier<NG>();                                                              \
   } while (0)
-
-  // group B idles through interval 0, issuing its share of that interval's
-  // gathers: K(1) and V(0)
-  if (!grp_a) {
-    DMA_GATHER(k1, v0);
-    gather_rows<NW>(nr, list, cnt, 3, wave, lane);  // group B's step 0 gathers K(2), V(1)
-    phase_barrier<false>();
-  }
-
-  // Step c (buffers: KC = K(c), KN = K(c+1), VC = V(c), VP = V(c-1)): G_c,
-  // barrier, S_c, barrier.  Interval 2c (G_c of group A, S_(c-1) of group B)
-  // gathers K(c+1) into KN and V(c) into VC: group A issues them at the end
-  // of G_c, after its own reads of K(c) and V(c-1); group B at the start of
-  // S_(c-1), i.e. its S phase gathers K(c+2) into KC and V(c+1) into VP,
-  // whose chunks it read in G_c.  No wave reads a K/V buffer between issuing
-  // gathers and waiting for them (group A waits after S_c, group B at the
-  // start of G_(c+1) and again after it), so the compiler's conservative
-  // waits for LDS-bound loads never stall a read early.  G_0 and G_nch run
-  // both MFMA halves: G_0's PV multiplies zeros, G_nch's scores (padding
-  // keys) are unused.  Wave 0 stores the metadata of chunk c+3 in S_c
-  // (interval 2c+1): its slot last held chunk c-1, read by group B in
-  // interval 2c.
-#define DMA_STEP(MASKED)                                                                 \
-  do {                                                                                   \
-    unsigned char* KC = (c & 1) ? k1 : k0;                                               \
-    unsigned char* KN = (c & 1) ? k0 : k1;                                               \
-    unsigned char* VC = (c & 1) ? v1 : v0;                                               \
-    unsigned char* VP = (c & 1) ? v0 : v1;                                               \
-    g_phase(acc, pb, s, qf, KC, VP, &sm.bias[c % kSlots][4 * hi], lane);                 \
-    if (grp_a) {                                                                         \
-      DMA_GATHER(KN, VC);                                                                \
-      phase_barrier<false>();                                                            \
-    } else {                                                                             \
-      phase_barrier<true>();                                                             \
-      DMA_GATHER(KC, VP);                                                                \
-    }                                                                                    \
-    gather_rows<NW>(nr, list, cnt, c + (grp_a ? 3 : 4), wave, lane);                     \
-    if (wave == 0) DMA_STORE_META((c + 3) % kSlots, c + 3, jC, dC, eC);                  \
-    jC = jB;                                                                             \
-    dC = dl[jB];                                                                         \
-    eC = ev[jB];                                                                         \
-    jB = DMA_LOAD_IDX(c + 5);                                                            \
-    if (c < nch) softmax_phase<MASKED>(acc, s, pb, sm, c % kSlots, hi, pos, scale2);     \
-    if (grp_a)                                                                           \
-      phase_barrier<true>();                                                             \
-    else                                                                                 \
-      phase_barrier<false>();                                                            \
+#define DMA_STEP_B(MASKED)                                                              \
+  do {                                                                                  \
+    DMA_TILES(c);                                                                       \
+    g_phase<0>(acc, pb, s, qf, KC, VP, &sm.bias[c % kFin][4 * hi], lane, [](int) {});    \
+    gather_rows<NW>(kr, sm, c + 3, wave, lane);                                         \
+    gather_rows<NW>(vr, sm, c + 2, wave, lane);                                         \
+    phase_barrier<NG>();                                                                \
+    {                                                                                   \
+      const uint32_t kt_ = lds_k + b0_ * kTileB, vt_ = lds_v + b2_ * kTileB;            \
+      auto issue_ = [&](int i_) {                                                       \
+        gather_piece<NW>(i_, kt_, vt_, kr, vr, Kg, Vg, rowb, wave, lane);               \
+      };                                                                                \
+      if (c < nch)                                                                      \
+        softmax_phase<MASKED, NG>(acc, s, pb, sm, c % kFin, hi, pos, scale2, issue_);   \
+      else                                                                              \
+        for (int i_ = 0; i_ < NG; ++i_) issue_(i_);                                     \
+    }                                                                                   \
+    phase_barrier<-1>();                                                                \
   } while (0)
 
   // Chunks [0, nplain) hold only keys every row keeps; the rest need the
-  // per-element mask; two loops keep the two bodies' registers apart.  The
-  // last step (c == nch) only finishes the PV product of chunk nch-1.
-  for (int c = 0; c < nplain; ++c) DMA_STEP(false);
-  for (int c = nplain; c <= nch; ++c) DMA_STEP(true);
-  // group A closes with one more barrier so both groups meet equally often
-  if (grp_a) phase_barrier<false>();
-#undef DMA_STEP
-#undef DMA_GATHER
-#undef DMA_STORE_META
-#undef DMA_LOAD_IDX
+  // per-element mask; separate loops keep the two bodies' registers apart,
+  // and each group runs its own loops.  The last step (c == nch) only
+  // finishes the PV product of chunk nch-1.
+  if (grp_a) {
+    // batch -1: K(1) -> 1, V(0) -> 0
+    gather_rows<NW>(kr, sm, 1, wave, lane);
+    gather_rows<NW>(vr, sm, 0, wave, lane);
+    gather_tile<NW, false>(lds_k + 1 * kTileB, kr, Kg, rowb, wave, lane);
+    gather_tile<NW, true>(lds_v + 0 * kTileB, vr, Vg, rowb, wave, lane);
+    gather_rows<NW>(kr, sm, 2, wave, lane);
+    gather_rows<NW>(vr, sm, 1, wave, lane);
+    int c = 0;
+    for (; c < nplain; ++c) DMA_STEP_A(false);
+    for (; c <= nch; ++c) DMA_STEP_A(true);
+    // one more barrier so both groups meet equally often
+    phase_barrier<-1>();
+  } else {
+    // group B idles through interval 0, issuing batches -2 (K(1) -> 1,
+    // V(0) -> 0) and -1 (K(2) -> 2, V(1) -> 1)
+    gather_rows<NW>(kr, sm, 1, wave, lane);
+    gather_rows<NW>(vr, sm, 0, wave, lane);
+    gather_tile<NW, false>(lds_k + 1 * kTileB, kr, Kg, rowb, wave, lane);
+    gather_tile<NW, true>(lds_v + 0 * kTileB, vr, Vg, rowb, wave, lane);
+    gather_rows<NW>(kr, sm, 2, wave, lane);
+    gather_rows<NW>(vr, sm, 1, wave, lane);
+    gather_tile<NW, false>(lds_k + 2 * kTileB, kr, Kg, rowb, wave, lane);
+    gather_tile<NW, true>(lds_v + 1 * kTileB, vr, Vg, rowb, wave, lane);
+    phase_barrier<-1>();
+    int c = 0;
+    for (; c < nplain; ++c) DMA_STEP_B(false);
+    for (; c <= nch; ++c) DMA_STEP_B(true);
+  }
+  // no direct load may still be writing LDS when the workgroup ends
+  __builtin_amdgcn_s_waitcnt(7 << 4);
+#undef DMA_STEP_A
+#undef DMA_STEP_B
+#undef DMA_TILES
+#undef DMA_PREPARE
+#undef DMA_DELTA
+#undef DMA_LIST
 
   // epilogue: normalise and write O (and the log-sum-exp)
   const float lt = acc.l + __shfl_xor(acc.l, 32);
