@@ -149,7 +149,7 @@ def main():
     x = make_inputs(wl, device=dev)
     delta = torch.empty(wl.B, wl.Hkv, wl.Sk, dtype=torch.float32, device=dev)
     mask = dma.alloc_mask(wl.B, wl.Hkv, wl.Sq, wl.Sk, wl.q_offset, wl.w, dev)
-    ws_t = torch.empty(max(16, lib.dma_topk_workspace_bytes(wl.B, wl.Hkv, wl.Sq, wl.Sk)),
+    ws_t = torch.empty(max(16, lib.dma_topk_workspace_bytes(wl.B, wl.Hkv, wl.Sq, wl.Sk, wl.w)),
                        dtype=torch.uint8, device=dev)
     O = torch.empty_like(x["Q"])
     nbytes_a = lib.dma_attn_workspace_bytes(wl.B, wl.Hq, wl.Sq, wl.D, wl.w)

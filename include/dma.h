@@ -110,8 +110,8 @@ typedef struct {
 dma_status dma_mask_dims_for(int64_t B, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t q_offset,
                              int64_t w, dma_mask_dims* out);
 
-/* Workspace bytes dma_topk_mask needs (0 when Sq <= 1). */
-size_t dma_topk_workspace_bytes(int64_t B, int64_t Hkv, int64_t Sq, int64_t Sk);
+/* Workspace bytes dma_topk_mask needs for these arguments (0 when Sq <= 1). */
+size_t dma_topk_workspace_bytes(int64_t B, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t w);
 
 /* Workspace bytes dma_attn_fwd needs (split partials of the one-row path; 0
  * when Sq > 1). */

@@ -38,7 +38,7 @@ def test_exports_every_declared_function(lib):
 def test_status_strings_and_versions(lib):
     assert lib.dma_status_string(0) == b"ok"
     assert lib.dma_status_string(3) == b"workspace too small"
-    assert lib.dma_abi_version() == 1
+    assert lib.dma_abi_version() == 2
     bq, bk = ctypes.c_int32(), ctypes.c_int32()
     lib.dma_tile_sizes(ctypes.byref(bq), ctypes.byref(bk))
     assert (bq.value, bk.value) == (64, 64)
@@ -68,8 +68,9 @@ def test_mask_dims(lib):
 
 
 def test_workspace_sizes(lib):
-    assert lib.dma_topk_workspace_bytes(1, 8, 16384, 16384) >= 8 * 16384 * 20
-    assert lib.dma_topk_workspace_bytes(1, 8, 1, 16384) == 0
+    # sort buffers and ranks, plus 32 groups of 8 tiles with candidate lists (w + 512 keys, 8 bytes)
+    assert lib.dma_topk_workspace_bytes(1, 8, 16384, 16384, 2048) >= 8 * 16384 * 20 + 8 * 32 * 2560 * 8
+    assert lib.dma_topk_workspace_bytes(1, 8, 1, 16384, 2048) == 0
     assert lib.dma_attn_workspace_bytes(2, 32, 4096, 128, 2048) == 0
     assert lib.dma_attn_workspace_bytes(64, 32, 1, 128, 2048) == 64 * 32 * 8 * 130 * 4
 

@@ -40,9 +40,10 @@ def test_mask_small(gpu_lib, kind, S, w):
     check_mask(gm, d)
 
 
-@pytest.mark.parametrize("S,w", [(4097, 100), (8192, 3000), (12345, 2048)])
+@pytest.mark.parametrize("S,w", [(4097, 100), (8192, 3000), (12345, 2048), (9000, 6000)])
 def test_mask_multi_chunk_sort(gpu_lib, S, w):
-    # several 4096-key sort chunks, ragged tail, merge passes
+    # several 4096-key sort chunks, ragged tail, merge passes; w = 6000 gives
+    # tile groups with more candidates than one staging round
     d = _delta("ties", 1, 2, S, seed=S)
     gm = dma.topk_mask(d, S, 0, w)
     check_mask(gm, d)

@@ -123,7 +123,7 @@ def topk_mask(delta: torch.Tensor, Sq: int, q_offset: int, w: int, kt_lists: boo
     lib = load()
     if mask is None:
         mask = alloc_mask(B, Hkv, Sq, Sk, q_offset, w, delta.device, kt_lists)
-    nbytes = lib.dma_topk_workspace_bytes(B, Hkv, Sq, Sk)
+    nbytes = lib.dma_topk_workspace_bytes(B, Hkv, Sq, Sk, w)
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(16, nbytes), dtype=torch.uint8, device=delta.device)
     ms = mask.cstruct()

@@ -61,7 +61,7 @@ def load():
     lib.dma_mask_dims_for.argtypes = [_I64, _I64, _I64, _I64, _I64, _I64,
                                       ctypes.POINTER(DmaMaskDims)]
     lib.dma_mask_dims_for.restype = ctypes.c_int
-    lib.dma_topk_workspace_bytes.argtypes = [_I64, _I64, _I64, _I64]
+    lib.dma_topk_workspace_bytes.argtypes = [_I64, _I64, _I64, _I64, _I64]
     lib.dma_topk_workspace_bytes.restype = _SZ
     lib.dma_attn_workspace_bytes.argtypes = [_I64, _I64, _I64, _I64, _I64]
     lib.dma_attn_workspace_bytes.restype = _SZ

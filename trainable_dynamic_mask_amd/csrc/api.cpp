@@ -11,7 +11,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -82,9 +82,9 @@ dma_status dma_mask_dims_for(int64_t B, int64_t Hkv, int64_t Sq, int64_t Sk, int
   return DMA_OK;
 }
 
-size_t dma_topk_workspace_bytes(int64_t B, int64_t Hkv, int64_t Sq, int64_t Sk) {
-  if (B <= 0 || Hkv <= 0 || Sq <= 1 || Sk <= 0) return 0;
-  return dma_topk_ws_bytes(B * Hkv, Sk);
+size_t dma_topk_workspace_bytes(int64_t B, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t w) {
+  if (B <= 0 || Hkv <= 0 || Sq <= 1 || Sk <= 0 || w <= 0) return 0;
+  return dma_topk_ws_bytes(B * Hkv, Sq, Sk, w);
 }
 
 size_t dma_attn_workspace_bytes(int64_t B, int64_t Hq, int64_t Sq, int64_t D, int64_t w) {
@@ -144,7 +144,7 @@ dma_status dma_topk_mask(const float* delta, int64_t B, int64_t Hkv, int64_t Sq,
   a.ws = ws;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (Sq == 1) return hip_status(dma_launch_topk_decode(a, s));
-  const size_t need = dma_topk_workspace_bytes(B, Hkv, Sq, Sk);
+  const size_t need = dma_topk_workspace_bytes(B, Hkv, Sq, Sk, w);
   if (ws_bytes < need || !ws) return DMA_ERR_WORKSPACE;
   if (!aligned16(ws)) return DMA_ERR_INVALID_ARG;
   return hip_status(dma_launch_topk_prefill(a, s));

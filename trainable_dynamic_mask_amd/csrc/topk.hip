@@ -18,12 +18,15 @@
 //       The wave keeps a 2048-bit window of the bitmap in registers;
 //   T3  per 64-row query tile: the union of the rows' keep sets (keys with
 //       e_j > max(j, tile start) and j <= tile end), the keys every row keeps
-//       first, the natural key tiles touched, and the largest delta.
+//       first, the natural key tiles touched, and the largest delta; built
+//       from candidate lists shared by groups of 8 tiles.
 // A single query row (decode) skips T1-T3: one workgroup per sequence finds
 // the w-th largest delta by a bitwise search over the order-preserving
 // 32-bit codes and compacts the kept keys in index order.
+#include "../../include/dma.h"
 #include "common.h"
 
+#include <algorithm>
 #include <climits>
 
 namespace {
@@ -32,7 +35,6 @@ constexpr int kSortChunk = 4096;
 constexpr int kSortThreads = 1024;
 constexpr int kMergeItems = 8;
 constexpr int kListRows = 64;   // query rows per tile (Bq)
-constexpr int kPartialCap = 128;  // keys only some rows of a tile keep: at most 2*Bq-1
 
 // ---------------------------------------------------------------- T1: chunk sort
 __global__ __launch_bounds__(kSortThreads) void sort_chunk_kernel(const float* __restrict__ delta,
@@ -251,37 +253,71 @@ __global__ __launch_bounds__(256) void evict_kernel(const uint64_t* __restrict__
 }
 
 // ---------------------------------------------------------------- T3: tile lists
-// Wave w scans keys [w*L, (w+1)*L) of 0..p_hi (L a multiple of 64, so each
-// 64-key tile of the block-skip list belongs to one wave), 8 x 64 keys per
-// step with all loads issued first.  Pass 1 counts, one barrier turns counts
-// into offsets, pass 2 writes: no barrier per step.
-// The largest delta over U equals the largest delta over keys 0..p_hi: that
-// key is kept by row p_hi, and any key beating a member of U is itself kept by
-// row p_hi.
-constexpr int kListWaves = 8;
-constexpr int kListUnroll = 8;
+// Two levels.  Membership in a tile's union is a run of consecutive tiles
+// starting at the key's own tile (j is in U_t iff j <= p_hi(t) and
+// e_j > max(j, p_lo(t)), and p_lo grows with t), so the keys in the union of
+// any tile of a group of kSuperTiles (8) consecutive tiles are
+//   C = { j <= P_hi : e_j > max(j, P_lo) }
+// with P_lo, P_hi the group's first and last position: the min(w, P_lo+1)
+// keys kept at P_lo plus the keys born inside the group with e_j > j, at most
+// w + 511.  L1 builds C once per group by scanning keys 0..P_hi; L2 builds
+// the group's tile lists from C only, instead of rescanning each tile's whole
+// prefix.  Both keep ascending key order.
+constexpr int kListWaves = 16;  // L1: 16 waves x 16 x 64 keys per load batch
+constexpr int kListUnroll = 16;
+constexpr int kSuperTiles = 8;
 
-__global__ __launch_bounds__(kListWaves * 64) void lists_kernel(
+// L1.  Wave w scans keys [w*L, (w+1)*L) of 0..P_hi, 16 x 64 keys per step
+// with all loads issued first (one step covers 16K keys per workgroup).
+// Pass 1 counts, one barrier turns counts into offsets, pass 2 writes the
+// members' index and eviction row.  Pass 2 also gives each tile of the group
+// its largest delta, the largest over keys 0..p_hi (that key is kept by row
+// p_hi, so it is also the largest over U).
+__global__ __launch_bounds__(kListWaves * 64) void cand_kernel(
     const float* __restrict__ delta, const int32_t* __restrict__ evict, int Sk, int Sq, int q0,
-    int n_tiles, int u_stride, int kt_stride, int32_t* __restrict__ u_idx,
-    int32_t* __restrict__ u_cnt, int32_t* __restrict__ u_nfull, float* __restrict__ u_dmax,
-    int32_t* __restrict__ kt_idx, int32_t* __restrict__ kt_cnt) {
-  __shared__ int s_part[kPartialCap];
-  __shared__ int s_c[3][kListWaves];
-  __shared__ float s_m[kListWaves];
-  const int seg = blockIdx.y, t = blockIdx.x;
-  const int64_t g = (int64_t)seg * n_tiles + t;
+    int n_super, int n_tiles, int cap, int32_t* __restrict__ cj, int32_t* __restrict__ ce,
+    int32_t* __restrict__ ccnt, float* __restrict__ u_dmax) {
+  __shared__ int s_c[kListWaves];
+  // order codes of the largest delta per bucket: bucket i holds the keys of
+  // tile t0+i's own rows, bucket 0 also every key before the group
+  __shared__ uint32_t s_b[kSuperTiles];
+  if (threadIdx.x < kSuperTiles) s_b[threadIdx.x] = 0u;  // 0: below every code
+  const int seg = blockIdx.y, T = blockIdx.x;
+  const int64_t g = (int64_t)seg * n_super + T;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int p_lo = q0 + t * kListRows;
-  const int p_hi = q0 + min(Sq, t * kListRows + kListRows) - 1;
+  const int P_lo = q0 + T * kSuperTiles * kListRows;
+  const int P_hi = q0 + min(Sq, (T + 1) * kSuperTiles * kListRows) - 1;
   const int32_t* E = evict + (int64_t)seg * Sk;
   const float* Dl = delta + (int64_t)seg * Sk;
-  const int n = p_hi + 1;
+  const int n = P_hi + 1;
   const int L = ((n + 64 * kListWaves - 1) / (64 * kListWaves)) * 64;
   const int j0 = min(n, wave * L), j1 = min(n, j0 + L);
 
-  int nf = 0, np = 0, nk = 0;
-  float dm = -INFINITY;
+  int nc = 0;
+  for (int jb = j0; jb < j1; jb += 64 * kListUnroll) {
+    int e[kListUnroll];
+#pragma unroll
+    for (int u = 0; u < kListUnroll; ++u) {
+      const int j = jb + u * 64 + lane;
+      e[u] = j < j1 ? E[j] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kListUnroll; ++u) {
+      const int j = jb + u * 64 + lane;
+      nc += __popcll(dma::ballot(j < j1 && e[u] > max(j, P_lo)));
+    }
+  }
+  if (lane == 0) s_c[wave] = nc;
+  __syncthreads();
+  int oc = 0, tc = 0;
+#pragma unroll
+  for (int k = 0; k < kListWaves; ++k) {
+    if (k < wave) oc += s_c[k];
+    tc += s_c[k];
+  }
+  int32_t* oj = cj + g * cap;
+  int32_t* oe = ce + g * cap;
+  uint32_t m0 = 0u;  // this lane's largest code before the group
   for (int jb = j0; jb < j1; jb += 64 * kListUnroll) {
     int e[kListUnroll];
     float d[kListUnroll];
@@ -289,81 +325,226 @@ __global__ __launch_bounds__(kListWaves * 64) void lists_kernel(
     for (int u = 0; u < kListUnroll; ++u) {
       const int j = jb + u * 64 + lane;
       e[u] = j < j1 ? E[j] : 0;
-      d[u] = j < j1 ? Dl[j] : -INFINITY;
+      d[u] = j < j1 ? Dl[j] : 0.f;
     }
 #pragma unroll
     for (int u = 0; u < kListUnroll; ++u) {
       const int j = jb + u * 64 + lane;
-      dm = fmaxf(dm, d[u]);
-      const bool member = j < j1 && e[u] > max(j, p_lo);
-      const bool full = member && j <= p_lo && e[u] > p_hi;
-      const uint64_t bf = dma::ballot(full), bp = dma::ballot(member && !full);
-      nf += __popcll(bf);
-      np += __popcll(bp);
-      nk += (bf | bp) ? 1 : 0;
+      const bool member = j < j1 && e[u] > max(j, P_lo);
+      const uint64_t bm = dma::ballot(member);
+      if (member) {
+        const int pos = oc + dma::rank_below(bm);
+        if (pos < cap) {
+          oj[pos] = j;
+          oe[pos] = e[u];
+        }
+      }
+      if (j < j1) {
+        if (j < P_lo)
+          m0 = max(m0, dma::ord32(d[u]));
+        else
+          atomicMax(&s_b[(j - P_lo) >> 6], dma::ord32(d[u]));
+      }
+      oc += __popcll(bm);
     }
   }
-  dm = dma::wave_max(dm);
-  if (lane == 0) {
-    s_c[0][wave] = nf;
-    s_c[1][wave] = np;
-    s_c[2][wave] = nk;
-    s_m[wave] = dm;
+  if (threadIdx.x == 0) ccnt[g] = min(tc, cap);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m0 = max(m0, (uint32_t)__shfl_xor((int)m0, o));
+  if (lane == 0) atomicMax(&s_b[0], m0);
+  __syncthreads();
+  // tile t0+i: the largest delta over keys 0..p_hi, i.e. over buckets 0..i
+  const int t0 = T * kSuperTiles;
+  const int i = threadIdx.x;
+  if (i < min(kSuperTiles, n_tiles - t0)) {
+    uint32_t m = 0u;
+    for (int k = 0; k <= i; ++k) m = max(m, s_b[k]);
+    const uint32_t bits = (m & 0x80000000u) ? (m & 0x7fffffffu) : ~m;  // inverse of ord32
+    u_dmax[(int64_t)seg * n_tiles + t0 + i] = __uint_as_float(bits);
+  }
+}
+
+// L2.  One workgroup per group writes the lists of all its tiles: each
+// candidate is tested against every tile of the group at once (its member
+// tiles and the tiles whose every row keeps it), and per-tile ballots give
+// exact positions in both ascending runs.  Pass 1 counts per tile and wave
+// and marks the key tiles in LDS bitmaps; one barrier turns the counts into
+// offsets; pass 2 writes.
+constexpr int kGroupWaves = 8;
+constexpr int kGroupUnroll = 8;  // staged per wave: 8 x 64 candidates (8 waves: 4096)
+constexpr int kMaxKtWords = DMA_MAX_SK / DMA_BLOCK_K / 32;
+
+__global__ __launch_bounds__(kGroupWaves * 64) void group_lists_kernel(
+    const int32_t* __restrict__ cj, const int32_t* __restrict__ ce,
+    const int32_t* __restrict__ ccnt, int Sq, int q0, int n_tiles, int n_super, int cap,
+    int u_stride, int kt_stride, int32_t* __restrict__ u_idx, int32_t* __restrict__ u_cnt,
+    int32_t* __restrict__ u_nfull, int32_t* __restrict__ kt_idx, int32_t* __restrict__ kt_cnt) {
+  extern __shared__ uint32_t s_kt[];  // per tile of the group: key-tile bitmap of kw words
+  __shared__ int s_c[kGroupWaves][kSuperTiles][2];
+  __shared__ int s_sj[kGroupWaves][64 * kGroupUnroll];
+  __shared__ int s_se[kGroupWaves][64 * kGroupUnroll];
+  const int seg = blockIdx.y, T = blockIdx.x;
+  const int64_t gs = (int64_t)seg * n_super + T;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t0 = T * kSuperTiles;
+  const int ng = min(kSuperTiles, n_tiles - t0);  // tiles in this group
+  const int P_lo = q0 + t0 * kListRows;
+  const int Pend = q0 + Sq - 1;  // last position
+  const int nc = ccnt[gs];
+  const int32_t* Cj = cj + gs * cap;
+  const int32_t* Ce = ce + gs * cap;
+  const int kw = kt_idx ? (kt_stride + 31) / 32 : 0;
+  for (int k = threadIdx.x; k < ng * kw; k += kGroupWaves * 64) s_kt[k] = 0u;
+  const int L = ((nc + 64 * kGroupWaves - 1) / (64 * kGroupWaves)) * 64;
+  const int k0 = min(nc, wave * L), k1 = min(nc, k0 + L);
+  __syncthreads();
+
+  // Member and full tile masks of one candidate (bit i: tile t0 + i), in
+  // closed form: with r = j - P_lo, key j is in U of tile i iff e > j,
+  // j <= Pend and floor(r/64) <= i <= floor((e-1-P_lo)/64); every row of
+  // tile i keeps it iff also ceil(r/64) <= i and (e > Pend or
+  // i <= floor((e-64-P_lo)/64)).
+  auto span = [](int a, int b) -> uint32_t {  // bits a..b
+    return (a > b || b < 0) ? 0u : (uint32_t)((2ull << b) - (1ull << a));
+  };
+  auto masks = [&](int j, int e, bool valid, uint32_t& mm, uint32_t& mf) {
+    const int r = j - P_lo;
+    const bool any = valid && e > j && j <= Pend;
+    mm = any ? span(r < 0 ? 0 : r >> 6, min((e - 1 - P_lo) >> 6, ng - 1)) : 0u;
+    const int fb = e > Pend ? ng - 1 : min((e - 64 - P_lo) >> 6, ng - 1);
+    mf = mm & span(r <= 0 ? 0 : (r + 63) >> 6, fb);
+  };
+
+  // Each wave stages up to 64*kGroupUnroll of its candidates at a time in a
+  // private LDS region, with all global loads issued together, then walks
+  // them 64 at a time.
+  auto stage = [&](int kb) {
+    int jv[kGroupUnroll], ev[kGroupUnroll];
+#pragma unroll
+    for (int u = 0; u < kGroupUnroll; ++u) {  // clamped positions, validity applied later
+      const int k = min(kb + u * 64 + lane, k1 - 1);
+      jv[u] = Cj[k];
+      ev[u] = Ce[k];
+    }
+#pragma unroll
+    for (int u = 0; u < kGroupUnroll; ++u) {
+      s_sj[wave][u * 64 + lane] = jv[u];
+      s_se[wave][u * 64 + lane] = ev[u];
+    }
+  };
+
+  // Key tiles touched by tile i's members: runs of lanes with one key tile
+  // (candidates ascend), marked by the run's first lane when any lane of the
+  // run is a member.
+  auto run_mask = [&](int j, uint64_t& runm) -> bool {
+    const int kt = j >> 6;
+    const int ktp = __shfl_up(kt, 1);
+    const bool start = lane == 0 || ktp != kt;
+    const uint64_t rs = dma::ballot(start);
+    const uint64_t above = lane == 63 ? 0ull : rs & (~0ull << (lane + 1));
+    const uint64_t upto = above ? (above & (0ull - above)) - 1ull : ~0ull;  // bits below next start
+    runm = upto & (~0ull << lane);
+    return start;
+  };
+
+  // per-tile counts and offsets live in lane i of the wave (tile t0 + i)
+  int nfv = 0, npv = 0;
+  for (int kb = k0; kb < k1; kb += 64 * kGroupUnroll) {
+    stage(kb);
+    const int nb = min(kGroupUnroll, (k1 - kb + 63) / 64);
+#pragma unroll 1
+    for (int u = 0; u < nb; ++u) {
+      const int j = s_sj[wave][u * 64 + lane], e = s_se[wave][u * 64 + lane];
+      uint32_t mm, mf;
+      masks(j, e, kb + u * 64 + lane < k1, mm, mf);
+      uint64_t runm = 0ull;
+      const bool rstart = kw ? run_mask(j, runm) : false;
+#pragma unroll
+      for (int i = 0; i < kSuperTiles; ++i) {
+        const bool member = (mm >> i) & 1u, full = (mf >> i) & 1u;
+        const uint64_t bf = dma::ballot(full), bp = dma::ballot(member && !full);
+        nfv += lane == i ? (int)__popcll(bf) : 0;
+        npv += lane == i ? (int)__popcll(bp) : 0;
+        if (rstart && ((bf | bp) & runm)) atomicOr(&s_kt[i * kw + (j >> 11)], 1u << ((j >> 6) & 31));
+      }
+    }
+  }
+  if (lane < kSuperTiles) {
+    s_c[wave][lane][0] = nfv;
+    s_c[wave][lane][1] = npv;
   }
   __syncthreads();
-  int of = 0, op = 0, ok = 0, tf = 0, tp = 0, tk = 0;
-  float dmax = -INFINITY;
-#pragma unroll
-  for (int k = 0; k < kListWaves; ++k) {
-    if (k < wave) {
-      of += s_c[0][k];
-      op += s_c[1][k];
-      ok += s_c[2][k];
-    }
-    tf += s_c[0][k];
-    tp += s_c[1][k];
-    tk += s_c[2][k];
-    dmax = fmaxf(dmax, s_m[k]);
-  }
-  int32_t* out = u_idx + g * u_stride;
-  int32_t* kout = kt_idx ? kt_idx + g * kt_stride : nullptr;
-  for (int jb = j0; jb < j1; jb += 64 * kListUnroll) {
-    int e[kListUnroll];
-#pragma unroll
-    for (int u = 0; u < kListUnroll; ++u) {
-      const int j = jb + u * 64 + lane;
-      e[u] = j < j1 ? E[j] : 0;
-    }
-#pragma unroll
-    for (int u = 0; u < kListUnroll; ++u) {
-      const int j = jb + u * 64 + lane;
-      const bool member = j < j1 && e[u] > max(j, p_lo);
-      const bool full = member && j <= p_lo && e[u] > p_hi;
-      const uint64_t bf = dma::ballot(full), bp = dma::ballot(member && !full);
-      if (full) {
-        const int pos = of + dma::rank_below(bf);
-        if (pos < u_stride) out[pos] = j;
-      } else if (member) {
-        const int pos = op + dma::rank_below(bp);
-        if (pos < kPartialCap) s_part[pos] = j;
+  // lane i: this wave's offsets in tile i's two runs
+  int ofv = 0, opv = 0;
+  if (lane < kSuperTiles) {
+    int a = 0, bsum = 0, tf = 0, tp = 0;
+    for (int w2 = 0; w2 < kGroupWaves; ++w2) {
+      const int cf = s_c[w2][lane][0], cp = s_c[w2][lane][1];
+      if (w2 < wave) {
+        a += cf;
+        bsum += cp;
       }
-      of += __popcll(bf);
-      op += __popcll(bp);
-      if (bf | bp) {
-        if (lane == 0 && kout && ok < kt_stride) kout[ok] = (jb >> 6) + u;
-        ++ok;
-      }
+      tf += cf;
+      tp += cp;
+    }
+    ofv = a;
+    opv = tf + bsum;  // the partial run follows the full run
+    if (wave == 0 && lane < ng) {
+      const int64_t g = (int64_t)seg * n_tiles + t0 + lane;
+      u_cnt[g] = min(tf + tp, u_stride);
+      u_nfull[g] = min(tf, u_stride);
     }
   }
-  __syncthreads();
-  const int npart = min(tp, kPartialCap);
-  for (int k = threadIdx.x; k < npart; k += kListWaves * 64)
-    if (tf + k < u_stride) out[tf + k] = s_part[k];
-  if (threadIdx.x == 0) {
-    u_cnt[g] = min(tf + tp, u_stride);
-    u_nfull[g] = min(tf, u_stride);
-    u_dmax[g] = dmax;
-    if (kt_cnt) kt_cnt[g] = min(tk, kt_stride);
+  int32_t* out0 = u_idx + ((int64_t)seg * n_tiles + t0) * u_stride;
+  for (int kb = k0; kb < k1; kb += 64 * kGroupUnroll) {
+    // a wave whose candidates fit one round still has them staged
+    if (k1 - k0 > 64 * kGroupUnroll) stage(kb);
+    const int nb = min(kGroupUnroll, (k1 - kb + 63) / 64);
+#pragma unroll 1
+    for (int u = 0; u < nb; ++u) {
+      const int j = s_sj[wave][u * 64 + lane], e = s_se[wave][u * 64 + lane];
+      uint32_t mm, mf;
+      masks(j, e, kb + u * 64 + lane < k1, mm, mf);
+#pragma unroll
+      for (int i = 0; i < kSuperTiles; ++i) {
+        const bool member = (mm >> i) & 1u, full = (mf >> i) & 1u;
+        const uint64_t bf = dma::ballot(full), bp = dma::ballot(member && !full);
+        const int of_i = __builtin_amdgcn_readlane(ofv, i), op_i = __builtin_amdgcn_readlane(opv, i);
+        const int pos = full ? of_i + dma::rank_below(bf) : op_i + dma::rank_below(bp);
+        if (member && pos < u_stride) out0[(int64_t)i * u_stride + pos] = j;
+        ofv += lane == i ? (int)__popcll(bf) : 0;
+        opv += lane == i ? (int)__popcll(bp) : 0;
+      }
+    }
+  }
+  if (kw) {
+    __syncthreads();
+    // one wave per tile: ordered compaction of its key-tile bitmap
+    for (int i = wave; i < ng; i += kGroupWaves) {
+      const uint32_t* bm = s_kt + i * kw;
+      int32_t* kout = kt_idx + ((int64_t)seg * n_tiles + t0 + i) * kt_stride;
+      int at = 0;
+      for (int k = 0; k < kw; k += 64) {
+        const uint32_t x = k + lane < kw ? bm[k + lane] : 0u;
+        const int c = __popc(x);
+        int incl = c;  // inclusive prefix over the wave
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int y = __shfl_up(incl, o);
+          if (lane >= o) incl += y;
+        }
+        int pos = at + incl - c;
+        uint32_t y = x;
+        while (y) {
+          const int b = __builtin_ctz(y);
+          y &= y - 1;
+          if (pos < kt_stride) kout[pos] = (k + lane) * 32 + b;
+          ++pos;
+        }
+        at += __shfl(incl, 63);
+      }
+      if (lane == 0) kt_cnt[(int64_t)seg * n_tiles + t0 + i] = min(at, kt_stride);
+    }
   }
 }
 
@@ -488,11 +669,23 @@ __global__ __launch_bounds__(kDecThreads) void decode_select_kernel(
 
 // rank rows are padded to a multiple of 4 keys so each row starts 16-byte aligned
 static int64_t rank_stride(int64_t Sk) { return (Sk + 3) & ~int64_t(3); }
+static int64_t n_super_of(int64_t Sq) {
+  const int64_t nt = (Sq + kListRows - 1) / kListRows;
+  return (nt + kSuperTiles - 1) / kSuperTiles;
+}
+// candidates per tile group: keys kept at its first position plus keys born
+// inside it, rounded up to whole 16-byte rows
+static int64_t cand_cap(int64_t Sk, int64_t w) {
+  const int64_t c = std::min<int64_t>(Sk, w + kSuperTiles * kListRows);
+  return (c + 3) & ~int64_t(3);
+}
 
-size_t dma_topk_ws_bytes(int64_t BH, int64_t Sk) {
-  // two key buffers (ping-pong merges) + ranks
+size_t dma_topk_ws_bytes(int64_t BH, int64_t Sq, int64_t Sk, int64_t w) {
+  // two key buffers (ping-pong merges), ranks, then the candidate lists
   const size_t n = (size_t)BH * (size_t)Sk;
-  return n * 2 * sizeof(uint64_t) + (size_t)BH * rank_stride(Sk) * sizeof(int32_t) + 256;
+  const size_t ns = (size_t)BH * (size_t)n_super_of(Sq);
+  return n * 2 * sizeof(uint64_t) + (size_t)BH * rank_stride(Sk) * sizeof(int32_t) +
+         ns * (size_t)cand_cap(Sk, w) * 8 + ns * sizeof(int32_t) + 256;
 }
 
 hipError_t dma_launch_topk_prefill(const DmaTopkArgs& a, hipStream_t st) {
@@ -525,9 +718,24 @@ hipError_t dma_launch_topk_prefill(const DmaTopkArgs& a, hipStream_t st) {
                             (int)(nwords * sizeof(uint32_t)));
   hipLaunchKernelGGL(evict_kernel, dim3((Sk + R - 1) / R, BH), dim3(256),
                      (size_t)nwords * sizeof(uint32_t), st, src, rank, Sk, rs, (int)a.w, R, a.evict);
-  hipLaunchKernelGGL(lists_kernel, dim3((unsigned)a.n_tiles, BH), dim3(kListWaves * 64), 0, st, a.delta,
-                     a.evict, Sk, (int)a.Sq, (int)a.q0, (int)a.n_tiles, (int)a.u_stride,
-                     (int)a.kt_stride, a.u_idx, a.u_cnt, a.u_nfull, a.u_dmax, a.kt_idx, a.kt_cnt);
+  const int n_super = (int)n_super_of(a.Sq);
+  const int cap = (int)cand_cap(a.Sk, a.w);
+  int32_t* cj = rank + BH * rs;
+  int32_t* ce = cj + (size_t)BH * n_super * cap;
+  int32_t* ccnt = ce + (size_t)BH * n_super * cap;
+  hipLaunchKernelGGL(cand_kernel, dim3(n_super, BH), dim3(kListWaves * 64), 0, st, a.delta,
+                     a.evict, Sk, (int)a.Sq, (int)a.q0, n_super, (int)a.n_tiles, cap, cj, ce, ccnt,
+                     a.u_dmax);
+  const size_t kt_lds =
+      a.kt_idx ? (size_t)kSuperTiles * ((a.kt_stride + 31) / 32) * sizeof(uint32_t) : 0;
+  if (kt_lds > (size_t)kSuperTiles * kMaxKtWords * sizeof(uint32_t)) return hipErrorInvalidValue;
+  if (kt_lds > 0)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&group_lists_kernel),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kt_lds);
+  hipLaunchKernelGGL(group_lists_kernel, dim3(n_super, BH), dim3(kGroupWaves * 64), kt_lds, st,
+                     cj, ce, ccnt, (int)a.Sq, (int)a.q0, (int)a.n_tiles, n_super, cap,
+                     (int)a.u_stride, (int)a.kt_stride, a.u_idx, a.u_cnt, a.u_nfull, a.kt_idx,
+                     a.kt_cnt);
   return hipGetLastError();
 }
 
