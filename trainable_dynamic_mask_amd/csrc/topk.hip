@@ -133,19 +133,65 @@ __device__ __forceinline__ int block_excl_scan(int v, int* s_w, int& total) {
 }
 
 // ---------------------------------------------------------------- T2: eviction rows
-__global__ __launch_bounds__(256) void evict_kernel(const uint64_t* __restrict__ sorted,
-                                                    const int32_t* __restrict__ rank, int Sk,
-                                                    int rstride, int w, int R,
+// Bitmap of { j : rank[j] < rs } over nw 32-bit words in LDS: thread t
+// builds words [t*per, (t+1)*per) from its contiguous ranks with 16-byte
+// loads (unconditional, clamped into the sequence's padded rank row, so they
+// all issue before the first is used; indices >= Sk are masked).
+template <int NT>
+__device__ __forceinline__ void rank_bitmap(const int32_t* __restrict__ rk, int Sk, int rstride,
+                                            int rs, int nw, uint32_t* bm) {
+  const int per = (nw + NT - 1) / NT;
+  const int wlo = min(nw, (int)threadIdx.x * per), whi = min(nw, wlo + per);
+  const int jmax = rstride - 4;
+  for (int wi = wlo; wi < whi; wi += 2) {
+    uint32_t word[2] = {0u, 0u};
+    int4 v[2][8];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        v[u][q] = *reinterpret_cast<const int4*>(rk + min((wi + u) * 32 + q * 4, jmax));
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int j = (wi + u) * 32 + q * 4;
+        word[u] |= (j < Sk && v[u][q].x < rs ? 1u : 0u) << (q * 4);
+        word[u] |= (j + 1 < Sk && v[u][q].y < rs ? 1u : 0u) << (q * 4 + 1);
+        word[u] |= (j + 2 < Sk && v[u][q].z < rs ? 1u : 0u) << (q * 4 + 2);
+        word[u] |= (j + 3 < Sk && v[u][q].w < rs ? 1u : 0u) << (q * 4 + 3);
+      }
+      if (wi + u < whi) bm[wi + u] = word[u];
+    }
+  }
+}
+
+// T2a: checkpoint bitmaps { j : rank[j] < c * chk } for c = 1 .. n_chk-1,
+// nwr words each, so an eviction block needs at most chk-1 insertions.
+__global__ __launch_bounds__(256) void ckpt_kernel(const int32_t* __restrict__ rank, int Sk,
+                                                   int rstride, int chk, int n_chk, int nwr,
+                                                   uint32_t* __restrict__ ckpt) {
+  extern __shared__ __align__(16) uint32_t bm[];
+  const int seg = blockIdx.y, c = blockIdx.x + 1;
+  const int nw = (Sk + 31) >> 5;
+  rank_bitmap<256>(rank + (int64_t)seg * rstride, Sk, rstride, c * chk, nw, bm);
+  __syncthreads();
+  uint32_t* out = ckpt + ((int64_t)seg * n_chk + c) * nwr;
+  for (int k = threadIdx.x; k < nwr; k += 256) out[k] = k < nw ? bm[k] : 0u;
+}
+
+// T2b: eviction rows of the keys of ranks [r0, r0 + R), one wave walking them.
+__global__ __launch_bounds__(256) void evict_kernel(const uint64_t* __restrict__ sorted, int Sk,
+                                                    int w, int R, int chk, int n_chk, int nwr,
+                                                    const uint32_t* __restrict__ ckpt,
                                                     int32_t* __restrict__ evict) {
   // Dynamic LDS only, so the bitmap starts at byte 0 (8-byte aligned for the
   // 64-bit word reads): bitmap of indices in whole 64-bit words, then s_w, s_f.
   extern __shared__ __align__(16) uint32_t bm[];
-  const int nw64 = (Sk + 63) >> 6;
-  int* s_w = reinterpret_cast<int*>(bm + 2 * nw64);
+  int* s_w = reinterpret_cast<int*>(bm + nwr);
   int& s_f = s_w[4];
   const int seg = blockIdx.y;
   const uint64_t* K = sorted + (int64_t)seg * Sk;
-  const int32_t* rk = rank + (int64_t)seg * rstride;
   int32_t* E = evict + (int64_t)seg * Sk;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r0 = blockIdx.x * R, r1 = min(Sk, r0 + R);
@@ -153,60 +199,38 @@ __global__ __launch_bounds__(256) void evict_kernel(const uint64_t* __restrict__
   for (int r = r0 + (int)threadIdx.x; r < min(r1, w); r += 256) E[dma::index_of(K[r])] = Sk;
   const int rs = max(r0, w);
   if (rs >= r1) return;
-  const int nw = (Sk + 31) >> 5;
-  if (threadIdx.x == 0 && (nw & 1)) bm[nw] = 0u;  // pad to whole 64-bit words
 
-  // Bitmap of { j : rank[j] < rs }: thread t builds words [t*per, (t+1)*per) from
-  // its contiguous ranks with 16-byte loads, then selects the w-th smallest set
-  // bit from per-thread popcounts and one block scan.
+  // Bitmap of { j : rank[j] < rs }: the nearest checkpoint below rs, then
+  // the keys of the ranks in between, then the w-th smallest set bit from
+  // per-thread popcounts and one block scan.
+  const int c = rs / chk;
+  const uint32_t* cp = ckpt + ((int64_t)seg * n_chk + c) * nwr;
+  for (int k = threadIdx.x; k < nwr; k += 256) bm[k] = c > 0 ? cp[k] : 0u;
+  __syncthreads();
+  for (int r = c * chk + (int)threadIdx.x; r < rs; r += 256) {
+    const uint32_t x = dma::index_of(K[r]);
+    atomicOr(&bm[x >> 5], 1u << (x & 31));
+  }
+  __syncthreads();
+  const int nw = (Sk + 31) >> 5;
   const int per = (nw + 255) / 256;
   const int wlo = min(nw, (int)threadIdx.x * per), whi = min(nw, wlo + per);
   int cnt = 0;
-  for (int wi = wlo; wi < whi; wi += 2) {
-    uint32_t word[2] = {0u, 0u};
-    int4 v[2][8];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int j = (wi + u) * 32 + q * 4;
-        v[u][q] = (wi + u < whi && j + 3 < Sk) ? *reinterpret_cast<const int4*>(rk + j)
-                                               : make_int4(INT_MAX, INT_MAX, INT_MAX, INT_MAX);
-        if (wi + u < whi && j + 3 >= Sk) {  // ragged tail of the last word
-          v[u][q].x = j < Sk ? rk[j] : INT_MAX;
-          v[u][q].y = j + 1 < Sk ? rk[j + 1] : INT_MAX;
-          v[u][q].z = j + 2 < Sk ? rk[j + 2] : INT_MAX;
-        }
-      }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        word[u] |= (v[u][q].x < rs ? 1u : 0u) << (q * 4);
-        word[u] |= (v[u][q].y < rs ? 1u : 0u) << (q * 4 + 1);
-        word[u] |= (v[u][q].z < rs ? 1u : 0u) << (q * 4 + 2);
-        word[u] |= (v[u][q].w < rs ? 1u : 0u) << (q * 4 + 3);
-      }
-      if (wi + u < whi) {
-        bm[wi + u] = word[u];
-        cnt += __popc(word[u]);
-      }
-    }
-  }
+  for (int k = wlo; k < whi; ++k) cnt += __popc(bm[k]);
   int total;
-  const int before = block_excl_scan<256>(cnt, s_w, total);  // its barriers publish bm
+  const int before = block_excl_scan<256>(cnt, s_w, total);
   if (threadIdx.x == 0 && total < w) s_f = -1;  // unreachable: rs >= w ranks are set
   if (before < w && before + cnt >= w) {
     int need = w - before;
     for (int k = wlo; k < whi; ++k) {
       uint32_t x = bm[k];
-      const int c = __popc(x);
-      if (need <= c) {
+      const int cc = __popc(x);
+      if (need <= cc) {
         for (int q = 1; q < need; ++q) x &= x - 1;
         s_f = k * 32 + __builtin_ctz(x);
         break;
       }
-      need -= c;
+      need -= cc;
     }
   }
   __syncthreads();
@@ -214,36 +238,49 @@ __global__ __launch_bounds__(256) void evict_kernel(const uint64_t* __restrict__
 
   // Walk the block's ranks in order on one wave.  Everything the walk carries
   // is wave-uniform (scalar registers): f, the 64-bit bitmap word holding f
-  // (with this walk's own insertions), and its index.  Insertions below that
-  // word go to LDS; f only ever moves down, so words above it are never read
-  // again.  Each lane records the key and eviction row of one step; they are
-  // stored 64 at a time.
+  // and the word below it (both with this walk's own insertions), and f's
+  // word index.  Insertions further down go to LDS, which is read again only
+  // when f gets there; f only ever moves down.  Per 64 keys, a ballot of
+  // x < f picks the keys that can move f (f only decreases, so no other key
+  // can); they are visited in order and the others keep e = x.
   uint64_t* bm64 = reinterpret_cast<uint64_t*>(bm);
   int f = s_f;
   if (f < 0) return;  // unreachable (see above)
   int cwi = f >> 6;
   uint64_t cw = bm64[cwi];
+  uint64_t pw = cwi > 0 ? bm64[cwi - 1] : 0ull;
   for (int g0 = rs; g0 < r1; g0 += 64) {
     const int steps = min(64, r1 - g0);
-    const int xl = lane < steps ? (int)dma::index_of(K[g0 + lane]) : 0;  // one key per lane
-    int el = 0;
-    for (int s = 0; s < steps; ++s) {
-      const int x = __builtin_amdgcn_readlane(xl, s);
-      const int e = x < f ? f : x;
-      if (lane == s) el = e;
+    const int xl = lane < steps ? (int)dma::index_of(K[g0 + lane]) : INT_MAX;  // one key per lane
+    int el = xl;  // e = x unless the key moves f
+    uint64_t cand = dma::ballot(xl < f);
+    while (cand) {
+      const int sl = __builtin_ctzll(cand);
+      cand &= cand - 1ull;
+      const int x = __builtin_amdgcn_readlane(xl, sl);
       if (x < f) {
+        el = lane == sl ? f : el;  // e = f for this key
         const int xw = x >> 6;
+        const uint64_t bit = 1ull << (x & 63);
         if (xw == cwi) {
-          cw |= 1ull << (x & 63);
+          cw |= bit;
+        } else if (xw == cwi - 1) {
+          pw |= bit;
         } else if (lane == 0) {
           atomicOr(&bm[x >> 5], 1u << (x & 31));  // ds_or_b32: no return, no wait
         }
         // f <- largest set index below f (x itself qualifies)
         uint64_t m = cw & ((1ull << (f & 63)) - 1ull);
-        while (m == 0ull && cwi > 0) {
+        if (m == 0ull) {
+          cw = pw;
           --cwi;
-          cw = bm64[cwi];
           m = cw;
+          while (m == 0ull && cwi > 0) {
+            --cwi;
+            cw = bm64[cwi];
+            m = cw;
+          }
+          pw = cwi > 0 ? bm64[cwi - 1] : 0ull;
         }
         f = m ? (cwi << 6) + 63 - __builtin_clzll(m) : -1;  // -1: unreachable (w bits below f)
       }
@@ -680,12 +717,22 @@ static int64_t cand_cap(int64_t Sk, int64_t w) {
   return (c + 3) & ~int64_t(3);
 }
 
+// eviction checkpoints: every chk ranks, at most 64 per sequence
+static int64_t ckpt_every(int64_t Sk) {
+  const int64_t c = std::max<int64_t>(1024, (Sk + 63) / 64);
+  return (c + 1023) & ~int64_t(1023);
+}
+static int64_t ckpt_words(int64_t Sk) { return (((Sk + 31) >> 5) + 3) & ~int64_t(3); }
+
 size_t dma_topk_ws_bytes(int64_t BH, int64_t Sq, int64_t Sk, int64_t w) {
-  // two key buffers (ping-pong merges), ranks, then the candidate lists
+  // two key buffers (ping-pong merges), ranks, the candidate lists, then the
+  // eviction checkpoints
   const size_t n = (size_t)BH * (size_t)Sk;
   const size_t ns = (size_t)BH * (size_t)n_super_of(Sq);
+  const size_t nck = (size_t)BH * (size_t)((Sk + ckpt_every(Sk) - 1) / ckpt_every(Sk));
   return n * 2 * sizeof(uint64_t) + (size_t)BH * rank_stride(Sk) * sizeof(int32_t) +
-         ns * (size_t)cand_cap(Sk, w) * 8 + ns * sizeof(int32_t) + 256;
+         ns * (size_t)cand_cap(Sk, w) * 8 + ns * sizeof(int32_t) +
+         nck * (size_t)ckpt_words(Sk) * sizeof(uint32_t) + 256;
 }
 
 hipError_t dma_launch_topk_prefill(const DmaTopkArgs& a, hipStream_t st) {
@@ -711,18 +758,28 @@ hipError_t dma_launch_topk_prefill(const DmaTopkArgs& a, hipStream_t st) {
   }
   const int rs = (int)rank_stride(Sk);
   hipLaunchKernelGGL(rank_kernel, dim3((Sk + 255) / 256, BH), dim3(256), 0, st, src, Sk, rs, rank);
-  const int R = Sk > 16384 ? 512 : 256;
-  const int nwords = ((Sk + 63) / 64) * 2 + 8;  // bitmap + s_w[4], s_f (padded)
-  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&evict_kernel),
-                            hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)(nwords * sizeof(uint32_t)));
-  hipLaunchKernelGGL(evict_kernel, dim3((Sk + R - 1) / R, BH), dim3(256),
-                     (size_t)nwords * sizeof(uint32_t), st, src, rank, Sk, rs, (int)a.w, R, a.evict);
   const int n_super = (int)n_super_of(a.Sq);
   const int cap = (int)cand_cap(a.Sk, a.w);
   int32_t* cj = rank + BH * rs;
   int32_t* ce = cj + (size_t)BH * n_super * cap;
   int32_t* ccnt = ce + (size_t)BH * n_super * cap;
+  uint32_t* ckpt = reinterpret_cast<uint32_t*>(ccnt + (size_t)BH * n_super);
+  const int chk = (int)ckpt_every(Sk);
+  const int n_chk = (Sk + chk - 1) / chk;
+  const int nwr = (int)ckpt_words(Sk);
+  const size_t bm_bytes = (size_t)nwr * sizeof(uint32_t);
+  if (n_chk > 1) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&ckpt_kernel),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)bm_bytes);
+    hipLaunchKernelGGL(ckpt_kernel, dim3(n_chk - 1, BH), dim3(256), bm_bytes, st, rank, Sk, rs,
+                       chk, n_chk, nwr, ckpt);
+  }
+  const int R = 64;
+  const size_t ev_lds = bm_bytes + 8 * sizeof(int);  // bitmap, then s_w[4], s_f (padded)
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&evict_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)ev_lds);
+  hipLaunchKernelGGL(evict_kernel, dim3((Sk + R - 1) / R, BH), dim3(256), ev_lds, st, src, Sk,
+                     (int)a.w, R, chk, n_chk, nwr, ckpt, a.evict);
   hipLaunchKernelGGL(cand_kernel, dim3(n_super, BH), dim3(kListWaves * 64), 0, st, a.delta,
                      a.evict, Sk, (int)a.Sq, (int)a.q0, n_super, (int)a.n_tiles, cap, cj, ce, ccnt,
                      a.u_dmax);
