@@ -11,11 +11,12 @@
 //   T1  sort the keys by the 64-bit composite (delta order, reversed index):
 //       bitonic sort of 4096-key chunks in LDS, then merge-path merges;
 //   T1b rank[j] = position of key j in that order;
-//   T2  eviction rows: ranks are cut into blocks; a block builds the bitmap of
-//       the indices of all better-ranked keys, selects its w-th smallest set
-//       bit b, then walks its own ranks in order with one wave: each key gets
-//       e = max(j, b) and, when j < b, b steps down to the previous set bit.
-//       The wave keeps a 2048-bit window of the bitmap in registers;
+//   T2  eviction rows: ranks are cut into blocks of 64; a block builds the
+//       bitmap of the indices of all better-ranked keys (a checkpoint bitmap
+//       kept every 1024 ranks plus the keys in between), selects its w-th
+//       smallest set bit b, then walks its own ranks in order with one wave:
+//       each key gets e = max(j, b) and, when j < b, b steps down to the
+//       previous set bit;
 //   T3  per 64-row query tile: the union of the rows' keep sets (keys with
 //       e_j > max(j, tile start) and j <= tile end), the keys every row keeps
 //       first, the natural key tiles touched, and the largest delta; built
