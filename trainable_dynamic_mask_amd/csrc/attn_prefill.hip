@@ -486,8 +486,9 @@ __global__ __launch_bounds__(NH * 128, 1) void attn_prefill_bf16_kernel(DmaAttnA
     sm.bias[sf_][lane] = pad_ ? -INFINITY : (sm.draw[sr_][lane] - dmax) * bias_div; \
   } while (0)
 
-  // prologue: list entries of chunks 0..4, delta of chunks 0..2, K(0), the
-  // mask and bias of chunk 0; every load of it has landed when it ends
+  // prologue: list entries of chunks 0..4, then delta of chunks 0..2
+  // together with K(0), then the mask and bias of chunk 0; every load of it
+  // has landed when it ends (two load latencies in a row)
   if (wave == 0) {
 #pragma unroll
     for (int x = 0; x < 5; ++x) DMA_LIST(x);
@@ -503,7 +504,7 @@ __global__ __launch_bounds__(NH * 128, 1) void attn_prefill_bf16_kernel(DmaAttnA
       DMA_DELTA(x, jj);
     }
   }
-  phase_barrier<0>();
+  phase_barrier<-1>();  // the list entries are visible; delta is still in flight
   int kr[16 / NW], vr[16 / NW];
   gather_rows<NW>(kr, sm, 0, wave, lane);
   gather_tile<NW, false>(lds_k, kr, Kg, rowb, wave, lane);

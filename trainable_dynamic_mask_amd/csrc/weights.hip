@@ -77,9 +77,22 @@ __global__ __launch_bounds__(256) void weights_kernel(const T* __restrict__ V, i
   float* sout = smem + C * HB;      // [HB][kRowsPerBlock]
   const int b = blockIdx.y;
   const int j0 = blockIdx.x * kRowsPerBlock;
-  for (int i = threadIdx.x; i < C * HB; i += blockDim.x) {
-    const int c = i / HB, h = i % HB;
-    Ds[(h * EPC + c % EPC) * NC + c / EPC] = (h0 + h < Hkv) ? Delta[(int64_t)c * Hkv + h0 + h] : 0.f;
+  // 8 loads per thread in flight at a time (clamped addresses, masked after)
+  constexpr int kFill = 8;
+  for (int i0 = threadIdx.x; i0 < C * HB; i0 += 256 * kFill) {
+    float v[kFill];
+#pragma unroll
+    for (int u = 0; u < kFill; ++u) {
+      const int i = min(i0 + u * 256, C * HB - 1);
+      const int c = i / HB, h = i % HB;
+      v[u] = Delta[(int64_t)c * Hkv + min(h0 + h, Hkv - 1)];
+    }
+#pragma unroll
+    for (int u = 0; u < kFill; ++u) {
+      const int i = i0 + u * 256;
+      const int c = i / HB, h = i % HB;
+      if (i < C * HB) Ds[(h * EPC + c % EPC) * NC + c / EPC] = (h0 + h < Hkv) ? v[u] : 0.f;
+    }
   }
   __syncthreads();
 
@@ -96,9 +109,9 @@ __global__ __launch_bounds__(256) void weights_kernel(const T* __restrict__ V, i
       uint4 raw[kRowsPerGroup];
 #pragma unroll
       for (int r = 0; r < kRowsPerGroup; ++r) {
-        const int j = jb + r;
-        raw[r] = (j < Sk) ? *reinterpret_cast<const uint4*>(Vb + (int64_t)j * ss + k * EPC)
-                          : make_uint4(0, 0, 0, 0);
+        // rows past the end read the last row; their sums are not written
+        const int j = min(jb + r, Sk - 1);
+        raw[r] = *reinterpret_cast<const uint4*>(Vb + (int64_t)j * ss + k * EPC);
       }
 #pragma unroll
       for (int e = 0; e < EPC; ++e) {
