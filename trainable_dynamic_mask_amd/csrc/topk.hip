@@ -9,8 +9,11 @@
 // index among the keys that beat j (Sk when fewer than w beat it).  The mask
 // is built from that form in four steps per (batch, kv head) sequence:
 //   T1  sort the keys by the 64-bit composite (delta order, reversed index):
-//       bitonic sort of 4096-key chunks in LDS, then merge-path merges;
-//   T1b rank[j] = position of key j in that order;
+//       bitonic sort of 4096-key chunks (registers, lane shuffles and LDS),
+//       then merge-path merges;
+//   T1b rank[j] = position of key j in that order; up to four chunks skip the
+//       merges: a key's rank is the sum over the chunks of the keys that beat
+//       it, found by binary searches over the chunks held in LDS;
 //   T2  eviction rows: ranks are cut into blocks of 64; a block builds the
 //       bitmap of the indices of all better-ranked keys (a checkpoint bitmap
 //       kept every 1024 ranks plus the keys in between), selects its w-th
@@ -33,41 +36,92 @@
 namespace {
 
 constexpr int kSortChunk = 4096;
-constexpr int kSortThreads = 1024;
+#ifndef DMA_SORT_PER
+#define DMA_SORT_PER 4
+#endif
+constexpr int kSortPer = DMA_SORT_PER;  // keys per thread: element i = thread * kSortPer + register
+constexpr int kSortThreads = kSortChunk / kSortPer;
+constexpr int kSortRegBits = kSortPer == 8 ? 3 : kSortPer == 4 ? 2 : 4;
 constexpr int kMergeItems = 8;
 constexpr int kListRows = 64;   // query rows per tile (Bq)
 
 // ---------------------------------------------------------------- T1: chunk sort
+__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
+  const int lo = __shfl_xor((int)(uint32_t)v, m);
+  const int hi = __shfl_xor((int)(uint32_t)(v >> 32), m);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+// Bitonic sort (descending) of a 4096-key chunk, in the form whose comparators
+// all point one way: phase k (block size 2, 4, ..., 4096) first pairs i with
+// its mirror i ^ (k-1) in the block, then with i ^ j for j = k/4, ..., 1, and
+// the lower index of every pair keeps the larger key.  Element i lives in
+// register i%8 of thread i/8, so pairs at distance < 8 stay inside a thread,
+// pairs that differ in bits 3..8 pair lanes of one wave, and only pairs that
+// differ in bits 9..11 cross waves, through LDS (two buffers, one barrier
+// each).  Every element is updated by its owner, which takes the larger or the
+// smaller of itself and its partner.
 __global__ __launch_bounds__(kSortThreads) void sort_chunk_kernel(const float* __restrict__ delta,
                                                                   int Sk,
                                                                   uint64_t* __restrict__ out) {
-  __shared__ uint64_t s[kSortChunk];
+  __shared__ uint64_t s[2][kSortChunk];
   const int seg = blockIdx.y;
   const int c0 = blockIdx.x * kSortChunk;
+  const int lane = threadIdx.x & 63;
+  const int base = threadIdx.x * kSortPer;
   const float* d = delta + (int64_t)seg * Sk;
-  for (int i = threadIdx.x; i < kSortChunk; i += kSortThreads) {
-    const int j = c0 + i;
-    s[i] = (j < Sk) ? dma::key_of(d[j], (uint32_t)j) : 0ull;  // 0 sorts after every real key
+  uint64_t a[kSortPer];
+#pragma unroll
+  for (int r = 0; r < kSortPer; ++r) {
+    const int j = c0 + base + r;
+    a[r] = (j < Sk) ? dma::key_of(d[j], (uint32_t)j) : 0ull;  // 0 sorts after every real key
   }
-  __syncthreads();
-  for (int k = 2; k <= kSortChunk; k <<= 1) {
-    for (int jj = k >> 1; jj > 0; jj >>= 1) {
-      for (int p = threadIdx.x; p < kSortChunk / 2; p += kSortThreads) {
-        const int i = ((p & ~(jj - 1)) << 1) | (p & (jj - 1));
-        const int l = i + jj;
-        const bool desc = (i & k) == 0;
-        const uint64_t a = s[i], b = s[l];
-        if ((a < b) == desc) {
-          s[i] = b;
-          s[l] = a;
+  int lds_stage = 0;  // LDS stages alternate buffers, so a buffer is rewritten
+                      // only after the barrier of the stage in between
+#pragma unroll
+  for (int m = 1; m <= 12; ++m) {
+#pragma unroll
+    for (int b = m - 1; b >= 0; --b) {
+      // partner = i ^ x; the pair's lower index has bit b clear
+      const int x = b == m - 1 ? (1 << m) - 1 : 1 << b;
+      if (b < kSortRegBits) {
+        // both elements belong to this thread
+#pragma unroll
+        for (int r = 0; r < kSortPer; ++r) {
+          if (r & (1 << b)) continue;
+          const uint64_t u = a[r], v = a[r ^ x];
+          const bool gt = u > v;
+          a[r] = gt ? u : v;
+          a[r ^ x] = gt ? v : u;
+        }
+      } else if (b < kSortRegBits + 6) {
+        // partner lane = lane ^ (x >> reg bits), partner register = r ^ (x % kSortPer)
+        const int lm = x >> kSortRegBits;
+        const bool lower = (lane & (1 << (b - kSortRegBits))) == 0;
+        uint64_t p[kSortPer];
+#pragma unroll
+        for (int r = 0; r < kSortPer; ++r) p[r] = shfl_xor64(a[r ^ (x & (kSortPer - 1))], lm);
+#pragma unroll
+        for (int r = 0; r < kSortPer; ++r) a[r] = ((a[r] > p[r]) == lower) ? a[r] : p[r];
+      } else {
+        uint64_t* sb = s[lds_stage & 1];
+        ++lds_stage;
+#pragma unroll
+        for (int r = 0; r < kSortPer; ++r) sb[base + r] = a[r];
+        __syncthreads();
+        const bool lower = (base & (1 << b)) == 0;
+#pragma unroll
+        for (int r = 0; r < kSortPer; ++r) {
+          const uint64_t p = sb[(base + r) ^ x];
+          a[r] = ((a[r] > p) == lower) ? a[r] : p;
         }
       }
-      __syncthreads();
     }
   }
   uint64_t* o = out + (int64_t)seg * Sk;
-  for (int i = threadIdx.x; i < kSortChunk; i += kSortThreads)
-    if (c0 + i < Sk) o[c0 + i] = s[i];
+#pragma unroll
+  for (int r = 0; r < kSortPer; ++r)
+    if (c0 + base + r < Sk) o[c0 + base + r] = a[r];
 }
 
 // ---------------------------------------------------------------- T1: merge
@@ -107,6 +161,80 @@ __global__ __launch_bounds__(256) void rank_kernel(const uint64_t* __restrict__ 
   if (r >= Sk) return;
   const uint32_t j = dma::index_of(sorted[(int64_t)seg * Sk + r]);
   rank[(int64_t)seg * rstride + j] = r;
+}
+
+// T1 + T1b for a sequence of at most four sorted 4096-key runs (up to 16K
+// keys), in place of the merges: the rank of a key is its position in its own
+// run plus, for each other run, the number of keys there that beat it (keys
+// are distinct, so this is a binary search).  A workgroup holds every run of
+// its sequence in LDS and ranks the keys of one run; it writes rank[j] and
+// the merged order.
+constexpr int kRankRunsMax = 4;
+constexpr int kRankRunsThreads = 256;
+constexpr int kRankRunsKeys = 1024;   // keys ranked per workgroup
+
+__global__ __launch_bounds__(kRankRunsThreads) void rank_runs_kernel(
+    const uint64_t* __restrict__ runs, int Sk, int rstride, int32_t* __restrict__ rank,
+    uint64_t* __restrict__ merged) {
+  extern __shared__ __align__(16) uint64_t s_runs[];
+  const int seg = blockIdx.y;
+  const int nr = (Sk + kSortChunk - 1) / kSortChunk;
+  const uint64_t* src = runs + (int64_t)seg * Sk;
+  // all runs of the sequence into LDS; a sequence starts 8-byte aligned only
+  // (odd Sk), so 8-byte loads, all of a thread's in flight at once
+  constexpr int kFill = kRankRunsMax * kSortChunk / kRankRunsThreads;
+  for (int i0 = threadIdx.x; i0 < Sk; i0 += kRankRunsThreads * kFill) {
+    uint64_t v[kFill];
+#pragma unroll
+    for (int u = 0; u < kFill; ++u) v[u] = src[min(i0 + u * kRankRunsThreads, Sk - 1)];
+#pragma unroll
+    for (int u = 0; u < kFill; ++u)
+      if (i0 + u * kRankRunsThreads < Sk) s_runs[i0 + u * kRankRunsThreads] = v[u];
+  }
+  __syncthreads();
+
+  // rank = sum over all runs (its own included, where the count is its
+  // position) of the keys that beat it; the 4 keys x 4 runs searches of a
+  // thread advance together, one halving step at a time
+  constexpr int kU = kRankRunsKeys / kRankRunsThreads;
+  const int r = blockIdx.x / (kSortChunk / kRankRunsKeys);
+  const int q0 = (blockIdx.x % (kSortChunk / kRankRunsKeys)) * kRankRunsKeys + threadIdx.x;
+  const int len_r = min(kSortChunk, Sk - r * kSortChunk);
+  uint64_t x[kU];
+  int cnt[kU][kRankRunsMax];
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    x[u] = s_runs[r * kSortChunk + min(q0 + u * kRankRunsThreads, len_r - 1)];
+#pragma unroll
+    for (int o = 0; o < kRankRunsMax; ++o) cnt[u][o] = 0;
+  }
+#pragma unroll
+  for (int step = kSortChunk; step > 0; step >>= 1) {
+#pragma unroll
+    for (int o = 0; o < kRankRunsMax; ++o) {
+      // no branch on the run count, so all 16 reads of a step are in flight
+      // together; a missing run (n = 0) reads key 0 and never counts
+      const int n = o < nr ? min(kSortChunk, Sk - o * kSortChunk) : 0;
+      const uint64_t* A = s_runs + (o < nr ? o * kSortChunk : 0);
+      uint64_t v[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) v[u] = A[max(min(cnt[u][o] + step, n), 1) - 1];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int i = cnt[u][o] + step;
+        cnt[u][o] = (i <= n && v[u] > x[u]) ? i : cnt[u][o];
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    if (q0 + u * kRankRunsThreads >= len_r) continue;
+    int pos = 0;
+#pragma unroll
+    for (int o = 0; o < kRankRunsMax; ++o) pos += cnt[u][o];
+    rank[(int64_t)seg * rstride + dma::index_of(x[u])] = pos;
+    merged[(int64_t)seg * Sk + pos] = x[u];
+  }
 }
 
 // Exclusive prefix sum over a block of NT threads (NT/64 waves); also returns the total.
@@ -749,16 +877,26 @@ hipError_t dma_launch_topk_prefill(const DmaTopkArgs& a, hipStream_t st) {
                      kA);
   uint64_t* src = kA;
   uint64_t* dst = kB;
-  for (int L = kSortChunk; L < Sk; L <<= 1) {
-    const int nthr = (Sk + kMergeItems - 1) / kMergeItems;
-    hipLaunchKernelGGL(merge_kernel, dim3((nthr + 255) / 256, BH), dim3(256), 0, st, src, dst, Sk,
-                       L);
-    uint64_t* t = src;
-    src = dst;
-    dst = t;
-  }
   const int rs = (int)rank_stride(Sk);
-  hipLaunchKernelGGL(rank_kernel, dim3((Sk + 255) / 256, BH), dim3(256), 0, st, src, Sk, rs, rank);
+  if (nch > 1 && nch <= kRankRunsMax) {
+    const size_t lds = (size_t)Sk * sizeof(uint64_t);
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&rank_runs_kernel),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipLaunchKernelGGL(rank_runs_kernel, dim3(nch * (kSortChunk / kRankRunsKeys), BH),
+                       dim3(kRankRunsThreads), lds, st, src, Sk, rs, rank, dst);
+    src = dst;
+  } else {
+    for (int L = kSortChunk; L < Sk; L <<= 1) {
+      const int nthr = (Sk + kMergeItems - 1) / kMergeItems;
+      hipLaunchKernelGGL(merge_kernel, dim3((nthr + 255) / 256, BH), dim3(256), 0, st, src, dst,
+                         Sk, L);
+      uint64_t* t = src;
+      src = dst;
+      dst = t;
+    }
+    hipLaunchKernelGGL(rank_kernel, dim3((Sk + 255) / 256, BH), dim3(256), 0, st, src, Sk, rs,
+                       rank);
+  }
   const int n_super = (int)n_super_of(a.Sq);
   const int cap = (int)cand_cap(a.Sk, a.w);
   int32_t* cj = rank + BH * rs;
