@@ -148,6 +148,25 @@ dma_status dma_topk_mask(const float* delta, int64_t B, int64_t Hkv, int64_t Sq,
                          size_t ws_bytes, void* stream);
 
 /*
+ * Step 2, one decode step (DMA blog, m_t equation; the keep set of position
+ * p is the top w of keys 0..p).  Keep sets nest, so keep(p) is the top w of
+ * keep(p-1) plus key p: key p enters exactly when it beats the worst kept key
+ * (smaller delta, or equal delta and higher index), which it replaces.
+ * delta  float [B, Hkv, Sk]; key p = Sk-1 is the new key.
+ * mask   on entry the one-row lists of position Sk-2 over keys 0..Sk-2, as
+ *        written by dma_topk_mask(delta, B, Hkv, 1, Sk-1, Sk-2, w) or by a
+ *        previous call of this function; on return those of position Sk-1,
+ *        identical to what dma_topk_mask(delta, B, Hkv, 1, Sk, Sk-1, w) writes.
+ *        u_idx [B*Hkv, w], u_cnt, u_nfull, u_dmax [B*Hkv]; kt_idx and kt_cnt
+ *        must be NULL (key-tile lists are not maintained).
+ * Requires Sk-1 >= w (the list is full, stride w) and Sk <= 32768; sequences
+ * whose list does not hold w keys are left unchanged.  Updated in place on
+ * the stream; O(w) work per sequence instead of a selection over all Sk keys.
+ */
+dma_status dma_decode_keep_append(const float* delta, int64_t B, int64_t Hkv, int64_t Sk,
+                                  int64_t w, const dma_mask* mask, void* stream);
+
+/*
  * Step 3: masked attention (DMA blog, o_t equation with additive mask).
  *   For query row i of head hq (position p = q_offset + i, kv head h):
  *   s_j = scale * (q . k_j) + delta[b,h,j] over the keys j row p keeps,

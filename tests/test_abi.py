@@ -38,7 +38,7 @@ def test_exports_every_declared_function(lib):
 def test_status_strings_and_versions(lib):
     assert lib.dma_status_string(0) == b"ok"
     assert lib.dma_status_string(3) == b"workspace too small"
-    assert lib.dma_abi_version() == 2
+    assert lib.dma_abi_version() == 3
     bq, bk = ctypes.c_int32(), ctypes.c_int32()
     lib.dma_tile_sizes(ctypes.byref(bq), ctypes.byref(bk))
     assert (bq.value, bk.value) == (64, 64)
@@ -115,6 +115,22 @@ def test_topk_validation(lib):
     assert lib.dma_topk_mask(FAKE, 1, 2, 16, 16, 0, 4, ctypes.byref(m), FAKE, 1 << 30, None) == INVALID
     m = DmaMask(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)       # kt_idx without kt_cnt
     assert lib.dma_topk_mask(FAKE, 1, 2, 16, 16, 0, 4, ctypes.byref(m), FAKE, 1 << 30, None) == INVALID
+
+
+def _append(lib, B=2, Hkv=2, Sk=17, w=16, kt=False, mask=True, delta=FAKE):
+    m = DmaMask(None, FAKE, FAKE, FAKE, FAKE, FAKE if kt else None, FAKE if kt else None)
+    return lib.dma_decode_keep_append(delta, B, Hkv, Sk, w, ctypes.byref(m) if mask else None,
+                                      None)
+
+
+def test_decode_append_validation(lib):
+    assert _append(lib, Sk=16) == INVALID                    # keep(Sk-2) would not be full
+    assert _append(lib, w=0) == INVALID
+    assert _append(lib, kt=True) == INVALID                  # key-tile lists are not kept
+    assert _append(lib, mask=False) == INVALID
+    assert _append(lib, delta=None) == INVALID
+    assert _append(lib, Sk=40000, w=16) == UNSUPPORTED       # beyond the one-row limit
+    assert _append(lib, B=0) == OK                           # empty: nothing launched
 
 
 def _attn(lib, t=1, B=1, Sq=16, Sk=16, Hq=4, Hkv=2, D=128, qs=None, ks=None, q0=0, w=4,

@@ -133,6 +133,25 @@ def topk_mask(delta: torch.Tensor, Sq: int, q_offset: int, w: int, kt_lists: boo
     return mask
 
 
+def decode_keep_append(delta: torch.Tensor, mask: Mask) -> Mask:
+    """One decode step of a one-row keep set: `mask` holds keep(Sk-2) over keys
+    0..Sk-2 (built with kt_lists=False); delta [B,Hkv,Sk] adds key Sk-1.  The
+    lists are updated in place to keep(Sk-1) and `mask` describes that row."""
+    _need_cuda(delta)
+    delta = delta.contiguous()
+    B, Hkv, Sk = delta.shape
+    if mask.Sq != 1 or mask.kt_idx is not None or (B, Hkv) != (mask.B, mask.Hkv) \
+            or Sk != mask.Sk + 1:
+        raise ValueError("decode_keep_append needs a one-row mask without key-tile lists "
+                         "over one key fewer than delta")
+    ms = mask.cstruct()
+    check("dma_decode_keep_append", load().dma_decode_keep_append(
+        _ptr(delta), B, Hkv, Sk, mask.w, ctypes.byref(ms), _stream(delta.device)))
+    mask.Sk, mask.q_offset = Sk, Sk - 1
+    mask.dims = mask_dims(B, Hkv, 1, Sk, Sk - 1, mask.w)
+    return mask
+
+
 def attn_fwd(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, delta: torch.Tensor, mask: Mask,
              scale: Optional[float] = None, return_lse: bool = False,
              out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):

@@ -33,7 +33,7 @@ class DmaMaskDims(ctypes.Structure):
 
 EXPORTS = ["dma_status_string", "dma_abi_version", "dma_tile_sizes", "dma_mask_dims_for",
            "dma_topk_workspace_bytes", "dma_attn_workspace_bytes", "dma_weights",
-           "dma_topk_mask", "dma_attn_fwd"]
+           "dma_topk_mask", "dma_decode_keep_append", "dma_attn_fwd"]
 
 _lib = None
 
@@ -71,6 +71,8 @@ def load():
     lib.dma_topk_mask.argtypes = [_P, _I64, _I64, _I64, _I64, _I64, _I64,
                                   ctypes.POINTER(DmaMask), _P, _SZ, _P]
     lib.dma_topk_mask.restype = ctypes.c_int
+    lib.dma_decode_keep_append.argtypes = [_P, _I64, _I64, _I64, _I64, ctypes.POINTER(DmaMask), _P]
+    lib.dma_decode_keep_append.restype = ctypes.c_int
     lib.dma_attn_fwd.argtypes = [_P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _I64, _I64, _I64,
                                  ctypes.POINTER(_I64), ctypes.POINTER(_I64), _I64, _I64, _P,
                                  ctypes.POINTER(DmaMask), ctypes.c_float, _P, _P, _P, _SZ, _P]

@@ -11,7 +11,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 2;
+constexpr int kAbiVersion = 3;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -148,6 +148,22 @@ dma_status dma_topk_mask(const float* delta, int64_t B, int64_t Hkv, int64_t Sq,
   if (ws_bytes < need || !ws) return DMA_ERR_WORKSPACE;
   if (!aligned16(ws)) return DMA_ERR_INVALID_ARG;
   return hip_status(dma_launch_topk_prefill(a, s));
+}
+
+dma_status dma_decode_keep_append(const float* delta, int64_t B, int64_t Hkv, int64_t Sk,
+                                  int64_t w, const dma_mask* mask, void* stream) {
+  if (B < 0 || Hkv < 1 || w < 1 || Sk < 0) return DMA_ERR_INVALID_ARG;
+  if (!mask) return DMA_ERR_INVALID_ARG;
+  if (Sk - 1 < w) return DMA_ERR_INVALID_ARG;  // keep(Sk-2) must hold w keys
+  if (Sk > 32768) return DMA_ERR_UNSUPPORTED;    // the one-row limit of dma_topk_mask
+  if (B * Hkv > 65535) return DMA_ERR_UNSUPPORTED;
+  if (mask->kt_idx || mask->kt_cnt) return DMA_ERR_INVALID_ARG;  // key-tile lists are not kept
+  if (B == 0) return DMA_OK;
+  if (!delta || !mask->u_idx || !mask->u_cnt || !mask->u_nfull || !mask->u_dmax)
+    return DMA_ERR_INVALID_ARG;
+  return hip_status(dma_launch_decode_append(delta, B * Hkv, Sk, w, mask->u_idx, mask->u_cnt,
+                                             mask->u_nfull, mask->u_dmax,
+                                             static_cast<hipStream_t>(stream)));
 }
 
 dma_status dma_attn_fwd(const void* Q, const void* K, const void* V, dma_dtype t, int64_t B,

@@ -83,6 +83,9 @@ struct DmaTopkArgs {
 };
 hipError_t dma_launch_topk_prefill(const DmaTopkArgs& a, hipStream_t st);
 hipError_t dma_launch_topk_decode(const DmaTopkArgs& a, hipStream_t st);
+hipError_t dma_launch_decode_append(const float* delta, int64_t BH, int64_t Sk, int64_t w,
+                                   int32_t* u_idx, int32_t* u_cnt, int32_t* u_nfull,
+                                   float* u_dmax, hipStream_t st);
 size_t dma_topk_ws_bytes(int64_t BH, int64_t Sq, int64_t Sk, int64_t w);
 
 struct DmaAttnArgs {

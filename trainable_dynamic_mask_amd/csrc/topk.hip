@@ -831,6 +831,79 @@ __global__ __launch_bounds__(kDecThreads) void decode_select_kernel(
   }
 }
 
+// One decode step of the keep set (Hugging Face blog "Trainable Dynamic Mask
+// Sparse Attention", section "Mask Combination with Causal Constraints": the
+// keep set of position p is the top w of keys 0..p).  Because the sets nest,
+// keep(p) is the top w of keep(p-1) plus key p: once keep(p-1) holds w keys,
+// key p enters exactly when it beats the worst kept key, which it then
+// replaces.  One workgroup per sequence: the w-entry ascending list goes to
+// LDS, the worst entry (smallest 64-bit key) is found by a block reduction,
+// and when key p enters the entries after the worst one shift down by one
+// and p (the largest index) goes last.
+constexpr int kAppThreads = 256;
+
+__global__ __launch_bounds__(kAppThreads) void decode_append_kernel(
+    const float* __restrict__ delta, int Sk, int w, int32_t* __restrict__ u_idx,
+    int32_t* __restrict__ u_cnt, int32_t* __restrict__ u_nfull, float* __restrict__ u_dmax) {
+  extern __shared__ __align__(16) int32_t s_list[];  // [w]
+  __shared__ uint64_t s_k[kAppThreads / 64];
+  __shared__ float s_m[kAppThreads / 64];
+  __shared__ int s_pos;
+  const int seg = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float* Dl = delta + (int64_t)seg * Sk;
+  int32_t* list = u_idx + (int64_t)seg * w;
+  if (u_cnt[seg] != w) return;  // keep(p-1) must be full: the caller's precondition
+  const int p = Sk - 1;
+  uint64_t kmin = ~0ull;
+  int pmin = 0;
+  float dmax = -INFINITY;
+  for (int i = tid; i < w; i += kAppThreads) {
+    const int j = list[i];
+    s_list[i] = j;
+    const float d = Dl[j];
+    const uint64_t k = dma::key_of(d, (uint32_t)j);
+    if (k < kmin) {
+      kmin = k;
+      pmin = i;
+    }
+    dmax = fmaxf(dmax, d);
+  }
+  // block minimum of the keys (all distinct) and maximum of delta
+  uint64_t wk = kmin;
+  float wm = dmax;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint64_t ok = ((uint64_t)(uint32_t)__shfl_xor((int)(wk >> 32), o) << 32) |
+                        (uint32_t)__shfl_xor((int)(uint32_t)wk, o);
+    wk = ok < wk ? ok : wk;
+    wm = fmaxf(wm, __shfl_xor(wm, o));
+  }
+  if (lane == 0) {
+    s_k[wave] = wk;
+    s_m[wave] = wm;
+  }
+  __syncthreads();
+  uint64_t gk = s_k[0];
+  float gm = s_m[0];
+  for (int k = 1; k < kAppThreads / 64; ++k) {
+    gk = s_k[k] < gk ? s_k[k] : gk;
+    gm = fmaxf(gm, s_m[k]);
+  }
+  if (kmin == gk) s_pos = pmin;  // exactly one thread holds the minimum
+  __syncthreads();
+  const float dp = Dl[p];
+  const bool enters = dma::key_of(dp, (uint32_t)p) > gk;
+  if (enters) {
+    const int pm = s_pos;
+    for (int i = pm + tid; i < w; i += kAppThreads) list[i] = i + 1 < w ? s_list[i + 1] : p;
+  }
+  if (tid == 0) {
+    u_nfull[seg] = w;
+    u_dmax[seg] = enters ? (w == 1 ? dp : fmaxf(gm, dp)) : gm;
+  }
+}
+
 }  // namespace
 
 // rank rows are padded to a multiple of 4 keys so each row starts 16-byte aligned
@@ -932,6 +1005,17 @@ hipError_t dma_launch_topk_prefill(const DmaTopkArgs& a, hipStream_t st) {
                      cj, ce, ccnt, (int)a.Sq, (int)a.q0, (int)a.n_tiles, n_super, cap,
                      (int)a.u_stride, (int)a.kt_stride, a.u_idx, a.u_cnt, a.u_nfull, a.kt_idx,
                      a.kt_cnt);
+  return hipGetLastError();
+}
+
+hipError_t dma_launch_decode_append(const float* delta, int64_t BH, int64_t Sk, int64_t w,
+                                   int32_t* u_idx, int32_t* u_cnt, int32_t* u_nfull,
+                                   float* u_dmax, hipStream_t st) {
+  const size_t lds = (size_t)w * sizeof(int32_t);
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_append_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipLaunchKernelGGL(decode_append_kernel, dim3((unsigned)BH), dim3(kAppThreads), lds, st, delta,
+                     (int)Sk, (int)w, u_idx, u_cnt, u_nfull, u_dmax);
   return hipGetLastError();
 }
 
