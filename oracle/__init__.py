@@ -11,6 +11,8 @@ Functions (all inputs are copied to contiguous numpy arrays first):
   mask(delta, q0, Sq, w, Bq, Bk)            -> dict(evict, row_cnt, u_cnt, u_idx, kt_cnt, kt_idx)
   attn_rows(Q, K, V, delta, q0, w, rows, scale=None) -> (O [n, D], lse [n])
   attn(Q, K, V, delta, q0, w, scale=None)   -> (O [B, Sq, Hq, D], lse [B, Hq, Sq])
+  attn_bwd(Q, K, V, delta, dO, q0, w, scale=None) -> (dQ, dK, dV, ddelta) float64
+  weights_bwd(V, Delta, A, ddelta)          -> (dV [B, Sk, Hkv, D], dDelta, dA) float64
 """
 import ctypes
 import os
@@ -42,6 +44,11 @@ def _load():
     lib.orc_attn_rows.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _I64,
                                   _I64, ctypes.c_double, _P, _I64, _P, _P]
     lib.orc_attn_rows.restype = None
+    lib.orc_attn_bwd.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _I64,
+                                 _I64, ctypes.c_double, _P, _P, _P, _P]
+    lib.orc_attn_bwd.restype = None
+    lib.orc_weights_bwd.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _P, _P]
+    lib.orc_weights_bwd.restype = None
     _lib = lib
     return lib
 
@@ -148,3 +155,41 @@ def attn(Q, K, V, delta, q0, w, scale=None):
     rows = np.stack([b.ravel(), h.ravel(), i.ravel()], 1)
     O, lse = attn_rows(Q, K, V, delta, q0, w, rows, scale)
     return (O.reshape(B, Hq, Sq, D).transpose(0, 2, 1, 3).copy(), lse.reshape(B, Hq, Sq))
+
+
+def attn_bwd(Q, K, V, delta, dO, q0, w, scale=None):
+    """Gradients of sum(dO * O) with the keep sets held fixed:
+    dQ [B,Sq,Hq,D], dK and dV [B,Sk,Hkv,D], ddelta [B,Hkv,Sk] (float64)."""
+    lib = _load()
+    Qn, Kn, Vn, gn = (_np(x, np.float32) for x in (Q, K, V, dO))
+    d = _np(delta, np.float64)
+    B, Sq, Hq, D = Qn.shape
+    _, Sk, Hkv, _ = Kn.shape
+    assert d.shape == (B, Hkv, Sk) and gn.shape == Qn.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    dQ = np.empty((B, Sq, Hq, D), np.float64)
+    dK = np.empty((B, Sk, Hkv, D), np.float64)
+    dV = np.empty((B, Sk, Hkv, D), np.float64)
+    dd = np.empty((B, Hkv, Sk), np.float64)
+    lib.orc_attn_bwd(_ptr(Qn), _ptr(Kn), _ptr(Vn), _ptr(d), _ptr(gn), B, Sq, Sk, Hq, Hkv, D, q0,
+                     w, float(scale), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dd))
+    return dQ, dK, dV, dd
+
+
+def weights_bwd(V, Delta, A, ddelta):
+    """Gradients through delta = exp(softplus(V . Delta) * A) given ddelta:
+    dV [B,Sk,Hkv,D], dDelta [Hkv*D, Hkv], dA [Hkv] (float64)."""
+    lib = _load()
+    Vn = _np(V, np.float32)
+    Dn = _np(Delta, np.float32)
+    An = _np(A, np.float32)
+    gd = _np(ddelta, np.float64)
+    B, Sk, Hkv, D = Vn.shape
+    assert gd.shape == (B, Hkv, Sk)
+    dV = np.empty((B, Sk, Hkv, D), np.float64)
+    dDelta = np.empty((Hkv * D, Hkv), np.float64)
+    dA = np.empty((Hkv,), np.float64)
+    lib.orc_weights_bwd(_ptr(Vn), _ptr(Dn), _ptr(An), _ptr(gd), B, Sk, Hkv, D, _ptr(dV),
+                        _ptr(dDelta), _ptr(dA))
+    return dV, dDelta, dA

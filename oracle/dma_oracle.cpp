@@ -1,4 +1,4 @@
-// fp64 CPU oracle for the Dynamic Mask Attention (DMA) forward.
+// fp64 CPU oracle for the Dynamic Mask Attention (DMA) forward and backward.
 //
 // TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU
 // baseline leg of the benchmark may load this library.  It shares no code,
@@ -212,6 +212,130 @@ void orc_attn_rows(const float* Q, const float* K, const float* V, const double*
       }
       for (int64_t c = 0; c < D; ++c) O[r * D + c] = acc[c] / z;
       lse[r] = m + std::log(z);
+    }
+  }
+}
+
+// Backward of the attention (gradient of L = sum over rows of dO . O, the
+// keep sets held fixed: they are piecewise constant in delta).  For row
+// (b, hq, i) at position p = q0 + i over its kept keys J, with
+// P_j = exp(s_j - lse) and O = sum_j P_j v_j as in orc_attn_rows:
+//   Dr   = dO . O
+//   dP_j = dO . v_j,   dS_j = P_j (dP_j - Dr)       (softmax Jacobian)
+//   dQ_i = scale sum_j dS_j k_j
+//   dK_j += scale dS_j q_i,   dV_j += P_j dO,   ddelta[b,h,j] += dS_j
+// Every (batch, kv head) sequence owns its dK/dV/ddelta rows, so sequences run
+// in parallel and each walks its G query heads and Sq rows in order.
+// Layouts as orc_attn_rows; dO [B,Sq,Hq,D]; dQ [B,Sq,Hq,D]; dK, dV
+// [B,Sk,Hkv,D]; ddelta [B,Hkv,Sk]; all outputs are overwritten.
+void orc_attn_bwd(const float* Q, const float* K, const float* V, const double* delta,
+                  const float* dO, int64_t B, int64_t Sq, int64_t Sk, int64_t Hq, int64_t Hkv,
+                  int64_t D, int64_t q0, int64_t w, double scale, double* dQ, double* dK,
+                  double* dV, double* ddelta) {
+  const int64_t G = Hq / Hkv;
+  std::fill(dK, dK + B * Sk * Hkv * D, 0.0);
+  std::fill(dV, dV + B * Sk * Hkv * D, 0.0);
+  std::fill(ddelta, ddelta + B * Hkv * Sk, 0.0);
+#pragma omp parallel
+  {
+    std::vector<int32_t> scratch, keep(Sk > 0 ? Sk : 1);
+    std::vector<double> s(Sk > 0 ? Sk : 1), P(Sk > 0 ? Sk : 1), o(D), dq(D);
+#pragma omp for collapse(2) schedule(dynamic, 1)
+    for (int64_t b = 0; b < B; ++b)
+      for (int64_t h = 0; h < Hkv; ++h) {
+        const double* d = delta + (b * Hkv + h) * Sk;
+        for (int64_t hq = h * G; hq < (h + 1) * G; ++hq)
+          for (int64_t i = 0; i < Sq; ++i) {
+            const int64_t p = q0 + i;
+            const int64_t nk = keep_row(d, p, w, keep.data(), scratch);
+            const float* q = Q + ((b * Sq + i) * Hq + hq) * D;
+            const float* g = dO + ((b * Sq + i) * Hq + hq) * D;
+            double m = -INFINITY;
+            for (int64_t k = 0; k < nk; ++k) {
+              const float* kr = K + ((b * Sk + keep[k]) * Hkv + h) * D;
+              double dot = 0.0;
+              for (int64_t c = 0; c < D; ++c) dot += (double)q[c] * (double)kr[c];
+              s[k] = scale * dot + d[keep[k]];
+              m = std::max(m, s[k]);
+            }
+            double z = 0.0;
+            for (int64_t k = 0; k < nk; ++k) z += std::exp(s[k] - m);
+            const double lse = m + std::log(z);
+            std::fill(o.begin(), o.end(), 0.0);
+            for (int64_t k = 0; k < nk; ++k) {
+              P[k] = std::exp(s[k] - lse);
+              const float* vr = V + ((b * Sk + keep[k]) * Hkv + h) * D;
+              for (int64_t c = 0; c < D; ++c) o[c] += P[k] * (double)vr[c];
+            }
+            double Dr = 0.0;
+            for (int64_t c = 0; c < D; ++c) Dr += (double)g[c] * o[c];
+            std::fill(dq.begin(), dq.end(), 0.0);
+            for (int64_t k = 0; k < nk; ++k) {
+              const int64_t j = keep[k];
+              const float* kr = K + ((b * Sk + j) * Hkv + h) * D;
+              const float* vr = V + ((b * Sk + j) * Hkv + h) * D;
+              double dp = 0.0;
+              for (int64_t c = 0; c < D; ++c) dp += (double)g[c] * (double)vr[c];
+              const double ds = P[k] * (dp - Dr);
+              double* dk = dK + ((b * Sk + j) * Hkv + h) * D;
+              double* dv = dV + ((b * Sk + j) * Hkv + h) * D;
+              for (int64_t c = 0; c < D; ++c) {
+                dq[c] += ds * (double)kr[c];
+                dk[c] += scale * ds * (double)q[c];
+                dv[c] += P[k] * (double)g[c];
+              }
+              ddelta[(b * Hkv + h) * Sk + j] += ds;
+            }
+            double* dqo = dQ + ((b * Sq + i) * Hq + hq) * D;
+            for (int64_t c = 0; c < D; ++c) dqo[c] = scale * dq[c];
+          }
+      }
+  }
+}
+
+// Backward of the dynamic weights, given ddelta = dL/ddelta:
+//   pre = sum_c V[b,j,c] Delta[c,h],  sp = softplus(pre),  delta = exp(sp A[h])
+//   dpre = ddelta * delta * A[h] * sigmoid(pre)      (softplus' = sigmoid)
+//   dA[h]       += ddelta * delta * sp
+//   dDelta[c,h] += V[b,j,c] * dpre
+//   dV[b,j,c]    = sum_h dpre[h] * Delta[c,h]
+// dV [B,Sk,Hkv*D] (overwritten; add the attention's dV separately),
+// dDelta [Hkv*D, Hkv], dA [Hkv] (overwritten).
+void orc_weights_bwd(const float* V, const float* Delta, const float* A, const double* ddelta,
+                     int64_t B, int64_t Sk, int64_t Hkv, int64_t D, double* dV, double* dDelta,
+                     double* dA) {
+  const int64_t C = Hkv * D;
+  std::fill(dDelta, dDelta + C * Hkv, 0.0);
+  std::fill(dA, dA + Hkv, 0.0);
+#pragma omp parallel
+  {
+    std::vector<double> gD(C * Hkv, 0.0), gA(Hkv, 0.0), dpre(Hkv);
+#pragma omp for collapse(2) schedule(static)
+    for (int64_t b = 0; b < B; ++b)
+      for (int64_t j = 0; j < Sk; ++j) {
+        const float* v = V + (b * Sk + j) * C;
+        for (int64_t h = 0; h < Hkv; ++h) {
+          double pre = 0.0;
+          for (int64_t c = 0; c < C; ++c) pre += (double)v[c] * (double)Delta[c * Hkv + h];
+          const double sp = softplus(pre);
+          const double dl = std::exp(sp * (double)A[h]);
+          const double gd = ddelta[(b * Hkv + h) * Sk + j];
+          const double sig = 1.0 / (1.0 + std::exp(-pre));
+          dpre[h] = gd * dl * (double)A[h] * sig;
+          gA[h] += gd * dl * sp;
+          for (int64_t c = 0; c < C; ++c) gD[c * Hkv + h] += (double)v[c] * dpre[h];
+        }
+        double* dv = dV + (b * Sk + j) * C;
+        for (int64_t c = 0; c < C; ++c) {
+          double acc = 0.0;
+          for (int64_t h = 0; h < Hkv; ++h) acc += dpre[h] * (double)Delta[c * Hkv + h];
+          dv[c] = acc;
+        }
+      }
+#pragma omp critical
+    {
+      for (int64_t k = 0; k < C * Hkv; ++k) dDelta[k] += gD[k];
+      for (int64_t h = 0; h < Hkv; ++h) dA[h] += gA[h];
     }
   }
 }
