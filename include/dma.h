@@ -190,6 +190,51 @@ dma_status dma_attn_fwd(const void* Q, const void* K, const void* V, dma_dtype t
                         int64_t w, const float* delta, const dma_mask* mask, float scale, void* O,
                         float* lse, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Step 3 for training: dma_attn_fwd (bf16, D == 128, Sq > 1, no workspace)
+ * that also writes O_res [B,Sq,Hq,D] bf16, the rounding residual of O (the
+ * fp32 result minus the stored bf16 O).  O + O_res carries O to ~2^-18, which
+ * dma_attn_bwd needs for dO . O where the attention is nearly one-hot (there
+ * the exact gradient is a small difference that bf16 O alone would swamp).
+ * lse is required.
+ */
+dma_status dma_attn_fwd_train(const void* Q, const void* K, const void* V, dma_dtype t,
+                              int64_t B, int64_t Sq, int64_t Sk, int64_t Hq, int64_t Hkv,
+                              int64_t D, const int64_t q_strides[3],
+                              const int64_t kv_strides[3], int64_t q_offset, int64_t w,
+                              const float* delta, const dma_mask* mask, float scale, void* O,
+                              float* lse, void* O_res, void* stream);
+
+/* Workspace bytes dma_attn_bwd needs (0 when Sq <= 1). */
+size_t dma_attn_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Sk,
+                                    int64_t w);
+
+/*
+ * Backward of step 3 (DMA blog, o_t equation; masked keys get exactly zero
+ * gradient, section "Efficient Sparse Attention Computation", "Backward Pass
+ * Safety").  Gradients of L = sum(dO * O) with the keep sets held fixed:
+ *   P_ij = exp(s_ij - lse_i),  dS_ij = P_ij (dO_i . v_j - dO_i . O_i)
+ *   dQ_i = scale sum_j dS_ij k_j       dK_j = scale sum_i dS_ij q_i
+ *   dV_j = sum_i P_ij dO_i             ddelta[b,h,j] = sum_i dS_ij
+ * (i over the query rows and the Hq/Hkv query heads of kv head h).
+ * Arguments as dma_attn_fwd, plus: O and lse the outputs of the forward
+ * (lse required); O_res the residual from dma_attn_fwd_train, or NULL (then
+ * dO . O uses the bf16 O alone); dO [B,Sq,Hq,D] contiguous, type t.  Outputs, float,
+ * contiguous, overwritten: dQ [B,Sq,Hq,D], dK and dV [B,Sk,Hkv,D], ddelta
+ * [B,Hkv,Sk] (add the weights backward's dV separately).  ws:
+ * dma_attn_bwd_workspace_bytes bytes, 256-byte aligned.
+ * Arithmetic: bf16 MFMA products with fp32 accumulation; the per-row
+ * partial sums of dK/dV/ddelta are added in fp32.  Limits: BF16, D == 128,
+ * Sq > 1; query, dO and key rows within 4 GiB of their (b, h) base.
+ */
+dma_status dma_attn_bwd(const void* Q, const void* K, const void* V, dma_dtype t, int64_t B,
+                        int64_t Sq, int64_t Sk, int64_t Hq, int64_t Hkv, int64_t D,
+                        const int64_t q_strides[3], const int64_t kv_strides[3], int64_t q_offset,
+                        int64_t w, const float* delta, const dma_mask* mask, float scale,
+                        const void* O, const void* O_res, const float* lse, const void* dO,
+                        float* dQ, float* dK, float* dV, float* ddelta, void* ws,
+                        size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

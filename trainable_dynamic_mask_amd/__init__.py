@@ -187,3 +187,59 @@ def forward(Q, K, V, Delta, A, w, q_offset=0, scale=None, return_all=False):
     if return_all:
         return O, delta, mask
     return O
+
+
+def attn_fwd_train(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, delta: torch.Tensor,
+                   mask: Mask, scale: Optional[float] = None):
+    """attn_fwd for training (bf16 prefill): returns O, lse and O_res, the
+    rounding residual of O that attn_bwd uses for dO . O."""
+    _need_cuda(Q, K, V, delta)
+    B, Sq, Hq, D = Q.shape
+    _, Sk, Hkv, _ = K.shape
+    if K.stride() != V.stride() or Q.stride(3) != 1 or K.stride(3) != 1:
+        raise ValueError("K and V must share strides; the D values must be contiguous")
+    O = torch.empty(B, Sq, Hq, D, dtype=Q.dtype, device=Q.device)
+    Ores = torch.empty_like(O)
+    lse = torch.empty(B, Hq, Sq, dtype=torch.float32, device=Q.device)
+    qs = (ctypes.c_int64 * 3)(Q.stride(0), Q.stride(1), Q.stride(2))
+    ks = (ctypes.c_int64 * 3)(K.stride(0), K.stride(1), K.stride(2))
+    ms = mask.cstruct()
+    check("dma_attn_fwd_train", load().dma_attn_fwd_train(
+        _ptr(Q), _ptr(K), _ptr(V), _dtype_code(Q.dtype), B, Sq, Sk, Hq, Hkv, D, qs, ks,
+        mask.q_offset, mask.w, _ptr(delta.contiguous()), ctypes.byref(ms),
+        0.0 if scale is None else float(scale), _ptr(O), _ptr(lse), _ptr(Ores), _stream(Q.device)))
+    return O, lse, Ores
+
+
+def attn_bwd(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, delta: torch.Tensor, mask: Mask,
+             O: torch.Tensor, lse: torch.Tensor, dO: torch.Tensor,
+             O_res: Optional[torch.Tensor] = None,
+             scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None):
+    """Gradients of sum(dO * O) of attn_fwd (keep sets fixed): float32 dQ
+    [B,Sq,Hq,D], dK and dV [B,Sk,Hkv,D], ddelta [B,Hkv,Sk].  O and lse are
+    the forward's outputs; O_res (from attn_fwd_train) makes dO . O exact."""
+    _need_cuda(Q, K, V, delta, O, lse, dO)
+    B, Sq, Hq, D = Q.shape
+    _, Sk, Hkv, _ = K.shape
+    if K.stride() != V.stride() or Q.stride(3) != 1 or K.stride(3) != 1:
+        raise ValueError("K and V must share strides; the D values must be contiguous")
+    lib = load()
+    dev = Q.device
+    dQ = torch.empty(B, Sq, Hq, D, dtype=torch.float32, device=dev)
+    dK = torch.empty(B, Sk, Hkv, D, dtype=torch.float32, device=dev)
+    dV = torch.empty(B, Sk, Hkv, D, dtype=torch.float32, device=dev)
+    dd = torch.empty(B, Hkv, Sk, dtype=torch.float32, device=dev)
+    nbytes = lib.dma_attn_bwd_workspace_bytes(B, Hq, Hkv, Sq, Sk, mask.w)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(256, nbytes), dtype=torch.uint8, device=dev)
+    qs = (ctypes.c_int64 * 3)(Q.stride(0), Q.stride(1), Q.stride(2))
+    ks = (ctypes.c_int64 * 3)(K.stride(0), K.stride(1), K.stride(2))
+    ms = mask.cstruct()
+    check("dma_attn_bwd", lib.dma_attn_bwd(
+        _ptr(Q), _ptr(K), _ptr(V), _dtype_code(Q.dtype), B, Sq, Sk, Hq, Hkv, D, qs, ks,
+        mask.q_offset, mask.w, _ptr(delta.contiguous()), ctypes.byref(ms),
+        0.0 if scale is None else float(scale), _ptr(O.contiguous()),
+        _ptr(O_res.contiguous()) if O_res is not None else None, _ptr(lse.contiguous()),
+        _ptr(dO.contiguous()), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dd), _ptr(workspace), nbytes,
+        _stream(dev)))
+    return dQ, dK, dV, dd

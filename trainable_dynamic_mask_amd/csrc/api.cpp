@@ -166,11 +166,13 @@ dma_status dma_decode_keep_append(const float* delta, int64_t B, int64_t Hkv, in
                                              static_cast<hipStream_t>(stream)));
 }
 
-dma_status dma_attn_fwd(const void* Q, const void* K, const void* V, dma_dtype t, int64_t B,
-                        int64_t Sq, int64_t Sk, int64_t Hq, int64_t Hkv, int64_t D,
-                        const int64_t q_strides[3], const int64_t kv_strides[3], int64_t q_offset,
-                        int64_t w, const float* delta, const dma_mask* mask, float scale, void* O,
-                        float* lse, void* ws, size_t ws_bytes, void* stream) {
+namespace {
+dma_status attn_fwd_impl(const void* Q, const void* K, const void* V, dma_dtype t, int64_t B,
+                         int64_t Sq, int64_t Sk, int64_t Hq, int64_t Hkv, int64_t D,
+                         const int64_t q_strides[3], const int64_t kv_strides[3],
+                         int64_t q_offset, int64_t w, const float* delta, const dma_mask* mask,
+                         float scale, void* O, float* lse, void* O_res, void* ws,
+                         size_t ws_bytes, void* stream) {
   if (t != DMA_F32 && t != DMA_BF16) return DMA_ERR_INVALID_ARG;
   if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || D < 1) return DMA_ERR_INVALID_ARG;
   const dma_status st = check_mask_shape(B, Hkv, Sq, Sk, q_offset, w);
@@ -225,6 +227,7 @@ dma_status dma_attn_fwd(const void* Q, const void* K, const void* V, dma_dtype t
   a.O = O;
   a.lse = lse;
   a.ws = ws;
+  a.ores = O_res;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (Sq == 1) {
     const size_t need = dma_attn_decode_ws_bytes(B, Hq, D, d.u_stride);
@@ -234,6 +237,110 @@ dma_status dma_attn_fwd(const void* Q, const void* K, const void* V, dma_dtype t
   }
   if (t == DMA_BF16) return hip_status(dma_launch_attn_prefill_bf16(a, s));
   return hip_status(dma_launch_attn_prefill_f32(a, s));
+}
+}  // namespace
+
+dma_status dma_attn_fwd(const void* Q, const void* K, const void* V, dma_dtype t, int64_t B,
+                        int64_t Sq, int64_t Sk, int64_t Hq, int64_t Hkv, int64_t D,
+                        const int64_t q_strides[3], const int64_t kv_strides[3], int64_t q_offset,
+                        int64_t w, const float* delta, const dma_mask* mask, float scale, void* O,
+                        float* lse, void* ws, size_t ws_bytes, void* stream) {
+  return attn_fwd_impl(Q, K, V, t, B, Sq, Sk, Hq, Hkv, D, q_strides, kv_strides, q_offset, w,
+                       delta, mask, scale, O, lse, nullptr, ws, ws_bytes, stream);
+}
+
+dma_status dma_attn_fwd_train(const void* Q, const void* K, const void* V, dma_dtype t,
+                              int64_t B, int64_t Sq, int64_t Sk, int64_t Hq, int64_t Hkv,
+                              int64_t D, const int64_t q_strides[3],
+                              const int64_t kv_strides[3], int64_t q_offset, int64_t w,
+                              const float* delta, const dma_mask* mask, float scale, void* O,
+                              float* lse, void* O_res, void* stream) {
+  if (t != DMA_BF16 || D != 128 || Sq == 1) return DMA_ERR_UNSUPPORTED;
+  if (B > 0 && Sq > 0 && (!lse || !O_res || !aligned16(O_res))) return DMA_ERR_INVALID_ARG;
+  return attn_fwd_impl(Q, K, V, t, B, Sq, Sk, Hq, Hkv, D, q_strides, kv_strides, q_offset, w,
+                       delta, mask, scale, O, lse, O_res, nullptr, 0, stream);
+}
+
+size_t dma_attn_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Sk,
+                                    int64_t w) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 1 || Sk <= 0 || w <= 0) return 0;
+  return dma_attn_bwd_ws_bytes(B, Hq, Hkv, Sq, Sk, w);
+}
+
+dma_status dma_attn_bwd(const void* Q, const void* K, const void* V, dma_dtype t, int64_t B,
+                        int64_t Sq, int64_t Sk, int64_t Hq, int64_t Hkv, int64_t D,
+                        const int64_t q_strides[3], const int64_t kv_strides[3], int64_t q_offset,
+                        int64_t w, const float* delta, const dma_mask* mask, float scale,
+                        const void* O, const void* O_res, const float* lse, const void* dO,
+                        float* dQ, float* dK, float* dV, float* ddelta, void* ws,
+                        size_t ws_bytes, void* stream) {
+  if (t != DMA_F32 && t != DMA_BF16) return DMA_ERR_INVALID_ARG;
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || D < 1) return DMA_ERR_INVALID_ARG;
+  const dma_status st = check_mask_shape(B, Hkv, Sq, Sk, q_offset, w);
+  if (st != DMA_OK) return st;
+  if (t != DMA_BF16 || D != 128 || Sq == 1) return DMA_ERR_UNSUPPORTED;
+  if (std::isnan(scale)) return DMA_ERR_INVALID_ARG;
+  if (B == 0 || Sq == 0) return DMA_OK;
+  if (!Q || !K || !V || !delta || !mask || !O || !lse || !dO || !dQ || !dK || !dV || !ddelta ||
+      !q_strides || !kv_strides)
+    return DMA_ERR_INVALID_ARG;
+  if (!mask->evict || !mask->u_idx || !mask->u_cnt || !mask->u_nfull || !mask->u_dmax)
+    return DMA_ERR_INVALID_ARG;
+  for (int i = 0; i < 3; ++i)
+    if (q_strides[i] < 0 || kv_strides[i] < 0 || (q_strides[i] * 2) % 16 != 0 ||
+        (kv_strides[i] * 2) % 16 != 0)
+      return DMA_ERR_INVALID_ARG;
+  if ((Hq > 1 && q_strides[2] < D) || (Hkv > 1 && kv_strides[2] < D)) return DMA_ERR_INVALID_ARG;
+  // key rows, query rows and dO rows are addressed by 32-bit byte offsets
+  const int64_t lim = (int64_t)1 << 32;
+  if ((Sk - 1) * kv_strides[1] * 2 + 256 > lim || (Sq - 1) * q_strides[1] * 2 + 256 > lim ||
+      (Sq - 1) * Hq * D * 2 + 256 > lim)
+    return DMA_ERR_UNSUPPORTED;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(dO) ||
+      !aligned16(dQ) || !aligned16(dK) || !aligned16(dV) || (O_res && !aligned16(O_res)))
+    return DMA_ERR_INVALID_ARG;
+  const size_t need = dma_attn_bwd_ws_bytes(B, Hq, Hkv, Sq, Sk, w);
+  if (ws_bytes < need || !ws) return DMA_ERR_WORKSPACE;
+  if (((uintptr_t)ws & 255) != 0) return DMA_ERR_INVALID_ARG;
+  const Dims d = dims_of(Sq, Sk, w);
+  DmaBwdArgs a{};
+  DmaAttnArgs& f = a.f;
+  f.Q = Q;
+  f.K = K;
+  f.V = V;
+  f.B = B;
+  f.Sq = Sq;
+  f.Sk = Sk;
+  f.Hq = Hq;
+  f.Hkv = Hkv;
+  f.D = D;
+  f.qsb = q_strides[0];
+  f.qss = q_strides[1];
+  f.qsh = q_strides[2];
+  f.ksb = kv_strides[0];
+  f.kss = kv_strides[1];
+  f.ksh = kv_strides[2];
+  f.q0 = q_offset;
+  f.w = w;
+  f.delta = delta;
+  f.evict = mask->evict;
+  f.u_idx = mask->u_idx;
+  f.u_cnt = mask->u_cnt;
+  f.u_nfull = mask->u_nfull;
+  f.u_dmax = mask->u_dmax;
+  f.n_tiles = d.n_tiles;
+  f.u_stride = d.u_stride;
+  f.scale = scale > 0.f ? scale : 1.f / std::sqrt((float)D);
+  f.O = const_cast<void*>(O);
+  f.lse = const_cast<float*>(lse);
+  f.ws = ws;
+  f.ores = const_cast<void*>(O_res);
+  a.dO = dO;
+  a.dQ = dQ;
+  a.dK = dK;
+  a.dV = dV;
+  a.ddelta = ddelta;
+  return hip_status(dma_launch_attn_bwd(a, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -1,0 +1,648 @@
+// Backward of the masked attention of the DMA forward, bf16 prefill (Hugging
+// Face blog "Trainable Dynamic Mask Sparse Attention", section "Efficient
+// Sparse Attention Computation"; a masked key has weight exactly 0 and so
+// gradient exactly 0, the section's "Backward Pass Safety" item).  Gradients
+// of L = sum(dO * O) with the keep sets held fixed (they are piecewise
+// constant in delta):
+//   P_ij  = exp(scale q_i.k_j + delta_j - lse_i),   Dv_i = dO_i . O_i
+//   dS_ij = P_ij (dO_i . v_j - Dv_i)
+//   dQ_i = scale sum_j dS_ij k_j,   dK_j = scale sum_i dS_ij q_i,
+//   dV_j = sum_i P_ij dO_i,         ddelta_j = sum_i dS_ij
+// (i over the rows and the G query heads of the key's kv head).
+//
+// Kernels:
+//   dot     Dv_i = dO_i . O_i.
+//   dq      query-major with the forward's work split: a workgroup walks the
+//           compacted key list of its 64-row tile, 64 keys per chunk, one
+//           wave per (query head, 32-row half).  S^T = K Q^T and dP^T = V dO^T
+//           read K and V rows; dQ^T += K^T dS^T reads K transposed.  Q^T and
+//           dO^T stay in registers.
+//   dkv     key-major over groups of 512 rows (8 query tiles).  The keys some
+//           row of a group keeps (at most w + 511: the candidate lists of the
+//           mask step) are cut into slices of 128, one per workgroup and 32
+//           per wave, with K and V held in registers.  The workgroup streams
+//           the group's 64-row tiles of Q and dO (every query head) through
+//           LDS and accumulates dK^T, dV^T and ddelta, which it writes as the
+//           group's partial sums.  Natural 64-key tiles would do 4x (16K
+//           keys) to 8x (64K) the kept work, since the best key of a tile
+//           stays kept to the end of the sequence; within a group a
+//           candidate is kept on most rows.
+//   reduce  key j is kept on rows [j, e_j), i.e. in groups j/512 ..
+//           (e_j-1)/512; it sums its partials over those groups, finding its
+//           place in each group's ascending list by binary search.
+// LDS tiles are 64 rows of 256 bytes.  The 16-byte chunk c of row r is
+// stored at c ^ (((r & 3) << 2) | ((r >> 2) & 3)): 16 consecutive rows put
+// one chunk on 16 distinct chunk slots (row reads), and 4 consecutive rows
+// put a 32-byte piece on 4 distinct 32-byte slots (transposing reads), so
+// both access patterns are free of bank conflicts.
+#include "common.h"
+
+#include <algorithm>
+
+namespace {
+
+constexpr int kBq = 64;
+constexpr int kBk = 64;
+constexpr int kD = 128;
+constexpr int kRowB = kD * 2;
+constexpr int kTileB = 64 * kRowB;
+constexpr int kGroupRows = 512;   // rows per key-side group
+constexpr int kSliceKeys = 128;   // candidate keys per key-side workgroup (4 waves x 32)
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(lds_void*)p;
+}
+
+// Direct global-to-LDS loads (inline asm, so the compiler neither tracks nor
+// waits for them; every wait is an explicit vmcnt).  Lane L's data lands at
+// LDS byte m0 + size*L.
+__device__ __forceinline__ void dma_b128(const void* src, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(src), "s"(lds)
+      : "m0");
+}
+__device__ __forceinline__ void dma_b32(const void* src, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %0, off"
+      :
+      : "v"(src), "s"(lds)
+      : "m0");
+}
+
+// All of this wave's direct loads have landed; then the workgroup barrier.
+__device__ __forceinline__ void wait_all_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) expcnt(0) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// A or B operand of a 32x32x16 MFMA read along a tile row: row `row`,
+// logical 16-byte chunk lc (elements 8*lc .. 8*lc+7).
+__device__ __forceinline__ dma::bf16x8 row_operand(const unsigned char* tile, int row, int lc) {
+  return *reinterpret_cast<const dma::bf16x8*>(tile + row * kRowB + ((lc ^ swz(row)) << 4));
+}
+
+// A operand of an MFMA that contracts over 16 tile rows: element (m, k) =
+// tile[row(k)][dbase + m] for m = lane % 32 and k = 8*hi + t, where row(k) is
+// rbase + 4*hi + t for t < 4 and rbase + 8 + 4*hi + (t - 4) otherwise: the
+// row order of the B operands built from a 32x32 accumulator (register i of
+// lane (l32, hi) holds row 8*(i/4) + 4*hi + i%4).  Two transposing reads: a
+// 16-lane group g addresses rows rbase + 4*(g/2) + r/4 (and 8 rows further),
+// columns dbase + 16*(g%2) + 4*(r%4), and lane i of the group receives the
+// 4 rows of column dbase + 16*(g%2) + i.
+__device__ __forceinline__ dma::bf16x8 tr_operand(const unsigned char* tile, int rbase, int dbase,
+                                                  int lane) {
+  const int g = lane >> 4, r = lane & 15;
+  const int k0 = rbase + 4 * (g >> 1) + (r >> 2);
+  const int d0 = dbase + 16 * (g & 1) + 4 * (r & 3);
+  const int lc = d0 >> 3, byte = (d0 & 7) * 2;
+  const lds_u8* base = (const lds_u8*)tile;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)(base + k0 * kRowB + ((lc ^ swz(k0)) << 4) + byte));
+  const i16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)(base + (k0 + 8) * kRowB + ((lc ^ swz(k0 + 8)) << 4) + byte));
+  const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), up2 = __builtin_bit_cast(u32x2, up);
+  const u32x4 vv = {lo2[0], lo2[1], up2[0], up2[1]};
+  return __builtin_bit_cast(dma::bf16x8, vv);
+}
+
+__device__ __forceinline__ dma::bf16x8 to_bf16x8(const float* p) {
+  dma::bf16x8 r;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) r[t] = (__bf16)p[t];
+  return r;
+}
+
+__device__ __forceinline__ dma::f32x16 mfma(dma::bf16x8 a, dma::bf16x8 b, dma::f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- dot
+// One row (b, i, hq) of 128 values per 16 lanes.
+// O + O_res (when given) restores the forward's fp32 O.
+__global__ __launch_bounds__(256) void bwd_dot_kernel(const uint16_t* __restrict__ O,
+                                                      const uint16_t* __restrict__ Ores,
+                                                      const uint16_t* __restrict__ dO,
+                                                      int64_t nrows, int Sq, int Hq,
+                                                      float* __restrict__ Dv) {
+  const int64_t r = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int l = threadIdx.x & 15;
+  float acc = 0.f;
+  if (r < nrows) {
+    const u32x4 a = reinterpret_cast<const u32x4*>(O + r * kD)[l];
+    const u32x4 b = reinterpret_cast<const u32x4*>(dO + r * kD)[l];
+    u32x4 c = {0u, 0u, 0u, 0u};
+    if (Ores) c = reinterpret_cast<const u32x4*>(Ores + r * kD)[l];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      acc += (dma::bf16_lo(a[e]) + dma::bf16_lo(c[e])) * dma::bf16_lo(b[e]) +
+             (dma::bf16_hi(a[e]) + dma::bf16_hi(c[e])) * dma::bf16_hi(b[e]);
+  }
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+  if (l == 0 && r < nrows) {
+    const int64_t hq = r % Hq, bi = r / Hq, i = bi % Sq, b = bi / Sq;
+    Dv[(b * Hq + hq) * Sq + i] = acc;
+  }
+}
+
+// ---------------------------------------------------------------- dq
+struct DqSmem {
+  unsigned char k[2][kTileB];  // K chunk tiles (gathered rows)
+  unsigned char v[2][kTileB];  // V chunk tiles
+  int jl[3][kBk];              // list entries: chunk c in slot c % 3
+  float dl[2][kBk];            // delta of chunk c's keys in slot c % 2
+  int ev[2][kBk];              // their eviction rows
+};
+
+template <int NH>
+__global__ __launch_bounds__(NH * 128, 1) void bwd_dq_kernel(DmaBwdArgs a) {
+  constexpr int NW = NH * 2;
+  __shared__ __align__(16) DqSmem sm;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hi = lane >> 5;
+  const DmaAttnArgs& f = a.f;
+  const int G = (int)(f.Hq / f.Hkv);
+  const int ngrp = G / NH;
+  const int t = blockIdx.x, h = blockIdx.y;
+  const int b = blockIdx.z / ngrp, hgrp = blockIdx.z % ngrp;
+  const int hq = h * G + hgrp * NH + (wave >> 1);
+  const int half = wave & 1;
+  const int64_t seg = (int64_t)b * f.Hkv + h;
+  const int64_t g = seg * f.n_tiles + t;
+  const int r_lo = t * kBq;
+  const int rows = min(kBq, (int)f.Sq - r_lo);
+  const int cnt = f.u_cnt[g];
+  const float dmax = f.u_dmax[g];
+  const int32_t* list = f.u_idx + g * f.u_stride;
+  const float* dlg = f.delta + seg * f.Sk;
+  const int32_t* evg = f.evict + seg * f.Sk;
+  const int nch = (cnt + kBk - 1) / kBk;
+  const int clast = max(cnt - 1, 0);
+  const unsigned char* Kg = static_cast<const unsigned char*>(f.K) + (b * f.ksb + h * f.ksh) * 2;
+  const unsigned char* Vg = static_cast<const unsigned char*>(f.V) + (b * f.ksb + h * f.ksh) * 2;
+  const uint32_t rowb = (uint32_t)(f.kss * 2);
+  const float scale2 = f.scale * kLog2e;
+
+  // this lane's query column n, its Q^T and dO^T operands, lse and Dv
+  const int n = half * 32 + l32;
+  const int nr = r_lo + (n < rows ? n : 0);  // rows past the tile repeat its first row
+  const int pos = (int)f.q0 + r_lo + n;
+  dma::bf16x8 qf[8], gf[8];
+  {
+    const uint16_t* qrow =
+        static_cast<const uint16_t*>(f.Q) + b * f.qsb + hq * f.qsh + (int64_t)nr * f.qss;
+    const uint16_t* grow = static_cast<const uint16_t*>(a.dO) + ((b * f.Sq + nr) * f.Hq + hq) * kD;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      qf[kk] = __builtin_bit_cast(dma::bf16x8,
+                                  *reinterpret_cast<const u32x4*>(qrow + kk * 16 + hi * 8));
+      gf[kk] = __builtin_bit_cast(dma::bf16x8,
+                                  *reinterpret_cast<const u32x4*>(grow + kk * 16 + hi * 8));
+    }
+  }
+  const float lse_q = f.lse[((int64_t)b * f.Hq + hq) * f.Sq + nr];
+  const float lq = (lse_q - dmax) * kLog2e;
+  const float dv_q = a.Dv[((int64_t)b * f.Hq + hq) * f.Sq + nr];
+
+  const uint32_t lds_k = lds_addr(&sm.k[0][0]), lds_v = lds_addr(&sm.v[0][0]);
+  const uint32_t lds_j = lds_addr(&sm.jl[0][0]), lds_d = lds_addr(&sm.dl[0][0]),
+                 lds_e = lds_addr(&sm.ev[0][0]);
+  // the K and V rows of chunk x into buffer x % 2: 16 pieces of 4 rows per
+  // tile, piece p by wave p % NW; lane L fills row 4p + L/16, chunk slot L%16
+  auto gather = [&](int x) {
+    const int buf = x & 1;
+#pragma unroll
+    for (int u = 0; u < 16 / NW; ++u) {
+      const int piece = wave + u * NW;
+      const int row = piece * 4 + (lane >> 4);
+      const int lc = (lane & 15) ^ swz(row);
+      const uint32_t j = (uint32_t)sm.jl[x % 3][row];
+      dma_b128(Kg + j * rowb + lc * 16, lds_k + buf * kTileB + piece * 1024);
+      dma_b128(Vg + j * rowb + lc * 16, lds_v + buf * kTileB + piece * 1024);
+    }
+    if (wave == 0) {
+      const int j = sm.jl[x % 3][lane];
+      dma_b32(dlg + j, lds_d + buf * 256);
+      dma_b32(evg + j, lds_e + buf * 256);
+    }
+  };
+
+  // prologue: list entries of chunks 0 and 1, then chunk 0's rows
+  if (wave == 0) {
+    dma_b32(list + min(lane, clast), lds_j);
+    dma_b32(list + min(kBk + lane, clast), lds_j + 256);
+  }
+  wait_all_barrier();
+  gather(0);
+  wait_all_barrier();
+
+  dma::f32x16 dq[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dq[db][i] = 0.f;
+
+  for (int c = 0; c < nch; ++c) {
+    // chunk c+2's list entries and chunk c+1's rows go out first
+    if (wave == 0) dma_b32(list + min((c + 2) * kBk + lane, clast), lds_j + ((c + 2) % 3) * 256);
+    if (c + 1 < nch) gather(c + 1);
+
+    const unsigned char* KT = sm.k[c & 1];
+    const unsigned char* VT = sm.v[c & 1];
+    dma::f32x16 s[2], dp[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        s[mb][i] = 0.f;
+        dp[mb][i] = 0.f;
+      }
+    // S^T = K Q^T and dP^T = V dO^T: lane (l32, hi) reads key row mb*32 + l32
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const int row = mb * 32 + l32;
+        s[mb] = mfma(row_operand(KT, row, 2 * kk + hi), qf[kk], s[mb]);
+        dp[mb] = mfma(row_operand(VT, row, 2 * kk + hi), gf[kk], dp[mb]);
+      }
+    // dS^T = P^T (dP^T - Dv); register i of block mb is key mb*32 + 8(i/4) + 4hi + i%4
+    dma::bf16x8 dsb[2][2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        float ds[8];
+#pragma unroll
+        for (int t8 = 0; t8 < 8; ++t8) {
+          const int i = hf * 8 + t8;
+          const int key = mb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
+          const int j = sm.jl[c % 3][key];
+          const int e = sm.ev[c & 1][key];
+          const float dlt = sm.dl[c & 1][key];
+          const bool kept = c * kBk + key < cnt && (uint32_t)(pos - j) < (uint32_t)(e - j);
+          const float v = fmaf(s[mb][i], scale2, (dlt - dmax) * kLog2e) - lq;
+          const float p = kept ? __builtin_amdgcn_exp2f(v) : 0.f;
+          ds[t8] = p * (dp[mb][i] - dv_q);
+        }
+        dsb[mb][hf] = to_bf16x8(ds);
+      }
+    // dQ^T += K^T dS^T: k-step (mb, hf) covers keys mb*32 + 16*hf + [0, 16)
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+          dq[db] = mfma(tr_operand(KT, mb * 32 + 16 * hf, db * 32, lane), dsb[mb][hf], dq[db]);
+    wait_all_barrier();
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+
+  if (n < rows) {
+    float* orow = a.dQ + (((int64_t)b * f.Sq + r_lo + n) * f.Hq + hq) * kD;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d = db * 32 + 8 * q4 + 4 * hi;
+        float4 o;
+        o.x = f.scale * dq[db][4 * q4 + 0];
+        o.y = f.scale * dq[db][4 * q4 + 1];
+        o.z = f.scale * dq[db][4 * q4 + 2];
+        o.w = f.scale * dq[db][4 * q4 + 3];
+        *reinterpret_cast<float4*>(orow + d) = o;
+      }
+  }
+}
+
+// ---------------------------------------------------------------- dkv
+struct DkvSmem {
+  unsigned char q[2][kTileB];   // Q rows of one (row tile, query head)
+  unsigned char g[2][kTileB];   // dO rows
+  float lse[2][64];
+  float dv[2][64];
+  int alive[4];
+};
+
+__global__ __launch_bounds__(256) void bwd_dkv_kernel(DmaBwdArgs a) {
+  __shared__ __align__(16) DkvSmem sm;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hi = lane >> 5;
+  const DmaAttnArgs& f = a.f;
+  const int G = (int)(f.Hq / f.Hkv);
+  const int slice = blockIdx.x, grp = blockIdx.y;
+  const int64_t seg = blockIdx.z;
+  const int b = (int)(seg / f.Hkv), h = (int)(seg % f.Hkv);
+  const int64_t gi = seg * a.n_super + grp;
+  const int count = a.ccnt[gi];
+  if (slice * kSliceKeys >= count) return;
+  const int32_t* cj = a.cj + gi * a.cap;
+  const int32_t* ce = a.ce + gi * a.cap;
+  const int slot = slice * kSliceKeys + wave * 32 + l32;
+  const bool real = slot < count;
+  const int sl = min(slot, count - 1);
+  const int j = cj[sl];
+  const int p_end = (int)(f.q0 + f.Sq);
+  // padding lanes get an empty row range, so they never count
+  const int e = real ? min(ce[sl], p_end) : j;
+  const float dlt = f.delta[seg * f.Sk + j];
+  // K^T and V^T operands of this lane's key: K[j][kk*16 + 8*hi + 0..7]
+  dma::bf16x8 kf[8], vf[8];
+  {
+    const uint16_t* krow = static_cast<const uint16_t*>(f.K) + b * f.ksb + h * f.ksh + (int64_t)j * f.kss;
+    const uint16_t* vrow = static_cast<const uint16_t*>(f.V) + b * f.ksb + h * f.ksh + (int64_t)j * f.kss;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      kf[kk] = __builtin_bit_cast(dma::bf16x8,
+                                  *reinterpret_cast<const u32x4*>(krow + kk * 16 + hi * 8));
+      vf[kk] = __builtin_bit_cast(dma::bf16x8,
+                                  *reinterpret_cast<const u32x4*>(vrow + kk * 16 + hi * 8));
+    }
+  }
+  // row tiles of the group in which some key of the slice is kept
+  const int g_lo = grp * kGroupRows;                          // first row (relative to q0)
+  const int ntile = min(kGroupRows, (int)f.Sq - g_lo + kBq - 1) / kBq;
+  int am = 0;
+  for (int rt = 0; rt < ntile; ++rt) {
+    const int p_lo = (int)f.q0 + g_lo + rt * kBq;
+    const int p_hi = min(p_lo + kBq, p_end) - 1;
+    if (j <= p_hi && e > max(j, p_lo)) am |= 1 << rt;
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) am |= __shfl_xor(am, o);
+  if (lane == 0) sm.alive[wave] = am;
+  __syncthreads();
+  const int alive = sm.alive[0] | sm.alive[1] | sm.alive[2] | sm.alive[3];
+  const int nt = __popc(alive);
+  const int nsteps = nt * G;
+
+  const float scale2 = f.scale * kLog2e;
+  const uint32_t lds_q = lds_addr(&sm.q[0][0]), lds_g = lds_addr(&sm.g[0][0]);
+  const uint32_t lds_l = lds_addr(&sm.lse[0][0]), lds_dv = lds_addr(&sm.dv[0][0]);
+  // step st = (k-th alive row tile, head st % G)
+  auto tile_of = [&](int st) {
+    int k = st / G, m = alive;
+    for (int u = 0; u < k; ++u) m &= m - 1;
+    return __builtin_ctz(m);
+  };
+  // Q and dO rows of step st into buffer st % 2: 16 pieces of 4 rows per tile,
+  // piece p by wave p % 4; rows past the sequence repeat its last row
+  auto stage = [&](int st) {
+    const int buf = st & 1;
+    const int rt = tile_of(st);
+    const int hq = h * G + st % G;
+    const int r0 = g_lo + rt * kBq;
+    const unsigned char* Qb = static_cast<const unsigned char*>(f.Q) + (b * f.qsb + hq * f.qsh) * 2;
+    const unsigned char* Gb = static_cast<const unsigned char*>(a.dO) + ((int64_t)b * f.Sq * f.Hq + hq) * kD * 2;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int piece = wave + u * 4;
+      const int row = piece * 4 + (lane >> 4);
+      const int lc = (lane & 15) ^ swz(row);
+      const uint32_t r = (uint32_t)min(r0 + row, (int)f.Sq - 1);
+      dma_b128(Qb + r * (uint32_t)(f.qss * 2) + lc * 16, lds_q + buf * kTileB + piece * 1024);
+      dma_b128(Gb + r * (uint32_t)(f.Hq * kD * 2) + lc * 16, lds_g + buf * kTileB + piece * 1024);
+    }
+    if (wave < 2) {
+      const int r = min(r0 + lane, (int)f.Sq - 1);
+      const int64_t o = ((int64_t)b * f.Hq + hq) * f.Sq + r;
+      if (wave == 0)
+        dma_b32(f.lse + o, lds_l + buf * 256);
+      else
+        dma_b32(a.Dv + o, lds_dv + buf * 256);
+    }
+  };
+
+  dma::f32x16 dk[4], dv[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      dk[db][i] = 0.f;
+      dv[db][i] = 0.f;
+    }
+  float dd = 0.f;
+
+  if (nsteps > 0) stage(0);
+  wait_all_barrier();
+  for (int st = 0; st < nsteps; ++st) {
+    if (st + 1 < nsteps) stage(st + 1);
+    const int buf = st & 1;
+    const int rt = tile_of(st);
+    const int p0 = (int)f.q0 + g_lo + rt * kBq;
+    const unsigned char* QT = sm.q[buf];
+    const unsigned char* GT = sm.g[buf];
+#pragma unroll
+    for (int rh = 0; rh < 2; ++rh) {
+      dma::f32x16 s, dp;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        s[i] = 0.f;
+        dp[i] = 0.f;
+      }
+      // S = Q K^T and dP = dO V^T (rows x keys): lane (l32, hi) reads row rh*32 + l32
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const int row = rh * 32 + l32;
+        s = mfma(row_operand(QT, row, 2 * kk + hi), kf[kk], s);
+        dp = mfma(row_operand(GT, row, 2 * kk + hi), vf[kk], dp);
+      }
+      // register i: row rh*32 + 8(i/4) + 4hi + i%4 of this lane's key
+      dma::bf16x8 pb[2], dsb[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        float pv[8], dsv[8];
+#pragma unroll
+        for (int q4 = 0; q4 < 2; ++q4) {
+          const int rb = rh * 32 + 16 * kb + 8 * q4 + 4 * hi;
+          const float4 lv = *reinterpret_cast<const float4*>(&sm.lse[buf][rb]);
+          const float4 dvv = *reinterpret_cast<const float4*>(&sm.dv[buf][rb]);
+          const float lr[4] = {lv.x, lv.y, lv.z, lv.w};
+          const float dr[4] = {dvv.x, dvv.y, dvv.z, dvv.w};
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int i = kb * 8 + q4 * 4 + r4;
+            const int p = p0 + rb + r4;
+            const bool kept = (uint32_t)(p - j) < (uint32_t)(e - j);
+            const float v = fmaf(s[i], scale2, (dlt - lr[r4]) * kLog2e);
+            const float pp = kept ? __builtin_amdgcn_exp2f(v) : 0.f;
+            const float ds = pp * (dp[i] - dr[r4]);
+            pv[q4 * 4 + r4] = pp;
+            dsv[q4 * 4 + r4] = ds;
+            dd += ds;
+          }
+        }
+        pb[kb] = to_bf16x8(pv);
+        dsb[kb] = to_bf16x8(dsv);
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS over this half's two 16-row k-steps
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          dv[db] = mfma(tr_operand(GT, rh * 32 + 16 * kb, db * 32, lane), pb[kb], dv[db]);
+          dk[db] = mfma(tr_operand(QT, rh * 32 + 16 * kb, db * 32, lane), dsb[kb], dk[db]);
+        }
+    }
+    wait_all_barrier();
+  }
+
+  // partial sums of this group for the lane's key; register i of block db is
+  // d = db*32 + 8(i/4) + 4hi + i%4
+  dd += __shfl_xor(dd, 32);
+  if (real) {
+    const int64_t o = gi * a.cap + slot;
+    float* pk = a.pk + o * kD;
+    float* pvv = a.pv + o * kD;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d = db * 32 + 8 * q4 + 4 * hi;
+        float4 x, y;
+        x.x = f.scale * dk[db][4 * q4 + 0];
+        x.y = f.scale * dk[db][4 * q4 + 1];
+        x.z = f.scale * dk[db][4 * q4 + 2];
+        x.w = f.scale * dk[db][4 * q4 + 3];
+        y.x = dv[db][4 * q4 + 0];
+        y.y = dv[db][4 * q4 + 1];
+        y.z = dv[db][4 * q4 + 2];
+        y.w = dv[db][4 * q4 + 3];
+        *reinterpret_cast<float4*>(pk + d) = x;
+        *reinterpret_cast<float4*>(pvv + d) = y;
+      }
+    if (hi == 0) a.pd[o] = dd;
+  }
+}
+
+// ---------------------------------------------------------------- reduce
+// One wave per key: lane L sums d = 2L, 2L+1 over the key's groups.
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(DmaBwdArgs a) {
+  const DmaAttnArgs& f = a.f;
+  const int64_t seg = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (j >= f.Sk) return;
+  const int b = (int)(seg / f.Hkv), h = (int)(seg % f.Hkv);
+  const int e = f.evict[seg * f.Sk + j];
+  // rows (relative to q0) on which key j is kept
+  const int r0 = max(j, (int)f.q0) - (int)f.q0;
+  const int r1 = min(e, (int)(f.q0 + f.Sq)) - (int)f.q0;
+  float2 sk = {0.f, 0.f}, sv = {0.f, 0.f};
+  float sd = 0.f;
+  if (r0 < r1) {
+    for (int grp = r0 / kGroupRows; grp <= (r1 - 1) / kGroupRows; ++grp) {
+      const int64_t gi = seg * a.n_super + grp;
+      const int32_t* cl = a.cj + gi * a.cap;
+      const int n = a.ccnt[gi];
+      int lo = 0, hi = n;  // first position with cl[pos] >= j
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (cl[mid] < j)
+          lo = mid + 1;
+        else
+          hi = mid;
+      }
+      if (lo >= n || cl[lo] != j) continue;  // a kept key is always listed
+      const int64_t o = gi * a.cap + lo;
+      const float2 x = reinterpret_cast<const float2*>(a.pk + o * kD)[lane];
+      const float2 y = reinterpret_cast<const float2*>(a.pv + o * kD)[lane];
+      sk.x += x.x;
+      sk.y += x.y;
+      sv.x += y.x;
+      sv.y += y.y;
+      sd += a.pd[o];
+    }
+  }
+  const int64_t orow = (((int64_t)b * f.Sk + j) * f.Hkv + h) * kD;
+  reinterpret_cast<float2*>(a.dK + orow)[lane] = sk;
+  reinterpret_cast<float2*>(a.dV + orow)[lane] = sv;
+  if (lane == 0) a.ddelta[seg * f.Sk + j] = sd;
+}
+
+template <int NH>
+hipError_t launch_dq(DmaBwdArgs& a, hipStream_t st) {
+  const int G = (int)(a.f.Hq / a.f.Hkv);
+  dim3 grid((unsigned)a.f.n_tiles, (unsigned)a.f.Hkv, (unsigned)(a.f.B * (G / NH)));
+  hipLaunchKernelGGL(bwd_dq_kernel<NH>, grid, dim3(NH * 128), 0, st, a);
+  return hipGetLastError();
+}
+
+size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+size_t dma_attn_bwd_ws_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Sk,
+                             int64_t w) {
+  int64_t ns = 0, cap = 0;
+  dma_cand_dims(Sq, Sk, w, &ns, &cap);
+  const size_t BH = (size_t)(B * Hkv);
+  const size_t nt = (size_t)((Sq + kBq - 1) / kBq);
+  const size_t nc = BH * (size_t)ns * (size_t)cap;
+  return al256((size_t)(B * Hq * Sq) * 4) + 2 * al256(nc * 4) + al256(BH * ns * 4) +
+         al256(BH * nt * 4) + 2 * al256(nc * kD * 4) + al256(nc * 4);
+}
+
+hipError_t dma_launch_attn_bwd(DmaBwdArgs& a, hipStream_t st) {
+  const DmaAttnArgs& f = a.f;
+  const int64_t BH = f.B * f.Hkv;
+  dma_cand_dims(f.Sq, f.Sk, f.w, &a.n_super, &a.cap);
+  const size_t nt = (size_t)f.n_tiles;
+  const size_t nc = (size_t)BH * (size_t)a.n_super * (size_t)a.cap;
+  unsigned char* p = static_cast<unsigned char*>(f.ws);
+  a.Dv = reinterpret_cast<float*>(p);
+  p += al256((size_t)(f.B * f.Hq * f.Sq) * 4);
+  a.cj = reinterpret_cast<int32_t*>(p);
+  p += al256(nc * 4);
+  a.ce = reinterpret_cast<int32_t*>(p);
+  p += al256(nc * 4);
+  a.ccnt = reinterpret_cast<int32_t*>(p);
+  p += al256((size_t)BH * a.n_super * 4);
+  a.cdmax = reinterpret_cast<float*>(p);
+  p += al256((size_t)BH * nt * 4);
+  a.pk = reinterpret_cast<float*>(p);
+  p += al256(nc * kD * 4);
+  a.pv = reinterpret_cast<float*>(p);
+  p += al256(nc * kD * 4);
+  a.pd = reinterpret_cast<float*>(p);
+
+  const int64_t nrows = f.B * f.Sq * f.Hq;
+  hipLaunchKernelGGL(bwd_dot_kernel, dim3((unsigned)((nrows + 15) / 16)), dim3(256), 0, st,
+                     static_cast<const uint16_t*>(f.O), static_cast<const uint16_t*>(f.ores),
+                     static_cast<const uint16_t*>(a.dO), nrows,
+                     (int)f.Sq, (int)f.Hq, a.Dv);
+  hipError_t e = dma_launch_cand(f.delta, f.evict, BH, f.Sk, f.Sq, f.q0, f.w, a.cj, a.ce, a.ccnt,
+                                 a.cdmax, st);
+  if (e != hipSuccess) return e;
+  // two query heads per workgroup (four waves): with four, the 8 waves'
+  // registers would exceed 256 each and spill
+  const int G = (int)(f.Hq / f.Hkv);
+  e = G % 2 == 0 ? launch_dq<2>(a, st) : launch_dq<1>(a, st);
+  if (e != hipSuccess) return e;
+  dim3 g2((unsigned)((a.cap + kSliceKeys - 1) / kSliceKeys), (unsigned)a.n_super, (unsigned)BH);
+  hipLaunchKernelGGL(bwd_dkv_kernel, g2, dim3(256), 0, st, a);
+  hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((f.Sk + 3) / 4), (unsigned)BH), dim3(256),
+                     0, st, a);
+  return hipGetLastError();
+}

@@ -645,10 +645,20 @@ __global__ __launch_bounds__(NH * 128, 1) void attn_prefill_bf16_kernel(DmaAttnA
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int d = db * 32 + 8 * q4 + 4 * hi;
+        float x[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) x[k] = acc.o[db][q4 * 4 + k] * inv;
         u32x2 u;
-        u[0] = pack_bf16x2(acc.o[db][q4 * 4 + 0] * inv, acc.o[db][q4 * 4 + 1] * inv);
-        u[1] = pack_bf16x2(acc.o[db][q4 * 4 + 2] * inv, acc.o[db][q4 * 4 + 3] * inv);
+        u[0] = pack_bf16x2(x[0], x[1]);
+        u[1] = pack_bf16x2(x[2], x[3]);
         *reinterpret_cast<u32x2*>(orow + d) = u;
+        if (a.ores) {
+          // x - bf16(x) is exact in fp32; stored in bf16 it carries x to ~2^-18
+          u32x2 r;
+          r[0] = pack_bf16x2(x[0] - dma::bf16_lo(u[0]), x[1] - dma::bf16_hi(u[0]));
+          r[1] = pack_bf16x2(x[2] - dma::bf16_lo(u[1]), x[3] - dma::bf16_hi(u[1]));
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.ores) + (orow - static_cast<uint16_t*>(a.O)) + d) = r;
+        }
       }
     if (a.lse && hi == 0)
       a.lse[((int64_t)b * a.Hq + hq) * a.Sq + r_lo + n] = (acc.m + __log2f(lt)) * kLn2 + dmax;

@@ -107,8 +107,38 @@ struct DmaAttnArgs {
   void* O;
   float* lse;
   void* ws;
+  void* ores = nullptr;  // bf16 prefill only: O's rounding residual (fp32 O - bf16 O), or null
 };
 hipError_t dma_launch_attn_prefill_bf16(const DmaAttnArgs& a, hipStream_t st);
+
+// Candidate lists of groups of 8 query tiles (512 rows): the keys some row of
+// the group keeps, ascending, with their eviction rows (mask step T3).
+void dma_cand_dims(int64_t Sq, int64_t Sk, int64_t w, int64_t* n_super, int64_t* cap);
+hipError_t dma_launch_cand(const float* delta, const int32_t* evict, int64_t BH, int64_t Sk,
+                           int64_t Sq, int64_t q0, int64_t w, int32_t* cj, int32_t* ce,
+                           int32_t* ccnt, float* tile_dmax, hipStream_t st);
+
+struct DmaBwdArgs {
+  DmaAttnArgs f;      // forward arguments; f.O is the forward output, f.lse its log-sum-exp
+  const void* dO;     // [B,Sq,Hq,D] contiguous, bf16
+  float* dQ;          // [B,Sq,Hq,D] fp32
+  float* dK;          // [B,Sk,Hkv,D] fp32
+  float* dV;          // [B,Sk,Hkv,D] fp32
+  float* ddelta;      // [B,Hkv,Sk] fp32
+  // workspace
+  float* Dv;          // [B,Hq,Sq]: dO . O per row
+  int32_t* cj;        // candidate keys [B*Hkv, n_super, cap]
+  int32_t* ce;        // their eviction rows
+  int32_t* ccnt;      // [B*Hkv, n_super]
+  float* cdmax;       // [B*Hkv, n_tiles] (written by the candidate kernel, unused)
+  float* pk;          // dK partials [B*Hkv, n_super, cap, D]
+  float* pv;          // dV partials
+  float* pd;          // ddelta partials [B*Hkv, n_super, cap]
+  int64_t n_super, cap;
+};
+size_t dma_attn_bwd_ws_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Sk,
+                             int64_t w);
+hipError_t dma_launch_attn_bwd(DmaBwdArgs& a, hipStream_t st);
 hipError_t dma_launch_attn_prefill_f32(const DmaAttnArgs& a, hipStream_t st);
 hipError_t dma_launch_attn_decode(const DmaAttnArgs& a, int is_bf16, hipStream_t st);
 size_t dma_attn_decode_ws_bytes(int64_t B, int64_t Hq, int64_t D, int64_t u_stride);

@@ -1008,6 +1008,23 @@ hipError_t dma_launch_topk_prefill(const DmaTopkArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+void dma_cand_dims(int64_t Sq, int64_t Sk, int64_t w, int64_t* n_super, int64_t* cap) {
+  *n_super = n_super_of(Sq);
+  *cap = cand_cap(Sk, w);
+}
+
+hipError_t dma_launch_cand(const float* delta, const int32_t* evict, int64_t BH, int64_t Sk,
+                           int64_t Sq, int64_t q0, int64_t w, int32_t* cj, int32_t* ce,
+                           int32_t* ccnt, float* tile_dmax, hipStream_t st) {
+  const int n_super = (int)n_super_of(Sq);
+  const int cap = (int)cand_cap(Sk, w);
+  const int n_tiles = (int)((Sq + kListRows - 1) / kListRows);
+  hipLaunchKernelGGL(cand_kernel, dim3(n_super, (unsigned)BH), dim3(kListWaves * 64), 0, st,
+                     delta, evict, (int)Sk, (int)Sq, (int)q0, n_super, n_tiles, cap, cj, ce, ccnt,
+                     tile_dmax);
+  return hipGetLastError();
+}
+
 hipError_t dma_launch_decode_append(const float* delta, int64_t BH, int64_t Sk, int64_t w,
                                    int32_t* u_idx, int32_t* u_cnt, int32_t* u_nfull,
                                    float* u_dmax, hipStream_t st) {

@@ -14,6 +14,9 @@ seed; draws in this order):
   A        ~ U(0.5, 1.5), fp32, shape [Hkv].
 K and V are drawn one batch slab at a time so that peak fp32 scratch stays
 at one slab even for the 32K-token cache of the decode workload.
+The backward's upstream gradient (make_grad) comes from a second generator
+seeded with seed + 7919: dO ~ N(0, 1) in fp32, rounded to the storage dtype,
+shape [B, Sq, Hq, D].
 """
 import torch
 
@@ -49,3 +52,10 @@ def make_small(B, Hq, Hkv, Sq, Sk, D, w, dtype="bf16", q_offset=0, delta_std=0.0
     wl = Workload("adhoc", dtype, B=B, Hq=Hq, Hkv=Hkv, Sq=Sq, Sk=Sk, q_offset=q_offset,
                   D=D, w=w, delta_std=delta_std, seed=seed)
     return wl, make_inputs(wl, device=device)
+
+
+def make_grad(wl: Workload, device="cpu", seed=None):
+    """Upstream gradient dO [B, Sq, Hq, D] for workload ``wl``."""
+    g = torch.Generator(device=device)
+    g.manual_seed((wl.seed if seed is None else seed) + 7919)
+    return _randn_slabs(g, (wl.B, wl.Sq, wl.Hq, wl.D), _DT[wl.dtype], device)
