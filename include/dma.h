@@ -205,6 +205,28 @@ dma_status dma_attn_fwd_train(const void* Q, const void* K, const void* V, dma_d
                               const float* delta, const dma_mask* mask, float scale, void* O,
                               float* lse, void* O_res, void* stream);
 
+/* Workspace bytes dma_weights_bwd needs: the pre-activation gradient [B,Sk,Hkv]. */
+size_t dma_weights_bwd_workspace_bytes(int64_t B, int64_t Sk, int64_t Hkv);
+
+/*
+ * Backward of step 1 (DMA blog, delta equation), given ddelta = dL/ddelta:
+ *   dpre[b,j,h]  = ddelta * delta * A[h] * sigmoid(pre)   (softplus' = sigmoid)
+ *   dA[h]        = sum_{b,j} ddelta * delta * softplus(pre)
+ *   dDelta[c,h]  = sum_{b,j} V[b,j,c] * dpre[b,j,h]
+ *   dV[b,j,c]   += sum_h dpre[b,j,h] * Delta[c,h]
+ * pre is recomputed from V and Delta as in dma_weights (exact bf16 products).
+ * V, Delta, A, strides as dma_weights (BF16 only); ddelta float [B,Hkv,Sk];
+ * dV float [B,Sk,Hkv*D] contiguous, accumulated into (pass the attention's
+ * dV); dDelta float [Hkv*D,Hkv] and dA float [Hkv] overwritten.
+ * ws: dma_weights_bwd_workspace_bytes bytes (16-byte aligned).
+ * dDelta and dA are sums of per-workgroup partials added atomically, so their
+ * last bits may differ from run to run.
+ */
+dma_status dma_weights_bwd(const void* V, dma_dtype vt, int64_t B, int64_t Sk, int64_t Hkv,
+                           int64_t D, int64_t v_stride_b, int64_t v_stride_s, const float* Delta,
+                           const float* A, const float* ddelta, float* dV, float* dDelta,
+                           float* dA, void* ws, size_t ws_bytes, void* stream);
+
 /* Workspace bytes dma_attn_bwd needs (0 when Sq <= 1). */
 size_t dma_attn_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Sk,
                                     int64_t w);

@@ -243,3 +243,28 @@ def attn_bwd(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, delta: torch.Ten
         _ptr(dO.contiguous()), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dd), _ptr(workspace), nbytes,
         _stream(dev)))
     return dQ, dK, dV, dd
+
+
+def weights_bwd(V: torch.Tensor, Delta: torch.Tensor, A: torch.Tensor, ddelta: torch.Tensor,
+                dV: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Backward of weights() given ddelta [B,Hkv,Sk]: returns (dV, dDelta, dA), float32.
+    dV [B,Sk,Hkv,D] is accumulated into when given (the attention's dV)."""
+    _need_cuda(V, Delta, A, ddelta)
+    B, Sk, Hkv, D = V.shape
+    if V.stride(3) != 1 or V.stride(2) != D:
+        raise ValueError("V rows must be contiguous over (kv head, channel)")
+    dev = V.device
+    if dV is None:
+        dV = torch.zeros(B, Sk, Hkv, D, dtype=torch.float32, device=dev)
+    dDelta = torch.empty(Hkv * D, Hkv, dtype=torch.float32, device=dev)
+    dA = torch.empty(Hkv, dtype=torch.float32, device=dev)
+    lib = load()
+    nbytes = lib.dma_weights_bwd_workspace_bytes(B, Sk, Hkv)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(16, nbytes), dtype=torch.uint8, device=dev)
+    check("dma_weights_bwd", lib.dma_weights_bwd(
+        _ptr(V), _dtype_code(V.dtype), B, Sk, Hkv, D, V.stride(0), V.stride(1),
+        _ptr(Delta.contiguous().float()), _ptr(A.contiguous().float()),
+        _ptr(ddelta.contiguous()), _ptr(dV), _ptr(dDelta), _ptr(dA), _ptr(workspace), nbytes,
+        _stream(dev)))
+    return dV, dDelta, dA

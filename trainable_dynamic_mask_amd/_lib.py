@@ -34,7 +34,8 @@ class DmaMaskDims(ctypes.Structure):
 EXPORTS = ["dma_status_string", "dma_abi_version", "dma_tile_sizes", "dma_mask_dims_for",
            "dma_topk_workspace_bytes", "dma_attn_workspace_bytes", "dma_weights",
            "dma_topk_mask", "dma_decode_keep_append", "dma_attn_fwd",
-           "dma_attn_fwd_train", "dma_attn_bwd_workspace_bytes", "dma_attn_bwd"]
+           "dma_attn_fwd_train", "dma_attn_bwd_workspace_bytes", "dma_attn_bwd",
+           "dma_weights_bwd_workspace_bytes", "dma_weights_bwd"]
 
 _lib = None
 
@@ -90,6 +91,11 @@ def load():
                                        _I64, _P, ctypes.POINTER(DmaMask), ctypes.c_float, _P, _P,
                                        _P, _P]
     lib.dma_attn_fwd_train.restype = ctypes.c_int
+    lib.dma_weights_bwd_workspace_bytes.argtypes = [_I64, _I64, _I64]
+    lib.dma_weights_bwd_workspace_bytes.restype = _SZ
+    lib.dma_weights_bwd.argtypes = [_P, ctypes.c_int, _I64, _I64, _I64, _I64, _I64, _I64, _P, _P,
+                                    _P, _P, _P, _P, _P, _SZ, _P]
+    lib.dma_weights_bwd.restype = ctypes.c_int
     _lib = lib
     return lib
 

@@ -261,6 +261,39 @@ dma_status dma_attn_fwd_train(const void* Q, const void* K, const void* V, dma_d
                        delta, mask, scale, O, lse, O_res, nullptr, 0, stream);
 }
 
+size_t dma_weights_bwd_workspace_bytes(int64_t B, int64_t Sk, int64_t Hkv) {
+  if (B <= 0 || Sk <= 0 || Hkv <= 0) return 0;
+  return (size_t)(B * Sk * Hkv) * sizeof(float);
+}
+
+dma_status dma_weights_bwd(const void* V, dma_dtype vt, int64_t B, int64_t Sk, int64_t Hkv,
+                           int64_t D, int64_t v_stride_b, int64_t v_stride_s, const float* Delta,
+                           const float* A, const float* ddelta, float* dV, float* dDelta,
+                           float* dA, void* ws, size_t ws_bytes, void* stream) {
+  if (vt != DMA_F32 && vt != DMA_BF16) return DMA_ERR_INVALID_ARG;
+  if (B < 0 || Sk < 0 || Hkv < 1 || D < 1) return DMA_ERR_INVALID_ARG;
+  if (vt != DMA_BF16 || (D != 64 && D != 128)) return DMA_ERR_UNSUPPORTED;
+  if (Hkv * D > 2048) return DMA_ERR_UNSUPPORTED;
+  if (Sk > ((int64_t)1 << 31) - 64 || B > 65535) return DMA_ERR_UNSUPPORTED;
+  if (!Delta || !A || !dDelta || !dA) return DMA_ERR_INVALID_ARG;
+  if (v_stride_s < Hkv * D || v_stride_b < 0 || (B > 1 && v_stride_b < v_stride_s * Sk))
+    return DMA_ERR_INVALID_ARG;
+  if (B == 0 || Sk == 0) {
+    // no keys: the gradients of Delta and A are zero
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    dma_launch_fill_zero(dDelta, Hkv * D * Hkv, s);
+    return hip_status(dma_launch_fill_zero(dA, Hkv, s));
+  }
+  if (!V || !ddelta || !dV) return DMA_ERR_INVALID_ARG;
+  if (!aligned16(V) || (v_stride_s * 2) % 16 != 0 || (v_stride_b * 2) % 16 != 0)
+    return DMA_ERR_INVALID_ARG;
+  if (ws_bytes < dma_weights_bwd_workspace_bytes(B, Sk, Hkv) || !ws) return DMA_ERR_WORKSPACE;
+  if (!aligned16(ws)) return DMA_ERR_INVALID_ARG;
+  return hip_status(dma_launch_weights_bwd(V, B, Sk, Hkv, D, v_stride_b, v_stride_s, Delta, A,
+                                           ddelta, dV, dDelta, dA, static_cast<float*>(ws),
+                                           static_cast<hipStream_t>(stream)));
+}
+
 size_t dma_attn_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Sk,
                                     int64_t w) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 1 || Sk <= 0 || w <= 0) return 0;

@@ -64,6 +64,11 @@ __device__ __forceinline__ int rank_below(uint64_t m) {
 
 // ---- host-side launchers (defined next to their kernels) -------------------
 // Each returns hipGetLastError() after enqueueing.
+hipError_t dma_launch_fill_zero(float* p, int64_t n, hipStream_t st);
+hipError_t dma_launch_weights_bwd(const void* V, int64_t B, int64_t Sk, int64_t Hkv, int64_t D,
+                                  int64_t sb, int64_t ss, const float* Delta, const float* A,
+                                  const float* ddelta, float* dV, float* dDelta, float* dA,
+                                  float* dpre, hipStream_t st);
 hipError_t dma_launch_weights(const void* V, int is_bf16, int64_t B, int64_t Sk, int64_t Hkv,
                               int64_t D, int64_t sb, int64_t ss, const float* Delta,
                               const float* A, float* delta, hipStream_t st);

@@ -155,10 +155,15 @@ __device__ __forceinline__ void split3(float d, uint32_t& hi, uint32_t& mid, uin
   lo = dma::f32_to_bf16_bits(r2);
 }
 
-template <int W, int NS>
+// BWD: instead of delta, the epilogue forms the gradient of the
+// pre-activation from ddelta = dL/ddelta (its load travels with the tile's
+// values): dpre[b,j,h] = ddelta * delta * A[h] * sigmoid(pre), and adds
+// ddelta * delta * softplus(pre) over the tile's keys into dA[h].
+template <int W, int NS, bool BWD>
 __global__ __launch_bounds__(64 * W, 2) void weights_mfma_kernel(
     const __bf16* __restrict__ V, int64_t sb, int64_t ss, int Sk, int B, int C, int Hkv, int h0,
-    const float* __restrict__ Delta, const float* __restrict__ A, float* __restrict__ delta) {
+    const float* __restrict__ Delta, const float* __restrict__ A, float* __restrict__ delta,
+    const float* __restrict__ ddelta, float* __restrict__ dpre, float* __restrict__ dA) {
   extern __shared__ __align__(16) unsigned char smem_m[];
   const int nchunks = C / 8;
   uint4* ds = reinterpret_cast<uint4*>(smem_m);        // [C/8][25] chunks of 8 bf16
@@ -174,7 +179,9 @@ __global__ __launch_bounds__(64 * W, 2) void weights_mfma_kernel(
 
   // every load is issued (steps past this wave's range repeat its last chunk,
   // keys past the end repeat the last key), so the load count never branches
-  auto issue = [&](uint4 (&buf)[NS], int t) {
+  // the epilogue thread (key nn, head h) of this thread's index
+  const int e_nn = threadIdx.x % kKeysPerTile, e_h = min((int)threadIdx.x / kKeysPerTile, 7);
+  auto issue = [&](uint4 (&buf)[NS], float& gd, int t) {
     const int b = t / tps;
     const int j = min((t - b * tps) * kKeysPerTile + n, Sk - 1);
     const __bf16* row = V + (int64_t)b * sb + (int64_t)j * ss;
@@ -183,13 +190,17 @@ __global__ __launch_bounds__(64 * W, 2) void weights_mfma_kernel(
       const int kc = 2 * max(0, min(s0 + min(s, ns - 1), nsteps - 1)) + hh;
       buf[s] = *reinterpret_cast<const uint4*>(row + kc * 8);
     }
+    if constexpr (BWD) {
+      const int je = min((t - b * tps) * kKeysPerTile + e_nn, Sk - 1);
+      gd = ddelta[((int64_t)b * Hkv + min(h0 + e_h, Hkv - 1)) * Sk + je];
+    }
   };
 
   // the epilogue thread (key nn, head h) needs A[h0+h]: loaded once, up front,
   // since a load inside the loop would also wait for the prefetched tile
   const float a_h = A[min(h0 + (int)(threadIdx.x / kKeysPerTile) % 8, Hkv - 1)];
 
-  auto consume = [&](const uint4 (&buf)[NS], int t, float* rb) {
+  auto consume = [&](const uint4 (&buf)[NS], float gd, int t, float* rb) {
     dma::f32x16 acc = {};
     const uint4* arow = ds + (2 * s0 + hh) * kSplitRows + min(n, kSplitRows - 1);
 #pragma unroll
@@ -218,8 +229,20 @@ __global__ __launch_bounds__(64 * W, 2) void weights_mfma_kernel(
       const float x = xh + (xm + xl);
       const int b = t / tps;
       const int j = (t - b * tps) * kKeysPerTile + nn;
-      if (j < Sk && h0 + h < Hkv)
-        delta[((int64_t)b * Hkv + h0 + h) * Sk + j] = expf(softplus_f(x) * a_h);
+      const bool valid = j < Sk && h0 + h < Hkv;
+      if constexpr (!BWD) {
+        if (valid) delta[((int64_t)b * Hkv + h0 + h) * Sk + j] = expf(softplus_f(x) * a_h);
+      } else {
+        const float sp = softplus_f(x);
+        const float dl = expf(sp * a_h);
+        const float sig = 1.f / (1.f + expf(-x));
+        if (valid) dpre[((int64_t)b * Sk + j) * Hkv + h0 + h] = gd * dl * a_h * sig;
+        // dA[h]: sum over the tile's 32 keys (one 32-lane half of a wave)
+        float g = valid ? gd * dl * sp : 0.f;
+#pragma unroll
+        for (int o = 16; o >= 1; o >>= 1) g += __shfl_xor(g, o);
+        if (nn == 0 && h0 + h < Hkv) atomicAdd(&dA[h0 + h], g);
+      }
     }
   };
 
@@ -237,8 +260,9 @@ __global__ __launch_bounds__(64 * W, 2) void weights_mfma_kernel(
     for (int e = 0; e < 8; ++e) d[u][e] = Delta[(int64_t)(kc * 8 + e) * Hkv + min(h0 + h, Hkv - 1)];
   }
   uint4 b0[NS], b1[NS];
+  float g0 = 0.f, g1 = 0.f;
   int t = blockIdx.x;  // the grid never exceeds the tile count
-  issue(b0, t);
+  issue(b0, g0, t);
 #pragma unroll
   for (int u = 0; u < kSlots; ++u) {
     const int q = u * 64 * W + (int)threadIdx.x;
@@ -266,20 +290,95 @@ __global__ __launch_bounds__(64 * W, 2) void weights_mfma_kernel(
   while (true) {
     const int t1 = t + gridDim.x;
     if (t1 >= ntiles) {
-      consume(b0, t, red0);
+      consume(b0, g0, t, red0);
       break;
     }
-    issue(b1, t1);
-    consume(b0, t, red0);
+    issue(b1, g1, t1);
+    consume(b0, g0, t, red0);
     const int t2 = t1 + gridDim.x;
     if (t2 >= ntiles) {
-      consume(b1, t1, red1);
+      consume(b1, g1, t1, red1);
       break;
     }
-    issue(b0, t2);
-    consume(b1, t1, red1);
+    issue(b0, g0, t2);
+    consume(b1, g1, t1, red1);
     t = t2;
   }
+}
+
+// Backward of the contraction, given dpre [B,Sk,Hkv]: one workgroup per
+// (batch, 256 keys), thread t owning channels t, t+256, ... (KC of them) and
+// eight heads at a time:
+//   dV[b,j,c]   += sum_h dpre[b,j,h] Delta[c,h]     (added to the attention's dV)
+//   dDelta[c,h] += sum_j V[b,j,c] dpre[b,j,h]       (per-workgroup sums, then atomics)
+constexpr int kBwdKeys = 256;
+
+template <int KC>
+__global__ __launch_bounds__(256) void weights_bwd_kernel(const __bf16* __restrict__ V, int64_t sb,
+                                                          int64_t ss, int Sk, int C, int Hkv,
+                                                          const float* __restrict__ Delta,
+                                                          const float* __restrict__ dpre,
+                                                          float* __restrict__ dV,
+                                                          float* __restrict__ dDelta) {
+  __shared__ float s_p[64][8];
+  const int b = blockIdx.y, jb0 = blockIdx.x * kBwdKeys, tid = threadIdx.x;
+  const __bf16* Vb = V + (int64_t)b * sb;
+  for (int h0 = 0; h0 < Hkv; h0 += 8) {
+    float dD[KC][8], Dl[KC][8];
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+      const int c = min(tid + 256 * k, C - 1);
+#pragma unroll
+      for (int h = 0; h < 8; ++h) {
+        dD[k][h] = 0.f;
+        Dl[k][h] = h0 + h < Hkv ? Delta[(int64_t)c * Hkv + h0 + h] : 0.f;
+      }
+    }
+    for (int jb = jb0; jb < min(jb0 + kBwdKeys, Sk); jb += 64) {
+      __syncthreads();
+      for (int e = tid; e < 64 * 8; e += 256) {
+        const int jj = e >> 3, h = e & 7;
+        const int j = jb + jj;
+        s_p[jj][h] = (j < Sk && h0 + h < Hkv) ? dpre[((int64_t)b * Sk + j) * Hkv + h0 + h] : 0.f;
+      }
+      __syncthreads();
+      const int nj = min(64, Sk - jb);
+      for (int jj = 0; jj < nj; ++jj) {
+        const int j = jb + jj;
+        float p[8];
+#pragma unroll
+        for (int h = 0; h < 8; ++h) p[h] = s_p[jj][h];
+#pragma unroll
+        for (int k = 0; k < KC; ++k) {
+          const int c = tid + 256 * k;
+          if (c < C) {
+            const float v = (float)Vb[(int64_t)j * ss + c];
+            float acc = 0.f;
+#pragma unroll
+            for (int h = 0; h < 8; ++h) {
+              dD[k][h] = fmaf(v, p[h], dD[k][h]);
+              acc = fmaf(p[h], Dl[k][h], acc);
+            }
+            dV[((int64_t)b * Sk + j) * C + c] += acc;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < KC; ++k) {
+      const int c = tid + 256 * k;
+      if (c < C)
+#pragma unroll
+        for (int h = 0; h < 8; ++h)
+          if (h0 + h < Hkv) atomicAdd(&dDelta[(int64_t)c * Hkv + h0 + h], dD[k][h]);
+    }
+  }
+}
+
+__global__ void fill_zero_kernel(float* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0.f;
 }
 
 int cu_count() {
@@ -296,25 +395,41 @@ int cu_count() {
   return cached[dev];
 }
 
-template <int W, int NS>
+template <int W, int NS, bool BWD = false>
 hipError_t launch_mfma(const __bf16* V, int64_t B, int64_t Sk, int64_t Hkv, int64_t D, int64_t sb,
                        int64_t ss, const float* Delta, const float* A, float* delta,
-                       hipStream_t st) {
+                       hipStream_t st, const float* ddelta = nullptr, float* dpre = nullptr,
+                       float* dA = nullptr) {
   const int C = (int)(Hkv * D);
   const size_t lds = (size_t)C / 8 * kSplitRows * 16 + (size_t)2 * W * kRedRows * 64 * 4;
   const int64_t ntiles = B * ((Sk + kKeysPerTile - 1) / kKeysPerTile);
   const int per_cu = std::max<int>(1, (int)((160 * 1024) / lds));
   const int64_t grid = std::min<int64_t>(ntiles, (int64_t)cu_count() * per_cu);
-  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&weights_mfma_kernel<W, NS>),
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&weights_mfma_kernel<W, NS, BWD>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   for (int h0 = 0; h0 < Hkv; h0 += 8)
-    hipLaunchKernelGGL((weights_mfma_kernel<W, NS>), dim3((unsigned)grid), dim3(64 * W), lds, st,
-                       V, sb, ss, (int)Sk, (int)B, C, (int)Hkv, h0, Delta, A, delta);
+    hipLaunchKernelGGL((weights_mfma_kernel<W, NS, BWD>), dim3((unsigned)grid), dim3(64 * W), lds,
+                       st, V, sb, ss, (int)Sk, (int)B, C, (int)Hkv, h0, Delta, A, delta, ddelta,
+                       dpre, dA);
   return hipGetLastError();
 }
 
 // k-steps of 16 channels: C/16 = Hkv*D/16 <= 128; four waves share them up to
 // C = 1024, eight above, so that no wave takes more than 16.
+hipError_t launch_bf16_bwd(const __bf16* V, int64_t B, int64_t Sk, int64_t Hkv, int64_t D,
+                           int64_t sb, int64_t ss, const float* Delta, const float* A,
+                           const float* ddelta, float* dpre, float* dA, hipStream_t st) {
+  const int64_t nsteps = Hkv * D / 16;
+  if (nsteps > 64)
+    return launch_mfma<8, 16, true>(V, B, Sk, Hkv, D, sb, ss, Delta, A, nullptr, st, ddelta, dpre, dA);
+  const int64_t per = (nsteps + 3) / 4;
+  if (per > 8)
+    return launch_mfma<4, 16, true>(V, B, Sk, Hkv, D, sb, ss, Delta, A, nullptr, st, ddelta, dpre, dA);
+  if (per > 4)
+    return launch_mfma<4, 8, true>(V, B, Sk, Hkv, D, sb, ss, Delta, A, nullptr, st, ddelta, dpre, dA);
+  return launch_mfma<4, 4, true>(V, B, Sk, Hkv, D, sb, ss, Delta, A, nullptr, st, ddelta, dpre, dA);
+}
+
 hipError_t launch_bf16(const __bf16* V, int64_t B, int64_t Sk, int64_t Hkv, int64_t D, int64_t sb,
                        int64_t ss, const float* Delta, const float* A, float* delta,
                        hipStream_t st) {
@@ -350,6 +465,35 @@ hipError_t launch_f32_t(const float* V, int64_t B, int64_t Sk, int64_t Hkv, int6
 }
 
 }  // namespace
+
+hipError_t dma_launch_fill_zero(float* p, int64_t n, hipStream_t st) {
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(64), dim3(256), 0, st, p, n);
+  return hipGetLastError();
+}
+
+hipError_t dma_launch_weights_bwd(const void* V, int64_t B, int64_t Sk, int64_t Hkv, int64_t D,
+                                  int64_t sb, int64_t ss, const float* Delta, const float* A,
+                                  const float* ddelta, float* dV, float* dDelta, float* dA,
+                                  float* dpre, hipStream_t st) {
+  const int C = (int)(Hkv * D);
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(64), dim3(256), 0, st, dDelta, (int64_t)C * Hkv);
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(1), dim3(256), 0, st, dA, Hkv);
+  const __bf16* Vb = static_cast<const __bf16*>(V);
+  hipError_t e = launch_bf16_bwd(Vb, B, Sk, Hkv, D, sb, ss, Delta, A, ddelta, dpre, dA, st);
+  if (e != hipSuccess) return e;
+  dim3 grid((unsigned)((Sk + kBwdKeys - 1) / kBwdKeys), (unsigned)B);
+  const int kc = (C + 255) / 256;
+  if (kc <= 2)
+    hipLaunchKernelGGL(weights_bwd_kernel<2>, grid, dim3(256), 0, st, Vb, sb, ss, (int)Sk, C,
+                       (int)Hkv, Delta, dpre, dV, dDelta);
+  else if (kc <= 4)
+    hipLaunchKernelGGL(weights_bwd_kernel<4>, grid, dim3(256), 0, st, Vb, sb, ss, (int)Sk, C,
+                       (int)Hkv, Delta, dpre, dV, dDelta);
+  else
+    hipLaunchKernelGGL(weights_bwd_kernel<8>, grid, dim3(256), 0, st, Vb, sb, ss, (int)Sk, C,
+                       (int)Hkv, Delta, dpre, dV, dDelta);
+  return hipGetLastError();
+}
 
 hipError_t dma_launch_weights(const void* V, int is_bf16, int64_t B, int64_t Sk, int64_t Hkv,
                               int64_t D, int64_t sb, int64_t ss, const float* Delta,
