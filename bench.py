@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU time budget of the oracle sample")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the training backward instead (attention and weights "
+                         "gradients after a training forward); prints its own JSON line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (the reference "
                          "reading of the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -127,6 +130,60 @@ def cpu_baseline(x, wl, budget_s):
             "seconds": round(t_w + t_rows, 2)}
 
 
+def backward_bench(args, wl, x, dev):
+    """Backward of the DMA forward: attention gradients (dQ, dK, dV, ddelta) then the
+    weights gradients (dDelta, dA, the value-row part of dV), timed with events on the
+    launch stream.  Effective FLOPs: 8*D per kept pair (the dQ, dK, dV and dP
+    products; the recomputed scores are not counted)."""
+    import torch
+    import trainable_dynamic_mask_amd as dma
+    from trainable_dynamic_mask_amd.inputs import make_grad
+
+    dO = make_grad(wl, device=dev)
+    delta = dma.weights(x["V"], x["Delta"], x["A"])
+    mask = dma.topk_mask(delta, wl.Sq, wl.q_offset, wl.w)
+    O, lse, Ores = dma.attn_fwd_train(x["Q"], x["K"], x["V"], delta, mask)
+    lib = dma.load()
+    ws = torch.empty(max(256, lib.dma_attn_bwd_workspace_bytes(wl.B, wl.Hq, wl.Hkv, wl.Sq,
+                                                                 wl.Sk, wl.w)),
+                     dtype=torch.uint8, device=dev)
+    wsw = torch.empty(max(16, lib.dma_weights_bwd_workspace_bytes(wl.B, wl.Sk, wl.Hkv)),
+                      dtype=torch.uint8, device=dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+
+    def step(e=None):
+        if e:
+            e[0].record()
+        dQ, dK, dV, dd = dma.attn_bwd(x["Q"], x["K"], x["V"], delta, mask, O, lse, dO,
+                                      O_res=Ores, workspace=ws)
+        if e:
+            e[1].record()
+        dma.weights_bwd(x["V"], x["Delta"], x["A"], dd, dV=dV, workspace=wsw)
+        if e:
+            e[2].record()
+        return dQ
+
+    for _ in range(max(3, args.warmup // 10)):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        dQ = step(ev[k])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    ta = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    tw = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    assert torch.isfinite(dQ).all(), "non-finite gradient"
+    flops = 2 * wl.effective_flops()
+    out = {"metric": "effective TFLOP/s (kept pairs) of the DMA backward, 1 MI355X",
+           "value": round(flops / (ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
+           "ms_per_step": round(ms, 4), "steps": args.steps, "dtype": wl.dtype,
+           "data": "synthetic", "config": {"workload": wl.name, "effective_flop": flops},
+           "stages_ms": {"attention_bwd": round(ta, 4), "weights_bwd": round(tw, 4)},
+           "attention_bwd_tflops": round(flops / (ta * 1e-3) / 1e12, 2)}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -147,6 +204,9 @@ def main():
     torch.cuda.set_device(dev)
     lib = dma.load()
     x = make_inputs(wl, device=dev)
+    if args.backward:
+        backward_bench(args, wl, x, dev)
+        return
     delta = torch.empty(wl.B, wl.Hkv, wl.Sk, dtype=torch.float32, device=dev)
     mask = dma.alloc_mask(wl.B, wl.Hkv, wl.Sq, wl.Sk, wl.q_offset, wl.w, dev)
     ws_t = torch.empty(max(16, lib.dma_topk_workspace_bytes(wl.B, wl.Hkv, wl.Sq, wl.Sk, wl.w)),

@@ -29,7 +29,8 @@
 //           candidate is kept on most rows.
 //   reduce  key j is kept on rows [j, e_j), i.e. in groups j/512 ..
 //           (e_j-1)/512; it sums its partials over those groups, finding its
-//           place in each group's ascending list by binary search.
+//           place in each group's list through a dense (group, key) map that
+//           the dkv kernel writes.
 // LDS tiles are 64 rows of 256 bytes.  The 16-byte chunk c of row r is
 // stored at c ^ (((r & 3) << 2) | ((r >> 2) & 3)): 16 consecutive rows put
 // one chunk on 16 distinct chunk slots (row reads), and 4 consecutive rows
@@ -532,12 +533,16 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(DmaBwdArgs a) {
         *reinterpret_cast<float4*>(pk + d) = x;
         *reinterpret_cast<float4*>(pvv + d) = y;
       }
-    if (hi == 0) a.pd[o] = dd;
+    if (hi == 0) {
+      a.pd[o] = dd;
+      a.pmap[gi * f.Sk + j] = slot;
+    }
   }
 }
 
 // ---------------------------------------------------------------- reduce
-// One wave per key: lane L sums d = 2L, 2L+1 over the key's groups.
+// One wave per key: lane L sums d = 2L, 2L+1 over the key's groups; the
+// groups' partial rows are independent loads, four in flight.
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(DmaBwdArgs a) {
   const DmaAttnArgs& f = a.f;
   const int64_t seg = blockIdx.y;
@@ -552,27 +557,29 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(DmaBwdArgs a) {
   float2 sk = {0.f, 0.f}, sv = {0.f, 0.f};
   float sd = 0.f;
   if (r0 < r1) {
-    for (int grp = r0 / kGroupRows; grp <= (r1 - 1) / kGroupRows; ++grp) {
-      const int64_t gi = seg * a.n_super + grp;
-      const int32_t* cl = a.cj + gi * a.cap;
-      const int n = a.ccnt[gi];
-      int lo = 0, hi = n;  // first position with cl[pos] >= j
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (cl[mid] < j)
-          lo = mid + 1;
-        else
-          hi = mid;
+    const int g0 = r0 / kGroupRows, g1 = (r1 - 1) / kGroupRows;
+    for (int gb = g0; gb <= g1; gb += 4) {
+      int64_t o[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t gi = seg * a.n_super + min(gb + u, g1);
+        // a kept key is a candidate of each of these groups; the clamp only keeps
+        // the read inside the group's rows whatever the map holds
+        o[u] = gi * a.cap + min(max(a.pmap[gi * f.Sk + j], 0), (int)a.cap - 1);
       }
-      if (lo >= n || cl[lo] != j) continue;  // a kept key is always listed
-      const int64_t o = gi * a.cap + lo;
-      const float2 x = reinterpret_cast<const float2*>(a.pk + o * kD)[lane];
-      const float2 y = reinterpret_cast<const float2*>(a.pv + o * kD)[lane];
-      sk.x += x.x;
-      sk.y += x.y;
-      sv.x += y.x;
-      sv.y += y.y;
-      sd += a.pd[o];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float2 x = reinterpret_cast<const float2*>(a.pk + o[u] * kD)[lane];
+        const float2 y = reinterpret_cast<const float2*>(a.pv + o[u] * kD)[lane];
+        const float z = a.pd[o[u]];
+        if (gb + u <= g1) {
+          sk.x += x.x;
+          sk.y += x.y;
+          sv.x += y.x;
+          sv.y += y.y;
+          sd += z;
+        }
+      }
     }
   }
   const int64_t orow = (((int64_t)b * f.Sk + j) * f.Hkv + h) * kD;
@@ -601,7 +608,8 @@ size_t dma_attn_bwd_ws_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int
   const size_t nt = (size_t)((Sq + kBq - 1) / kBq);
   const size_t nc = BH * (size_t)ns * (size_t)cap;
   return al256((size_t)(B * Hq * Sq) * 4) + 2 * al256(nc * 4) + al256(BH * ns * 4) +
-         al256(BH * nt * 4) + 2 * al256(nc * kD * 4) + al256(nc * 4);
+         al256(BH * nt * 4) + 2 * al256(nc * kD * 4) + al256(nc * 4) +
+         al256(BH * (size_t)ns * (size_t)Sk * 4);
 }
 
 hipError_t dma_launch_attn_bwd(DmaBwdArgs& a, hipStream_t st) {
@@ -626,6 +634,8 @@ hipError_t dma_launch_attn_bwd(DmaBwdArgs& a, hipStream_t st) {
   a.pv = reinterpret_cast<float*>(p);
   p += al256(nc * kD * 4);
   a.pd = reinterpret_cast<float*>(p);
+  p += al256(nc * 4);
+  a.pmap = reinterpret_cast<int32_t*>(p);
 
   const int64_t nrows = f.B * f.Sq * f.Hq;
   hipLaunchKernelGGL(bwd_dot_kernel, dim3((unsigned)((nrows + 15) / 16)), dim3(256), 0, st,

@@ -139,6 +139,7 @@ struct DmaBwdArgs {
   float* pk;          // dK partials [B*Hkv, n_super, cap, D]
   float* pv;          // dV partials
   float* pd;          // ddelta partials [B*Hkv, n_super, cap]
+  int32_t* pmap;      // [B*Hkv, n_super, Sk]: a group's candidate position of key j
   int64_t n_super, cap;
 };
 size_t dma_attn_bwd_ws_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Sk,

@@ -307,71 +307,66 @@ __global__ __launch_bounds__(64 * W, 2) void weights_mfma_kernel(
 }
 
 // Backward of the contraction, given dpre [B,Sk,Hkv]: one workgroup per
-// (batch, 256 keys), thread t owning channels t, t+256, ... (KC of them) and
-// eight heads at a time:
+// (batch, 256 keys, 256 channels), one channel per thread, eight heads at a
+// time, eight keys per step so that their loads are in flight together:
 //   dV[b,j,c]   += sum_h dpre[b,j,h] Delta[c,h]     (added to the attention's dV)
 //   dDelta[c,h] += sum_j V[b,j,c] dpre[b,j,h]       (per-workgroup sums, then atomics)
 constexpr int kBwdKeys = 256;
 
-template <int KC>
 __global__ __launch_bounds__(256) void weights_bwd_kernel(const __bf16* __restrict__ V, int64_t sb,
                                                           int64_t ss, int Sk, int C, int Hkv,
                                                           const float* __restrict__ Delta,
                                                           const float* __restrict__ dpre,
                                                           float* __restrict__ dV,
                                                           float* __restrict__ dDelta) {
-  __shared__ float s_p[64][8];
-  const int b = blockIdx.y, jb0 = blockIdx.x * kBwdKeys, tid = threadIdx.x;
-  const __bf16* Vb = V + (int64_t)b * sb;
+  __shared__ float s_p[kBwdKeys][8];
+  const int b = blockIdx.z, jb = blockIdx.x * kBwdKeys, tid = threadIdx.x;
+  const int c = blockIdx.y * 256 + tid;
+  const int cc = min(c, C - 1);
+  const int nj = min(kBwdKeys, Sk - jb);
+  const __bf16* Vb = V + (int64_t)b * sb + (int64_t)jb * ss + cc;
+  float* dVb = dV + ((int64_t)b * Sk + jb) * C + cc;
   for (int h0 = 0; h0 < Hkv; h0 += 8) {
-    float dD[KC][8], Dl[KC][8];
+    float dD[8], Dl[8];
 #pragma unroll
-    for (int k = 0; k < KC; ++k) {
-      const int c = min(tid + 256 * k, C - 1);
-#pragma unroll
-      for (int h = 0; h < 8; ++h) {
-        dD[k][h] = 0.f;
-        Dl[k][h] = h0 + h < Hkv ? Delta[(int64_t)c * Hkv + h0 + h] : 0.f;
-      }
+    for (int h = 0; h < 8; ++h) {
+      dD[h] = 0.f;
+      Dl[h] = h0 + h < Hkv ? Delta[(int64_t)cc * Hkv + h0 + h] : 0.f;
     }
-    for (int jb = jb0; jb < min(jb0 + kBwdKeys, Sk); jb += 64) {
-      __syncthreads();
-      for (int e = tid; e < 64 * 8; e += 256) {
-        const int jj = e >> 3, h = e & 7;
-        const int j = jb + jj;
-        s_p[jj][h] = (j < Sk && h0 + h < Hkv) ? dpre[((int64_t)b * Sk + j) * Hkv + h0 + h] : 0.f;
+    __syncthreads();
+    for (int e = tid; e < kBwdKeys * 8; e += 256) {
+      const int jj = e >> 3, h = e & 7;
+      s_p[jj][h] = (jj < nj && h0 + h < Hkv) ? dpre[((int64_t)b * Sk + jb + jj) * Hkv + h0 + h]
+                                             : 0.f;
+    }
+    __syncthreads();
+    for (int j8 = 0; j8 < nj; j8 += 8) {
+      float v[8], o[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int jj = min(j8 + u, nj - 1);
+        v[u] = (float)Vb[(int64_t)jj * ss];
+        o[u] = dVb[(int64_t)jj * C];
       }
-      __syncthreads();
-      const int nj = min(64, Sk - jb);
-      for (int jj = 0; jj < nj; ++jj) {
-        const int j = jb + jj;
-        float p[8];
 #pragma unroll
-        for (int h = 0; h < 8; ++h) p[h] = s_p[jj][h];
+      for (int u = 0; u < 8; ++u) {
+        const int jj = j8 + u;
+        if (jj < nj) {
+          float acc = 0.f;
 #pragma unroll
-        for (int k = 0; k < KC; ++k) {
-          const int c = tid + 256 * k;
-          if (c < C) {
-            const float v = (float)Vb[(int64_t)j * ss + c];
-            float acc = 0.f;
-#pragma unroll
-            for (int h = 0; h < 8; ++h) {
-              dD[k][h] = fmaf(v, p[h], dD[k][h]);
-              acc = fmaf(p[h], Dl[k][h], acc);
-            }
-            dV[((int64_t)b * Sk + j) * C + c] += acc;
+          for (int h = 0; h < 8; ++h) {
+            const float p = s_p[jj][h];
+            dD[h] = fmaf(v[u], p, dD[h]);
+            acc = fmaf(p, Dl[h], acc);
           }
+          if (c < C) dVb[(int64_t)jj * C] = o[u] + acc;
         }
       }
     }
+    if (c < C)
 #pragma unroll
-    for (int k = 0; k < KC; ++k) {
-      const int c = tid + 256 * k;
-      if (c < C)
-#pragma unroll
-        for (int h = 0; h < 8; ++h)
-          if (h0 + h < Hkv) atomicAdd(&dDelta[(int64_t)c * Hkv + h0 + h], dD[k][h]);
-    }
+      for (int h = 0; h < 8; ++h)
+        if (h0 + h < Hkv) atomicAdd(&dDelta[(int64_t)c * Hkv + h0 + h], dD[h]);
   }
 }
 
@@ -481,17 +476,9 @@ hipError_t dma_launch_weights_bwd(const void* V, int64_t B, int64_t Sk, int64_t 
   const __bf16* Vb = static_cast<const __bf16*>(V);
   hipError_t e = launch_bf16_bwd(Vb, B, Sk, Hkv, D, sb, ss, Delta, A, ddelta, dpre, dA, st);
   if (e != hipSuccess) return e;
-  dim3 grid((unsigned)((Sk + kBwdKeys - 1) / kBwdKeys), (unsigned)B);
-  const int kc = (C + 255) / 256;
-  if (kc <= 2)
-    hipLaunchKernelGGL(weights_bwd_kernel<2>, grid, dim3(256), 0, st, Vb, sb, ss, (int)Sk, C,
-                       (int)Hkv, Delta, dpre, dV, dDelta);
-  else if (kc <= 4)
-    hipLaunchKernelGGL(weights_bwd_kernel<4>, grid, dim3(256), 0, st, Vb, sb, ss, (int)Sk, C,
-                       (int)Hkv, Delta, dpre, dV, dDelta);
-  else
-    hipLaunchKernelGGL(weights_bwd_kernel<8>, grid, dim3(256), 0, st, Vb, sb, ss, (int)Sk, C,
-                       (int)Hkv, Delta, dpre, dV, dDelta);
+  dim3 grid((unsigned)((Sk + kBwdKeys - 1) / kBwdKeys), (unsigned)((C + 255) / 256), (unsigned)B);
+  hipLaunchKernelGGL(weights_bwd_kernel, grid, dim3(256), 0, st, Vb, sb, ss, (int)Sk, C, (int)Hkv,
+                     Delta, dpre, dV, dDelta);
   return hipGetLastError();
 }
 
