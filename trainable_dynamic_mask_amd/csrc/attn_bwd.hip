@@ -174,7 +174,7 @@ struct DqSmem {
 };
 
 template <int NH>
-__global__ __launch_bounds__(NH * 128, 1) void bwd_dq_kernel(DmaBwdArgs a) {
+__global__ __launch_bounds__(NH * 128, 2) void bwd_dq_kernel(DmaBwdArgs a) {
   constexpr int NW = NH * 2;
   __shared__ __align__(16) DqSmem sm;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -231,11 +231,15 @@ __global__ __launch_bounds__(NH * 128, 1) void bwd_dq_kernel(DmaBwdArgs a) {
   // tile, piece p by wave p % NW; lane L fills row 4p + L/16, chunk slot L%16
   auto gather = [&](int x) {
     const int buf = x & 1;
+    // recomputed on every call: hoisted out of the loop, these lane constants
+    // would be held (and spilled) across it
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
 #pragma unroll
     for (int u = 0; u < 16 / NW; ++u) {
       const int piece = wave + u * NW;
-      const int row = piece * 4 + (lane >> 4);
-      const int lc = (lane & 15) ^ swz(row);
+      const int row = piece * 4 + (ln >> 4);
+      const int lc = (ln & 15) ^ swz(row);
       const uint32_t j = (uint32_t)sm.jl[x % 3][row];
       dma_b128(Kg + j * rowb + lc * 16, lds_k + buf * kTileB + piece * 1024);
       dma_b128(Vg + j * rowb + lc * 16, lds_v + buf * kTileB + piece * 1024);
@@ -269,44 +273,53 @@ __global__ __launch_bounds__(NH * 128, 1) void bwd_dq_kernel(DmaBwdArgs a) {
 
     const unsigned char* KT = sm.k[c & 1];
     const unsigned char* VT = sm.v[c & 1];
-    dma::f32x16 s[2], dp[2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        s[mb][i] = 0.f;
-        dp[mb][i] = 0.f;
-      }
-    // S^T = K Q^T and dP^T = V dO^T: lane (l32, hi) reads key row mb*32 + l32
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const int row = mb * 32 + l32;
-        s[mb] = mfma(row_operand(KT, row, 2 * kk + hi), qf[kk], s[mb]);
-        dp[mb] = mfma(row_operand(VT, row, 2 * kk + hi), gf[kk], dp[mb]);
-      }
-    // dS^T = P^T (dP^T - Dv); register i of block mb is key mb*32 + 8(i/4) + 4hi + i%4
+    // one 32-key block at a time: S^T = K Q^T and dP^T = V dO^T (two
+    // interleaved accumulator chains; lane (l32, hi) reads key row mb*32 + l32),
+    // then dS^T = P^T (dP^T - Dv) as bf16 B operands; register i of the block
+    // is key mb*32 + 8(i/4) + 4hi + i%4
     dma::bf16x8 dsb[2][2];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < 2; ++mb) {
+      dma::f32x16 s, dp;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        s[i] = 0.f;
+        dp[i] = 0.f;
+      }
+      const int row = mb * 32 + l32;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        s = mfma(row_operand(KT, row, 2 * kk + hi), qf[kk], s);
+        dp = mfma(row_operand(VT, row, 2 * kk + hi), gf[kk], dp);
+      }
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         float ds[8];
 #pragma unroll
-        for (int t8 = 0; t8 < 8; ++t8) {
-          const int i = hf * 8 + t8;
-          const int key = mb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-          const int j = sm.jl[c % 3][key];
-          const int e = sm.ev[c & 1][key];
-          const float dlt = sm.dl[c & 1][key];
-          const bool kept = c * kBk + key < cnt && (uint32_t)(pos - j) < (uint32_t)(e - j);
-          const float v = fmaf(s[mb][i], scale2, (dlt - dmax) * kLog2e) - lq;
-          const float p = kept ? __builtin_amdgcn_exp2f(v) : 0.f;
-          ds[t8] = p * (dp[mb][i] - dv_q);
+        for (int h4 = 0; h4 < 2; ++h4) {
+          // registers 4*q4 .. 4*q4+3 are keys kb .. kb+3
+          const int q4 = 2 * hf + h4;
+          const int kb = mb * 32 + 8 * q4 + 4 * hi;
+          const int4 j4 = *reinterpret_cast<const int4*>(&sm.jl[c % 3][kb]);
+          const int4 e4 = *reinterpret_cast<const int4*>(&sm.ev[c & 1][kb]);
+          const float4 d4 = *reinterpret_cast<const float4*>(&sm.dl[c & 1][kb]);
+          const int jv[4] = {j4.x, j4.y, j4.z, j4.w};
+          const int ev[4] = {e4.x, e4.y, e4.z, e4.w};
+          const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = 4 * q4 + r;
+            // list padding (positions past cnt) and rows outside [j, e) get weight 0
+            const bool kept = (c * kBk + kb + r < cnt) &
+                              ((uint32_t)(pos - jv[r]) < (uint32_t)(ev[r] - jv[r]));
+            const float v = fmaf(s[i], scale2, (dv[r] - dmax) * kLog2e) - lq;
+            const float p = __builtin_amdgcn_exp2f(kept ? v : -INFINITY);
+            ds[4 * h4 + r] = p * (dp[i] - dv_q);
+          }
         }
         dsb[mb][hf] = to_bf16x8(ds);
       }
+    }
     // dQ^T += K^T dS^T: k-step (mb, hf) covers keys mb*32 + 16*hf + [0, 16)
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
@@ -487,7 +500,7 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(DmaBwdArgs a) {
             const int p = p0 + rb + r4;
             const bool kept = (uint32_t)(p - j) < (uint32_t)(e - j);
             const float v = fmaf(s[i], scale2, (dlt - lr[r4]) * kLog2e);
-            const float pp = kept ? __builtin_amdgcn_exp2f(v) : 0.f;
+            const float pp = __builtin_amdgcn_exp2f(kept ? v : -INFINITY);
             const float ds = pp * (dp[i] - dr[r4]);
             pv[q4 * 4 + r4] = pp;
             dsv[q4 * 4 + r4] = ds;
@@ -645,10 +658,8 @@ hipError_t dma_launch_attn_bwd(DmaBwdArgs& a, hipStream_t st) {
   hipError_t e = dma_launch_cand(f.delta, f.evict, BH, f.Sk, f.Sq, f.q0, f.w, a.cj, a.ce, a.ccnt,
                                  a.cdmax, st);
   if (e != hipSuccess) return e;
-  // two query heads per workgroup (four waves): with four, the 8 waves'
-  // registers would exceed 256 each and spill
   const int G = (int)(f.Hq / f.Hkv);
-  e = G % 2 == 0 ? launch_dq<2>(a, st) : launch_dq<1>(a, st);
+  e = G % 4 == 0 ? launch_dq<4>(a, st) : G % 2 == 0 ? launch_dq<2>(a, st) : launch_dq<1>(a, st);
   if (e != hipSuccess) return e;
   dim3 g2((unsigned)((a.cap + kSliceKeys - 1) / kSliceKeys), (unsigned)a.n_super, (unsigned)BH);
   hipLaunchKernelGGL(bwd_dkv_kernel, g2, dim3(256), 0, st, a);
