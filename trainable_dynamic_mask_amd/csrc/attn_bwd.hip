@@ -17,7 +17,8 @@
 //           wave per (query head, 32-row half).  S^T = K Q^T and dP^T = V dO^T
 //           read K and V rows; dQ^T += K^T dS^T reads K transposed.  Q^T and
 //           dO^T stay in registers.
-//   dkv     key-major over groups of 512 rows (8 query tiles).  The keys some
+//   dkv     key-major over groups of 512 rows (8 query tiles), in two passes
+//           (dV, then dK and ddelta) so that two waves fit per SIMD.  The keys some
 //           row of a group keeps (at most w + 511: the candidate lists of the
 //           mask step) are cut into slices of 128, one per workgroup and 32
 //           per wave, with K and V held in registers.  The workgroup streams
@@ -358,7 +359,12 @@ struct DkvSmem {
   int alive[4];
 };
 
-__global__ __launch_bounds__(256) void bwd_dkv_kernel(DmaBwdArgs a) {
+// MODE 0 accumulates dV (from P), MODE 1 dK and ddelta (from dS).  Split in
+// two passes, each wave holds one accumulator block (64 registers) and at most
+// two stationary operand sets, so two waves fit per SIMD; together the passes
+// redo the score product once more.
+template <int MODE>
+__global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(DmaBwdArgs a) {
   __shared__ __align__(16) DkvSmem sm;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -381,7 +387,7 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(DmaBwdArgs a) {
   // padding lanes get an empty row range, so they never count
   const int e = real ? min(ce[sl], p_end) : j;
   const float dlt = f.delta[seg * f.Sk + j];
-  // K^T and V^T operands of this lane's key: K[j][kk*16 + 8*hi + 0..7]
+  // K^T (and, for dK, V^T) operands of this lane's key: K[j][kk*16 + 8*hi + 0..7]
   dma::bf16x8 kf[8], vf[8];
   {
     const uint16_t* krow = static_cast<const uint16_t*>(f.K) + b * f.ksb + h * f.ksh + (int64_t)j * f.kss;
@@ -390,8 +396,9 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(DmaBwdArgs a) {
     for (int kk = 0; kk < 8; ++kk) {
       kf[kk] = __builtin_bit_cast(dma::bf16x8,
                                   *reinterpret_cast<const u32x4*>(krow + kk * 16 + hi * 8));
-      vf[kk] = __builtin_bit_cast(dma::bf16x8,
-                                  *reinterpret_cast<const u32x4*>(vrow + kk * 16 + hi * 8));
+      if constexpr (MODE == 1)
+        vf[kk] = __builtin_bit_cast(dma::bf16x8,
+                                    *reinterpret_cast<const u32x4*>(vrow + kk * 16 + hi * 8));
     }
   }
   // row tiles of the group in which some key of the slice is kept
@@ -448,14 +455,11 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(DmaBwdArgs a) {
     }
   };
 
-  dma::f32x16 dk[4], dv[4];
+  dma::f32x16 acc[4];  // dV^T (MODE 0) or dK^T (MODE 1)
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      dk[db][i] = 0.f;
-      dv[db][i] = 0.f;
-    }
+    for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
   float dd = 0.f;
 
   if (nsteps > 0) stage(0);
@@ -475,15 +479,15 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(DmaBwdArgs a) {
         s[i] = 0.f;
         dp[i] = 0.f;
       }
-      // S = Q K^T and dP = dO V^T (rows x keys): lane (l32, hi) reads row rh*32 + l32
+      // S = Q K^T (and dP = dO V^T) (rows x keys): lane (l32, hi) reads row rh*32 + l32
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
         const int row = rh * 32 + l32;
         s = mfma(row_operand(QT, row, 2 * kk + hi), kf[kk], s);
-        dp = mfma(row_operand(GT, row, 2 * kk + hi), vf[kk], dp);
+        if constexpr (MODE == 1) dp = mfma(row_operand(GT, row, 2 * kk + hi), vf[kk], dp);
       }
       // register i: row rh*32 + 8(i/4) + 4hi + i%4 of this lane's key
-      dma::bf16x8 pb[2], dsb[2];
+      dma::bf16x8 ob[2];  // P (MODE 0) or dS (MODE 1) as B operands
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         float pv[8], dsv[8];
@@ -501,23 +505,24 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(DmaBwdArgs a) {
             const bool kept = (uint32_t)(p - j) < (uint32_t)(e - j);
             const float v = fmaf(s[i], scale2, (dlt - lr[r4]) * kLog2e);
             const float pp = __builtin_amdgcn_exp2f(kept ? v : -INFINITY);
-            const float ds = pp * (dp[i] - dr[r4]);
-            pv[q4 * 4 + r4] = pp;
-            dsv[q4 * 4 + r4] = ds;
-            dd += ds;
+            if constexpr (MODE == 0) {
+              pv[q4 * 4 + r4] = pp;
+            } else {
+              const float ds = pp * (dp[i] - dr[r4]);
+              dsv[q4 * 4 + r4] = ds;
+              dd += ds;
+            }
           }
         }
-        pb[kb] = to_bf16x8(pv);
-        dsb[kb] = to_bf16x8(dsv);
+        ob[kb] = to_bf16x8(MODE == 0 ? pv : dsv);
       }
-      // dV^T += dO^T P and dK^T += Q^T dS over this half's two 16-row k-steps
+      // dV^T += dO^T P, or dK^T += Q^T dS, over this half's two 16-row k-steps
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          dv[db] = mfma(tr_operand(GT, rh * 32 + 16 * kb, db * 32, lane), pb[kb], dv[db]);
-          dk[db] = mfma(tr_operand(QT, rh * 32 + 16 * kb, db * 32, lane), dsb[kb], dk[db]);
-        }
+        for (int db = 0; db < 4; ++db)
+          acc[db] = mfma(tr_operand(MODE == 0 ? GT : QT, rh * 32 + 16 * kb, db * 32, lane),
+                         ob[kb], acc[db]);
     }
     wait_all_barrier();
   }
@@ -527,26 +532,21 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(DmaBwdArgs a) {
   dd += __shfl_xor(dd, 32);
   if (real) {
     const int64_t o = gi * a.cap + slot;
-    float* pk = a.pk + o * kD;
-    float* pvv = a.pv + o * kD;
+    float* out = (MODE == 0 ? a.pv : a.pk) + o * kD;
+    const float sc = MODE == 0 ? 1.f : f.scale;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int d = db * 32 + 8 * q4 + 4 * hi;
-        float4 x, y;
-        x.x = f.scale * dk[db][4 * q4 + 0];
-        x.y = f.scale * dk[db][4 * q4 + 1];
-        x.z = f.scale * dk[db][4 * q4 + 2];
-        x.w = f.scale * dk[db][4 * q4 + 3];
-        y.x = dv[db][4 * q4 + 0];
-        y.y = dv[db][4 * q4 + 1];
-        y.z = dv[db][4 * q4 + 2];
-        y.w = dv[db][4 * q4 + 3];
-        *reinterpret_cast<float4*>(pk + d) = x;
-        *reinterpret_cast<float4*>(pvv + d) = y;
+        float4 x;
+        x.x = sc * acc[db][4 * q4 + 0];
+        x.y = sc * acc[db][4 * q4 + 1];
+        x.z = sc * acc[db][4 * q4 + 2];
+        x.w = sc * acc[db][4 * q4 + 3];
+        *reinterpret_cast<float4*>(out + d) = x;
       }
-    if (hi == 0) {
+    if (MODE == 1 && hi == 0) {
       a.pd[o] = dd;
       a.pmap[gi * f.Sk + j] = slot;
     }
@@ -662,7 +662,8 @@ hipError_t dma_launch_attn_bwd(DmaBwdArgs& a, hipStream_t st) {
   e = G % 4 == 0 ? launch_dq<4>(a, st) : G % 2 == 0 ? launch_dq<2>(a, st) : launch_dq<1>(a, st);
   if (e != hipSuccess) return e;
   dim3 g2((unsigned)((a.cap + kSliceKeys - 1) / kSliceKeys), (unsigned)a.n_super, (unsigned)BH);
-  hipLaunchKernelGGL(bwd_dkv_kernel, g2, dim3(256), 0, st, a);
+  hipLaunchKernelGGL(bwd_dkv_kernel<0>, g2, dim3(256), 0, st, a);
+  hipLaunchKernelGGL(bwd_dkv_kernel<1>, g2, dim3(256), 0, st, a);
   hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((f.Sk + 3) / 4), (unsigned)BH), dim3(256),
                      0, st, a);
   return hipGetLastError();
