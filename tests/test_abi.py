@@ -155,3 +155,48 @@ def test_attn_validation(lib):
     assert _attn(lib, Sq=1, Sk=16, q0=15) == WORKSPACE       # decode row needs split partials
     assert _attn(lib, Sq=0, q0=16) == OK
     assert _attn(lib, B=0) == OK
+
+
+def _bwd(lib, t=1, B=1, Sq=16, Sk=16, Hq=4, Hkv=2, D=128, q0=0, w=4, lse=FAKE, Ores=None,
+         dQ=FAKE, ws=FAKE, ws_bytes=1 << 30):
+    qs = (Sq * Hq * D, Hq * D, D)
+    ks = (Sk * Hkv * D, Hkv * D, D)
+    m = DmaMask(FAKE, FAKE, FAKE, FAKE, FAKE, None, None)
+    return lib.dma_attn_bwd(FAKE, FAKE, FAKE, t, B, Sq, Sk, Hq, Hkv, D,
+                            (ctypes.c_int64 * 3)(*qs), (ctypes.c_int64 * 3)(*ks), q0, w, FAKE,
+                            ctypes.byref(m), 0.0, FAKE, Ores, lse, FAKE, dQ, FAKE, FAKE, FAKE, ws,
+                            ws_bytes, None)
+
+
+def test_attn_bwd_validation(lib):
+    assert _bwd(lib, t=0) == UNSUPPORTED                     # fp32 backward is not built
+    assert _bwd(lib, D=64) == UNSUPPORTED
+    assert _bwd(lib, Sq=1, Sk=16, q0=15) == UNSUPPORTED       # one decode row
+    assert _bwd(lib, lse=None) == INVALID                     # the forward's lse is required
+    assert _bwd(lib, dQ=MISALIGNED) == INVALID
+    assert _bwd(lib, Ores=MISALIGNED) == INVALID
+    assert _bwd(lib, ws_bytes=100) == WORKSPACE
+    assert _bwd(lib, ws=ctypes.c_void_p(0x10010)) == INVALID  # workspace is 256-byte aligned
+    assert _bwd(lib, B=0) == OK
+    assert lib.dma_attn_bwd_workspace_bytes(1, 4, 2, 1, 16, 4) == 0
+    assert lib.dma_attn_bwd_workspace_bytes(1, 32, 8, 16384, 16384, 2048) > 0
+
+
+def test_fwd_train_and_weights_bwd_validation(lib):
+    qs = (ctypes.c_int64 * 3)(16 * 4 * 128, 4 * 128, 128)
+    ks = (ctypes.c_int64 * 3)(16 * 2 * 128, 2 * 128, 128)
+    m = DmaMask(FAKE, FAKE, FAKE, FAKE, FAKE, None, None)
+    fwd = lambda t, Ores: lib.dma_attn_fwd_train(FAKE, FAKE, FAKE, t, 1, 16, 16, 4, 2, 128, qs,
+                                                  ks, 0, 4, FAKE, ctypes.byref(m), 0.0, FAKE,
+                                                  FAKE, Ores, None)
+    assert fwd(0, FAKE) == UNSUPPORTED                        # fp32: no residual output
+    assert fwd(1, None) == INVALID                            # the residual buffer is required
+    assert fwd(1, MISALIGNED) == INVALID
+    wb = lambda vt=1, D=128, Hkv=2, ws_bytes=1 << 20: lib.dma_weights_bwd(
+        FAKE, vt, 1, 16, Hkv, D, 16 * Hkv * D, Hkv * D, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+        ws_bytes, None)
+    assert wb(vt=0) == UNSUPPORTED
+    assert wb(D=96) == UNSUPPORTED
+    assert wb(Hkv=32) == UNSUPPORTED                          # Hkv*D above 2048
+    assert wb(ws_bytes=4) == WORKSPACE
+    assert lib.dma_weights_bwd_workspace_bytes(2, 10, 3) == 2 * 10 * 3 * 4
