@@ -13,6 +13,8 @@ Functions (all inputs are copied to contiguous numpy arrays first):
   attn(Q, K, V, delta, q0, w, scale=None)   -> (O [B, Sq, Hq, D], lse [B, Hq, Sq])
   attn_bwd(Q, K, V, delta, dO, q0, w, scale=None) -> (dQ, dK, dV, ddelta) float64
   weights_bwd(V, Delta, A, ddelta)          -> (dV [B, Sk, Hkv, D], dDelta, dA) float64
+  attn_bwd_rows(Q, K, V, delta, dO, q0, w, rows)  -> dQ of (b, hq, i) rows [n, D]
+  attn_bwd_keys(Q, K, V, delta, dO, q0, w, keys)  -> (dK, dV [m, D], ddelta [m]) of (b, h, j) keys
 """
 import ctypes
 import os
@@ -47,6 +49,12 @@ def _load():
     lib.orc_attn_bwd.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _I64,
                                  _I64, ctypes.c_double, _P, _P, _P, _P]
     lib.orc_attn_bwd.restype = None
+    lib.orc_attn_bwd_rows.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64,
+                                      _I64, ctypes.c_double, _P, _I64, _P]
+    lib.orc_attn_bwd_rows.restype = None
+    lib.orc_attn_bwd_keys.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64,
+                                      _I64, ctypes.c_double, _P, _I64, _P, _P, _P]
+    lib.orc_attn_bwd_keys.restype = None
     lib.orc_weights_bwd.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _P, _P]
     lib.orc_weights_bwd.restype = None
     _lib = lib
@@ -193,3 +201,39 @@ def weights_bwd(V, Delta, A, ddelta):
     lib.orc_weights_bwd(_ptr(Vn), _ptr(Dn), _ptr(An), _ptr(gd), B, Sk, Hkv, D, _ptr(dV),
                         _ptr(dDelta), _ptr(dA))
     return dV, dDelta, dA
+
+
+def _bwd_inputs(Q, K, V, delta, dO):
+    Qn, Kn, Vn, gn = (_np(x, np.float32) for x in (Q, K, V, dO))
+    return Qn, Kn, Vn, _np(delta, np.float64), gn
+
+
+def attn_bwd_rows(Q, K, V, delta, dO, q0, w, rows, scale=None):
+    """dQ of the listed (b, hq, i) rows, float64 [n, D]."""
+    lib = _load()
+    Qn, Kn, Vn, d, gn = _bwd_inputs(Q, K, V, delta, dO)
+    B, Sq, Hq, D = Qn.shape
+    _, Sk, Hkv, _ = Kn.shape
+    rows = np.ascontiguousarray(np.asarray(rows, np.int64).reshape(-1, 3))
+    out = np.empty((rows.shape[0], D), np.float64)
+    lib.orc_attn_bwd_rows(_ptr(Qn), _ptr(Kn), _ptr(Vn), _ptr(d), _ptr(gn), Sq, Sk, Hq, Hkv, D, q0,
+                          w, float(scale or 1.0 / np.sqrt(D)), _ptr(rows), rows.shape[0],
+                          _ptr(out))
+    return out
+
+
+def attn_bwd_keys(Q, K, V, delta, dO, q0, w, keys, scale=None):
+    """dK, dV [m, D] and ddelta [m] of the listed (b, h, j) keys (float64)."""
+    lib = _load()
+    Qn, Kn, Vn, d, gn = _bwd_inputs(Q, K, V, delta, dO)
+    B, Sq, Hq, D = Qn.shape
+    _, Sk, Hkv, _ = Kn.shape
+    keys = np.ascontiguousarray(np.asarray(keys, np.int64).reshape(-1, 3))
+    m = keys.shape[0]
+    dK = np.empty((m, D), np.float64)
+    dV = np.empty((m, D), np.float64)
+    dd = np.empty((m,), np.float64)
+    lib.orc_attn_bwd_keys(_ptr(Qn), _ptr(Kn), _ptr(Vn), _ptr(d), _ptr(gn), Sq, Sk, Hq, Hkv, D,
+                          q0, w, float(scale or 1.0 / np.sqrt(D)), _ptr(keys), m, _ptr(dK),
+                          _ptr(dV), _ptr(dd))
+    return dK, dV, dd

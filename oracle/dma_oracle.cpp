@@ -293,6 +293,130 @@ void orc_attn_bwd(const float* Q, const float* K, const float* V, const double* 
   }
 }
 
+// The same backward for sampled outputs, for sizes where the whole backward
+// is too slow.  orc_attn_bwd_rows: dQ of the listed (b, hq, i) rows (a row's
+// dQ depends on that row only).  orc_attn_bwd_keys: dK, dV and ddelta of the
+// listed (b, h, j) keys, summing over every row p >= j whose keep set holds
+// j, for each of the G query heads of kv head h.  dQ [n, D]; dK, dV [m, D];
+// ddelta [m].
+namespace {
+// P, s and the keep set of row (b, hq, i); returns its size; fills O.
+int64_t row_probs(const float* Q, const float* K, const float* V, const double* d, int64_t b,
+                  int64_t hq, int64_t i, int64_t h, int64_t Sq, int64_t Sk, int64_t Hq,
+                  int64_t Hkv, int64_t D, int64_t q0, int64_t w, double scale,
+                  std::vector<int32_t>& keep, std::vector<int32_t>& scratch,
+                  std::vector<double>& s, std::vector<double>& P, std::vector<double>& o) {
+  const int64_t nk = keep_row(d, q0 + i, w, keep.data(), scratch);
+  const float* q = Q + ((b * Sq + i) * Hq + hq) * D;
+  double m = -INFINITY;
+  for (int64_t k = 0; k < nk; ++k) {
+    const float* kr = K + ((b * Sk + keep[k]) * Hkv + h) * D;
+    double dot = 0.0;
+    for (int64_t c = 0; c < D; ++c) dot += (double)q[c] * (double)kr[c];
+    s[k] = scale * dot + d[keep[k]];
+    m = std::max(m, s[k]);
+  }
+  double z = 0.0;
+  for (int64_t k = 0; k < nk; ++k) z += std::exp(s[k] - m);
+  const double lse = m + std::log(z);
+  std::fill(o.begin(), o.end(), 0.0);
+  for (int64_t k = 0; k < nk; ++k) {
+    P[k] = std::exp(s[k] - lse);
+    const float* vr = V + ((b * Sk + keep[k]) * Hkv + h) * D;
+    for (int64_t c = 0; c < D; ++c) o[c] += P[k] * (double)vr[c];
+  }
+  return nk;
+}
+}  // namespace
+
+void orc_attn_bwd_rows(const float* Q, const float* K, const float* V, const double* delta,
+                       const float* dO, int64_t Sq, int64_t Sk, int64_t Hq, int64_t Hkv,
+                       int64_t D, int64_t q0, int64_t w, double scale, const int64_t* rows,
+                       int64_t n, double* dQ) {
+  const int64_t G = Hq / Hkv;
+#pragma omp parallel
+  {
+    std::vector<int32_t> scratch, keep(Sk > 0 ? Sk : 1);
+    std::vector<double> s(Sk > 0 ? Sk : 1), P(Sk > 0 ? Sk : 1), o(D);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n; ++r) {
+      const int64_t b = rows[3 * r], hq = rows[3 * r + 1], i = rows[3 * r + 2], h = hq / G;
+      const double* d = delta + (b * Hkv + h) * Sk;
+      const int64_t nk = row_probs(Q, K, V, d, b, hq, i, h, Sq, Sk, Hq, Hkv, D, q0, w, scale,
+                                   keep, scratch, s, P, o);
+      const float* g = dO + ((b * Sq + i) * Hq + hq) * D;
+      double Dr = 0.0;
+      for (int64_t c = 0; c < D; ++c) Dr += (double)g[c] * o[c];
+      double* out = dQ + r * D;
+      std::fill(out, out + D, 0.0);
+      for (int64_t k = 0; k < nk; ++k) {
+        const float* kr = K + ((b * Sk + keep[k]) * Hkv + h) * D;
+        const float* vr = V + ((b * Sk + keep[k]) * Hkv + h) * D;
+        double dp = 0.0;
+        for (int64_t c = 0; c < D; ++c) dp += (double)g[c] * (double)vr[c];
+        const double ds = P[k] * (dp - Dr);
+        for (int64_t c = 0; c < D; ++c) out[c] += scale * ds * (double)kr[c];
+      }
+    }
+  }
+}
+
+void orc_attn_bwd_keys(const float* Q, const float* K, const float* V, const double* delta,
+                       const float* dO, int64_t Sq, int64_t Sk, int64_t Hq, int64_t Hkv,
+                       int64_t D, int64_t q0, int64_t w, double scale, const int64_t* keys,
+                       int64_t m, double* dK, double* dV, double* ddelta) {
+  const int64_t G = Hq / Hkv;
+  for (int64_t t = 0; t < m; ++t) {
+    const int64_t b = keys[3 * t], h = keys[3 * t + 1], j = keys[3 * t + 2];
+    const double* d = delta + (b * Hkv + h) * Sk;
+    std::vector<double> gk(D, 0.0), gv(D, 0.0);
+    double gd = 0.0;
+#pragma omp parallel
+    {
+      std::vector<int32_t> scratch, keep(Sk > 0 ? Sk : 1);
+      std::vector<double> s(Sk > 0 ? Sk : 1), P(Sk > 0 ? Sk : 1), o(D), lk(D, 0.0), lv(D, 0.0);
+      double ld = 0.0;
+#pragma omp for collapse(2) schedule(dynamic, 4)
+      for (int64_t hq = h * G; hq < (h + 1) * G; ++hq)
+        for (int64_t i = std::max<int64_t>(0, j - q0); i < Sq; ++i) {
+          const int64_t nk = row_probs(Q, K, V, d, b, hq, i, h, Sq, Sk, Hq, Hkv, D, q0, w, scale,
+                                       keep, scratch, s, P, o);
+          int64_t kj = -1;
+          for (int64_t k = 0; k < nk; ++k)
+            if (keep[k] == j) kj = k;
+          if (kj < 0) continue;
+          const float* g = dO + ((b * Sq + i) * Hq + hq) * D;
+          const float* q = Q + ((b * Sq + i) * Hq + hq) * D;
+          const float* vr = V + ((b * Sk + j) * Hkv + h) * D;
+          double Dr = 0.0, dp = 0.0;
+          for (int64_t c = 0; c < D; ++c) {
+            Dr += (double)g[c] * o[c];
+            dp += (double)g[c] * (double)vr[c];
+          }
+          const double ds = P[kj] * (dp - Dr);
+          for (int64_t c = 0; c < D; ++c) {
+            lk[c] += scale * ds * (double)q[c];
+            lv[c] += P[kj] * (double)g[c];
+          }
+          ld += ds;
+        }
+#pragma omp critical
+      {
+        for (int64_t c = 0; c < D; ++c) {
+          gk[c] += lk[c];
+          gv[c] += lv[c];
+        }
+        gd += ld;
+      }
+    }
+    for (int64_t c = 0; c < D; ++c) {
+      dK[t * D + c] = gk[c];
+      dV[t * D + c] = gv[c];
+    }
+    ddelta[t] = gd;
+  }
+}
+
 // Backward of the dynamic weights, given ddelta = dL/ddelta:
 //   pre = sum_c V[b,j,c] Delta[c,h],  sp = softplus(pre),  delta = exp(sp A[h])
 //   dpre = ddelta * delta * A[h] * sigmoid(pre)      (softplus' = sigmoid)

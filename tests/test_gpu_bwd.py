@@ -93,3 +93,43 @@ def test_bwd_without_residual(gpu_lib):
     got, want = _run(1, 4, 2, 600, 600, 150, seed=12, residual=False)
     for g, r, name in zip(got, want, ("dQ", "dK", "dV", "ddelta")):
         _close(g, r, name)
+
+
+def test_bwd_prefill_16k_sampled(gpu_lib):
+    # the bench workload at full size: dQ of sampled rows and dK/dV/ddelta of sampled
+    # keys against the oracle's one-at-a-time backward, ddelta summing to zero per
+    # head, and exact zeros for keys no row keeps
+    from trainable_dynamic_mask_amd.configs import WORKLOADS
+    from trainable_dynamic_mask_amd.inputs import make_inputs
+    wl = WORKLOADS["prefill_16k"]
+    x = make_inputs(wl, device="cuda")
+    dO = make_grad(wl, device="cuda")
+    print("bwd prefill_16k sampled", flush=True)
+    d = dma.weights(x["V"], x["Delta"], x["A"])
+    m = dma.topk_mask(d, wl.Sq, 0, wl.w)
+    O, lse, Ores = dma.attn_fwd_train(x["Q"], x["K"], x["V"], d, m)
+    dQ, dK, dV, dd = dma.attn_bwd(x["Q"], x["K"], x["V"], d, m, O, lse, dO, O_res=Ores)
+    torch.cuda.synchronize()
+    d64 = to64(d)
+    rows = [(0, hq, i) for hq, i in ((0, 0), (5, 2047), (9, 2048), (31, 16383), (17, 8191),
+                                      (2, 64), (30, 12345), (12, 4095))]
+    want = oracle.attn_bwd_rows(x["Q"], x["K"], x["V"], d64, dO, 0, wl.w, rows)
+    got = np.stack([to64(dQ[b, i, hq]) for b, hq, i in rows])
+    _close(got, want, "dQ rows")
+    ev = m.evict.view(wl.B, wl.Hkv, wl.Sk).cpu().numpy()
+    # two kept keys (a late one and one kept for thousands of rows) and two never kept
+    late = [j for j in range(16300, 16384) if ev[0, 3, j] > j][0]
+    mid = [j for j in range(12000, 12400) if ev[0, 6, j] - j > 2000][0]
+    dead = [j for j in range(9000, 16384) if ev[0, 1, j] == j][:2]
+    keys = [(0, 3, late), (0, 6, mid)]
+    wk, wv, wd = oracle.attn_bwd_keys(x["Q"], x["K"], x["V"], d64, dO, 0, wl.w, keys)
+    for t, (b, h, j) in enumerate(keys):
+        _close(to64(dK[b, j, h]), wk[t], f"dK key {j}")
+        _close(to64(dV[b, j, h]), wv[t], f"dV key {j}")
+        scale = np.abs(to64(dd[b, h])).max()
+        assert abs(float(dd[b, h, j]) - wd[t]) <= 3e-2 * scale, f"ddelta key {j}"
+    for j in dead:
+        assert float(dK[0, j, 1].abs().max()) == 0 and float(dV[0, j, 1].abs().max()) == 0
+        assert float(dd[0, 1, j]) == 0
+    ddn = to64(dd)
+    assert np.abs(ddn.sum(-1)).max() < 1e-3 * np.abs(ddn).sum(-1).max()

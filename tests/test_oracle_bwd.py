@@ -158,3 +158,19 @@ def test_weights_bwd_finite_differences_and_autograd():
             fm = L(*(Xm if k == name else args[k] for k in ("V", "Delta", "A")))
             fd = (fp - fm) / (2 * h)
             assert abs(fd - Gr[idx]) <= 1e-6 + 1e-4 * abs(Gr[idx]), (name, idx, fd, Gr[idx])
+
+
+def test_sampled_backward_equals_full():
+    # the per-row and per-key oracles agree with the full backward
+    Q, K, V, dO, delta = _inputs(2, 70, 4, 2, 16, seed=31)
+    dQ, dK, dV, dd = oracle.attn_bwd(Q, K, V, delta, dO, 0, 20)
+    rows = [(0, 0, 0), (1, 3, 69), (0, 2, 33), (1, 1, 19)]
+    got = oracle.attn_bwd_rows(Q, K, V, delta, dO, 0, 20, rows)
+    for r, (b, hq, i) in enumerate(rows):
+        np.testing.assert_allclose(got[r], dQ[b, i, hq], rtol=1e-12, atol=1e-14)
+    keys = [(0, 0, 0), (1, 1, 69), (0, 1, 40), (1, 0, 5)]
+    gk, gv, gd = oracle.attn_bwd_keys(Q, K, V, delta, dO, 0, 20, keys)
+    for t, (b, h, j) in enumerate(keys):
+        np.testing.assert_allclose(gk[t], dK[b, j, h], rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(gv[t], dV[b, j, h], rtol=1e-12, atol=1e-14)
+        assert abs(gd[t] - dd[b, h, j]) <= 1e-12 * max(1.0, abs(dd[b, h, j]))
