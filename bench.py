@@ -32,7 +32,8 @@ PEAK_HBM_GBS = 8000.0
 # the hash of the kernel sources it was taken on; a stale file reports null.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_prefill_bf16_kernel.prefill_16k.traffic.txt")
 ATTN_SOURCES = ("trainable_dynamic_mask_amd/csrc/attn_prefill.hip",
-                "trainable_dynamic_mask_amd/csrc/common.h")
+                "trainable_dynamic_mask_amd/csrc/common.h",
+                "trainable_dynamic_mask_amd/csrc/lds_dma.h")
 
 
 def parse():

@@ -37,7 +37,7 @@
 // one chunk on 16 distinct chunk slots (row reads), and 4 consecutive rows
 // put a 32-byte piece on 4 distinct 32-byte slots (transposing reads), so
 // both access patterns are free of bank conflicts.
-#include "common.h"
+#include "lds_dma.h"
 
 #include <algorithm>
 
@@ -52,40 +52,17 @@ constexpr int kGroupRows = 512;   // rows per key-side group
 constexpr int kSliceKeys = 128;   // candidate keys per key-side workgroup (4 waves x 32)
 constexpr float kLog2e = 1.4426950408889634f;
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef __attribute__((address_space(3))) void lds_void;
+using dma::dma_b128;
+using dma::dma_b32;
+using dma::i16x4;
+using dma::lds_addr;
+using dma::lds_i16x4;
+using dma::to_bf16x8;
+using dma::u32x2;
+using dma::u32x4;
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
 __device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(lds_void*)p;
-}
-
-// Direct global-to-LDS loads (inline asm, so the compiler neither tracks nor
-// waits for them; every wait is an explicit vmcnt).  Lane L's data lands at
-// LDS byte m0 + size*L.
-__device__ __forceinline__ void dma_b128(const void* src, uint32_t lds) {
-  asm volatile(
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, off"
-      :
-      : "v"(src), "s"(lds)
-      : "m0");
-}
-__device__ __forceinline__ void dma_b32(const void* src, uint32_t lds) {
-  asm volatile(
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dword %0, off"
-      :
-      : "v"(src), "s"(lds)
-      : "m0");
-}
 
 // All of this wave's direct loads have landed; then the workgroup barrier.
 __device__ __forceinline__ void wait_all_barrier() {
@@ -123,13 +100,6 @@ __device__ __forceinline__ dma::bf16x8 tr_operand(const unsigned char* tile, int
   const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), up2 = __builtin_bit_cast(u32x2, up);
   const u32x4 vv = {lo2[0], lo2[1], up2[0], up2[1]};
   return __builtin_bit_cast(dma::bf16x8, vv);
-}
-
-__device__ __forceinline__ dma::bf16x8 to_bf16x8(const float* p) {
-  dma::bf16x8 r;
-#pragma unroll
-  for (int t = 0; t < 8; ++t) r[t] = (__bf16)p[t];
-  return r;
 }
 
 __device__ __forceinline__ dma::f32x16 mfma(dma::bf16x8 a, dma::bf16x8 b, dma::f32x16 c) {

@@ -47,7 +47,7 @@
 // constant cancels in the softmax and is added back to the log-sum-exp.  The
 // bias, divided by the score scale, is the initial value of the score
 // accumulator, so the MFMAs add q.k to it.
-#include "common.h"
+#include "lds_dma.h"
 
 namespace {
 
@@ -70,11 +70,14 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.f;  // base-2 headroom before O is rescaled (weights stay <= 2^8)
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef __attribute__((address_space(3))) void lds_void;
+using dma::dma_b128;
+using dma::dma_b32;
+using dma::i16x4;
+using dma::lds_addr;
+using dma::lds_i16x4;
+using dma::to_bf16x8;
+using dma::u32x2;
+using dma::u32x4;
 
 // Everything the workgroup keeps in LDS (105 KB).
 struct Smem {
@@ -88,49 +91,12 @@ struct Smem {
   float bias[kFin][kBk];           // (delta - dmax) * log2(e) / score scale, -inf for padding
 };
 
-__device__ __forceinline__ dma::bf16x8 to_bf16x8(const float (&p)[8]) {
-  dma::bf16x8 r;
-#pragma unroll
-  for (int t = 0; t < 8; ++t) r[t] = (__bf16)p[t];  // v_cvt_pk_bf16_f32, round to nearest even
-  return r;
-}
-
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   bf16x2 r;
   r[0] = (__bf16)lo;
   r[1] = (__bf16)hi;
   return __builtin_bit_cast(uint32_t, r);
-}
-
-// Direct global-to-LDS loads, written as inline asm so that the compiler
-// neither tracks them nor inserts waits for them: every wait for them is an
-// explicit s_waitcnt vmcnt below.  Lane L's data lands at the LDS byte
-// address m0 + size*L; the instruction after an m0 write needs one wait
-// state.  They have no register results, and their address registers are
-// read when they issue.
-__device__ __forceinline__ void dma_b128(const void* src, uint32_t lds) {
-  asm volatile(
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, off"
-      :
-      : "v"(src), "s"(lds)
-      : "m0");
-}
-__device__ __forceinline__ void dma_b32(const void* src, uint32_t lds) {
-  asm volatile(
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dword %0, off"
-      :
-      : "v"(src), "s"(lds)
-      : "m0");
-}
-
-// LDS byte address of a location in the workgroup's shared memory
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(lds_void*)p;
 }
 
 // Gather the 64 rows of one K or V chunk into the tile at LDS address tile,
