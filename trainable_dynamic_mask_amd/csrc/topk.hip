@@ -715,118 +715,176 @@ __global__ __launch_bounds__(kGroupWaves * 64) void group_lists_kernel(
 }
 
 // ---------------------------------------------------------------- decode: one row
-// Keys 0..p of one sequence; keeps the w best.  KPT codes per thread stay in
-// registers; the threshold is found bit by bit from the top: the largest code
-// T with #{code >= T} >= w.
-constexpr int kDecThreads = 1024;
-constexpr int kDecKPT = 32;  // rows up to 32768 keys
+// Keys 0..p of one sequence; keeps the w best.  Thread t holds the codes of
+// keys k*512 + t (coalesced loads, 64 registers).  The threshold, the largest
+// code T with #{code >= T} >= w, is found bit by bit from the top.  The
+// leading bits run over every key; the keys that can still reach the
+// threshold (code >= the partial T, a few thousand for real rows) then move
+// through LDS into 16 registers per thread for the remaining bits, unless
+// there are more than kDecCand of them (ties), when the search stays on the
+// full set.  The ordered output comes from two LDS bitmaps (code > T, and
+// code == T for the ties, kept lowest index first), one 64-key tile per
+// thread, which also gives the key-tile list.
+constexpr int kDecThreads = 512;
+constexpr int kDecWaves = kDecThreads / 64;
+constexpr int kDecKPT = 64;          // rows up to 32768 keys
+constexpr int kDecLead = 12;         // bits fixed over the full set
+constexpr int kDecCand = 8192;       // candidates carried to the remaining bits
+constexpr int kDecCPT = kDecCand / kDecThreads;
 
-__global__ __launch_bounds__(kDecThreads) void decode_select_kernel(
+// Block total of per-thread counts in [0, 128): the wave sums its counts bit
+// plane by bit plane with ballots (no cross-lane chains), one LDS slot per
+// wave, one barrier.  Callers alternate two slot sets, which makes the one
+// barrier enough: a wave cannot write a set again before every wave has
+// passed the next call's barrier, i.e. finished reading it.
+__device__ __forceinline__ int dec_block_count(int c, int* s_slots) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int tw = 0;
+#pragma unroll
+  for (int b = 0; b < 7; ++b) tw += __popcll(__ballot((c >> b) & 1)) << b;
+  if (lane == 0) s_slots[wave] = tw;
+  __syncthreads();
+  int tot = 0;
+#pragma unroll
+  for (int v = 0; v < kDecWaves; ++v) tot += s_slots[v];
+  return tot;
+}
+
+// One bit per round, hi down to lo: T | bit is taken when at least w codes
+// reach it.  Padding codes are 0 and never reach a candidate (all >= 1).
+// cge tracks #{code >= T}.
+template <int K>
+__device__ __forceinline__ uint32_t dec_bit_search(const uint32_t (&x)[K], uint32_t T, int hi,
+                                                   int lo, int w, int* s_cnt, int& round,
+                                                   int& cge) {
+  for (int bit = hi; bit >= lo; --bit) {
+    const uint32_t cand = T | (1u << bit);
+    int c = 0;
+#pragma unroll
+    for (int k = 0; k < K; ++k) c += x[k] >= cand ? 1 : 0;
+    const int tot = dec_block_count(c, s_cnt + (round & 1) * kDecWaves);
+    ++round;
+    if (tot >= w) {
+      T = cand;
+      cge = tot;
+    }
+  }
+  return T;
+}
+
+template <int K>
+__device__ __forceinline__ int dec_count_above(const uint32_t (&x)[K], uint32_t T, int* s_cnt,
+                                               int& round) {
+  int c = 0;
+#pragma unroll
+  for (int k = 0; k < K; ++k) c += x[k] > T ? 1 : 0;
+  const int tot = dec_block_count(c, s_cnt + (round & 1) * kDecWaves);
+  ++round;
+  return tot;
+}
+
+__global__ __launch_bounds__(kDecThreads, 2) void decode_select_kernel(
     const float* __restrict__ delta, int Sk, int p, int w, int u_stride, int kt_stride,
     int32_t* __restrict__ u_idx, int32_t* __restrict__ u_cnt, int32_t* __restrict__ u_nfull,
     float* __restrict__ u_dmax, int32_t* __restrict__ kt_idx, int32_t* __restrict__ kt_cnt) {
-  __shared__ int s_w[kDecThreads / 64];
-  __shared__ float s_m[kDecThreads / 64];
-  __shared__ uint32_t s_kt[(1 << 20) / 64 / 32];  // key-tile flags as bits
+  __shared__ int s_w[kDecWaves];
+  __shared__ int s_cnt[2 * kDecWaves];
+  __shared__ float s_m[kDecWaves];
+  __shared__ __align__(8) uint32_t s_gt[kDecThreads * kDecKPT / 32];  // code > T (or all, n <= w)
+  __shared__ __align__(8) uint32_t s_eq[kDecThreads * kDecKPT / 32];  // code == T
+  __shared__ uint32_t s_cand[kDecCand];
   const int seg = blockIdx.x;
   const int n = p + 1;
   const float* Dl = delta + (int64_t)seg * Sk;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int j0 = tid * kDecKPT;
   uint32_t code[kDecKPT];
   float mx = -INFINITY;
 #pragma unroll
   for (int k = 0; k < kDecKPT; ++k) {
-    const int j = j0 + k;
-    const float v = (j < n) ? Dl[j] : 0.f;
+    const int j = k * kDecThreads + tid;
+    const float v = Dl[min(j, n - 1)];  // every load issues before the first use
     code[k] = (j < n) ? dma::ord32(v) : 0u;
-    if (j < n) mx = fmaxf(mx, v);
+    mx = fmaxf(mx, v);  // the clamped key is a real one
   }
   mx = dma::wave_max(mx);
   if (lane == 0) s_m[wave] = mx;
-  int32_t* out = u_idx + (int64_t)seg * u_stride;
-  const int nkt = (n + 63) / 64;
-  for (int k = tid; k < (nkt + 31) / 32; k += kDecThreads) s_kt[k] = 0u;
 
-  uint32_t T = 0;  // codes >= T: at least w of them (0 counts every real key)
-  int need_eq = 0, tot;
+  uint32_t T = 0;
+  int need_eq = 0;
   if (n > w) {
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t cand = T | (1u << bit);
-      int c = 0;
+    int round = 0, cge = n;
+    T = dec_bit_search(code, T, 31, 32 - kDecLead, w, s_cnt, round, cge);
+    int gt_tot;
+    if (cge <= kDecCand) {
+      // order-free compaction of the keys with code >= T
+      int sc = 0;
 #pragma unroll
-      for (int k = 0; k < kDecKPT; ++k) c += (code[k] >= cand && j0 + k < n) ? 1 : 0;
-      block_excl_scan<kDecThreads>(c, s_w, tot);
-      if (tot >= w) T = cand;
+      for (int k = 0; k < kDecKPT; ++k) sc += (k * kDecThreads + tid < n && code[k] >= T) ? 1 : 0;
+      int stot;
+      int at = block_excl_scan<kDecThreads>(sc, s_w, stot);
+#pragma unroll
+      for (int k = 0; k < kDecKPT; ++k)
+        if (k * kDecThreads + tid < n && code[k] >= T && at < kDecCand) s_cand[at++] = code[k];
+      __syncthreads();
+      uint32_t cr[kDecCPT];
+#pragma unroll
+      for (int i = 0; i < kDecCPT; ++i) {
+        const int q = i * kDecThreads + tid;
+        cr[i] = q < stot ? s_cand[q] : 0u;
+      }
+      T = dec_bit_search(cr, T, 31 - kDecLead, 0, w, s_cnt, round, cge);
+      gt_tot = dec_count_above(cr, T, s_cnt, round);
+    } else {
+      T = dec_bit_search(code, T, 31 - kDecLead, 0, w, s_cnt, round, cge);
+      gt_tot = dec_count_above(code, T, s_cnt, round);
     }
-    int gt = 0;
-#pragma unroll
-    for (int k = 0; k < kDecKPT; ++k) gt += (code[k] > T && j0 + k < n) ? 1 : 0;
-    block_excl_scan<kDecThreads>(gt, s_w, tot);
-    need_eq = w - tot;  // how many of the keys whose code equals T are kept (lowest index first)
+    need_eq = w - gt_tot;  // keys with code == T that are kept, lowest index first
   }
-  // ordered compaction
-  int eq = 0, keep = 0;
+  // bitmaps of the verdicts: key k*512 + 64*wave + lane is bit lane of the
+  // 64-bit word k*8 + wave
 #pragma unroll
   for (int k = 0; k < kDecKPT; ++k) {
-    const bool in = j0 + k < n;
-    eq += (in && n > w && code[k] == T) ? 1 : 0;
-  }
-  const int eq_before = block_excl_scan<kDecThreads>(eq, s_w, tot);
-  int eq_left = max(0, need_eq - eq_before);
-#pragma unroll
-  for (int k = 0; k < kDecKPT; ++k) {
-    const bool in = j0 + k < n;
-    bool kept = in && (n <= w || code[k] > T);
-    if (in && n > w && code[k] == T && eq_left > 0) {
-      kept = true;
-      --eq_left;
-    }
-    keep += kept ? 1 : 0;
-  }
-  const int pos0 = block_excl_scan<kDecThreads>(keep, s_w, tot);
-  eq_left = max(0, need_eq - eq_before);
-  int pos = pos0;
-#pragma unroll
-  for (int k = 0; k < kDecKPT; ++k) {
-    const int j = j0 + k;
-    const bool in = j < n;
-    bool kept = in && (n <= w || code[k] > T);
-    if (in && n > w && code[k] == T && eq_left > 0) {
-      kept = true;
-      --eq_left;
-    }
-    if (kept) {
-      if (pos < u_stride) out[pos] = j;
-      ++pos;
-      atomicOr(&s_kt[j >> 11], 1u << ((j >> 6) & 31));
+    const bool in = k * kDecThreads + tid < n;
+    const uint64_t g = __ballot(in && (n <= w || code[k] > T));
+    const uint64_t e = __ballot(in && n > w && code[k] == T);
+    if (lane == 0) {
+      reinterpret_cast<uint64_t*>(s_gt)[k * kDecWaves + wave] = g;
+      reinterpret_cast<uint64_t*>(s_eq)[k * kDecWaves + wave] = e;
     }
   }
   __syncthreads();
+  // thread t: keys [64t, 64t + 64), i.e. key tile t
+  const uint64_t gt64 = reinterpret_cast<const uint64_t*>(s_gt)[tid];
+  const uint64_t eq64 = reinterpret_cast<const uint64_t*>(s_eq)[tid];
+  const int ne = __popcll(eq64);
+  int etot;
+  const int eb = block_excl_scan<kDecThreads>(ne, s_w, etot);
+  const int allow = min(ne, max(0, need_eq - eb));
+  uint64_t kept = gt64, x = eq64;
+  for (int r = 0; r < allow; ++r) {
+    kept |= x & (~x + 1ull);
+    x &= x - 1ull;
+  }
+  const int nk = __popcll(kept);
+  int tot;
+  int pos = block_excl_scan<kDecThreads>(nk, s_w, tot);
+  int32_t* out = u_idx + (int64_t)seg * u_stride;
+  for (uint64_t y = kept; y; y &= y - 1ull) {
+    if (pos < u_stride) out[pos] = 64 * tid + __builtin_ctzll(y);
+    ++pos;
+  }
   if (tid == 0) {
     float m = s_m[0];
-    for (int k = 1; k < kDecThreads / 64; ++k) m = fmaxf(m, s_m[k]);
+    for (int k = 1; k < kDecWaves; ++k) m = fmaxf(m, s_m[k]);
     u_cnt[seg] = min(tot, u_stride);
     u_nfull[seg] = min(tot, u_stride);
     u_dmax[seg] = m;
   }
   if (kt_idx) {
-    // ordered compaction of the key-tile flags
-    int c = 0;
-    const int kw = (nkt + 31) / 32;
-    const int per = (kw + kDecThreads - 1) / kDecThreads;
-    for (int k = tid * per; k < min(kw, tid * per + per); ++k) c += __popc(s_kt[k]);
+    const int f = kept != 0ull ? 1 : 0;
     int ktot;
-    int at = block_excl_scan<kDecThreads>(c, s_w, ktot);
-    for (int k = tid * per; k < min(kw, tid * per + per); ++k) {
-      uint32_t x = s_kt[k];
-      while (x) {
-        const int b = __builtin_ctz(x);
-        x &= x - 1;
-        if (at < kt_stride) kt_idx[(int64_t)seg * kt_stride + at] = k * 32 + b;
-        ++at;
-      }
-    }
+    const int at = block_excl_scan<kDecThreads>(f, s_w, ktot);
+    if (f && at < kt_stride) kt_idx[(int64_t)seg * kt_stride + at] = tid;
     if (tid == 0) kt_cnt[seg] = min(ktot, kt_stride);
   }
 }
