@@ -49,6 +49,11 @@ def parse():
     ap.add_argument("--backward", action="store_true",
                     help="time the training backward instead (attention and weights "
                          "gradients after a training forward); prints its own JSON line")
+    ap.add_argument("--hbm-stages", action="store_true",
+                    help="time the HBM-bound stages of the workload one at a time, each "
+                         "repetition after a 512 MiB flush of the caches, and print their "
+                         "achieved GB/s against the algorithmic bytes (own JSON line)")
+    ap.add_argument("--reps", type=int, default=20, help="repetitions per stage (--hbm-stages)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (the reference "
                          "reading of the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -185,12 +190,86 @@ def backward_bench(args, wl, x, dev):
     print(json.dumps(out), flush=True)
 
 
+def hbm_stages(args, wl, x, dev):
+    """The HBM-bound stages one at a time.  Before every repetition a 512 MiB
+    buffer is read and written, which evicts the 256 MB Infinity Cache and the
+    L2s, so each repetition reads its inputs from HBM.  Algorithmic bytes:
+      weights    V read + delta written
+      mask       prefill: delta read + eviction rows and the kept-key / key-tile
+                 lists written (their actual lengths); decode (one row): delta
+                 of the row's keys read + the w indices written
+      attention  decode only (prefill attention is MFMA bound): the kept K and V
+                 rows gathered + Q read + O written + indices and their delta
+    """
+    import statistics
+    import torch
+    import trainable_dynamic_mask_amd as dma
+
+    lib = dma.load()
+    es = x["V"].element_size()
+    delta = torch.empty(wl.B, wl.Hkv, wl.Sk, dtype=torch.float32, device=dev)
+    mask = dma.alloc_mask(wl.B, wl.Hkv, wl.Sq, wl.Sk, wl.q_offset, wl.w, dev)
+    ws_t = torch.empty(max(16, lib.dma_topk_workspace_bytes(wl.B, wl.Hkv, wl.Sq, wl.Sk, wl.w)),
+                       dtype=torch.uint8, device=dev)
+    O = torch.empty_like(x["Q"])
+    ws_a = torch.empty(max(16, lib.dma_attn_workspace_bytes(wl.B, wl.Hq, wl.Sq, wl.D, wl.w)),
+                       dtype=torch.uint8, device=dev)
+    flush = torch.zeros(512 << 20, dtype=torch.uint8, device=dev)
+
+    def run_w():
+        dma.weights(x["V"], x["Delta"], x["A"], out=delta)
+
+    def run_t():
+        dma.topk_mask(delta, wl.Sq, wl.q_offset, wl.w, mask=mask, workspace=ws_t)
+
+    def run_a():
+        dma.attn_fwd(x["Q"], x["K"], x["V"], delta, mask, out=O, workspace=ws_a)
+
+    for _ in range(max(args.warmup, 1)):  # clock ramp; also leaves delta and the mask set
+        run_w()
+        run_t()
+        run_a()
+    torch.cuda.synchronize()
+    n_keys = wl.B * wl.Hkv * wl.Sk
+    w_bytes = n_keys * wl.D * es + n_keys * 4  # V is [B, Sk, Hkv, D]
+    n = mask.dims["n_tiles_total"]
+    if wl.Sq == 1:
+        rows = wl.B * wl.Hkv
+        t_bytes = rows * (wl.q_offset + 1) * 4 + int(mask.u_cnt[:n].sum().item()) * 4
+    else:
+        t_bytes = (2 * n_keys * 4 + int(mask.u_cnt[:n].sum().item()) * 4
+                   + int(mask.kt_cnt[:n].sum().item()) * 4)
+    stages = [("weights", run_w, w_bytes), ("mask", run_t, t_bytes)]
+    if wl.Sq == 1:
+        kept = int(mask.u_cnt[:n].sum().item())
+        a_bytes = (kept * 2 * wl.D * es + 2 * wl.B * wl.Hq * wl.D * es + kept * 8)
+        stages.append(("attention", run_a, a_bytes))
+    out = {"mode": "hbm_stages", "workload": wl.name, "flush_mib": 512, "reps": args.reps,
+           "peak_GBps": PEAK_HBM_GBS, "stages": {}}
+    for name, fn, nbytes in stages:
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.reps)]
+        for e0, e1 in ev:
+            flush.add_(1)
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+        med = statistics.median(ms)
+        gbs = nbytes / (med * 1e-3) / 1e9
+        out["stages"][name] = {"ms_median": round(med, 4), "ms_min": round(min(ms), 4),
+                               "bytes": nbytes, "GBps": round(gbs, 1),
+                               "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the DMA forward "
-              "here is the single-GPU hot path, see DESIGN.md for how it would shard.",
-              file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build of "
+              "the DMA forward is the single-GPU hot path; across GPUs a prefill would shard "
+              "by kv-head group and a decode batch by sequence.", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
@@ -207,6 +286,9 @@ def main():
     x = make_inputs(wl, device=dev)
     if args.backward:
         backward_bench(args, wl, x, dev)
+        return
+    if args.hbm_stages:
+        hbm_stages(args, wl, x, dev)
         return
     delta = torch.empty(wl.B, wl.Hkv, wl.Sk, dtype=torch.float32, device=dev)
     mask = dma.alloc_mask(wl.B, wl.Hkv, wl.Sq, wl.Sk, wl.q_offset, wl.w, dev)
@@ -274,13 +356,23 @@ def main():
         "config": {"workload": wl.name, "B": wl.B, "Hq": wl.Hq, "Hkv": wl.Hkv, "Sq": wl.Sq,
                    "Sk": wl.Sk, "D": wl.D, "w": wl.w, "kept_pairs": wl.kept_pairs(),
                    "effective_flop": flops},
-        "roofline": {"bound": "mfma", "kernel": "attn_prefill_bf16_kernel" if wl.Sq > 1
-                     else "decode_mfma_kernel",
+        "roofline": {"bound": "mfma", "kernel": "attn_prefill_bf16_kernel",
                      "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic(wl.name) if wl.Sq > 1 else None},
+                     "traffic": measured_traffic(wl.name)},
         "stages_ms": {k: round(v, 4) for k, v in st.items()},
     }
+    if decode:
+        # one query row per sequence: the attention is bound by the HBM gather of the
+        # kept K/V rows (plus Q, O, the indices and their delta); the stage covers the
+        # gathering kernel and the merge of its splits
+        kept = int(mask.u_cnt[:mask.dims["n_tiles_total"]].sum().item())
+        es = x["V"].element_size()
+        a_bytes = kept * 2 * wl.D * es + 2 * wl.B * wl.Hq * wl.D * es + kept * 8
+        gbs = a_bytes / (st["attention"] * 1e-3) / 1e9
+        out["roofline"] = {"bound": "hbm", "kernel": "decode_mfma_kernel",
+                           "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                           "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x, wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)
