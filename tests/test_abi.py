@@ -72,7 +72,11 @@ def test_workspace_sizes(lib):
     assert lib.dma_topk_workspace_bytes(1, 8, 16384, 16384, 2048) >= 8 * 16384 * 20 + 8 * 32 * 2560 * 8
     assert lib.dma_topk_workspace_bytes(1, 8, 1, 16384, 2048) == 0
     assert lib.dma_attn_workspace_bytes(2, 32, 4096, 128, 2048) == 0
-    assert lib.dma_attn_workspace_bytes(64, 32, 1, 128, 2048) == 64 * 32 * 8 * 130 * 4
+    # one-row attention: a (max, sum, o[128]) partial per query head and split; the
+    # bf16 kernel splits the 2048-entry list into 32 waves of 64 entries, the generic
+    # one into 8 pieces of 256: the workspace covers the larger count
+    assert lib.dma_attn_workspace_bytes(64, 32, 1, 128, 2048) == 64 * 32 * 32 * 130 * 4
+    assert lib.dma_attn_workspace_bytes(1, 2, 1, 64, 100) == 1 * 2 * 2 * 66 * 4
 
 
 def _weights(lib, V=FAKE, vt=1, B=1, Sk=16, Hkv=2, D=64, sb=None, ss=None, Dl=FAKE, A=FAKE,

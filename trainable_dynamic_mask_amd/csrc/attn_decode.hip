@@ -400,7 +400,7 @@ hipError_t launch_g(const DmaAttnArgs& a, hipStream_t st) {
 }  // namespace
 
 size_t dma_attn_decode_ws_bytes(int64_t B, int64_t Hq, int64_t D, int64_t u_stride) {
-  // enough for either path: 64-entry splits in pairs (bf16, D = 128) or 256-entry splits
+  // enough for either path: one split per 64-entry wave (bf16, D = 128) or per 256 entries
   const int64_t nw = (u_stride + kWaveKeys - 1) / kWaveKeys;
   const int64_t nsplit = std::max<int64_t>((nw + kMfmaWaves - 1) / kMfmaWaves * kMfmaWaves,
                                            (u_stride + kSplit - 1) / kSplit);
