@@ -177,6 +177,12 @@ dma_status dma_decode_keep_append(const float* delta, int64_t B, int64_t Hkv, in
  * delta, mask: from steps 1 and 2 for the same (B, Hkv, Sq, Sk, q_offset, w).
  * scale  <= 0 selects 1/sqrt(D).
  * O      [B,Sq,Hq,D] contiguous, type t (output).   lse float [B,Hq,Sq] or NULL.
+ *        bf16 prefill: with lse requested the logits are rounded exactly as
+ *        dma_attn_bwd recomputes them (O, lse and the gradients then agree to
+ *        the last bit in nearly one-hot rows, and O equals dma_attn_fwd_train's);
+ *        with lse NULL the score scale is applied inside the exponent, which
+ *        is faster.  The two O can differ in the last bit of bf16; both are
+ *        within the stated tolerance of the exact result.
  * ws     dma_attn_workspace_bytes(...) bytes (NULL allowed when 0).
  * Arithmetic: BF16 inputs use bf16 MFMA products with fp32 accumulation and
  * an fp32 online softmax; F32 inputs are computed in fp32 throughout.

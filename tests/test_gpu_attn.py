@@ -21,11 +21,14 @@ pytestmark = pytest.mark.gpu
 
 
 def _run(x, wl, scale=None):
+    """Both forwards: with the log-sum-exp (logits rounded as the backward
+    recomputes them) and without it (the score scale inside the exponent)."""
     d = dma.weights(x["V"], x["Delta"], x["A"])
     gm = dma.topk_mask(d, wl.Sq, wl.q_offset, wl.w)
     O, lse = dma.attn_fwd(x["Q"], x["K"], x["V"], d, gm, scale=scale, return_lse=True)
+    Oi = dma.attn_fwd(x["Q"], x["K"], x["V"], d, gm, scale=scale)
     torch.cuda.synchronize()
-    return d, gm, O, lse
+    return d, gm, O, lse, Oi
 
 
 def _oracle_rows(x, d, wl, rows, scale=None):
@@ -40,10 +43,11 @@ def _all_rows(wl):
 def test_tiny_f32_every_row(gpu_lib):
     wl = WORKLOADS["tiny_f32"]
     x = make_inputs(wl, device="cuda")
-    d, gm, O, lse = _run(x, wl)
+    d, gm, O, lse, Oi = _run(x, wl)
     rows = _all_rows(wl)
     Or, Lr = _oracle_rows(x, d, wl, rows)
     m, r = compare_rows(O, lse, Or, Lr, rows, "f32", "tiny_f32")
+    compare_rows(Oi, None, Or, Lr, rows, "f32", "tiny_f32 (no lse)")
     print(f"tiny_f32: max abs {m:.2e} rel L2 {r:.2e}")
 
 
@@ -60,15 +64,16 @@ def test_tiny_f32_every_row(gpu_lib):
 def test_small_every_row(gpu_lib, B, Hq, Hkv, S, w, dtype, D):
     wl, x = make_small(B, Hq, Hkv, S, S, D, w, dtype=dtype, delta_std=0.05, seed=S + w,
                        device="cuda")
-    d, gm, O, lse = _run(x, wl)
+    d, gm, O, lse, Oi = _run(x, wl)
     rows = _all_rows(wl)
     Or, Lr = _oracle_rows(x, d, wl, rows)
     compare_rows(O, lse, Or, Lr, rows, dtype, f"{(B, Hq, Hkv, S, w, dtype, D)}")
+    compare_rows(Oi, None, Or, Lr, rows, dtype, f"{(B, Hq, Hkv, S, w, dtype, D)} (no lse)")
 
 
 def test_window_one_copies_value_rows_exactly(gpu_lib):
     wl, x = make_small(1, 4, 2, 200, 200, 128, 1, dtype="bf16", seed=5, device="cuda")
-    d, gm, O, lse = _run(x, wl)
+    d, gm, O, lse, Oi = _run(x, wl)
     d64 = to64(d)
     for hq in range(4):
         h = hq // 2
@@ -91,30 +96,34 @@ def test_custom_scale_and_strided_inputs(gpu_lib):
     d = dma.weights(x["V"], x["Delta"], x["A"])
     gm = dma.topk_mask(d, S, 0, w)
     O, lse = dma.attn_fwd(Q, kv[:, :, :Hkv], kv[:, :, Hkv:], d, gm, scale=0.05, return_lse=True)
+    Oi = dma.attn_fwd(Q, kv[:, :, :Hkv], kv[:, :, Hkv:], d, gm, scale=0.05)
     rows = _all_rows(wl)
     Or, Lr = oracle.attn_rows(x["Q"], x["K"], x["V"], to64(d), 0, w, rows, scale=0.05)
     compare_rows(O, lse, Or, Lr, rows, "bf16", "strided")
+    compare_rows(Oi, None, Or, Lr, rows, "bf16", "strided (no lse)")
 
 
 @pytest.mark.parametrize("q0,Sq,Sk,w", [(100, 70, 170, 30), (500, 129, 629, 200),
                                         (64, 64, 128, 64)])
 def test_chunked_prefill_query_offset(gpu_lib, q0, Sq, Sk, w):
     wl, x = make_small(1, 8, 2, Sq, Sk, 128, w, dtype="bf16", q_offset=q0, seed=q0, device="cuda")
-    d, gm, O, lse = _run(x, wl)
+    d, gm, O, lse, Oi = _run(x, wl)
     rows = _all_rows(wl)
     Or, Lr = _oracle_rows(x, d, wl, rows)
     compare_rows(O, lse, Or, Lr, rows, "bf16", "chunked")
+    compare_rows(Oi, None, Or, Lr, rows, "bf16", "chunked (no lse)")
 
 
 def test_heavy_tailed_delta(gpu_lib):
     # Delta std 0.5: delta spans many orders of magnitude within a tile
     wl, x = make_small(1, 4, 1, 500, 500, 128, 60, dtype="bf16", delta_std=0.5, seed=2,
                        device="cuda")
-    d, gm, O, lse = _run(x, wl)
+    d, gm, O, lse, Oi = _run(x, wl)
     assert float(d.max()) > 1e3
     rows = _all_rows(wl)
     Or, Lr = _oracle_rows(x, d, wl, rows)
     compare_rows(O, lse, Or, Lr, rows, "bf16", "heavy tail")
+    compare_rows(Oi, None, Or, Lr, rows, "bf16", "heavy tail (no lse)")
 
 
 @pytest.mark.parametrize("name,n_random", [("prefill_4k", 300), ("prefill_16k", 300),
@@ -122,11 +131,12 @@ def test_heavy_tailed_delta(gpu_lib):
 def test_workload_sampled_rows(gpu_lib, name, n_random):
     wl = WORKLOADS[name]
     x = make_inputs(wl, device="cuda")
-    d, gm, O, lse = _run(x, wl)
+    d, gm, O, lse, Oi = _run(x, wl)
     assert torch.isfinite(O.float()).all()
     rows = sample_rows(wl.B, wl.Hq, wl.Sq, wl.w, n_random, seed=wl.seed)
     Or, Lr = _oracle_rows(x, d, wl, rows)
     m, r = compare_rows(O, lse, Or, Lr, rows, wl.dtype, name)
+    compare_rows(Oi, None, Or, Lr, rows, wl.dtype, name + " (no lse)")
     print(f"{name}: {len(rows)} rows, max abs {m:.2e} rel L2 {r:.2e}")
 
 
@@ -134,7 +144,7 @@ def test_workload_sampled_rows(gpu_lib, name, n_random):
 def test_end_to_end_with_oracle_delta(gpu_lib, name):
     wl = WORKLOADS[name]
     x = make_inputs(wl, device="cuda")
-    d, gm, O, lse = _run(x, wl)
+    d, gm, O, lse, Oi = _run(x, wl)
     d64 = oracle.weights(x["V"], x["Delta"], x["A"])       # the oracle's own delta
     e_gpu = gm.evict.cpu().numpy().reshape(wl.B, wl.Hkv, wl.Sk)
     rows = sample_rows(wl.B, wl.Hq, wl.Sq, wl.w, 200, seed=wl.seed + 1)
@@ -155,6 +165,7 @@ def test_end_to_end_with_oracle_delta(gpu_lib, name):
     rows = np.array(keep, np.int64)
     Or, Lr = oracle.attn_rows(x["Q"], x["K"], x["V"], d64, wl.q_offset, wl.w, rows)
     m, r = compare_rows(O, lse, Or, Lr, rows, wl.dtype, name + " end-to-end")
+    compare_rows(Oi, None, Or, Lr, rows, wl.dtype, name + " end-to-end (no lse)")
     print(f"{name} end-to-end: {len(rows)} rows compared, {differ} left out (near ties); "
           f"max abs {m:.2e} rel L2 {r:.2e}")
 

@@ -288,7 +288,7 @@ __device__ __forceinline__ void g_phase(Acc& acc, const dma::bf16x8 (&pb)[2][2],
 // element; the others hold keys every row keeps.  Lane (l32, hi) holds
 // key(mb, i) = mb*32 + 8*(i/4) + 4*hi + i%4 of query l32; the other 32 keys
 // of the same query sit in lane ^ 32.
-template <bool MASKED, int NDMA, typename F>
+template <bool MASKED, bool ROUNDED, int NDMA, typename F>
 __device__ __forceinline__ void softmax_phase(Acc& acc, dma::f32x16 (&s)[2],
                                               dma::bf16x8 (&pb)[2][2], const Smem& sm, int slot,
                                               int hi, int pos, float scale2, F&& dma_issue) {
@@ -312,7 +312,10 @@ __device__ __forceinline__ void softmax_phase(Acc& acc, dma::f32x16 (&s)[2],
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = q4 * 4 + r;
-        float v = s[mb][i] * scale2;  // scale2 * (q.k + bias / scale2)
+        // the logit is scale2 * v with v = q.k + bias / scale2.  ROUNDED rounds
+        // it first, as the backward recomputes it; otherwise the factor goes
+        // into the exponent below (scale2 > 0 keeps the maximum)
+        float v = ROUNDED ? s[mb][i] * scale2 : s[mb][i];
         // kept iff pj <= pos < pe, one unsigned compare (pe <= pj: never)
         if constexpr (MASKED)
           v = ((uint32_t)(pos - pj[r]) < (uint32_t)(pe[r] - pj[r])) ? v : -INFINITY;
@@ -325,6 +328,7 @@ __device__ __forceinline__ void softmax_phase(Acc& acc, dma::f32x16 (&s)[2],
   // halves of each query (lane l and l ^ 32), so the common path has no
   // cross-lane exchange.
   float mx = fmaxf(fmaxf(mxp[0], mxp[1]), fmaxf(mxp[2], mxp[3]));
+  if constexpr (!ROUNDED) mx *= scale2;
   if (__ballot(mx > acc.m + kLazy) != 0ull) {
     // rare: a logit above the reference by more than the headroom
     mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -350,7 +354,8 @@ __device__ __forceinline__ void softmax_phase(Acc& acc, dma::f32x16 (&s)[2],
       float p[8];
 #pragma unroll
       for (int t8 = 0; t8 < 8; ++t8) {
-        p[t8] = __builtin_amdgcn_exp2f(s[mb][hf * 8 + t8] - m_use);
+        p[t8] = __builtin_amdgcn_exp2f(ROUNDED ? s[mb][hf * 8 + t8] - m_use
+                                               : fmaf(s[mb][hf * 8 + t8], scale2, -m_use));
         rsp[t8 & 3] += p[t8];
       }
       pb[mb][hf] = to_bf16x8(p);
@@ -358,7 +363,7 @@ __device__ __forceinline__ void softmax_phase(Acc& acc, dma::f32x16 (&s)[2],
   acc.l += (rsp[0] + rsp[1]) + (rsp[2] + rsp[3]);
 }
 
-template <int NH>
+template <int NH, bool ROUNDED>
 __global__ __launch_bounds__(NH * 128, 1) void attn_prefill_bf16_kernel(DmaAttnArgs a) {
   constexpr int NW = NH * 2;
   constexpr int NG = 2 * (16 / NW);  // direct loads per wave for one K and one V tile
@@ -531,7 +536,7 @@ __global__ __launch_bounds__(NH * 128, 1) void attn_prefill_bf16_kernel(DmaAttnA
     phase_barrier<-1>();                                                                \
     if (wave == 0) DMA_PREPARE(c + 1);                                                  \
     if (c < nch)                                                                        \
-      softmax_phase<MASKED, 0>(acc, s, pb, sm, c % kFin, hi, pos, scale2, [](int) {});  \
+      softmax_phase<MASKED, ROUNDED, 0>(acc, s, pb, sm, c % kFin, hi, pos, scale2, [](int) {});  \
     gather_rows<NW>(kr, sm, c + 3, wave, lane);                                         \
     gather_rows<NW>(vr, sm, c + 2, wave, lane);                                         \
     if (wave == 0)                                                                      \
@@ -552,7 +557,7 @@ __global__ __launch_bounds__(NH * 128, 1) void attn_prefill_bf16_kernel(DmaAttnA
         gather_piece<NW>(i_, kt_, vt_, kr, vr, Kg, Vg, rowb, wave, lane);               \
       };                                                                                \
       if (c < nch)                                                                      \
-        softmax_phase<MASKED, NG>(acc, s, pb, sm, c % kFin, hi, pos, scale2, issue_);   \
+        softmax_phase<MASKED, ROUNDED, NG>(acc, s, pb, sm, c % kFin, hi, pos, scale2, issue_);   \
       else                                                                              \
         for (int i_ = 0; i_ < NG; ++i_) issue_(i_);                                     \
     }                                                                                   \
@@ -635,7 +640,16 @@ template <int NH>
 hipError_t launch(const DmaAttnArgs& a, hipStream_t st) {
   const int G = (int)(a.Hq / a.Hkv);
   dim3 grid((unsigned)(a.n_tiles * a.Hkv * a.B * (G / NH)));
-  hipLaunchKernelGGL(attn_prefill_bf16_kernel<NH>, grid, dim3(NH * 128), 0, st, a);
+  // With the log-sum-exp requested (the statistic a backward consumes) the
+  // logits are rounded exactly as the backward recomputes them: in rows
+  // whose softmax is nearly one-hot the gradients are differences of nearly
+  // equal terms, and this keeps the forward's weights and lse consistent with
+  // the backward's to the last bit there.  Without it the score scale is
+  // applied inside the exponent (one fused multiply-add per score).
+  if (a.lse)
+    hipLaunchKernelGGL((attn_prefill_bf16_kernel<NH, true>), grid, dim3(NH * 128), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_prefill_bf16_kernel<NH, false>), grid, dim3(NH * 128), 0, st, a);
   return hipGetLastError();
 }
 
