@@ -715,7 +715,10 @@ __global__ __launch_bounds__(kGroupWaves * 64) void group_lists_kernel(
 }
 
 // ---------------------------------------------------------------- decode: one row
-// Keys 0..p of one sequence; keeps the w best.  Thread t holds the codes of
+// Keys 0..p of one sequence; keeps the w best (Hugging Face blog "Trainable
+// Dynamic Mask Sparse Attention", section "Mask Combination with Causal
+// Constraints": the top w of the causally visible keys by delta, ties to the
+// lower index).  Thread t holds the codes of
 // keys k*512 + t (coalesced loads, 64 registers).  The threshold, the largest
 // code T with #{code >= T} >= w, is found bit by bit from the top.  The
 // leading bits run over every key; the keys that can still reach the
