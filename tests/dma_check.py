@@ -117,3 +117,33 @@ def compare_rows(O_gpu, lse_gpu, O_ref, lse_ref, rows, dtype, what=""):
         bad = np.abs(lg - lse_ref) > lim
         assert not bad.any(), f"{what} lse err {np.abs(lg - lse_ref).max():.3e} at {rows[bad][:3]}"
     return max_abs, rel_l2
+
+
+def ddelta_term_sizes(Q, K, V, d64, dO, q0, w, scale=None):
+    """Per key j, the size of the terms its delta gradient sums:
+    T_j = sum over rows i keeping j of P_ij (|dP_ij| + |D_i|), with P the
+    row's softmax over its kept keys, dP_ij = dO_i . v_j and D_i = sum_j P_ij dP_ij
+    (fp64, from the oracle's keep sets).  dL/ddelta_j = sum_i P_ij (dP_ij - D_i)
+    can be far smaller than T_j (nearly one-hot rows cancel), so its fp32
+    error is bounded relative to T_j, not to the result."""
+    Qn = Q.float().cpu().double().numpy()
+    Kn = K.float().cpu().double().numpy()
+    Vn = V.float().cpu().double().numpy()
+    Gn = dO.float().cpu().double().numpy()
+    B, Sq, Hq, D = Qn.shape
+    Hkv, Sk = d64.shape[1], d64.shape[2]
+    G = Hq // Hkv
+    sc = 1.0 / np.sqrt(D) if scale is None else scale
+    T = np.zeros((B, Hkv, Sk))
+    for b in range(B):
+        for h in range(Hkv):
+            keep = [oracle.keep_row(d64[b, h], q0 + i, w) for i in range(Sq)]
+            for hq in range(h * G, (h + 1) * G):
+                for i in range(Sq):
+                    j = keep[i]
+                    s = Kn[b, j, h] @ Qn[b, i, hq] * sc + d64[b, h, j]
+                    p = np.exp(s - s.max())
+                    p /= p.sum()
+                    dp = Vn[b, j, h] @ Gn[b, i, hq]
+                    T[b, h, j] += p * (np.abs(dp) + abs((p * dp).sum()))
+    return T
