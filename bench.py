@@ -128,8 +128,14 @@ def cpu_baseline(x, wl, budget_s):
     t_rows = time.perf_counter() - t0
     kept = np.minimum(wl.q_offset + rows[:, 2] + 1, wl.w).sum()
     t = t_rows + t_w * n / total_rows
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next(l.split(":", 1)[1].strip() for l in fh if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
     return {"value": float(4 * wl.D * kept / t / 1e12), "unit": "TFLOP/s",
-            "cores": oracle.num_threads(), "kind": "oracle",
+            "cores": oracle.num_threads(), "cpu_model": model, "kind": "oracle",
             "sample": f"fp64 oracle: delta of all {wl.B * wl.Hkv * wl.Sk} keys ({t_w:.2f} s, "
                       f"prorated) + keep set and attention of {n} random query rows of "
                       f"{total_rows} ({t_rows:.2f} s)",
