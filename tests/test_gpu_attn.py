@@ -126,6 +126,21 @@ def test_heavy_tailed_delta(gpu_lib):
     compare_rows(Oi, None, Or, Lr, rows, "bf16", "heavy tail (no lse)")
 
 
+def test_f32_heavy_tail_every_row(gpu_lib):
+    # delta std 0.1 (delta up to ~1e8, fp32 spacing ~8 there): rows that do not
+    # see their tile's largest delta keep full precision because the fp32 path
+    # takes each row's bias relative to the largest delta it keeps
+    B, Hq, Hkv, S, w = 2, 3, 3, 1923, 605
+    wl, x = make_small(B, Hq, Hkv, S, S, 64, w, dtype="f32", seed=302831582, delta_std=0.1,
+                       device="cuda")
+    d, gm, O, lse, Oi = _run(x, wl)
+    rows = _all_rows(wl)
+    Or, Lr = _oracle_rows(x, d, wl, rows)
+    m, r = compare_rows(O, lse, Or, Lr, rows, "f32", "f32 heavy tail")
+    compare_rows(Oi, None, Or, Lr, rows, "f32", "f32 heavy tail (no lse)")
+    print(f"f32 heavy tail: max abs {m:.2e} rel L2 {r:.2e}")
+
+
 @pytest.mark.parametrize("name,n_random", [("prefill_4k", 300), ("prefill_16k", 300),
                                            ("prefill_64k", 200)])
 def test_workload_sampled_rows(gpu_lib, name, n_random):

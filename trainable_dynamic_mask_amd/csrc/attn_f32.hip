@@ -5,14 +5,16 @@
 // walks the compacted key list of that tile in chunks of 64 gathered keys;
 // its waves are query heads of the kv head.  Here each lane owns one query
 // row, so the softmax needs no cross-lane reductions; keys are read from LDS
-// as broadcasts.  This path favours exactness over speed.
+// as broadcasts.  This path favours exactness over speed: the bias is taken
+// relative to the largest delta among the row's own kept keys (found by a
+// first pass over the list), so delta - reference is exact for every key
+// within a factor 2 of it, whatever the range of delta across the tile.
 #include "common.h"
 
 namespace {
 
 constexpr int kBq = 64;
 constexpr int kBk = 64;
-constexpr int kGroup = 8;  // keys per online-softmax update
 
 template <int D>
 struct SmemF {
@@ -20,7 +22,7 @@ struct SmemF {
   float v[kBk][D];
   int pj[kBk];
   int e[kBk];
-  float bias[kBk];  // delta - dmax (natural units), -inf for padding
+  float dlt[kBk];   // delta of the key, -inf for padding
 };
 
 template <int D, int NH>
@@ -28,6 +30,8 @@ __global__ __launch_bounds__(NH * 64, 1) void attn_prefill_f32_kernel(DmaAttnArg
   extern __shared__ __align__(16) unsigned char smem_raw[];
   SmemF<D>& sm = *reinterpret_cast<SmemF<D>*>(smem_raw);
   constexpr int NT = NH * 64;
+  // keys per online-softmax update (4 with D = 128: q and o take 256 registers)
+  constexpr int kGroup = D == 128 ? 4 : 8;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = (int)(a.Hq / a.Hkv);
   const int ngrp = G / NH;
@@ -40,13 +44,29 @@ __global__ __launch_bounds__(NH * 64, 1) void attn_prefill_f32_kernel(DmaAttnArg
   const int rows = min(kBq, (int)a.Sq - r_lo);
   const int pos = (int)a.q0 + r_lo + lane;
   const int cnt = a.u_cnt[g];
-  const float dmax = a.u_dmax[g];
   const int32_t* list = a.u_idx + g * a.u_stride;
   const float* dl = a.delta + seg * a.Sk;
   const int32_t* ev = a.evict + seg * a.Sk;
   const float* Kg = static_cast<const float*>(a.K) + b * a.ksb + h * a.ksh;
   const float* Vg = static_cast<const float*>(a.V) + b * a.ksb + h * a.ksh;
 
+  // the row's reference: the largest delta among its kept keys
+  float rmax = -INFINITY;
+  for (int c0 = 0; c0 < cnt; c0 += kBk) {
+    __syncthreads();
+    for (int kk = tid; kk < kBk; kk += NT) {
+      const int idx = c0 + kk;
+      const bool pad = idx >= cnt;
+      const int j = pad ? 0 : list[idx];
+      sm.pj[kk] = pad ? 0x7fffffff : j;
+      sm.e[kk] = pad ? 0 : ev[j];
+      sm.dlt[kk] = pad ? -INFINITY : dl[j];
+    }
+    __syncthreads();
+    const int nk = min(kBk, cnt - c0);
+    for (int kk = 0; kk < nk; ++kk)
+      if (sm.pj[kk] <= pos && pos < sm.e[kk]) rmax = fmaxf(rmax, sm.dlt[kk]);
+  }
   float q[D], o[D];
   {
     const float* qrow = static_cast<const float*>(a.Q) + b * a.qsb + hq * a.qsh +
@@ -82,7 +102,7 @@ __global__ __launch_bounds__(NH * 64, 1) void attn_prefill_f32_kernel(DmaAttnArg
       const int j = pad ? 0 : list[idx];
       sm.pj[kk] = pad ? 0x7fffffff : j;
       sm.e[kk] = pad ? 0 : ev[j];
-      sm.bias[kk] = pad ? -INFINITY : dl[j] - dmax;
+      sm.dlt[kk] = pad ? -INFINITY : dl[j];
     }
     __syncthreads();
     const int nk = min(kBk, cnt - c0);
@@ -102,7 +122,7 @@ __global__ __launch_bounds__(NH * 64, 1) void attn_prefill_f32_kernel(DmaAttnArg
           dot = fmaf(q[d + 3], kv.w, dot);
         }
         const bool keep = kk < nk && sm.pj[kk] <= pos && pos < sm.e[kk];
-        x[r] = keep ? fmaf(dot, a.scale, sm.bias[kk]) : -INFINITY;
+        x[r] = keep ? fmaf(dot, a.scale, sm.dlt[kk] - rmax) : -INFINITY;
         mx = fmaxf(mx, x[r]);
       }
       const float m_new = fmaxf(m, mx);
@@ -143,7 +163,7 @@ __global__ __launch_bounds__(NH * 64, 1) void attn_prefill_f32_kernel(DmaAttnArg
     for (int d = 0; d < D; d += 4)
       *reinterpret_cast<float4*>(orow + d) =
           make_float4(o[d] * inv, o[d + 1] * inv, o[d + 2] * inv, o[d + 3] * inv);
-    if (a.lse) a.lse[((int64_t)b * a.Hq + hq) * a.Sq + r_lo + lane] = m + logf(l) + dmax;
+    if (a.lse) a.lse[((int64_t)b * a.Hq + hq) * a.Sq + r_lo + lane] = m + logf(l) + rmax;
   }
 }
 
