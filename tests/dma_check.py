@@ -121,11 +121,13 @@ def compare_rows(O_gpu, lse_gpu, O_ref, lse_ref, rows, dtype, what=""):
 
 def ddelta_term_sizes(Q, K, V, d64, dO, q0, w, scale=None):
     """Per key j, the size of the terms its delta gradient sums:
-    T_j = sum over rows i keeping j of P_ij (|dP_ij| + |D_i|), with P the
-    row's softmax over its kept keys, dP_ij = dO_i . v_j and D_i = sum_j P_ij dP_ij
+    T_j = sum over rows i keeping j of P_ij (|dP_ij| + S_i), with P the row's
+    softmax over its kept keys, dP_ij = dO_i . v_j and S_i = sum_j P_ij |dP_ij|
     (fp64, from the oracle's keep sets).  dL/ddelta_j = sum_i P_ij (dP_ij - D_i)
-    can be far smaller than T_j (nearly one-hot rows cancel), so its fp32
-    error is bounded relative to T_j, not to the result."""
+    with D_i = dO_i . O_i.  The forward forms O from bf16-rounded weights
+    (2^-9 relative each), so D_i carries errors up to 2^-9 S_i, and the result
+    can be far smaller than T_j (nearly one-hot rows cancel): its error is
+    bounded relative to T_j, not to the result."""
     Qn = Q.float().cpu().double().numpy()
     Kn = K.float().cpu().double().numpy()
     Vn = V.float().cpu().double().numpy()
@@ -145,5 +147,5 @@ def ddelta_term_sizes(Q, K, V, d64, dO, q0, w, scale=None):
                     p = np.exp(s - s.max())
                     p /= p.sum()
                     dp = Vn[b, j, h] @ Gn[b, i, hq]
-                    T[b, h, j] += p * (np.abs(dp) + abs((p * dp).sum()))
+                    T[b, h, j] += p * (np.abs(dp) + (p * np.abs(dp)).sum())
     return T

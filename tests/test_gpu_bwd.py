@@ -81,7 +81,9 @@ def test_bwd_heavy_tail_chunked(gpu_lib):
     # errors ~1e-4, and rows that do not see the tile's largest delta are not
     # shifted exactly.  dQ, dK and dV stay within the usual bounds; the delta
     # gradient sums terms up to ~1e3 times larger than itself (nearly one-hot
-    # rows), so each key's error is bounded relative to the size of its terms.
+    # rows), so each key's error is bounded relative to the size of its terms
+    # (twice the bf16 rounding of the forward's weights, which reaches dL/ddelta
+    # through D = dO . O).
     B, Hq, Hkv, Sq, Sk, q0, w = 2, 9, 3, 229, 773, 544, 344
     wl, x = make_small(B, Hq, Hkv, Sq, Sk, 128, w, dtype="bf16", q_offset=q0, seed=76114265,
                        delta_std=0.05, device="cuda")
@@ -99,7 +101,7 @@ def test_bwd_heavy_tail_chunked(gpu_lib):
     err = np.abs(to64(got[3]) - want[3])
     ratio = err / np.maximum(T, 1e-30)
     print(f"ddelta: error / term size max {ratio.max():.2e}, median {np.median(ratio[T > 0]):.2e}")
-    assert (err <= 2e-3 * T + 1e-6).all()
+    assert (err <= 4e-3 * T + 1e-6).all()
 
 
 def test_bwd_w1_only_dv(gpu_lib):
