@@ -28,3 +28,39 @@ def test_inputs_seeded_and_shaped():
     assert (a["A"] >= 0.5).all() and (a["A"] < 1.5).all()
     wl2, x = make_small(1, 4, 2, 10, 10, 128, 3, dtype="bf16")
     assert x["K"].dtype == torch.bfloat16 and x["K"].shape == (1, 10, 2, 128)
+
+
+def _bench_module():
+    import importlib.util
+    import os
+    path = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "bench.py")
+    spec = importlib.util.spec_from_file_location("bench_under_test", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod, path
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    import sys
+    _, path = _bench_module()
+    r = subprocess.run([sys.executable, path, "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_bench_traffic_follows_the_kernel_sources(tmp_path, monkeypatch):
+    bench, _ = _bench_module()
+    good = tmp_path / "traffic.txt"
+    good.write_text(f"kernel_source_sha256: {bench.attn_source_hash()}\n"
+                    "hbm_bytes_per_launch: 123456\n# a comment: 1\n")
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(good))
+    assert bench.measured_traffic("prefill_16k") == 123456.0
+    assert bench.measured_traffic("prefill_64k") is None   # taken on the 16K workload only
+    stale = tmp_path / "stale.txt"
+    stale.write_text("kernel_source_sha256: 0000000000000000\nhbm_bytes_per_launch: 1\n")
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(stale))
+    assert bench.measured_traffic("prefill_16k") is None  # sources changed since
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "missing.txt"))
+    assert bench.measured_traffic("prefill_16k") is None
