@@ -142,7 +142,7 @@ def test_f32_heavy_tail_every_row(gpu_lib):
 
 
 @pytest.mark.parametrize("name,n_random", [("prefill_4k", 300), ("prefill_16k", 300),
-                                           ("prefill_64k", 200)])
+                                           ("prefill_64k", 200), ("chunk_16k", 300)])
 def test_workload_sampled_rows(gpu_lib, name, n_random):
     wl = WORKLOADS[name]
     x = make_inputs(wl, device="cuda")

@@ -57,7 +57,8 @@ def test_mask_query_offset(gpu_lib, q0, Sq, Sk, w):
     check_mask(gm, d)
 
 
-@pytest.mark.parametrize("name", ["tiny_f32", "prefill_4k", "prefill_16k", "prefill_64k"])
+@pytest.mark.parametrize("name", ["tiny_f32", "prefill_4k", "prefill_16k", "prefill_64k",
+                                  "chunk_16k"])
 def test_mask_workloads(gpu_lib, name):
     wl = WORKLOADS[name]
     x = make_inputs(wl, device="cuda")

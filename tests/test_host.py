@@ -15,6 +15,8 @@ def test_kept_pairs_formula():
         wl = Workload("t", "bf16", 2, 4, 2, Sq, S, q0, 128, w, 0.02, 0)
         assert wl.kept_pairs() == _kept_brute(wl)
     assert WORKLOADS["prefill_16k"].kept_pairs() == 1_006_665_728
+    # chunked prefill: rows 12288..16383 all keep w = 2048 keys, 32 query heads
+    assert WORKLOADS["chunk_16k"].kept_pairs() == 4096 * 2048 * 32
     assert WORKLOADS["prefill_64k"].effective_flops() == 4 * 128 * 8_321_564_672
 
 

@@ -1,8 +1,10 @@
 """Workload shapes of the Dynamic Mask Attention forward.
 
-Five synthetic workloads: a tiny fp32 causal case, two bf16 GQA prefills
+Six synthetic workloads: a tiny fp32 causal case, two bf16 GQA prefills
 (4K and 16K tokens), a 64K-token prefill whose dynamic weights are heavy
-tailed, and a batched decode step against a 32K-token cache.  The method
+tailed, a batched decode step against a 32K-token cache, and a chunked
+prefill (the last 4K tokens of a 16K sequence, against the 12K before them
+as cache).  The method
 (dynamic weights, causal top-w keep mask, masked softmax attention) is the
 one stated on the Hugging Face blog "Trainable Dynamic Mask Sparse
 Attention" (sections "Dynamic Sparse Mask Generation", "Mask Combination
@@ -62,6 +64,8 @@ WORKLOADS = {
                             q_offset=0, D=128, w=4096, delta_std=0.05, seed=1003),
     "decode_32k": Workload("decode_32k", "bf16", B=64, Hq=32, Hkv=8, Sq=1, Sk=32768,
                            q_offset=32767, D=128, w=2048, delta_std=0.02, seed=1004),
+    "chunk_16k": Workload("chunk_16k", "bf16", B=1, Hq=32, Hkv=8, Sq=4096, Sk=16384,
+                          q_offset=12288, D=128, w=2048, delta_std=0.02, seed=1005),
 }
 
 HEADLINE = "prefill_16k"
