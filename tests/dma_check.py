@@ -2,7 +2,7 @@
 
 Tolerances (bf16 figures from the workload statement; fp32 from the same):
   delta           max relative error 1e-5 (fp32 V) / 3e-5 (bf16 V, 1024-term fp32 sums)
-  keep mask       bit-exact, judged on a shared delta: the oracle is fed the GPU's
+  keep mask       bit-exact, compared on a shared delta: the oracle is fed the GPU's
                   fp32 delta widened to fp64 (exact and order preserving)
   output (fp32)   max abs 1e-5
   output (bf16)   max abs 2e-2 and relative L2 5e-3
