@@ -137,7 +137,7 @@ dma_status dma_weights(const void* V, dma_dtype vt, int64_t B, int64_t Sk, int64
  * equation), for query positions q_offset .. q_offset+Sq-1 over keys 0..Sk-1.
  * delta  float [B, Hkv, Sk] (from dma_weights or any other source; NaN is
  *        not allowed).  Ordering is exact: larger delta wins, equal delta
- *        goes to the lower key index.
+ *        (IEEE equality, so -0 equals +0) goes to the lower key index.
  * out    arrays sized by dma_mask_dims_for (kt_idx/kt_cnt may be NULL).
  * ws     dma_topk_workspace_bytes(...) bytes of device scratch (16-byte aligned),
  *        may be NULL when that is 0.  Its contents are undefined afterwards.
@@ -188,7 +188,9 @@ dma_status dma_decode_keep_append(const float* delta, int64_t B, int64_t Hkv, in
  * an fp32 online softmax; F32 inputs are computed in fp32 throughout.
  * Limits: BF16 with Sq > 1 needs D == 128 and the rows of one (batch, kv
  * head) within 4 GiB: (Sk-1)*kv_strides[1]*2 + 256 <= 2^32; otherwise
- * DMA_ERR_UNSUPPORTED.
+ * DMA_ERR_UNSUPPORTED.  With Sq == 1 any strides are accepted: key rows
+ * further apart than that are gathered with 64-bit offsets by the (slower)
+ * vector kernel instead of the matrix-core one.
  */
 dma_status dma_attn_fwd(const void* Q, const void* K, const void* V, dma_dtype t, int64_t B,
                         int64_t Sq, int64_t Sk, int64_t Hq, int64_t Hkv, int64_t D,

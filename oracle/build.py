@@ -4,13 +4,12 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "dma_oracle.cpp")
-# DMA_ORACLE_LIB lets a test run load a differently built copy of the oracle.
-LIB_PATH = os.environ.get("DMA_ORACLE_LIB", os.path.join(HERE, "libdma_oracle.so"))
+LIB_PATH = os.path.join(HERE, "libdma_oracle.so")
 
 
-def build(verbose=False, src=SRC, out=None):
-    out = out or LIB_PATH
-    cmd = ["g++", "-O2", "-std=c++17", "-fopenmp", "-fPIC", "-shared", src, "-o", out + ".tmp"]
+def build(verbose=False):
+    out = LIB_PATH
+    cmd = ["g++", "-O2", "-std=c++17", "-fopenmp", "-fPIC", "-shared", SRC, "-o", out + ".tmp"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)

@@ -101,6 +101,26 @@ def sample_rows(B, Hq, Sq, w, n_random, seed=0):
     return np.array(sorted(set(rows)), np.int64)
 
 
+def tile_edge_rows(B, Hq, Sq, w, per_head, seed=0):
+    """(b, hq, i) triples: for every head, the first and last row of every query
+    tile (this includes rows 0, w-1, w and Sq-1 when w is a multiple of the
+    tile) plus rows w-1, w, and distinct random rows up to per_head rows."""
+    rng = np.random.default_rng(seed)
+    edges = set()
+    for t in range((Sq + BQ - 1) // BQ):
+        edges.update({t * BQ, min(Sq, t * BQ + BQ) - 1})
+    edges.update(i for i in (0, w - 1, w, Sq - 1) if 0 <= i < Sq)
+    edges = np.array(sorted(edges), np.int64)
+    rows = []
+    rest = np.setdiff1d(np.arange(Sq), edges)
+    for b in range(B):
+        for hq in range(Hq):
+            extra = max(0, min(len(rest), per_head - len(edges)))
+            pick = np.concatenate([edges, rng.choice(rest, extra, replace=False)])
+            rows.append(np.stack([np.full(len(pick), b), np.full(len(pick), hq), pick], 1))
+    return np.concatenate(rows).astype(np.int64)
+
+
 def compare_rows(O_gpu, lse_gpu, O_ref, lse_ref, rows, dtype, what=""):
     """O_gpu [B,Sq,Hq,D] tensor, lse_gpu [B,Hq,Sq]; reference rows in the order of `rows`."""
     tol = TOL[dtype]

@@ -15,7 +15,7 @@ import oracle
 import trainable_dynamic_mask_amd as dma
 from trainable_dynamic_mask_amd.configs import WORKLOADS
 from trainable_dynamic_mask_amd.inputs import make_inputs, make_small
-from tests.dma_check import compare_rows, sample_rows, to64
+from tests.dma_check import compare_rows, sample_rows, tile_edge_rows, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -141,18 +141,39 @@ def test_f32_heavy_tail_every_row(gpu_lib):
     print(f"f32 heavy tail: max abs {m:.2e} rel L2 {r:.2e}")
 
 
-@pytest.mark.parametrize("name,n_random", [("prefill_4k", 300), ("prefill_16k", 300),
-                                           ("prefill_64k", 200), ("chunk_16k", 300)])
-def test_workload_sampled_rows(gpu_lib, name, n_random):
+@pytest.mark.parametrize("name", ["prefill_4k", "prefill_16k", "chunk_16k"])
+def test_workload_every_row(gpu_lib, name):
+    # every output row of the workload against the oracle (both forwards)
     wl = WORKLOADS[name]
+    print(f"{name}: every row", flush=True)
     x = make_inputs(wl, device="cuda")
     d, gm, O, lse, Oi = _run(x, wl)
     assert torch.isfinite(O.float()).all()
-    rows = sample_rows(wl.B, wl.Hq, wl.Sq, wl.w, n_random, seed=wl.seed)
+    rows = _all_rows(wl)
     Or, Lr = _oracle_rows(x, d, wl, rows)
     m, r = compare_rows(O, lse, Or, Lr, rows, wl.dtype, name)
-    compare_rows(Oi, None, Or, Lr, rows, wl.dtype, name + " (no lse)")
-    print(f"{name}: {len(rows)} rows, max abs {m:.2e} rel L2 {r:.2e}")
+    mi, ri = compare_rows(Oi, None, Or, Lr, rows, wl.dtype, name + " (no lse)")
+    print(f"{name}: {len(rows)} rows (all), max abs {m:.2e} rel L2 {r:.2e}; "
+          f"no-lse forward max abs {mi:.2e} rel L2 {ri:.2e}")
+
+
+def test_workload_64k_tile_edges_and_random_rows(gpu_lib):
+    # the 64K workload has the largest delta range (the per-tile offset is least
+    # exact there): every query tile's first and last row of every head, plus
+    # random rows, at least 4096 rows per head
+    wl = WORKLOADS["prefill_64k"]
+    print("prefill_64k: tile edges + random rows", flush=True)
+    x = make_inputs(wl, device="cuda")
+    d, gm, O, lse, Oi = _run(x, wl)
+    assert torch.isfinite(O.float()).all()
+    rows = tile_edge_rows(wl.B, wl.Hq, wl.Sq, wl.w, per_head=4096, seed=wl.seed)
+    per_head = np.bincount(rows[:, 0] * wl.Hq + rows[:, 1], minlength=wl.B * wl.Hq)
+    assert per_head.min() >= 4096
+    Or, Lr = _oracle_rows(x, d, wl, rows)
+    m, r = compare_rows(O, lse, Or, Lr, rows, wl.dtype, "prefill_64k")
+    mi, ri = compare_rows(Oi, None, Or, Lr, rows, wl.dtype, "prefill_64k (no lse)")
+    print(f"prefill_64k: {len(rows)} rows ({per_head.min()} per head or more), max abs {m:.2e} "
+          f"rel L2 {r:.2e}; no-lse forward max abs {mi:.2e} rel L2 {ri:.2e}")
 
 
 @pytest.mark.parametrize("name", ["prefill_4k", "prefill_16k"])

@@ -164,3 +164,37 @@ def test_bwd_prefill_16k_sampled(gpu_lib):
         assert float(dd[0, 1, j]) == 0
     ddn = to64(dd)
     assert np.abs(ddn.sum(-1)).max() < 1e-3 * np.abs(ddn).sum(-1).max()
+
+
+def test_bwd_noncontiguous_views_match_contiguous(gpu_lib):
+    # O, O_res and dO handed over as non-contiguous views of one buffer each, and
+    # Delta/A in bf16: the binding makes contiguous float copies, which must all
+    # stay alive until the kernels have read them (a copy freed early could be
+    # overwritten by the next one).  Results must equal the contiguous call's.
+    B, Hq, Hkv, S, w = 1, 8, 2, 300, 64
+    wl, x = make_small(B, Hq, Hkv, S, S, 128, w, dtype="bf16", seed=31, device="cuda")
+    dO = make_grad(wl, device="cuda")
+    d = dma.weights(x["V"], x["Delta"], x["A"])
+    m = dma.topk_mask(d, S, 0, w)
+    O, lse, Ores = dma.attn_fwd_train(x["Q"], x["K"], x["V"], d, m)
+    ref = dma.attn_bwd(x["Q"], x["K"], x["V"], d, m, O, lse, dO, O_res=Ores)
+    # the same values behind transposed storage: [B, Hq, S, D] buffers viewed as [B, S, Hq, D]
+    def strided(t):
+        buf = t.transpose(1, 2).contiguous()
+        v = buf.transpose(1, 2)
+        assert not v.is_contiguous()
+        return v
+    lse_nc = lse.transpose(1, 2).contiguous().transpose(1, 2)
+    assert not lse_nc.is_contiguous()
+    got = dma.attn_bwd(x["Q"], x["K"], x["V"], d, m, strided(O), lse_nc, strided(dO),
+                       O_res=strided(Ores))
+    torch.cuda.synchronize()
+    for a, b, name in zip(got, ref, ("dQ", "dK", "dV", "ddelta")):
+        assert torch.equal(a, b), name
+    # weights backward with bf16 Delta and A: the float copies must survive the call
+    Dl, Al = x["Delta"].bfloat16(), x["A"].bfloat16()
+    dV1, dD1, dA1 = dma.weights_bwd(x["V"], Dl, Al, ref[3], dV=ref[2].clone())
+    dV2, dD2, dA2 = dma.weights_bwd(x["V"], Dl.float(), Al.float(), ref[3], dV=ref[2].clone())
+    torch.cuda.synchronize()
+    assert torch.equal(dV1, dV2)
+    assert torch.allclose(dD1, dD2, rtol=1e-5, atol=1e-7) and torch.allclose(dA1, dA2, rtol=1e-5)

@@ -27,6 +27,9 @@ def _delta(kind, B, Hkv, S, seed):
         d = torch.rand(B, Hkv, S, generator=g) * 10 + 1
     elif kind == "ties":         # three values only: the lower index must win every tie
         d = torch.randint(1, 4, (B, Hkv, S), generator=g).float()
+    elif kind == "signed_zeros":  # -0 and +0 tie: a new +0 never displaces a kept -0
+        vals = torch.tensor([-0.0, 0.0, -0.0, 0.0, -1.0, 1.0])
+        d = vals[torch.randint(0, 6, (B, Hkv, S), generator=g)]
     elif kind == "rising":       # every new key beats every kept key
         d = torch.arange(S, dtype=torch.float32).repeat(B, Hkv, 1) + 1
     else:                        # falling: no new key ever enters
@@ -36,7 +39,8 @@ def _delta(kind, B, Hkv, S, seed):
 
 @pytest.mark.parametrize("kind,B,Hkv,w,steps", [
     ("random", 2, 4, 256, 150), ("random", 1, 3, 1, 60), ("random", 2, 2, 7, 80),
-    ("ties", 2, 4, 33, 120), ("ties", 1, 2, 1, 40), ("rising", 1, 2, 16, 30),
+    ("ties", 2, 4, 33, 120), ("ties", 1, 2, 1, 40), ("signed_zeros", 2, 2, 1, 60),
+    ("signed_zeros", 2, 2, 2, 60), ("rising", 1, 2, 16, 30),
     ("falling", 1, 2, 16, 30)])
 def test_append_matches_selection(gpu_lib, kind, B, Hkv, w, steps):
     S0 = w + 1

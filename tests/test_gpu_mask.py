@@ -25,6 +25,9 @@ def _delta(kind, B, H, S, seed):
         d = torch.arange(S, dtype=torch.float32).expand(B, H, S).contiguous() + 1.0
     elif kind == "decreasing":  # oldest keys always best: the first w keys
         d = (S - torch.arange(S, dtype=torch.float32)).expand(B, H, S).contiguous()
+    elif kind == "signed_zeros":  # -0 and +0 are equal: they tie, the lower index wins
+        vals = torch.tensor([-0.0, 0.0, -0.0, 0.0, -1.0, 1.0])
+        d = vals[torch.randint(0, 6, (B, H, S), generator=g)]
     else:
         d = torch.exp(torch.randn(B, H, S, generator=g))
     return d.cuda()
@@ -37,6 +40,23 @@ def test_mask_small(gpu_lib, kind, S, w):
     d = _delta(kind, 2, 3, S, seed=S * 7 + w)
     gm = dma.topk_mask(d, S, 0, w)
     torch.cuda.synchronize()
+    check_mask(gm, d)
+
+
+@pytest.mark.parametrize("S,w", [(2, 1), (9, 1), (9, 2), (300, 1), (300, 2), (5000, 1),
+                                 (5000, 2), (20000, 2)])
+def test_mask_signed_zeros(gpu_lib, S, w):
+    # mixed -0 / +0 weights: the order code must treat them as one value
+    d = _delta("signed_zeros", 2, 2, S, seed=S + w)
+    assert torch.signbit(d[d == 0]).any() and (~torch.signbit(d[d == 0])).any()
+    gm = dma.topk_mask(d, S, 0, w)
+    check_mask(gm, d)
+
+
+@pytest.mark.parametrize("p,w", [(1, 1), (7, 2), (100, 1), (100, 2), (32767, 1), (32767, 2)])
+def test_decode_select_signed_zeros(gpu_lib, p, w):
+    d = _delta("signed_zeros", 3, 2, p + 1, seed=p * 3 + w)
+    gm = dma.topk_mask(d, 1, p, w)
     check_mask(gm, d)
 
 

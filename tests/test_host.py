@@ -66,3 +66,39 @@ def test_bench_traffic_follows_the_kernel_sources(tmp_path, monkeypatch):
     assert bench.measured_traffic("prefill_16k") is None  # sources changed since
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "missing.txt"))
     assert bench.measured_traffic("prefill_16k") is None
+
+
+def test_binding_rejects_mismatched_mask_and_delta():
+    # the kernels index the mask arrays and delta by the call's sizes, so the
+    # binding refuses arrays built for other sizes before anything reaches the
+    # C ABI (these checks run on the host, ahead of the device check)
+    import pytest
+    import trainable_dynamic_mask_amd as dma
+    B, S, Hq, Hkv, D, w = 1, 128, 4, 2, 128, 16
+    Q = torch.zeros(B, S, Hq, D, dtype=torch.bfloat16)
+    K = torch.zeros(B, S, Hkv, D, dtype=torch.bfloat16)
+    V = torch.zeros_like(K)
+    delta = torch.ones(B, Hkv, S)
+    short = dma.alloc_mask(B, Hkv, 64, S, 0, w, "cpu")
+    with pytest.raises(ValueError, match="mask was built"):
+        dma.attn_fwd(Q, K, V, delta, short)
+    other_sk = dma.alloc_mask(B, Hkv, 64, 64, 0, w, "cpu")
+    with pytest.raises(ValueError, match="mask was built"):
+        dma.attn_fwd(Q[:, :64], K, V, delta, other_sk)
+    good = dma.alloc_mask(B, Hkv, S, S, 0, w, "cpu")
+    with pytest.raises(ValueError, match="delta must be"):
+        dma.attn_fwd(Q, K, V, delta[:, :, :100], good)
+    with pytest.raises(ValueError, match="delta must be"):
+        dma.attn_fwd(Q, K, V, delta.double(), good)
+    good.u_idx = good.u_idx[:10]
+    with pytest.raises(ValueError, match="u_idx"):
+        dma.attn_fwd(Q, K, V, delta, good)
+    good = dma.alloc_mask(B, Hkv, S, S, 0, w, "cpu")
+    with pytest.raises(ValueError, match="lse must be"):
+        dma.attn_bwd(Q, K, V, delta, good, Q, torch.zeros(B, Hq, S, dtype=torch.float64), Q)
+    with pytest.raises(ValueError, match="O and dO"):
+        dma.attn_bwd(Q, K, V, delta, good, Q[:, :64], torch.zeros(B, Hq, S), Q)
+    with pytest.raises(ValueError, match="share one dtype"):
+        dma.attn_fwd(Q.float(), K, V, delta, good)
+    with pytest.raises(ValueError, match="GPU"):
+        dma.attn_fwd(Q, K, V, delta, good)   # every size matches: only the device is wrong

@@ -13,10 +13,13 @@ from tests import brute
 from tests.golden import load
 
 
-@pytest.mark.parametrize("name", ["keep_ties_w2.txt", "keep_ties_w3.txt"])
+@pytest.mark.parametrize("name", ["keep_ties_w2.txt", "keep_ties_w3.txt",
+                                  "keep_signed_zeros_w1.txt", "keep_signed_zeros_w2.txt"])
 def test_hand_derived_fixture(name):
     g = load(name)
     d = np.array(g["delta"])
+    if "signed_zeros" in name:
+        assert np.signbit(d[d == 0]).any() and (~np.signbit(d[d == 0])).any()
     w, Bq, Bk = int(g["w"][0]), int(g["Bq"][0]), int(g["Bk"][0])
     S = len(d)
     for p, want in g["row"].items():
@@ -34,10 +37,12 @@ def _rand_delta(rng, S, kind):
         return rng.integers(0, 4, S).astype(np.float64)
     if kind == "allequal":
         return np.full(S, 2.0)
+    if kind == "signed_zeros":  # -0 and +0 tie (IEEE equality); also -1 and 1
+        return rng.choice(np.array([-0.0, 0.0, -1.0, 1.0]), S)
     return rng.random(S) + 1.0
 
 
-@pytest.mark.parametrize("kind", ["ties", "random", "allequal"])
+@pytest.mark.parametrize("kind", ["ties", "random", "allequal", "signed_zeros"])
 def test_brute_force_enumeration(kind):
     rng = np.random.default_rng(7)
     for trial in range(40):

@@ -47,6 +47,38 @@ def _need_cuda(*ts):
             raise ValueError("DMA tensors must live on the GPU")
 
 
+def _check_delta(delta: torch.Tensor, B: int, Hkv: int, Sk: int):
+    if delta.dtype != torch.float32 or tuple(delta.shape) != (B, Hkv, Sk):
+        raise ValueError(f"delta must be float32 [B, Hkv, Sk] = {[B, Hkv, Sk]}, got "
+                         f"{delta.dtype} {list(delta.shape)}")
+
+
+def _check_mask(mask: "Mask", B: int, Hkv: int, Sq: int, Sk: int):
+    """The kernels index the mask arrays by these sizes, so a mask built for
+    other sizes would be read out of bounds."""
+    if (mask.B, mask.Hkv, mask.Sq, mask.Sk) != (B, Hkv, Sq, Sk):
+        raise ValueError(f"mask was built for (B, Hkv, Sq, Sk) = "
+                         f"{(mask.B, mask.Hkv, mask.Sq, mask.Sk)}, the call has {(B, Hkv, Sq, Sk)}")
+    d = mask_dims(B, Hkv, Sq, Sk, mask.q_offset, mask.w)
+    n = d["n_tiles_total"]
+    for name, t, need in (("u_idx", mask.u_idx, d["u_elems"]), ("u_cnt", mask.u_cnt, n),
+                          ("u_nfull", mask.u_nfull, n), ("u_dmax", mask.u_dmax, n),
+                          ("evict", mask.evict, d["evict_elems"])):
+        if need and (t is None or t.numel() < need):
+            raise ValueError(f"mask array {name} holds fewer than {need} entries")
+
+
+def _check_qkv(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor):
+    if Q.dim() != 4 or K.dim() != 4 or V.shape != K.shape:
+        raise ValueError("Q must be [B,Sq,Hq,D], K and V [B,Sk,Hkv,D]")
+    if Q.dtype != K.dtype or Q.dtype != V.dtype:
+        raise ValueError("Q, K and V must share one dtype")
+    if Q.shape[0] != K.shape[0] or Q.shape[3] != K.shape[3]:
+        raise ValueError("Q and K/V disagree on batch or head size")
+    if K.stride() != V.stride() or Q.stride(3) != 1 or K.stride(3) != 1:
+        raise ValueError("K and V must share strides; the D values must be contiguous")
+
+
 def tile_sizes():
     bq, bk = ctypes.c_int32(), ctypes.c_int32()
     load().dma_tile_sizes(ctypes.byref(bq), ctypes.byref(bk))
@@ -108,6 +140,8 @@ def weights(V: torch.Tensor, Delta: torch.Tensor, A: torch.Tensor,
     A = A.contiguous().float()
     if out is None:
         out = torch.empty(B, Hkv, Sk, dtype=torch.float32, device=V.device)
+    elif out.dtype != torch.float32 or tuple(out.shape) != (B, Hkv, Sk) or not out.is_contiguous():
+        raise ValueError("out must be contiguous float32 [B, Hkv, Sk]")
     check("dma_weights", load().dma_weights(_ptr(V), _dtype_code(V.dtype), B, Sk, Hkv, D,
                                             V.stride(0), V.stride(1), _ptr(Delta), _ptr(A),
                                             _ptr(out), _stream(V.device)))
@@ -120,6 +154,7 @@ def topk_mask(delta: torch.Tensor, Sq: int, q_offset: int, w: int, kt_lists: boo
     _need_cuda(delta)
     delta = delta.contiguous()
     B, Hkv, Sk = delta.shape
+    _check_delta(delta, B, Hkv, Sk)
     lib = load()
     if mask is None:
         mask = alloc_mask(B, Hkv, Sq, Sk, q_offset, w, delta.device, kt_lists)
@@ -156,11 +191,13 @@ def attn_fwd(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, delta: torch.Ten
              scale: Optional[float] = None, return_lse: bool = False,
              out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
     """Masked attention; Q [B,Sq,Hq,D], K/V [B,Sk,Hkv,D] (any b/s/h strides)."""
-    _need_cuda(Q, K, V, delta)
+    _check_qkv(Q, K, V)
     B, Sq, Hq, D = Q.shape
     _, Sk, Hkv, _ = K.shape
-    if K.stride() != V.stride() or Q.stride(3) != 1 or K.stride(3) != 1:
-        raise ValueError("K and V must share strides; the D values must be contiguous")
+    _check_delta(delta, B, Hkv, Sk)
+    _check_mask(mask, B, Hkv, Sq, Sk)
+    _need_cuda(Q, K, V, delta)
+    delta_c = delta.contiguous()  # bound to a name: it must outlive the enqueued kernels
     lib = load()
     if out is None:
         out = torch.empty(B, Sq, Hq, D, dtype=Q.dtype, device=Q.device)
@@ -173,7 +210,7 @@ def attn_fwd(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, delta: torch.Ten
     ms = mask.cstruct()
     check("dma_attn_fwd", lib.dma_attn_fwd(
         _ptr(Q), _ptr(K), _ptr(V), _dtype_code(Q.dtype), B, Sq, Sk, Hq, Hkv, D, qs, ks,
-        mask.q_offset, mask.w, _ptr(delta.contiguous()), ctypes.byref(ms),
+        mask.q_offset, mask.w, _ptr(delta_c), ctypes.byref(ms),
         float(scale) if scale is not None else 0.0, _ptr(out), _ptr(lse),
         _ptr(workspace) if nbytes else ctypes.c_void_p(0), nbytes, _stream(Q.device)))
     return (out, lse) if return_lse else out
@@ -193,11 +230,13 @@ def attn_fwd_train(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, delta: tor
                    mask: Mask, scale: Optional[float] = None):
     """attn_fwd for training (bf16 prefill): returns O, lse and O_res, the
     rounding residual of O that attn_bwd uses for dO . O."""
-    _need_cuda(Q, K, V, delta)
+    _check_qkv(Q, K, V)
     B, Sq, Hq, D = Q.shape
     _, Sk, Hkv, _ = K.shape
-    if K.stride() != V.stride() or Q.stride(3) != 1 or K.stride(3) != 1:
-        raise ValueError("K and V must share strides; the D values must be contiguous")
+    _check_delta(delta, B, Hkv, Sk)
+    _check_mask(mask, B, Hkv, Sq, Sk)
+    _need_cuda(Q, K, V, delta)
+    delta_c = delta.contiguous()
     O = torch.empty(B, Sq, Hq, D, dtype=Q.dtype, device=Q.device)
     Ores = torch.empty_like(O)
     lse = torch.empty(B, Hq, Sq, dtype=torch.float32, device=Q.device)
@@ -206,7 +245,7 @@ def attn_fwd_train(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, delta: tor
     ms = mask.cstruct()
     check("dma_attn_fwd_train", load().dma_attn_fwd_train(
         _ptr(Q), _ptr(K), _ptr(V), _dtype_code(Q.dtype), B, Sq, Sk, Hq, Hkv, D, qs, ks,
-        mask.q_offset, mask.w, _ptr(delta.contiguous()), ctypes.byref(ms),
+        mask.q_offset, mask.w, _ptr(delta_c), ctypes.byref(ms),
         0.0 if scale is None else float(scale), _ptr(O), _ptr(lse), _ptr(Ores), _stream(Q.device)))
     return O, lse, Ores
 
@@ -218,11 +257,22 @@ def attn_bwd(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, delta: torch.Ten
     """Gradients of sum(dO * O) of attn_fwd (keep sets fixed): float32 dQ
     [B,Sq,Hq,D], dK and dV [B,Sk,Hkv,D], ddelta [B,Hkv,Sk].  O and lse are
     the forward's outputs; O_res (from attn_fwd_train) makes dO . O exact."""
-    _need_cuda(Q, K, V, delta, O, lse, dO)
+    _check_qkv(Q, K, V)
     B, Sq, Hq, D = Q.shape
     _, Sk, Hkv, _ = K.shape
-    if K.stride() != V.stride() or Q.stride(3) != 1 or K.stride(3) != 1:
-        raise ValueError("K and V must share strides; the D values must be contiguous")
+    _check_delta(delta, B, Hkv, Sk)
+    _check_mask(mask, B, Hkv, Sq, Sk)
+    if O.shape != Q.shape or dO.shape != Q.shape or O.dtype != Q.dtype or dO.dtype != Q.dtype:
+        raise ValueError("O and dO must have Q's shape and dtype")
+    if O_res is not None and (O_res.shape != Q.shape or O_res.dtype != Q.dtype):
+        raise ValueError("O_res must have Q's shape and dtype")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Sq):
+        raise ValueError("lse must be float32 [B, Hq, Sq]")
+    _need_cuda(Q, K, V, delta, O, lse, dO)
+    # contiguous copies bound to names: each must outlive the enqueued kernels
+    # (a temporary freed at once could hand its memory to the next copy)
+    delta_c, O_c, lse_c, dO_c = (t.contiguous() for t in (delta, O, lse, dO))
+    Ores_c = O_res.contiguous() if O_res is not None else None
     lib = load()
     dev = Q.device
     dQ = torch.empty(B, Sq, Hq, D, dtype=torch.float32, device=dev)
@@ -237,10 +287,10 @@ def attn_bwd(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, delta: torch.Ten
     ms = mask.cstruct()
     check("dma_attn_bwd", lib.dma_attn_bwd(
         _ptr(Q), _ptr(K), _ptr(V), _dtype_code(Q.dtype), B, Sq, Sk, Hq, Hkv, D, qs, ks,
-        mask.q_offset, mask.w, _ptr(delta.contiguous()), ctypes.byref(ms),
-        0.0 if scale is None else float(scale), _ptr(O.contiguous()),
-        _ptr(O_res.contiguous()) if O_res is not None else None, _ptr(lse.contiguous()),
-        _ptr(dO.contiguous()), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dd), _ptr(workspace), nbytes,
+        mask.q_offset, mask.w, _ptr(delta_c), ctypes.byref(ms),
+        0.0 if scale is None else float(scale), _ptr(O_c),
+        _ptr(Ores_c) if Ores_c is not None else None, _ptr(lse_c),
+        _ptr(dO_c), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dd), _ptr(workspace), nbytes,
         _stream(dev)))
     return dQ, dK, dV, dd
 
@@ -253,6 +303,14 @@ def weights_bwd(V: torch.Tensor, Delta: torch.Tensor, A: torch.Tensor, ddelta: t
     B, Sk, Hkv, D = V.shape
     if V.stride(3) != 1 or V.stride(2) != D:
         raise ValueError("V rows must be contiguous over (kv head, channel)")
+    _check_delta(ddelta, B, Hkv, Sk)
+    if dV is not None and (dV.dtype != torch.float32 or tuple(dV.shape) != (B, Sk, Hkv, D)
+                           or not dV.is_contiguous()):
+        raise ValueError("dV must be contiguous float32 [B, Sk, Hkv, D]")
+    # converted copies bound to names: each must outlive the enqueued kernels
+    Delta_c = Delta.contiguous().float()
+    A_c = A.contiguous().float()
+    dd_c = ddelta.contiguous()
     dev = V.device
     if dV is None:
         dV = torch.zeros(B, Sk, Hkv, D, dtype=torch.float32, device=dev)
@@ -264,7 +322,7 @@ def weights_bwd(V: torch.Tensor, Delta: torch.Tensor, A: torch.Tensor, ddelta: t
         workspace = torch.empty(max(16, nbytes), dtype=torch.uint8, device=dev)
     check("dma_weights_bwd", lib.dma_weights_bwd(
         _ptr(V), _dtype_code(V.dtype), B, Sk, Hkv, D, V.stride(0), V.stride(1),
-        _ptr(Delta.contiguous().float()), _ptr(A.contiguous().float()),
-        _ptr(ddelta.contiguous()), _ptr(dV), _ptr(dDelta), _ptr(dA), _ptr(workspace), nbytes,
+        _ptr(Delta_c), _ptr(A_c), _ptr(dd_c), _ptr(dV), _ptr(dDelta), _ptr(dA), _ptr(workspace),
+        nbytes,
         _stream(dev)))
     return dV, dDelta, dA

@@ -263,7 +263,10 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void decode_mfma_kernel(DmaAttnArg
       mx = fmaxf(mx, v);
     }
   mx = fmaxf(mx, __shfl_xor(mx, 32));
-  float l = 0.f;
+  // l sums the weights (the log-sum-exp); lr sums them as rounded to bf16 for
+  // the PV product, which normalises this split's output, so a row dominated
+  // by one key returns that key's value row unaffected by the weight's rounding
+  float l = 0.f, lr = 0.f;
   dma::bf16x8 pb[2][2];
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
@@ -276,8 +279,11 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void decode_mfma_kernel(DmaAttnArg
         l += p[t8];
       }
       pb[mb][hf] = dma::to_bf16x8(p);
+#pragma unroll
+      for (int t8 = 0; t8 < 8; ++t8) lr += (float)pb[mb][hf][t8];
     }
   l += __shfl_xor(l, 32);
+  lr += __shfl_xor(lr, 32);
   // O^T += V^T P^T over four 16-key steps; V read with the transposing load
   dma::f32x16 o[4];
 #pragma unroll
@@ -308,8 +314,14 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void decode_mfma_kernel(DmaAttnArg
       }
     }
   // this wave's (max, sum, o) for query head n: register i of block db is
-  // d = db*32 + 8(i/4) + 4hi + i%4
+  // d = db*32 + 8(i/4) + 4hi + i%4.  o is stored as l/lr times the product, so
+  // that o / l, what the merge divides by, is the product over lr
   if (n < G) {
+    const float f = lr > 0.f ? l / lr : 0.f;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[db][i] *= f;
     if (hi == 0) {
       part[0] = mx;
       part[1] = l;
@@ -408,7 +420,11 @@ size_t dma_attn_decode_ws_bytes(int64_t B, int64_t Hq, int64_t D, int64_t u_stri
 }
 
 hipError_t dma_launch_attn_decode(const DmaAttnArgs& a, int is_bf16, hipStream_t st) {
-  if (is_bf16 && a.D == 128 && a.Hq / a.Hkv <= 32) return launch_mfma(a, st);
+  // the MFMA kernel gathers key rows by 32-bit byte offsets from the (b, h)
+  // base; caches whose rows lie further apart take the split kernel, whose
+  // offsets are 64-bit
+  const bool near = a.Sk <= 0 || (a.Sk - 1) * a.kss * 2 + 256 <= ((int64_t)1 << 32);
+  if (is_bf16 && a.D == 128 && a.Hq / a.Hkv <= 32 && near) return launch_mfma(a, st);
   if (is_bf16) return a.D == 64 ? launch_g<__bf16, 64>(a, st) : launch_g<__bf16, 128>(a, st);
   return a.D == 64 ? launch_g<float, 64>(a, st) : launch_g<float, 128>(a, st);
 }

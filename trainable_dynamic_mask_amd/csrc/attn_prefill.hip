@@ -91,8 +91,10 @@ struct Smem {
   float bias[kFin][kBk];           // (delta - dmax) * log2(e) / score scale, -inf for padding
 };
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   bf16x2 r;
   r[0] = (__bf16)lo;
   r[1] = (__bf16)hi;
@@ -168,7 +170,9 @@ __device__ __forceinline__ void phase_barrier() {
 // Running softmax state of one wave: 32 query rows.
 struct Acc {
   dma::f32x16 o[4];  // O^T: 4 blocks of 32 d x 32 queries
-  float m, l;        // base-2 reference and this lane's partial row sum
+  float m;           // base-2 reference
+  float l;           // this lane's partial row sum of the weights (the log-sum-exp)
+  float lr;          // the same sum of the weights as rounded to bf16 for the PV product
 };
 
 // V^T operands of PV k-step ks = (mb, hf) = (ks/2, ks%2) for the four d
@@ -339,6 +343,7 @@ __device__ __forceinline__ void softmax_phase(Acc& acc, dma::f32x16 (&s)[2],
     const float m_new = fmaxf(acc.m, mx);
     const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(acc.m - m_new);
     acc.l *= alpha;
+    acc.lr *= alpha;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -346,7 +351,13 @@ __device__ __forceinline__ void softmax_phase(Acc& acc, dma::f32x16 (&s)[2],
     acc.m = m_new;
   }
   const float m_use = (acc.m == -INFINITY) ? 0.f : acc.m;
+  // O is normalised by the sum of the weights exactly as the PV product sees
+  // them (rounded to bf16): then a row dominated by one key returns that
+  // key's value row with no error from the weight's rounding.  The sum of
+  // rounded pairs is one bf16 dot product with (1, 1) per two weights.  The
+  // log-sum-exp (ROUNDED: asked for) uses the unrounded weights.
   float rsp[4] = {0.f, 0.f, 0.f, 0.f};
+  float rsr[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -360,11 +371,17 @@ __device__ __forceinline__ void softmax_phase(Acc& acc, dma::f32x16 (&s)[2],
       for (int t8 = 0; t8 < 8; ++t8) {
         p[t8] = __builtin_amdgcn_exp2f(ROUNDED ? s[mb][hf * 8 + t8] - m_use
                                                : fmaf(s[mb][hf * 8 + t8], scale2, -m_use));
-        rsp[t8 & 3] += p[t8];
+        if constexpr (ROUNDED) rsp[t8 & 3] += p[t8];
       }
       pb[mb][hf] = to_bf16x8(p);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const bf16x2 pr = {pb[mb][hf][2 * k], pb[mb][hf][2 * k + 1]};
+        rsr[k] = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes2, rsr[k], false);
+      }
     }
-  acc.l += (rsp[0] + rsp[1]) + (rsp[2] + rsp[3]);
+  if constexpr (ROUNDED) acc.l += (rsp[0] + rsp[1]) + (rsp[2] + rsp[3]);
+  acc.lr += (rsr[0] + rsr[1]) + (rsr[2] + rsr[3]);
 }
 
 template <int NH, bool ROUNDED>
@@ -495,6 +512,7 @@ __global__ __launch_bounds__(NH * 128, 1) void attn_prefill_bf16_kernel(DmaAttnA
     for (int i = 0; i < 16; ++i) acc.o[db][i] = 0.f;
   acc.m = -INFINITY;
   acc.l = 0.f;
+  acc.lr = 0.f;
   dma::f32x16 s[2];
   // P(-1) = 0 against a zeroed V buffer: the PV half of G_0 adds nothing
   dma::bf16x8 pb[2][2];
@@ -612,7 +630,8 @@ __global__ __launch_bounds__(NH * 128, 1) void attn_prefill_bf16_kernel(DmaAttnA
 
   // epilogue: normalise and write O (and the log-sum-exp)
   const float lt = acc.l + __shfl_xor(acc.l, 32);
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const float ltr = acc.lr + __shfl_xor(acc.lr, 32);
+  const float inv = ltr > 0.f ? 1.f / ltr : 0.f;
   if (n < rows) {
     uint16_t* orow = static_cast<uint16_t*>(a.O) + (((int64_t)b * a.Sq + r_lo + n) * a.Hq + hq) * kD;
 #pragma unroll

@@ -24,9 +24,12 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 }
 
 // Order-preserving map of an fp32 value onto uint32: a < b  <=>  ord(a) < ord(b)
-// (for non-NaN values; -0 and +0 map to neighbouring codes).
+// and a == b  <=>  ord(a) == ord(b) (for non-NaN values).  -0 compares equal
+// to +0, so it takes +0's code; equal weights then fall to the index part of
+// the composite key below, as every other tie does.
 __device__ __forceinline__ uint32_t ord32(float f) {
   uint32_t u = __float_as_uint(f);
+  u = (u == 0x80000000u) ? 0u : u;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
