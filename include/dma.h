@@ -84,7 +84,14 @@ void dma_tile_sizes(int32_t* Bq, int32_t* Bk);
  *          [kt*Bk, (kt+1)*Bk) holding at least one key of U_g (the block-skip
  *          list: every other key tile is skipped).  May be NULL (not written).
  *   kt_cnt int32 [n_tiles_total]   length of that list (NULL iff kt_idx is NULL).
- * With Sq == 1 (one decode row) evict is not read or written and may be NULL.
+ *   u_dlo  float [n_tiles_total]   largest delta over the keys before the tile's
+ *          first row (j < q_offset + t*Bq; -inf when there are none).  Row p's
+ *          largest kept delta is the prefix maximum of delta over keys 0..p
+ *          (a row always keeps its best key); the attention derives it from
+ *          u_dlo and the tile's own keys.  May be NULL for dma_topk_mask
+ *          (then not written); the bf16 prefill attention requires it.
+ * With Sq == 1 (one decode row) evict and u_dlo are not read or written and
+ * may be NULL.
  */
 typedef struct {
   int32_t* evict;
@@ -94,6 +101,7 @@ typedef struct {
   float* u_dmax;
   int32_t* kt_idx;
   int32_t* kt_cnt;
+  float* u_dlo;
 } dma_mask;
 
 typedef struct {
@@ -186,6 +194,7 @@ dma_status dma_decode_keep_append(const float* delta, int64_t B, int64_t Hkv, in
  * ws     dma_attn_workspace_bytes(...) bytes (NULL allowed when 0).
  * Arithmetic: BF16 inputs use bf16 MFMA products with fp32 accumulation and
  * an fp32 online softmax; F32 inputs are computed in fp32 throughout.
+ * BF16 with Sq > 1 reads mask->u_dlo (required).
  * Limits: BF16 with Sq > 1 needs D == 128 and the rows of one (batch, kv
  * head) within 4 GiB: (Sk-1)*kv_strides[1]*2 + 256 <= 2^32; otherwise
  * DMA_ERR_UNSUPPORTED.  With Sq == 1 any strides are accepted: key rows

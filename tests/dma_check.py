@@ -58,6 +58,13 @@ def check_mask(gm, delta_gpu, om=None):
     u_dmax = gm.u_dmax[: B * Hkv * nT].cpu().numpy().reshape(B, Hkv, nT)
     d32 = delta_gpu.detach().cpu().numpy()
     np.testing.assert_array_equal(u_cnt, om["u_cnt"])
+    if Sq > 1 and gm.u_dlo is not None:
+        # largest delta over the keys before each tile's first row (-inf for none)
+        u_dlo = gm.u_dlo[: B * Hkv * nT].cpu().numpy().reshape(B, Hkv, nT)
+        for t in range(nT):
+            p_lo = q0 + t * BQ
+            want = d32[:, :, :p_lo].max(-1) if p_lo > 0 else np.full((B, Hkv), -np.inf)
+            np.testing.assert_array_equal(u_dlo[:, :, t], want, err_msg=f"u_dlo tile {t}")
     ev_o = om["evict"]
     for b in range(B):
         for h in range(Hkv):

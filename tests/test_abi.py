@@ -38,7 +38,7 @@ def test_exports_every_declared_function(lib):
 def test_status_strings_and_versions(lib):
     assert lib.dma_status_string(0) == b"ok"
     assert lib.dma_status_string(3) == b"workspace too small"
-    assert lib.dma_abi_version() == 3
+    assert lib.dma_abi_version() == 4
     bq, bk = ctypes.c_int32(), ctypes.c_int32()
     lib.dma_tile_sizes(ctypes.byref(bq), ctypes.byref(bk))
     assert (bq.value, bk.value) == (64, 64)
@@ -138,10 +138,10 @@ def test_decode_append_validation(lib):
 
 
 def _attn(lib, t=1, B=1, Sq=16, Sk=16, Hq=4, Hkv=2, D=128, qs=None, ks=None, q0=0, w=4,
-          scale=0.0, Q=FAKE, O=FAKE, ws=None, ws_bytes=0):
+          scale=0.0, Q=FAKE, O=FAKE, ws=None, ws_bytes=0, dlo=FAKE):
     qs = qs or (Sq * Hq * D, Hq * D, D)
     ks = ks or (Sk * Hkv * D, Hkv * D, D)
-    m = DmaMask(FAKE, FAKE, FAKE, FAKE, FAKE, None, None)
+    m = DmaMask(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, dlo)
     return lib.dma_attn_fwd(Q, FAKE, FAKE, t, B, Sq, Sk, Hq, Hkv, D, (ctypes.c_int64 * 3)(*qs),
                             (ctypes.c_int64 * 3)(*ks), q0, w, FAKE, ctypes.byref(m), scale, O,
                             None, ws, ws_bytes, None)
@@ -157,6 +157,7 @@ def test_attn_validation(lib):
     assert _attn(lib, qs=(16 * 4 * 128, 4 * 128, 100)) == INVALID   # head stride below D
     assert _attn(lib, ks=(16 * 2 * 128, 2 * 128 + 3, 128)) == INVALID  # odd row stride
     assert _attn(lib, Sq=1, Sk=16, q0=15) == WORKSPACE       # decode row needs split partials
+    assert _attn(lib, dlo=None) == INVALID                   # bf16 prefill reads u_dlo
     assert _attn(lib, Sq=0, q0=16) == OK
     assert _attn(lib, B=0) == OK
 

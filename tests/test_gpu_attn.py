@@ -212,3 +212,36 @@ def test_empty_query_rows(gpu_lib):
     gm = dma.topk_mask(d, 0, 10, 3)
     O = dma.attn_fwd(x["Q"][:, :0], x["K"], x["V"], d, gm)
     assert O.shape == (1, 0, 4, 128)
+
+
+@pytest.mark.parametrize("q0", [0, 70])
+def test_large_delta_born_inside_a_tile(gpu_lib, q0):
+    # delta ~ 1..5 except a few keys of 1e4..3e4 born in the middle of query
+    # tiles: the rows of a tile before such a key keep only small deltas, far
+    # below the tile's largest.  Their scores must keep full precision (the
+    # kernel takes a per-row reference there); every row's O and lse against
+    # the oracle on the same delta.
+    S = 520
+    wl, x = make_small(1, 8, 2, S - q0, S, 128, 48, dtype="bf16", q_offset=q0, seed=77,
+                       device="cuda")
+    g = torch.Generator().manual_seed(5)
+    d = (torch.rand(1, 2, S, generator=g) * 4 + 1)
+    for j, v in ((100, 1.0e4), (150, 2.5e4), (333, 3.0e4), (334, 3.0e4 + 1.0), (470, 8.0e3)):
+        d[0, j % 2, j] = v
+    d = d.cuda()
+    gm = dma.topk_mask(d, wl.Sq, q0, wl.w)
+    O, lse = dma.attn_fwd(x["Q"], x["K"], x["V"], d, gm, return_lse=True)
+    Oi = dma.attn_fwd(x["Q"], x["K"], x["V"], d, gm)
+    torch.cuda.synchronize()
+    rows = _all_rows(wl)
+    Or, Lr = oracle.attn_rows(x["Q"], x["K"], x["V"], to64(d), q0, wl.w, rows)
+    m, r = compare_rows(O, lse, Or, Lr, rows, "bf16", "large delta births")
+    compare_rows(Oi, None, Or, Lr, rows, "bf16", "large delta births (no lse)")
+    # the rows in front of a birth have lse near their own small deltas
+    lg = lse[0].cpu().double().numpy()
+    lr = Lr.reshape(wl.Hq, wl.Sq)
+    small = np.abs(lr) < 100
+    err = np.abs(lg - lr)[small]
+    print(f"large births q0={q0}: max abs {m:.2e}, lse err over {small.sum()} small-delta rows "
+          f"{err.max():.2e}")
+    assert small.sum() > 100 and err.max() <= 2e-4

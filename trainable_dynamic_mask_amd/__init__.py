@@ -63,7 +63,8 @@ def _check_mask(mask: "Mask", B: int, Hkv: int, Sq: int, Sk: int):
     n = d["n_tiles_total"]
     for name, t, need in (("u_idx", mask.u_idx, d["u_elems"]), ("u_cnt", mask.u_cnt, n),
                           ("u_nfull", mask.u_nfull, n), ("u_dmax", mask.u_dmax, n),
-                          ("evict", mask.evict, d["evict_elems"])):
+                          ("evict", mask.evict, d["evict_elems"]),
+                          ("u_dlo", mask.u_dlo, n if Sq > 1 else 0)):
         if need and (t is None or t.numel() < need):
             raise ValueError(f"mask array {name} holds fewer than {need} entries")
 
@@ -109,10 +110,11 @@ class Mask:
     u_dmax: torch.Tensor
     kt_idx: Optional[torch.Tensor]
     kt_cnt: Optional[torch.Tensor]
+    u_dlo: Optional[torch.Tensor] = None
 
     def cstruct(self):
         return DmaMask(_ptr(self.evict), _ptr(self.u_idx), _ptr(self.u_cnt), _ptr(self.u_nfull),
-                       _ptr(self.u_dmax), _ptr(self.kt_idx), _ptr(self.kt_cnt))
+                       _ptr(self.u_dmax), _ptr(self.kt_idx), _ptr(self.kt_cnt), _ptr(self.u_dlo))
 
 
 def alloc_mask(B, Hkv, Sq, Sk, q_offset, w, device, kt_lists=True) -> Mask:
@@ -126,7 +128,9 @@ def alloc_mask(B, Hkv, Sq, Sk, q_offset, w, device, kt_lists=True) -> Mask:
                 u_nfull=torch.empty(max(1, n), **i32),
                 u_dmax=torch.empty(max(1, n), dtype=torch.float32, device=device),
                 kt_idx=torch.empty(max(1, d["kt_elems"]), **i32) if kt_lists else None,
-                kt_cnt=torch.empty(max(1, n), **i32) if kt_lists else None)
+                kt_cnt=torch.empty(max(1, n), **i32) if kt_lists else None,
+                u_dlo=torch.empty(max(1, n), dtype=torch.float32, device=device)
+                if Sq > 1 else None)
 
 
 def weights(V: torch.Tensor, Delta: torch.Tensor, A: torch.Tensor,

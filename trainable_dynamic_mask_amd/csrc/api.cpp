@@ -11,7 +11,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 3;
+constexpr int kAbiVersion = 4;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -142,6 +142,7 @@ dma_status dma_topk_mask(const float* delta, int64_t B, int64_t Hkv, int64_t Sq,
   a.kt_idx = out->kt_idx;
   a.kt_cnt = out->kt_cnt;
   a.ws = ws;
+  a.u_dlo = Sq > 1 ? out->u_dlo : nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (Sq == 1) return hip_status(dma_launch_topk_decode(a, s));
   const size_t need = dma_topk_workspace_bytes(B, Hkv, Sq, Sk, w);
@@ -185,6 +186,7 @@ dma_status attn_fwd_impl(const void* Q, const void* K, const void* V, dma_dtype 
     return DMA_ERR_INVALID_ARG;
   if (!mask->u_idx || !mask->u_cnt || !mask->u_nfull || !mask->u_dmax) return DMA_ERR_INVALID_ARG;
   if (Sq > 1 && !mask->evict) return DMA_ERR_INVALID_ARG;
+  if (Sq > 1 && t == DMA_BF16 && !mask->u_dlo) return DMA_ERR_INVALID_ARG;
   const int64_t esz = t == DMA_BF16 ? 2 : 4;
   for (int i = 0; i < 3; ++i)
     if (q_strides[i] < 0 || kv_strides[i] < 0 || (q_strides[i] * esz) % 16 != 0 ||
@@ -221,6 +223,7 @@ dma_status attn_fwd_impl(const void* Q, const void* K, const void* V, dma_dtype 
   a.u_cnt = mask->u_cnt;
   a.u_nfull = mask->u_nfull;
   a.u_dmax = mask->u_dmax;
+  a.u_dlo = mask->u_dlo;
   a.n_tiles = d.n_tiles;
   a.u_stride = d.u_stride;
   a.scale = scale > 0.f ? scale : 1.f / std::sqrt((float)D);

@@ -163,7 +163,6 @@ __global__ __launch_bounds__(NH * 128, 2) void bwd_dq_kernel(DmaBwdArgs a) {
   const int r_lo = t * kBq;
   const int rows = min(kBq, (int)f.Sq - r_lo);
   const int cnt = f.u_cnt[g];
-  const float dmax = f.u_dmax[g];
   const int32_t* list = f.u_idx + g * f.u_stride;
   const float* dlg = f.delta + seg * f.Sk;
   const int32_t* evg = f.evict + seg * f.Sk;
@@ -191,8 +190,10 @@ __global__ __launch_bounds__(NH * 128, 2) void bwd_dq_kernel(DmaBwdArgs a) {
                                   *reinterpret_cast<const u32x4*>(grow + kk * 16 + hi * 8));
     }
   }
+  // the row's weights are exp(scale q.k + delta - lse): delta - lse is taken
+  // first, exact for every key near the row's maximum whatever the range of
+  // delta, so the logits carried stay small
   const float lse_q = f.lse[((int64_t)b * f.Hq + hq) * f.Sq + nr];
-  const float lq = (lse_q - dmax) * kLog2e;
   const float dv_q = a.Dv[((int64_t)b * f.Hq + hq) * f.Sq + nr];
 
   const uint32_t lds_k = lds_addr(&sm.k[0][0]), lds_v = lds_addr(&sm.v[0][0]);
@@ -283,7 +284,7 @@ __global__ __launch_bounds__(NH * 128, 2) void bwd_dq_kernel(DmaBwdArgs a) {
             // list padding (positions past cnt) and rows outside [j, e) get weight 0
             const bool kept = (c * kBk + kb + r < cnt) &
                               ((uint32_t)(pos - jv[r]) < (uint32_t)(ev[r] - jv[r]));
-            const float v = fmaf(s[i], scale2, (dv[r] - dmax) * kLog2e) - lq;
+            const float v = fmaf(s[i], scale2, (dv[r] - lse_q) * kLog2e);
             const float p = __builtin_amdgcn_exp2f(kept ? v : -INFINITY);
             ds[4 * h4 + r] = p * (dp[i] - dv_q);
           }

@@ -69,6 +69,10 @@ constexpr int kXcds = 8;        // accelerator complex dies, each with its own L
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.f;  // base-2 headroom before O is rescaled (weights stay <= 2^8)
+// largest gap between the tile's largest delta and a wave's first row's own
+// largest delta that the shared tile offset serves (scores up to kRefSpan /
+// scale ~ 724 in magnitude keep ~2^-14 absolute precision)
+constexpr float kRefSpan = 64.f;
 
 using dma::dma_b128;
 using dma::dma_b32;
@@ -89,6 +93,7 @@ struct Smem {
   int pj[kFin][kBk];               // key index for the mask (INT_MAX for padding)
   int e[kFin][kBk];                // eviction row (0 for padding)
   float bias[kFin][kBk];           // (delta - dmax) * log2(e) / score scale, -inf for padding
+  float dval[kFin][kBk];           // delta itself, -inf for padding (row-reference waves)
 };
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -217,24 +222,41 @@ template <int NDMA, typename F>
 __device__ __forceinline__ void g_phase(Acc& acc, const dma::bf16x8 (&pb)[2][2],
                                         dma::f32x16 (&s)[2], const dma::bf16x8 (&qf)[8],
                                         const unsigned char* kt, const unsigned char* vt,
-                                        const float* bias_row, int lane, F&& dma_issue) {
+                                        const float* bias_row, const float* dval_row,
+                                        bool rowref, float rref, float bias_div, int lane,
+                                        F&& dma_issue) {
   const int l32 = lane & 31, hi = lane >> 5;
   // the wave in its MFMA phase issues first on its SIMD, ahead of the
   // softmax wave sharing it (measured: slightly faster; the reverse, slower)
   __builtin_amdgcn_s_setprio(1);
   // the scores start from the keys' bias divided by the score scale, so the
   // MFMAs add q.k to it (register i of block mb holds key mb*32 + 8*(i/4) +
-  // 4*hi + i%4; bias_row points at key 4*hi of the chunk)
+  // 4*hi + i%4; the rows point at key 4*hi of the chunk).  Waves whose rows
+  // take their own reference (rowref) form the bias from delta and the
+  // lane's row reference: all 32 values of a lane belong to one query row.
+  if (rowref) {
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const float4 bv = *reinterpret_cast<const float4*>(bias_row + mb * 32 + 8 * q4);
-      s[mb][4 * q4 + 0] = bv.x;
-      s[mb][4 * q4 + 1] = bv.y;
-      s[mb][4 * q4 + 2] = bv.z;
-      s[mb][4 * q4 + 3] = bv.w;
-    }
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 dv = *reinterpret_cast<const float4*>(dval_row + mb * 32 + 8 * q4);
+        s[mb][4 * q4 + 0] = (dv.x - rref) * bias_div;
+        s[mb][4 * q4 + 1] = (dv.y - rref) * bias_div;
+        s[mb][4 * q4 + 2] = (dv.z - rref) * bias_div;
+        s[mb][4 * q4 + 3] = (dv.w - rref) * bias_div;
+      }
+  } else {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 bv = *reinterpret_cast<const float4*>(bias_row + mb * 32 + 8 * q4);
+        s[mb][4 * q4 + 0] = bv.x;
+        s[mb][4 * q4 + 1] = bv.y;
+        s[mb][4 * q4 + 2] = bv.z;
+        s[mb][4 * q4 + 3] = bv.w;
+      }
+  }
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
     // the direct loads handed to this phase go out evenly between the score
@@ -444,6 +466,22 @@ __global__ __launch_bounds__(NH * 128, 1) void attn_prefill_bf16_kernel(DmaAttnA
   // Q^T operand: lane holds query n = half*32 + l32, d = kk*16 + 8*hi + [0, 8)
   const int n = half * 32 + l32;
   const int pos = p_lo + n;
+  // Row reference.  Row p keeps its best key, so its largest kept delta is
+  // the prefix maximum r(p) of delta over keys 0..p: the largest delta before
+  // the tile (from the mask step), then the running maximum over the tile's
+  // own keys p_lo..p.  A wave whose first row's r lies far below the tile's
+  // dmax (a key with a much larger delta is born later in the tile) offsets
+  // its scores by each row's own r instead of dmax, so the scores it carries
+  // stay small and keep their precision.
+  float rref = (lane < rows) ? dl[p_lo + lane] : -INFINITY;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float y = __shfl_up(rref, o);
+    if (lane >= o) rref = fmaxf(rref, y);
+  }
+  rref = fmaxf(a.u_dlo[g], __shfl(rref, n));
+  const float rfirst = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(rref)));
+  const bool rowref = rfirst > -INFINITY && dmax - rfirst > kRefSpan;
   dma::bf16x8 qf[8];
   {
     const uint16_t* qrow = static_cast<const uint16_t*>(a.Q) + b * a.qsb + hq * a.qsh +
@@ -476,6 +514,7 @@ __global__ __launch_bounds__(NH * 128, 1) void attn_prefill_bf16_kernel(DmaAttnA
     sm.pj[sf_][lane] = pad_ ? 0x7fffffff : jj_;                                 \
     sm.e[sf_][lane] = pad_ ? 0 : sm.eraw[sr_][lane];                            \
     sm.bias[sf_][lane] = pad_ ? -INFINITY : (sm.draw[sr_][lane] - dmax) * bias_div; \
+    sm.dval[sf_][lane] = pad_ ? -INFINITY : sm.draw[sr_][lane];                 \
   } while (0)
 
   // prologue: list entries of chunks 0..4, then delta of chunks 0..2
@@ -548,7 +587,8 @@ __global__ __launch_bounds__(NH * 128, 1) void attn_prefill_bf16_kernel(DmaAttnA
     int jd = 0;                                                                         \
     if (wave == 0) jd = sm.jraw[(c + 3) % kRaw][lane];                                  \
     const uint32_t kt_ = lds_k + b2_ * kTileB, vt_ = lds_v + b1_ * kTileB;              \
-    g_phase<NG>(acc, pb, s, qf, KC, VP, &sm.bias[c % kFin][4 * hi], lane, [&](int i_) { \
+    g_phase<NG>(acc, pb, s, qf, KC, VP, &sm.bias[c % kFin][4 * hi],                     \
+                &sm.dval[c % kFin][4 * hi], rowref, rref, bias_div, lane, [&](int i_) {   \
       gather_piece<NW>(i_, kt_, vt_, kr, vr, Kg, Vg, rowb, wave, lane);                 \
     });                                                                                 \
     if (wave == 0) {                                                                    \
@@ -569,7 +609,8 @@ __global__ __launch_bounds__(NH * 128, 1) void attn_prefill_bf16_kernel(DmaAttnA
 #define DMA_STEP_B(MASKED)                                                              \
   do {                                                                                  \
     DMA_TILES(c);                                                                       \
-    g_phase<0>(acc, pb, s, qf, KC, VP, &sm.bias[c % kFin][4 * hi], lane, [](int) {});    \
+    g_phase<0>(acc, pb, s, qf, KC, VP, &sm.bias[c % kFin][4 * hi],                      \
+               &sm.dval[c % kFin][4 * hi], rowref, rref, bias_div, lane, [](int) {});       \
     gather_rows<NW>(kr, sm, c + 3, wave, lane);                                         \
     gather_rows<NW>(vr, sm, c + 2, wave, lane);                                         \
     phase_barrier<NG>();                                                                \
@@ -655,7 +696,8 @@ __global__ __launch_bounds__(NH * 128, 1) void attn_prefill_bf16_kernel(DmaAttnA
         }
       }
     if (a.lse && hi == 0)
-      a.lse[((int64_t)b * a.Hq + hq) * a.Sq + r_lo + n] = (acc.m + __log2f(lt)) * kLn2 + dmax;
+      a.lse[((int64_t)b * a.Hq + hq) * a.Sq + r_lo + n] =
+          (acc.m + __log2f(lt)) * kLn2 + (rowref ? rref : dmax);
   }
 }
 

@@ -88,6 +88,7 @@ struct DmaTopkArgs {
   int32_t* kt_idx;
   int32_t* kt_cnt;
   void* ws;
+  float* u_dlo = nullptr;  // prefill: largest delta before each tile's first row, or null
 };
 hipError_t dma_launch_topk_prefill(const DmaTopkArgs& a, hipStream_t st);
 hipError_t dma_launch_topk_decode(const DmaTopkArgs& a, hipStream_t st);
@@ -110,6 +111,7 @@ struct DmaAttnArgs {
   const int32_t* u_cnt;
   const int32_t* u_nfull;
   const float* u_dmax;
+  const float* u_dlo = nullptr;  // bf16 prefill: largest delta before each tile's first row
   int64_t n_tiles, u_stride;
   float scale;
   void* O;

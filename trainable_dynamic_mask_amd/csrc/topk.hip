@@ -442,12 +442,12 @@ constexpr int kSuperTiles = 8;
 __global__ __launch_bounds__(kListWaves * 64) void cand_kernel(
     const float* __restrict__ delta, const int32_t* __restrict__ evict, int Sk, int Sq, int q0,
     int n_super, int n_tiles, int cap, int32_t* __restrict__ cj, int32_t* __restrict__ ce,
-    int32_t* __restrict__ ccnt, float* __restrict__ u_dmax) {
+    int32_t* __restrict__ ccnt, float* __restrict__ u_dmax, float* __restrict__ u_dlo) {
   __shared__ int s_c[kListWaves];
   // order codes of the largest delta per bucket: bucket i holds the keys of
-  // tile t0+i's own rows, bucket 0 also every key before the group
-  __shared__ uint32_t s_b[kSuperTiles];
-  if (threadIdx.x < kSuperTiles) s_b[threadIdx.x] = 0u;  // 0: below every code
+  // tile t0+i's own rows, bucket kSuperTiles every key before the group
+  __shared__ uint32_t s_b[kSuperTiles + 1];
+  if (threadIdx.x <= kSuperTiles) s_b[threadIdx.x] = 0u;  // 0: below every code
   const int seg = blockIdx.y, T = blockIdx.x;
   const int64_t g = (int64_t)seg * n_super + T;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -517,16 +517,23 @@ __global__ __launch_bounds__(kListWaves * 64) void cand_kernel(
   if (threadIdx.x == 0) ccnt[g] = min(tc, cap);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) m0 = max(m0, (uint32_t)__shfl_xor((int)m0, o));
-  if (lane == 0) atomicMax(&s_b[0], m0);
+  if (lane == 0) atomicMax(&s_b[kSuperTiles], m0);
   __syncthreads();
-  // tile t0+i: the largest delta over keys 0..p_hi, i.e. over buckets 0..i
+  // tile t0+i: the largest delta over keys 0..p_hi (the keys before the
+  // group and buckets 0..i), and over the keys before its first row (before
+  // the group and buckets 0..i-1; minus infinity when there are none: code 0)
   const int t0 = T * kSuperTiles;
   const int i = threadIdx.x;
   if (i < min(kSuperTiles, n_tiles - t0)) {
-    uint32_t m = 0u;
-    for (int k = 0; k <= i; ++k) m = max(m, s_b[k]);
-    const uint32_t bits = (m & 0x80000000u) ? (m & 0x7fffffffu) : ~m;  // inverse of ord32
-    u_dmax[(int64_t)seg * n_tiles + t0 + i] = __uint_as_float(bits);
+    uint32_t mlo = s_b[kSuperTiles];
+    for (int k = 0; k < i; ++k) mlo = max(mlo, s_b[k]);
+    const uint32_t m = max(mlo, s_b[i]);
+    auto value = [](uint32_t c) {  // inverse of ord32
+      return c == 0u ? -INFINITY
+                     : __uint_as_float((c & 0x80000000u) ? (c & 0x7fffffffu) : ~c);
+    };
+    u_dmax[(int64_t)seg * n_tiles + t0 + i] = value(m);
+    if (u_dlo) u_dlo[(int64_t)seg * n_tiles + t0 + i] = value(mlo);
   }
 }
 
@@ -1055,7 +1062,7 @@ hipError_t dma_launch_topk_prefill(const DmaTopkArgs& a, hipStream_t st) {
                      (int)a.w, R, chk, n_chk, nwr, ckpt, a.evict);
   hipLaunchKernelGGL(cand_kernel, dim3(n_super, BH), dim3(kListWaves * 64), 0, st, a.delta,
                      a.evict, Sk, (int)a.Sq, (int)a.q0, n_super, (int)a.n_tiles, cap, cj, ce, ccnt,
-                     a.u_dmax);
+                     a.u_dmax, a.u_dlo);
   const size_t kt_lds =
       a.kt_idx ? (size_t)kSuperTiles * ((a.kt_stride + 31) / 32) * sizeof(uint32_t) : 0;
   if (kt_lds > (size_t)kSuperTiles * kMaxKtWords * sizeof(uint32_t)) return hipErrorInvalidValue;
@@ -1082,7 +1089,7 @@ hipError_t dma_launch_cand(const float* delta, const int32_t* evict, int64_t BH,
   const int n_tiles = (int)((Sq + kListRows - 1) / kListRows);
   hipLaunchKernelGGL(cand_kernel, dim3(n_super, (unsigned)BH), dim3(kListWaves * 64), 0, st,
                      delta, evict, (int)Sk, (int)Sq, (int)q0, n_super, n_tiles, cap, cj, ce, ccnt,
-                     tile_dmax);
+                     tile_dmax, (float*)nullptr);
   return hipGetLastError();
 }
 
