@@ -218,13 +218,12 @@ __device__ __forceinline__ void v_operands(dma::bf16x8 (&vop)[4], const unsigned
 // V one PV k-step ahead, so the matrix cores do not wait on single LDS
 // reads.  The sched_group_barrier sequence pins that order (0x100 = LDS
 // read, 0x008 = MFMA) and bounds the registers held by operands in flight.
-template <int NDMA, typename F>
+template <int NDMA, bool ROWREF, typename F>
 __device__ __forceinline__ void g_phase(Acc& acc, const dma::bf16x8 (&pb)[2][2],
                                         dma::f32x16 (&s)[2], const dma::bf16x8 (&qf)[8],
                                         const unsigned char* kt, const unsigned char* vt,
                                         const float* bias_row, const float* dval_row,
-                                        bool rowref, float rref, float bias_div, int lane,
-                                        F&& dma_issue) {
+                                        float rref, float bias_div, int lane, F&& dma_issue) {
   const int l32 = lane & 31, hi = lane >> 5;
   // the wave in its MFMA phase issues first on its SIMD, ahead of the
   // softmax wave sharing it (measured: slightly faster; the reverse, slower)
@@ -232,9 +231,9 @@ __device__ __forceinline__ void g_phase(Acc& acc, const dma::bf16x8 (&pb)[2][2],
   // the scores start from the keys' bias divided by the score scale, so the
   // MFMAs add q.k to it (register i of block mb holds key mb*32 + 8*(i/4) +
   // 4*hi + i%4; the rows point at key 4*hi of the chunk).  Waves whose rows
-  // take their own reference (rowref) form the bias from delta and the
+  // take their own reference (ROWREF) form the bias from delta and the
   // lane's row reference: all 32 values of a lane belong to one query row.
-  if (rowref) {
+  if constexpr (ROWREF) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -581,14 +580,14 @@ __global__ __launch_bounds__(NH * 128, 1) void attn_prefill_bf16_kernel(DmaAttnA
   const int b1_ = b0_ == 2 ? 0 : b0_ + 1; /* (c+1) % 3 */              \
   const unsigned char* KC = sm.k[b0_];                                \
   const unsigned char* VP = sm.v[b2_]
-#define DMA_STEP_A(MASKED)                                                              \
+#define DMA_STEP_A(MASKED, RR)                                                          \
   do {                                                                                  \
     DMA_TILES(c);                                                                       \
     int jd = 0;                                                                         \
     if (wave == 0) jd = sm.jraw[(c + 3) % kRaw][lane];                                  \
     const uint32_t kt_ = lds_k + b2_ * kTileB, vt_ = lds_v + b1_ * kTileB;              \
-    g_phase<NG>(acc, pb, s, qf, KC, VP, &sm.bias[c % kFin][4 * hi],                     \
-                &sm.dval[c % kFin][4 * hi], rowref, rref, bias_div, lane, [&](int i_) {   \
+    g_phase<NG, RR>(acc, pb, s, qf, KC, VP, &sm.bias[c % kFin][4 * hi],                 \
+                    &sm.dval[c % kFin][4 * hi], rref, bias_div, lane, [&](int i_) {       \
       gather_piece<NW>(i_, kt_, vt_, kr, vr, Kg, Vg, rowb, wave, lane);                 \
     });                                                                                 \
     if (wave == 0) {                                                                    \
@@ -606,11 +605,11 @@ __global__ __launch_bounds__(NH * 128, 1) void attn_prefill_bf16_kernel(DmaAttnA
     else                                                                                \
       phase_barrier<NG>();                                                              \
   } while (0)
-#define DMA_STEP_B(MASKED)                                                              \
+#define DMA_STEP_B(MASKED, RR)                                                          \
   do {                                                                                  \
     DMA_TILES(c);                                                                       \
-    g_phase<0>(acc, pb, s, qf, KC, VP, &sm.bias[c % kFin][4 * hi],                      \
-               &sm.dval[c % kFin][4 * hi], rowref, rref, bias_div, lane, [](int) {});       \
+    g_phase<0, RR>(acc, pb, s, qf, KC, VP, &sm.bias[c % kFin][4 * hi],                  \
+                   &sm.dval[c % kFin][4 * hi], rref, bias_div, lane, [](int) {});           \
     gather_rows<NW>(kr, sm, c + 3, wave, lane);                                         \
     gather_rows<NW>(vr, sm, c + 2, wave, lane);                                         \
     phase_barrier<NG>();                                                                \
@@ -640,8 +639,13 @@ __global__ __launch_bounds__(NH * 128, 1) void attn_prefill_bf16_kernel(DmaAttnA
     gather_rows<NW>(kr, sm, 2, wave, lane);
     gather_rows<NW>(vr, sm, 1, wave, lane);
     int c = 0;
-    for (; c < nplain; ++c) DMA_STEP_A(false);
-    for (; c <= nch; ++c) DMA_STEP_A(true);
+    if (rowref) {  // a separate copy of the loops keeps the common one unchanged
+      for (; c < nplain; ++c) DMA_STEP_A(false, true);
+      for (; c <= nch; ++c) DMA_STEP_A(true, true);
+    } else {
+      for (; c < nplain; ++c) DMA_STEP_A(false, false);
+      for (; c <= nch; ++c) DMA_STEP_A(true, false);
+    }
     // one more barrier so both groups meet equally often
     phase_barrier<-1>();
   } else {
@@ -657,8 +661,13 @@ __global__ __launch_bounds__(NH * 128, 1) void attn_prefill_bf16_kernel(DmaAttnA
     gather_tile<NW, true>(lds_v + 1 * kTileB, vr, Vg, rowb, wave, lane);
     phase_barrier<-1>();
     int c = 0;
-    for (; c < nplain; ++c) DMA_STEP_B(false);
-    for (; c <= nch; ++c) DMA_STEP_B(true);
+    if (rowref) {
+      for (; c < nplain; ++c) DMA_STEP_B(false, true);
+      for (; c <= nch; ++c) DMA_STEP_B(true, true);
+    } else {
+      for (; c < nplain; ++c) DMA_STEP_B(false, false);
+      for (; c <= nch; ++c) DMA_STEP_B(true, false);
+    }
   }
   // no direct load may still be writing LDS when the workgroup ends
   __builtin_amdgcn_s_waitcnt(7 << 4);
