@@ -40,8 +40,11 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=100,
-                    help="untimed forwards first: the shader clock needs ~0.1 s of load to reach its sustained level")
+    ap.add_argument("--warmup", type=int, default=10, help="untimed steps before the timed ones")
+    ap.add_argument("--clock-ramp-ms", type=float, default=300.0,
+                    help="run untimed steps for this long before the warm-up: the shader clock "
+                         "takes ~0.1-0.3 s of load to reach its sustained level, so without it "
+                         "a short run times the kernels at a lower clock")
     ap.add_argument("--workload", default="prefill_16k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -85,6 +88,18 @@ def measured_traffic(workload):
         return float(kv["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def clock_ramp(step, ms):
+    """Untimed steps for `ms` milliseconds of wall time (the GPU busy throughout):
+    the shader clock ramps up under load, and the timed steps should see the
+    clock a sustained workload runs at."""
+    import torch
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(4):
+            step()
+        torch.cuda.synchronize()
 
 
 def copy_calibration(mib):
@@ -175,6 +190,7 @@ def backward_bench(args, wl, x, dev):
             e[2].record()
         return dQ
 
+    clock_ramp(step, args.clock_ramp_ms)
     for _ in range(max(3, args.warmup // 10)):
         step()
     torch.cuda.synchronize()
@@ -231,10 +247,13 @@ def hbm_stages(args, wl, x, dev):
     def run_a():
         dma.attn_fwd(x["Q"], x["K"], x["V"], delta, mask, out=O, workspace=ws_a)
 
-    for _ in range(max(args.warmup, 1)):  # clock ramp; also leaves delta and the mask set
+    def all_stages():
         run_w()
         run_t()
         run_a()
+
+    clock_ramp(all_stages, args.clock_ramp_ms)  # also leaves delta and the mask set
+    all_stages()
     torch.cuda.synchronize()
     n_keys = wl.B * wl.Hkv * wl.Sk
     w_bytes = n_keys * wl.D * es + n_keys * 4  # V is [B, Sk, Hkv, D]
@@ -327,6 +346,7 @@ def main():
         if e:
             e[3].record()
 
+    clock_ramp(step, args.clock_ramp_ms)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -336,11 +356,11 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
-    st = {"weights": 0.0, "mask": 0.0, "attention": 0.0}
-    for e in ev:
-        st["weights"] += e[0].elapsed_time(e[1]) / args.steps
-        st["mask"] += e[1].elapsed_time(e[2]) / args.steps
-        st["attention"] += e[2].elapsed_time(e[3]) / args.steps
+    import statistics
+    per = {"weights": [e[0].elapsed_time(e[1]) for e in ev],
+           "mask": [e[1].elapsed_time(e[2]) for e in ev],
+           "attention": [e[2].elapsed_time(e[3]) for e in ev]}
+    st = {k: sum(v) / len(v) for k, v in per.items()}
     assert torch.isfinite(O.float()).all(), "non-finite output"
 
     flops = wl.effective_flops()
@@ -353,6 +373,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "clock_ramp_ms": args.clock_ramp_ms,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -367,6 +388,8 @@ def main():
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(wl.name)},
         "stages_ms": {k: round(v, 4) for k, v in st.items()},
+        "stages_ms_median": {k: round(statistics.median(v), 4) for k, v in per.items()},
+        "stages_ms_min": {k: round(min(v), 4) for k, v in per.items()},
     }
     if decode:
         # one query row per sequence: the attention is bound by the HBM gather of the

@@ -205,3 +205,13 @@ def test_fwd_train_and_weights_bwd_validation(lib):
     assert wb(Hkv=32) == UNSUPPORTED                          # Hkv*D above 2048
     assert wb(ws_bytes=4) == WORKSPACE
     assert lib.dma_weights_bwd_workspace_bytes(2, 10, 3) == 2 * 10 * 3 * 4
+
+
+def test_safe_sync_build_loads_with_the_same_exports():
+    # the cross-check build (every attention barrier waits for all loads) is the
+    # same library: it loads and exports every declared function
+    safe = _lib.load_safe()
+    for n in declared_functions():
+        assert hasattr(safe, n), n
+    assert safe.dma_abi_version() == _lib.load().dma_abi_version()
+

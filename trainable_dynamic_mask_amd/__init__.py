@@ -193,8 +193,10 @@ def decode_keep_append(delta: torch.Tensor, mask: Mask) -> Mask:
 
 def attn_fwd(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, delta: torch.Tensor, mask: Mask,
              scale: Optional[float] = None, return_lse: bool = False,
-             out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
-    """Masked attention; Q [B,Sq,Hq,D], K/V [B,Sk,Hkv,D] (any b/s/h strides)."""
+             out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+             lib=None):
+    """Masked attention; Q [B,Sq,Hq,D], K/V [B,Sk,Hkv,D] (any b/s/h strides).
+    lib: the loaded library to call (default load(); the tests pass load_safe())."""
     _check_qkv(Q, K, V)
     B, Sq, Hq, D = Q.shape
     _, Sk, Hkv, _ = K.shape
@@ -202,7 +204,7 @@ def attn_fwd(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, delta: torch.Ten
     _check_mask(mask, B, Hkv, Sq, Sk)
     _need_cuda(Q, K, V, delta)
     delta_c = delta.contiguous()  # bound to a name: it must outlive the enqueued kernels
-    lib = load()
+    lib = lib or load()
     if out is None:
         out = torch.empty(B, Sq, Hq, D, dtype=Q.dtype, device=Q.device)
     lse = torch.empty(B, Hq, Sq, dtype=torch.float32, device=Q.device) if return_lse else None

@@ -9,6 +9,7 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdma_hip.so")
+LIB_SAFE_PATH = os.path.join(HERE, "libdma_hip_safe.so")
 
 DMA_F32 = 0
 DMA_BF16 = 1
@@ -38,6 +39,7 @@ EXPORTS = ["dma_status_string", "dma_abi_version", "dma_tile_sizes", "dma_mask_d
            "dma_weights_bwd_workspace_bytes", "dma_weights_bwd"]
 
 _lib = None
+_lib_safe = None
 
 
 class DmaError(RuntimeError):
@@ -49,12 +51,26 @@ class DmaError(RuntimeError):
 def load():
     """Load the library (once) and declare the C signatures."""
     global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with "
+    if _lib is None:
+        _lib = _open(LIB_PATH)
+    return _lib
+
+
+def load_safe():
+    """The cross-check build of the same library (every barrier of the
+    hand-synchronised attention waits for all loads in flight); the tests
+    compare its results bit for bit with load()'s."""
+    global _lib_safe
+    if _lib_safe is None:
+        _lib_safe = _open(LIB_SAFE_PATH)
+    return _lib_safe
+
+
+def _open(path):
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
                           "`python -m trainable_dynamic_mask_amd.build`")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     lib.dma_status_string.argtypes = [ctypes.c_int]
     lib.dma_status_string.restype = ctypes.c_char_p
     lib.dma_abi_version.restype = ctypes.c_int
@@ -96,7 +112,6 @@ def load():
     lib.dma_weights_bwd.argtypes = [_P, ctypes.c_int, _I64, _I64, _I64, _I64, _I64, _I64, _P, _P,
                                     _P, _P, _P, _P, _P, _SZ, _P]
     lib.dma_weights_bwd.restype = ctypes.c_int
-    _lib = lib
     return lib
 
 

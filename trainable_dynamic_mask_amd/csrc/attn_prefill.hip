@@ -160,14 +160,20 @@ __device__ __forceinline__ void gather_rows(int (&idx)[16 / NW], const Smem& sm,
 // it.  The empty asm statements keep the compiler from moving memory
 // accesses across the barrier; no fence is used, as a fence would wait for
 // every load in flight.
+// Built with DMA_SAFE_SYNC (the cross-check library), every barrier waits
+// for all of the wave's loads instead: the results must be bit-identical.
 template <int VM>
 __device__ __forceinline__ void phase_barrier() {
   static_assert(VM < 64, "vmcnt holds 6 bits");
   asm volatile("" ::: "memory");
+#ifdef DMA_SAFE_SYNC
+  __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) expcnt(0) lgkmcnt(0)
+#else
   if constexpr (VM >= 0)
     __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4));  // vmcnt(VM) lgkmcnt(0)
   else
     __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // lgkmcnt(0) only
+#endif
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }

@@ -36,12 +36,10 @@
 namespace {
 
 constexpr int kSortChunk = 4096;
-#ifndef DMA_SORT_PER
-#define DMA_SORT_PER 4
-#endif
-constexpr int kSortPer = DMA_SORT_PER;  // keys per thread: element i = thread * kSortPer + register
+constexpr int kSortPer = 4;  // keys per thread: element i = thread * kSortPer + register
 constexpr int kSortThreads = kSortChunk / kSortPer;
-constexpr int kSortRegBits = kSortPer == 8 ? 3 : kSortPer == 4 ? 2 : 4;
+constexpr int kSortRegBits = 2;  // log2(kSortPer)
+static_assert((1 << kSortRegBits) == kSortPer, "register bits");
 constexpr int kMergeItems = 8;
 constexpr int kListRows = 64;   // query rows per tile (Bq)
 
@@ -56,9 +54,9 @@ __device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
 // all point one way: phase k (block size 2, 4, ..., 4096) first pairs i with
 // its mirror i ^ (k-1) in the block, then with i ^ j for j = k/4, ..., 1, and
 // the lower index of every pair keeps the larger key.  Element i lives in
-// register i%8 of thread i/8, so pairs at distance < 8 stay inside a thread,
-// pairs that differ in bits 3..8 pair lanes of one wave, and only pairs that
-// differ in bits 9..11 cross waves, through LDS (two buffers, one barrier
+// register i%4 of thread i/4, so pairs at distance < 4 stay inside a thread,
+// pairs that differ in bits 2..7 pair lanes of one wave, and only pairs that
+// differ in bits 8..11 cross waves, through LDS (two buffers, one barrier
 // each).  Every element is updated by its owner, which takes the larger or the
 // smaller of itself and its partner.
 __global__ __launch_bounds__(kSortThreads) void sort_chunk_kernel(const float* __restrict__ delta,
@@ -314,8 +312,8 @@ __global__ __launch_bounds__(256) void evict_kernel(const uint64_t* __restrict__
                                                     int w, int R, int chk, int n_chk, int nwr,
                                                     const uint32_t* __restrict__ ckpt,
                                                     int32_t* __restrict__ evict) {
-  // Dynamic LDS only, so the bitmap starts at byte 0 (8-byte aligned for the
-  // 64-bit word reads): bitmap of indices in whole 64-bit words, then s_w, s_f.
+  // Dynamic LDS only: bitmap of indices in whole 64-bit words (read as 32-bit
+  // halves, below), then s_w, s_f.
   extern __shared__ __align__(16) uint32_t bm[];
   int* s_w = reinterpret_cast<int*>(bm + nwr);
   int& s_f = s_w[4];
@@ -372,12 +370,18 @@ __global__ __launch_bounds__(256) void evict_kernel(const uint64_t* __restrict__
   // when f gets there; f only ever moves down.  Per 64 keys, a ballot of
   // x < f picks the keys that can move f (f only decreases, so no other key
   // can); they are visited in order and the others keep e = x.
-  uint64_t* bm64 = reinterpret_cast<uint64_t*>(bm);
+  // 64-bit bitmap words are read as two 32-bit halves, so nothing depends on
+  // where dynamic LDS starts (an 8-byte access needs 8-byte alignment, and a
+  // 64-bit LDS atomic at an address 4 mod 8 faults the GPU); the only LDS
+  // atomics on the bitmap are 32-bit
+  auto bm64 = [&](int wi) -> uint64_t {
+    return ((uint64_t)bm[2 * wi + 1] << 32) | bm[2 * wi];
+  };
   int f = s_f;
   if (f < 0) return;  // unreachable (see above)
   int cwi = f >> 6;
-  uint64_t cw = bm64[cwi];
-  uint64_t pw = cwi > 0 ? bm64[cwi - 1] : 0ull;
+  uint64_t cw = bm64(cwi);
+  uint64_t pw = cwi > 0 ? bm64(cwi - 1) : 0ull;
   for (int g0 = rs; g0 < r1; g0 += 64) {
     const int steps = min(64, r1 - g0);
     const int xl = lane < steps ? (int)dma::index_of(K[g0 + lane]) : INT_MAX;  // one key per lane
@@ -406,10 +410,10 @@ __global__ __launch_bounds__(256) void evict_kernel(const uint64_t* __restrict__
           m = cw;
           while (m == 0ull && cwi > 0) {
             --cwi;
-            cw = bm64[cwi];
+            cw = bm64(cwi);
             m = cw;
           }
-          pw = cwi > 0 ? bm64[cwi - 1] : 0ull;
+          pw = cwi > 0 ? bm64(cwi - 1) : 0ull;
         }
         f = m ? (cwi << 6) + 63 - __builtin_clzll(m) : -1;  // -1: unreachable (w bits below f)
       }
@@ -800,8 +804,11 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_select_kernel(
   __shared__ int s_w[kDecWaves];
   __shared__ int s_cnt[2 * kDecWaves];
   __shared__ float s_m[kDecWaves];
+  // read and written as 64-bit words: static arrays of 8-byte alignment
   __shared__ __align__(8) uint32_t s_gt[kDecThreads * kDecKPT / 32];  // code > T (or all, n <= w)
   __shared__ __align__(8) uint32_t s_eq[kDecThreads * kDecKPT / 32];  // code == T
+  static_assert(__alignof__(s_gt) >= 8 && __alignof__(s_eq) >= 8,
+                "64-bit LDS words need 8-byte alignment");
   __shared__ uint32_t s_cand[kDecCand];
   const int seg = blockIdx.x;
   const int n = p + 1;
