@@ -156,6 +156,22 @@ dma_status dma_topk_mask(const float* delta, int64_t B, int64_t Hkv, int64_t Sq,
                          size_t ws_bytes, void* stream);
 
 /*
+ * dma_topk_mask for callers that cannot allocate device memory (code under
+ * graph capture, serving loops that forbid allocation): the same call and
+ * results, without the ws arguments.  The workspace is a static device
+ * array of DMA_TOPK_SCRATCH_BYTES that the library holds on each GPU it runs
+ * on until the process ends; this call allocates nothing.  Calls whose
+ * dma_topk_workspace_bytes(...) exceeds it return DMA_ERR_WORKSPACE (the
+ * 16K-token prefill needs ~8 MiB, the 64K one ~50 MiB).  Every call on a GPU
+ * shares that GPU's array, so calls that overlap in time on one GPU (other
+ * streams, other threads) race; calls on one stream run in order.
+ */
+#define DMA_TOPK_SCRATCH_BYTES ((size_t)64 << 20)
+dma_status dma_topk_mask_noalloc(const float* delta, int64_t B, int64_t Hkv, int64_t Sq,
+                                 int64_t Sk, int64_t q_offset, int64_t w, const dma_mask* out,
+                                 void* stream);
+
+/*
  * Step 2, one decode step (DMA blog, m_t equation; the keep set of position
  * p is the top w of keys 0..p).  Keep sets nest, so keep(p) is the top w of
  * keep(p-1) plus key p: key p enters exactly when it beats the worst kept key

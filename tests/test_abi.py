@@ -215,3 +215,12 @@ def test_safe_sync_build_loads_with_the_same_exports():
         assert hasattr(safe, n), n
     assert safe.dma_abi_version() == _lib.load().dma_abi_version()
 
+
+def test_noalloc_mask_rejects_more_than_its_scratch(lib):
+    # the static scratch holds 64 MiB; a call that needs more is refused on the
+    # host before anything is enqueued
+    m = DmaMask(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE)
+    assert lib.dma_topk_workspace_bytes(1, 16, 65536, 65536, 4096) > (64 << 20)
+    assert lib.dma_topk_mask_noalloc(FAKE, 1, 16, 65536, 65536, 0, 4096, ctypes.byref(m),
+                                     None) == WORKSPACE
+    assert lib.dma_topk_mask_noalloc(FAKE, 1, 8, 16, 16, 0, 0, ctypes.byref(m), None) == INVALID

@@ -153,8 +153,11 @@ def weights(V: torch.Tensor, Delta: torch.Tensor, A: torch.Tensor,
 
 
 def topk_mask(delta: torch.Tensor, Sq: int, q_offset: int, w: int, kt_lists: bool = True,
-              mask: Optional[Mask] = None, workspace: Optional[torch.Tensor] = None) -> Mask:
-    """Causal top-w keep mask of query positions q_offset..q_offset+Sq-1."""
+              mask: Optional[Mask] = None, workspace: Optional[torch.Tensor] = None,
+              noalloc: bool = False) -> Mask:
+    """Causal top-w keep mask of query positions q_offset..q_offset+Sq-1.
+    noalloc: use the library's static scratch (dma_topk_mask_noalloc) instead
+    of a workspace; `mask` must then be given for the call to allocate nothing."""
     _need_cuda(delta)
     delta = delta.contiguous()
     B, Hkv, Sk = delta.shape
@@ -162,6 +165,11 @@ def topk_mask(delta: torch.Tensor, Sq: int, q_offset: int, w: int, kt_lists: boo
     lib = load()
     if mask is None:
         mask = alloc_mask(B, Hkv, Sq, Sk, q_offset, w, delta.device, kt_lists)
+    if noalloc:
+        ms = mask.cstruct()
+        check("dma_topk_mask_noalloc", lib.dma_topk_mask_noalloc(
+            _ptr(delta), B, Hkv, Sq, Sk, q_offset, w, ctypes.byref(ms), _stream(delta.device)))
+        return mask
     nbytes = lib.dma_topk_workspace_bytes(B, Hkv, Sq, Sk, w)
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(16, nbytes), dtype=torch.uint8, device=delta.device)

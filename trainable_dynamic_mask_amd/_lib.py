@@ -34,7 +34,7 @@ class DmaMaskDims(ctypes.Structure):
 
 EXPORTS = ["dma_status_string", "dma_abi_version", "dma_tile_sizes", "dma_mask_dims_for",
            "dma_topk_workspace_bytes", "dma_attn_workspace_bytes", "dma_weights",
-           "dma_topk_mask", "dma_decode_keep_append", "dma_attn_fwd",
+           "dma_topk_mask", "dma_topk_mask_noalloc", "dma_decode_keep_append", "dma_attn_fwd",
            "dma_attn_fwd_train", "dma_attn_bwd_workspace_bytes", "dma_attn_bwd",
            "dma_weights_bwd_workspace_bytes", "dma_weights_bwd"]
 
@@ -89,6 +89,9 @@ def _open(path):
     lib.dma_topk_mask.argtypes = [_P, _I64, _I64, _I64, _I64, _I64, _I64,
                                   ctypes.POINTER(DmaMask), _P, _SZ, _P]
     lib.dma_topk_mask.restype = ctypes.c_int
+    lib.dma_topk_mask_noalloc.argtypes = [_P, _I64, _I64, _I64, _I64, _I64, _I64,
+                                          ctypes.POINTER(DmaMask), _P]
+    lib.dma_topk_mask_noalloc.restype = ctypes.c_int
     lib.dma_decode_keep_append.argtypes = [_P, _I64, _I64, _I64, _I64, ctypes.POINTER(DmaMask), _P]
     lib.dma_decode_keep_append.restype = ctypes.c_int
     lib.dma_attn_fwd.argtypes = [_P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _I64, _I64, _I64,

@@ -151,6 +151,20 @@ dma_status dma_topk_mask(const float* delta, int64_t B, int64_t Hkv, int64_t Sq,
   return hip_status(dma_launch_topk_prefill(a, s));
 }
 
+dma_status dma_topk_mask_noalloc(const float* delta, int64_t B, int64_t Hkv, int64_t Sq,
+                                 int64_t Sk, int64_t q_offset, int64_t w, const dma_mask* out,
+                                 void* stream) {
+  const dma_status st = check_mask_shape(B, Hkv, Sq, Sk, q_offset, w);
+  if (st != DMA_OK) return st;
+  const size_t need = dma_topk_workspace_bytes(B, Hkv, Sq, Sk, w);
+  if (need > DMA_TOPK_SCRATCH_BYTES) return DMA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (need > 0 && out && B > 0 && Sq > 0) {
+    if (dma_topk_scratch(&ws) != hipSuccess) return DMA_ERR_HIP;
+  }
+  return dma_topk_mask(delta, B, Hkv, Sq, Sk, q_offset, w, out, ws, need, stream);
+}
+
 dma_status dma_decode_keep_append(const float* delta, int64_t B, int64_t Hkv, int64_t Sk,
                                   int64_t w, const dma_mask* mask, void* stream) {
   if (B < 0 || Hkv < 1 || w < 1 || Sk < 0) return DMA_ERR_INVALID_ARG;

@@ -96,6 +96,8 @@ hipError_t dma_launch_decode_append(const float* delta, int64_t BH, int64_t Sk, 
                                    int32_t* u_idx, int32_t* u_cnt, int32_t* u_nfull,
                                    float* u_dmax, hipStream_t st);
 size_t dma_topk_ws_bytes(int64_t BH, int64_t Sq, int64_t Sk, int64_t w);
+// this device's copy of the static mask scratch (DMA_TOPK_SCRATCH_BYTES)
+hipError_t dma_topk_scratch(void** ptr);
 
 struct DmaAttnArgs {
   const void* Q;

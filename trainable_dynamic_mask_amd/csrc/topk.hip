@@ -32,6 +32,7 @@
 
 #include <algorithm>
 #include <climits>
+#include <mutex>
 
 namespace {
 
@@ -1010,6 +1011,32 @@ size_t dma_topk_ws_bytes(int64_t BH, int64_t Sq, int64_t Sk, int64_t w) {
   return n * 2 * sizeof(uint64_t) + (size_t)BH * rank_stride(Sk) * sizeof(int32_t) +
          ns * (size_t)cand_cap(Sk, w) * 8 + ns * sizeof(int32_t) +
          nck * (size_t)ckpt_words(Sk) * sizeof(uint32_t) + 256;
+}
+
+// Scratch for callers that cannot allocate (dma_topk_mask_noalloc): the
+// prefill mask workspace in a static device array, one per GPU, held until
+// the process ends.  Host code must not pass `scratch` itself to a kernel
+// (that names a host-side stand-in): each device's address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[DMA_TOPK_SCRATCH_BYTES];
+
+hipError_t dma_topk_scratch(void** ptr) {
+  constexpr int kMaxDev = 64;
+  static void* addr[kMaxDev] = {nullptr};
+  static std::mutex mu;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t dma_launch_topk_prefill(const DmaTopkArgs& a, hipStream_t st) {
