@@ -60,10 +60,14 @@ def test_decode_select_signed_zeros(gpu_lib, p, w):
     check_mask(gm, d)
 
 
-@pytest.mark.parametrize("S,w", [(4097, 100), (8192, 3000), (12345, 2048), (9000, 6000)])
+@pytest.mark.parametrize("S,w", [(4097, 100), (8192, 3000), (12345, 2048), (9000, 6000),
+                                 (12000, 9000), (20000, 9500), (16385, 700)])
 def test_mask_multi_chunk_sort(gpu_lib, S, w):
-    # several 4096-key sort chunks, ragged tail, merge passes; w = 6000 gives
-    # tile groups with more candidates than one staging round
+    # up to 16384 keys: 1024-key sort chunks ranked by binary searches (ties
+    # resolved by index); beyond: 4096-key chunks and merge passes (16385,
+    # 20000); w = 9000 and 9500 give tile groups with more candidates than
+    # the LDS of the one-kernel list path holds, so they take the two-kernel
+    # path
     d = _delta("ties", 1, 2, S, seed=S)
     gm = dma.topk_mask(d, S, 0, w)
     check_mask(gm, d)

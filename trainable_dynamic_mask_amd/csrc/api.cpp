@@ -5,6 +5,9 @@
 
 #include <cmath>
 #include <cstdint>
+#include <map>
+#include <mutex>
+#include <utility>
 
 #include "../../include/dma.h"
 #include "common.h"
@@ -45,6 +48,20 @@ Dims dims_of(int64_t Sq, int64_t Sk, int64_t w) {
 dma_status hip_status(hipError_t e) { return e == hipSuccess ? DMA_OK : DMA_ERR_HIP; }
 
 }  // namespace
+
+hipError_t dma_func_max_lds(const void* fn, size_t bytes) {
+  static std::mutex mu;
+  static std::map<std::pair<const void*, int>, size_t> set;  // (kernel, device) -> limit
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  size_t& cur = set[{fn, dev}];
+  if (bytes <= cur) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess) cur = bytes;
+  return e;
+}
 
 extern "C" {
 

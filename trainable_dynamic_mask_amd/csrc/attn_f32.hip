@@ -172,8 +172,7 @@ hipError_t launch(const DmaAttnArgs& a, hipStream_t st) {
   const int G = (int)(a.Hq / a.Hkv);
   dim3 grid((unsigned)a.n_tiles, (unsigned)a.Hkv, (unsigned)(a.B * (G / NH)));
   const size_t lds = sizeof(SmemF<D>);
-  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_prefill_f32_kernel<D, NH>),
-                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  (void)dma_func_max_lds(reinterpret_cast<const void*>(&attn_prefill_f32_kernel<D, NH>), lds);
   hipLaunchKernelGGL((attn_prefill_f32_kernel<D, NH>), grid, dim3(NH * 64), lds, st, a);
   return hipGetLastError();
 }

@@ -67,6 +67,11 @@ __device__ __forceinline__ int rank_below(uint64_t m) {
 
 // ---- host-side launchers (defined next to their kernels) -------------------
 // Each returns hipGetLastError() after enqueueing.
+
+// Raise the dynamic LDS limit of kernel `fn` on the current device to at
+// least `bytes`.  The runtime call is made only when the limit has to grow:
+// it costs host time that a chain of short launches shows as idle GPU time.
+hipError_t dma_func_max_lds(const void* fn, size_t bytes);
 hipError_t dma_launch_fill_zero(float* p, int64_t n, hipStream_t st);
 hipError_t dma_launch_weights_bwd(const void* V, int64_t B, int64_t Sk, int64_t Hkv, int64_t D,
                                   int64_t sb, int64_t ss, const float* Delta, const float* A,

@@ -9,14 +9,15 @@
 // index among the keys that beat j (Sk when fewer than w beat it).  The mask
 // is built from that form in four steps per (batch, kv head) sequence:
 //   T1  sort the keys by the 64-bit composite (delta order, reversed index):
-//       bitonic sort of 4096-key chunks (registers, lane shuffles and LDS),
-//       then merge-path merges;
-//   T1b rank[j] = position of key j in that order; up to four chunks skip the
-//       merges: a key's rank is the sum over the chunks of the keys that beat
-//       it, found by binary searches over the chunks held in LDS;
+//       bitonic sort of chunks (registers, DPP lane exchanges and LDS), then
+//       merge-path merges;
+//   T1b rank[j] = position of key j in that order; up to sixteen 1024-key
+//       chunks skip the merges: a key's rank is the sum over the chunks of
+//       the keys that beat it, found by binary searches over the chunks held
+//       in LDS;
 //   T2  eviction rows: ranks are cut into blocks of 64; a block builds the
 //       bitmap of the indices of all better-ranked keys (a checkpoint bitmap
-//       kept every 1024 ranks plus the keys in between), selects its w-th
+//       kept every 256 or more ranks plus the keys in between), selects its w-th
 //       smallest set bit b, then walks its own ranks in order with one wave:
 //       each key gets e = max(j, b) and, when j < b, b steps down to the
 //       previous set bit;
@@ -36,36 +37,78 @@
 
 namespace {
 
-constexpr int kSortChunk = 4096;
+// Chunk sizes of the bitonic sort: small chunks (more workgroups, fewer
+// stages each) when the ranks come from binary searches over at most
+// kRankRunsMax sorted runs, large chunks when merges follow.
+constexpr int kSortChunkSmall = 1024;
+constexpr int kSortChunkLarge = 4096;
 constexpr int kSortPer = 4;  // keys per thread: element i = thread * kSortPer + register
-constexpr int kSortThreads = kSortChunk / kSortPer;
 constexpr int kSortRegBits = 2;  // log2(kSortPer)
 static_assert((1 << kSortRegBits) == kSortPer, "register bits");
 constexpr int kMergeItems = 8;
 constexpr int kListRows = 64;   // query rows per tile (Bq)
 
 // ---------------------------------------------------------------- T1: chunk sort
-__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
-  const int lo = __shfl_xor((int)(uint32_t)v, m);
-  const int hi = __shfl_xor((int)(uint32_t)(v >> 32), m);
-  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+// Value of lane (lane ^ lm) within the wave, for the lane distances the sort
+// uses, without the LDS crossbar: DPP row permutations inside 16-lane rows
+// (quad permutes for 1, 2, 3; half-row mirror for 7; row mirror for 15; row
+// rotate by 8 for 8; 4 = 7 then 3) and the gfx950 row swaps across 16 and 32
+// lanes (31 = 15 then 16, 63 = 31 then 32).
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v, int ctrl) {
+  switch (ctrl) {  // the control must be an immediate
+    case 0xB1: return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);   // quad [1,0,3,2]
+    case 0x4E: return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);   // quad [2,3,0,1]
+    case 0x1B: return __builtin_amdgcn_mov_dpp(v, 0x1B, 0xF, 0xF, false);   // quad [3,2,1,0]
+    case 0x128: return __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false); // row rotate 8
+    case 0x140: return __builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, false); // row mirror
+    default: return __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false);    // half-row mirror
+  }
 }
-
-// Bitonic sort (descending) of a 4096-key chunk, in the form whose comparators
-// all point one way: phase k (block size 2, 4, ..., 4096) first pairs i with
-// its mirror i ^ (k-1) in the block, then with i ^ j for j = k/4, ..., 1, and
-// the lower index of every pair keeps the larger key.  Element i lives in
-// register i%4 of thread i/4, so pairs at distance < 4 stay inside a thread,
-// pairs that differ in bits 2..7 pair lanes of one wave, and only pairs that
-// differ in bits 8..11 cross waves, through LDS (two buffers, one barrier
-// each).  Every element is updated by its owner, which takes the larger or the
-// smaller of itself and its partner.
-__global__ __launch_bounds__(kSortThreads) void sort_chunk_kernel(const float* __restrict__ delta,
-                                                                  int Sk,
-                                                                  uint64_t* __restrict__ out) {
-  __shared__ uint64_t s[2][kSortChunk];
+__device__ __forceinline__ uint32_t swap16_u32(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return (__lane_id() & 16) ? r[0] : r[1];
+}
+__device__ __forceinline__ uint32_t swap32_u32(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return (__lane_id() & 32) ? r[0] : r[1];
+}
+__device__ __forceinline__ uint32_t lane_xor_u32(uint32_t v, int lm) {
+  switch (lm) {
+    case 1: return dpp_u32(v, 0xB1);
+    case 2: return dpp_u32(v, 0x4E);
+    case 3: return dpp_u32(v, 0x1B);
+    case 4: return dpp_u32(dpp_u32(v, 0x141), 0x1B);
+    case 7: return dpp_u32(v, 0x141);
+    case 8: return dpp_u32(v, 0x128);
+    case 15: return dpp_u32(v, 0x140);
+    case 16: return swap16_u32(v);
+    case 31: return swap16_u32(dpp_u32(v, 0x140));
+    case 32: return swap32_u32(v);
+    default: return swap32_u32(swap16_u32(dpp_u32(v, 0x140)));  // 63
+  }
+}
+__device__ __forceinline__ uint64_t lane_xor64(uint64_t v, int lm) {
+  const uint32_t lo = lane_xor_u32((uint32_t)v, lm);
+  const uint32_t hi = lane_xor_u32((uint32_t)(v >> 32), lm);
+  return ((uint64_t)hi << 32) | lo;
+}
+// Bitonic sort (descending) of a CHUNK-key chunk, in the form whose
+// comparators all point one way: phase k (block size 2, 4, ..., CHUNK) first
+// pairs i with its mirror i ^ (k-1) in the block, then with i ^ j for
+// j = k/4, ..., 1, and the lower index of every pair keeps the larger key.
+// Element i lives in register i%4 of thread i/4, so pairs at distance < 4 stay
+// inside a thread, pairs that differ in bits 2..7 pair lanes of one wave
+// (lane_xor64), and only pairs that differ in bits 8 and up cross waves,
+// through LDS (two buffers, one barrier each).  Every element is updated by
+// its owner, which takes the larger or the smaller of itself and its partner.
+template <int CHUNK>
+__global__ __launch_bounds__(CHUNK / kSortPer) void sort_chunk_kernel(
+    const float* __restrict__ delta, int Sk, uint64_t* __restrict__ out) {
+  constexpr int kBits = __builtin_ctz(CHUNK);
+  static_assert((1 << kBits) == CHUNK && kBits > kSortRegBits + 6, "chunk spans waves");
+  __shared__ uint64_t s[2][CHUNK];
   const int seg = blockIdx.y;
-  const int c0 = blockIdx.x * kSortChunk;
+  const int c0 = blockIdx.x * CHUNK;
   const int lane = threadIdx.x & 63;
   const int base = threadIdx.x * kSortPer;
   const float* d = delta + (int64_t)seg * Sk;
@@ -78,7 +121,7 @@ __global__ __launch_bounds__(kSortThreads) void sort_chunk_kernel(const float* _
   int lds_stage = 0;  // LDS stages alternate buffers, so a buffer is rewritten
                       // only after the barrier of the stage in between
 #pragma unroll
-  for (int m = 1; m <= 12; ++m) {
+  for (int m = 1; m <= kBits; ++m) {
 #pragma unroll
     for (int b = m - 1; b >= 0; --b) {
       // partner = i ^ x; the pair's lower index has bit b clear
@@ -99,7 +142,7 @@ __global__ __launch_bounds__(kSortThreads) void sort_chunk_kernel(const float* _
         const bool lower = (lane & (1 << (b - kSortRegBits))) == 0;
         uint64_t p[kSortPer];
 #pragma unroll
-        for (int r = 0; r < kSortPer; ++r) p[r] = shfl_xor64(a[r ^ (x & (kSortPer - 1))], lm);
+        for (int r = 0; r < kSortPer; ++r) p[r] = lane_xor64(a[r ^ (x & (kSortPer - 1))], lm);
 #pragma unroll
         for (int r = 0; r < kSortPer; ++r) a[r] = ((a[r] > p[r]) == lower) ? a[r] : p[r];
       } else {
@@ -162,77 +205,114 @@ __global__ __launch_bounds__(256) void rank_kernel(const uint64_t* __restrict__ 
   rank[(int64_t)seg * rstride + j] = r;
 }
 
-// T1 + T1b for a sequence of at most four sorted 4096-key runs (up to 16K
-// keys), in place of the merges: the rank of a key is its position in its own
-// run plus, for each other run, the number of keys there that beat it (keys
-// are distinct, so this is a binary search).  A workgroup holds every run of
-// its sequence in LDS and ranks the keys of one run; it writes rank[j] and
-// the merged order.
-constexpr int kRankRunsMax = 4;
+// T1 + T1b for a sequence of at most kRankRunsMax sorted runs of
+// kSortChunkSmall keys, in place of the merges: the rank of a key is the
+// number of keys that beat it, summed over the runs (its own run included,
+// where the count is its position; keys are distinct, so each count is a
+// binary search).  A workgroup holds every run of its sequence in LDS and
+// ranks kRankRunsKeys consecutive keys of one run (similar keys, so the
+// searches of a wave read nearby LDS words); it writes rank[j] and the merged
+// order.  The searches compare the 32-bit delta codes only (runs padded to
+// full length with code 0, which beats nothing); where a search stops on a
+// key of equal code, the keys of equal code are resolved by a second search
+// on the low 16 bits of the reversed index (Sk <= 16384, so those order the
+// indices).
+constexpr int kRankRunsMax = 16;
 constexpr int kRankRunsThreads = 256;
-constexpr int kRankRunsKeys = 1024;   // keys ranked per workgroup
+constexpr int kRankRunsU = 2;  // keys per thread
+constexpr int kRankRunsKeys = kRankRunsThreads * kRankRunsU;
+static_assert(kSortChunkSmall % kRankRunsKeys == 0, "a workgroup's keys lie in one run");
+static_assert(kRankRunsMax * kSortChunkSmall <= 65536, "16-bit reversed indices");
 
+template <int NR>  // runs searched (>= the sequence's run count)
 __global__ __launch_bounds__(kRankRunsThreads) void rank_runs_kernel(
     const uint64_t* __restrict__ runs, int Sk, int rstride, int32_t* __restrict__ rank,
     uint64_t* __restrict__ merged) {
-  extern __shared__ __align__(16) uint64_t s_runs[];
+  constexpr int kRun = kSortChunkSmall;
+  constexpr int kN = NR * kRun;
+  extern __shared__ __align__(16) uint32_t s_code[];            // [kN] delta codes
+  uint16_t* s_rev = reinterpret_cast<uint16_t*>(s_code + kN);  // [kN] reversed index, low 16 bits
   const int seg = blockIdx.y;
-  const int nr = (Sk + kSortChunk - 1) / kSortChunk;
+  const int tid = threadIdx.x;
   const uint64_t* src = runs + (int64_t)seg * Sk;
-  // all runs of the sequence into LDS; a sequence starts 8-byte aligned only
-  // (odd Sk), so 8-byte loads, all of a thread's in flight at once
-  constexpr int kFill = kRankRunsMax * kSortChunk / kRankRunsThreads;
-  for (int i0 = threadIdx.x; i0 < Sk; i0 += kRankRunsThreads * kFill) {
+  // a sequence starts 8-byte aligned only (odd Sk), so 8-byte loads, all of
+  // a thread's in flight at once
+  constexpr int kFill = kN / kRankRunsThreads;
+  {
     uint64_t v[kFill];
 #pragma unroll
-    for (int u = 0; u < kFill; ++u) v[u] = src[min(i0 + u * kRankRunsThreads, Sk - 1)];
+    for (int u = 0; u < kFill; ++u) v[u] = src[min(tid + u * kRankRunsThreads, Sk - 1)];
 #pragma unroll
-    for (int u = 0; u < kFill; ++u)
-      if (i0 + u * kRankRunsThreads < Sk) s_runs[i0 + u * kRankRunsThreads] = v[u];
+    for (int u = 0; u < kFill; ++u) {
+      const int i = tid + u * kRankRunsThreads;
+      const uint64_t k = i < Sk ? v[u] : 0ull;
+      s_code[i] = (uint32_t)(k >> 32);
+      s_rev[i] = (uint16_t)k;
+    }
   }
   __syncthreads();
 
-  // rank = sum over all runs (its own included, where the count is its
-  // position) of the keys that beat it; the 4 keys x 4 runs searches of a
-  // thread advance together, one halving step at a time
-  constexpr int kU = kRankRunsKeys / kRankRunsThreads;
-  const int r = blockIdx.x / (kSortChunk / kRankRunsKeys);
-  const int q0 = (blockIdx.x % (kSortChunk / kRankRunsKeys)) * kRankRunsKeys + threadIdx.x;
-  const int len_r = min(kSortChunk, Sk - r * kSortChunk);
-  uint64_t x[kU];
-  int cnt[kU][kRankRunsMax];
+  const int r = blockIdx.x / (kRun / kRankRunsKeys);
+  const int q0 = r * kRun + (blockIdx.x % (kRun / kRankRunsKeys)) * kRankRunsKeys + tid;
+  uint32_t c[kRankRunsU];
+  uint16_t rv[kRankRunsU];
+  int cnt[kRankRunsU][NR];  // LDS position: run base plus the count so far
 #pragma unroll
-  for (int u = 0; u < kU; ++u) {
-    x[u] = s_runs[r * kSortChunk + min(q0 + u * kRankRunsThreads, len_r - 1)];
+  for (int u = 0; u < kRankRunsU; ++u) {
+    const int q = min(q0 + u * kRankRunsThreads, Sk - 1);
+    c[u] = s_code[q];
+    rv[u] = s_rev[q];
 #pragma unroll
-    for (int o = 0; o < kRankRunsMax; ++o) cnt[u][o] = 0;
+    for (int o = 0; o < NR; ++o) cnt[u][o] = o * kRun;
   }
+  // all kRankRunsU x NR searches of a thread advance together, one halving
+  // step at a time; the first kRun - 1 keys of a run, then the last one
 #pragma unroll
-  for (int step = kSortChunk; step > 0; step >>= 1) {
+  for (int step = kRun / 2; step > 0; step >>= 1) {
 #pragma unroll
-    for (int o = 0; o < kRankRunsMax; ++o) {
-      // no branch on the run count, so all 16 reads of a step are in flight
-      // together; a missing run (n = 0) reads key 0 and never counts
-      const int n = o < nr ? min(kSortChunk, Sk - o * kSortChunk) : 0;
-      const uint64_t* A = s_runs + (o < nr ? o * kSortChunk : 0);
-      uint64_t v[kU];
+    for (int o = 0; o < NR; ++o) {
+      uint32_t v[kRankRunsU];
 #pragma unroll
-      for (int u = 0; u < kU; ++u) v[u] = A[max(min(cnt[u][o] + step, n), 1) - 1];
+      for (int u = 0; u < kRankRunsU; ++u) v[u] = s_code[cnt[u][o] + step - 1];
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int i = cnt[u][o] + step;
-        cnt[u][o] = (i <= n && v[u] > x[u]) ? i : cnt[u][o];
-      }
+      for (int u = 0; u < kRankRunsU; ++u) cnt[u][o] += v[u] > c[u] ? step : 0;
+    }
+  }
+  uint32_t tie[kRankRunsU];  // bit o: the search stopped on a key of equal code
+#pragma unroll
+  for (int u = 0; u < kRankRunsU; ++u) {
+    tie[u] = 0u;
+#pragma unroll
+    for (int o = 0; o < NR; ++o) {
+      const uint32_t v = s_code[cnt[u][o]];
+      cnt[u][o] += v > c[u] ? 1 : 0;
+      tie[u] |= (v == c[u] ? 1u : 0u) << o;
     }
   }
 #pragma unroll
-  for (int u = 0; u < kU; ++u) {
-    if (q0 + u * kRankRunsThreads >= len_r) continue;
+  for (int u = 0; u < kRankRunsU; ++u) {
     int pos = 0;
 #pragma unroll
-    for (int o = 0; o < kRankRunsMax; ++o) pos += cnt[u][o];
-    rank[(int64_t)seg * rstride + dma::index_of(x[u])] = pos;
-    merged[(int64_t)seg * Sk + pos] = x[u];
+    for (int o = 0; o < NR; ++o) pos += cnt[u][o] - o * kRun;
+    // equal codes: the keys of run o from cnt on with that code and a lower
+    // index (larger reversed index) also beat the key
+    for (uint32_t t = tie[u]; t; t &= t - 1u) {
+      const int o = __builtin_ctz(t);
+      const int n_o = min(kRun, Sk - o * kRun);
+      int lo = cnt[u][o], hi = o * kRun + n_o;  // first position that does not beat
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (s_code[mid] == c[u] && s_rev[mid] > rv[u]) lo = mid + 1;
+        else hi = mid;
+      }
+      pos += lo - cnt[u][o];
+    }
+    const int q = q0 + u * kRankRunsThreads;
+    if (q < Sk) {
+      const uint64_t x = src[q];
+      rank[(int64_t)seg * rstride + dma::index_of(x)] = pos;
+      merged[(int64_t)seg * Sk + pos] = x;
+    }
   }
 }
 
@@ -261,166 +341,170 @@ __device__ __forceinline__ int block_excl_scan(int v, int* s_w, int& total) {
 }
 
 // ---------------------------------------------------------------- T2: eviction rows
-// Bitmap of { j : rank[j] < rs } over nw 32-bit words in LDS: thread t
-// builds words [t*per, (t+1)*per) from its contiguous ranks with 16-byte
-// loads (unconditional, clamped into the sequence's padded rank row, so they
-// all issue before the first is used; indices >= Sk are masked).
-template <int NT>
-__device__ __forceinline__ void rank_bitmap(const int32_t* __restrict__ rk, int Sk, int rstride,
-                                            int rs, int nw, uint32_t* bm) {
-  const int per = (nw + NT - 1) / NT;
-  const int wlo = min(nw, (int)threadIdx.x * per), whi = min(nw, wlo + per);
-  const int jmax = rstride - 4;
-  for (int wi = wlo; wi < whi; wi += 2) {
-    uint32_t word[2] = {0u, 0u};
-    int4 v[2][8];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int q = 0; q < 8; ++q)
-        v[u][q] = *reinterpret_cast<const int4*>(rk + min((wi + u) * 32 + q * 4, jmax));
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int j = (wi + u) * 32 + q * 4;
-        word[u] |= (j < Sk && v[u][q].x < rs ? 1u : 0u) << (q * 4);
-        word[u] |= (j + 1 < Sk && v[u][q].y < rs ? 1u : 0u) << (q * 4 + 1);
-        word[u] |= (j + 2 < Sk && v[u][q].z < rs ? 1u : 0u) << (q * 4 + 2);
-        word[u] |= (j + 3 < Sk && v[u][q].w < rs ? 1u : 0u) << (q * 4 + 3);
-      }
-      if (wi + u < whi) bm[wi + u] = word[u];
-    }
-  }
-}
-
-// T2a: checkpoint bitmaps { j : rank[j] < c * chk } for c = 1 .. n_chk-1,
-// nwr words each, so an eviction block needs at most chk-1 insertions.
+// T2a: checkpoint bitmaps { j : rank[j] < c * chk } for c = 1 .. n_chk-1
+// (at most 64), nwr words each, so an eviction block needs at most chk-1
+// insertions on top of one.  One wave per 64 consecutive indices: a ballot
+// per checkpoint, and lane c-1 stores the two words of checkpoint c.
 __global__ __launch_bounds__(256) void ckpt_kernel(const int32_t* __restrict__ rank, int Sk,
                                                    int rstride, int chk, int n_chk, int nwr,
                                                    uint32_t* __restrict__ ckpt) {
-  extern __shared__ __align__(16) uint32_t bm[];
-  const int seg = blockIdx.y, c = blockIdx.x + 1;
-  const int nw = (Sk + 31) >> 5;
-  rank_bitmap<256>(rank + (int64_t)seg * rstride, Sk, rstride, c * chk, nw, bm);
-  __syncthreads();
-  uint32_t* out = ckpt + ((int64_t)seg * n_chk + c) * nwr;
-  for (int k = threadIdx.x; k < nwr; k += 256) out[k] = k < nw ? bm[k] : 0u;
+  const int seg = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int j0 = blockIdx.x * 256 + (int)threadIdx.x - lane;  // the wave's first index
+  if (j0 >= nwr * 32) return;  // past the padded words (wave-uniform)
+  const int j = j0 + lane;
+  const int r = j < Sk ? rank[(int64_t)seg * rstride + j] : INT_MAX;
+  uint64_t mine = 0ull;
+  for (int c = 1; c < n_chk; ++c) {
+    const uint64_t b = dma::ballot(r < c * chk);
+    mine = lane == c - 1 ? b : mine;
+  }
+  // nwr is a multiple of 4 and j0 of 64: the two words are 8-byte aligned
+  if (lane < n_chk - 1)
+    *reinterpret_cast<uint64_t*>(ckpt + ((int64_t)seg * n_chk + lane + 1) * nwr + (j0 >> 5)) =
+        mine;
 }
 
-// T2b: eviction rows of the keys of ranks [r0, r0 + R), one wave walking them.
-__global__ __launch_bounds__(256) void evict_kernel(const uint64_t* __restrict__ sorted, int Sk,
-                                                    int w, int R, int chk, int n_chk, int nwr,
-                                                    const uint32_t* __restrict__ ckpt,
-                                                    int32_t* __restrict__ evict) {
-  // Dynamic LDS only: bitmap of indices in whole 64-bit words (read as 32-bit
-  // halves, below), then s_w, s_f.
+// T2b: eviction rows of the keys of ranks [r0, r0 + 64), one wave per block.
+// Every global load of the block (its keys, the checkpoint words, the keys of
+// the ranks between the checkpoint and the block) is issued before the first
+// is used.
+//
+// The block's keys are taken in rank order, k = 0..63, key k with index x_k.
+// Let f_k be the w-th smallest index among the keys of rank < rs + k (the
+// bitmap S plus x_0..x_{k-1}); then e_k = max(x_k, f_k), and f moves only
+// when a key with x_k < f_k (a mover) arrives: to the largest index below
+// f_k in S plus the movers so far (x_k itself qualifies).  Let M be the 64
+// largest indices of S at or below f_0, descending (M[0] = f_0).  After t
+// moves, f is entry t of M with the movers inserted in order (a mover enters
+// below the current f, so entries 0..t are final once t moves are made).  A
+// key with x < M[63] is a mover whatever happened before it, and enters
+// below every entry f reaches in 64 keys, so it only counts as a move; keys
+// with M[63] <= x < f_0 are decided one at a time in rank order against
+// M[t], and the movers among them are inserted into M (a lane-parallel
+// shift).  Then mover k gets e_k = M[t_k], with t_k the movers before it.
+constexpr int kEvictR = 64;  // ranks per block: one wave's keys
+constexpr int kEvictThreads = 256;
+constexpr int kEvictWordsPer = 8;  // checkpoint words per thread and load batch
+constexpr int kEvictInsPer = 4;    // inserted keys per thread and load batch
+
+__global__ __launch_bounds__(kEvictThreads) void evict_kernel(
+    const uint64_t* __restrict__ sorted, int Sk, int w, int chk, int n_chk, int nwr,
+    const uint32_t* __restrict__ ckpt, int32_t* __restrict__ evict) {
+  // Dynamic LDS only: bitmap of indices (nwr words), s_w[8] (scan slots),
+  // s_m[64] (M).
   extern __shared__ __align__(16) uint32_t bm[];
   int* s_w = reinterpret_cast<int*>(bm + nwr);
-  int& s_f = s_w[4];
+  int* s_m = s_w + 8;
   const int seg = blockIdx.y;
+  const int tid = threadIdx.x;
   const uint64_t* K = sorted + (int64_t)seg * Sk;
   int32_t* E = evict + (int64_t)seg * Sk;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r0 = blockIdx.x * R, r1 = min(Sk, r0 + R);
+  const int lane = tid & 63, wave = tid >> 6;
+  const int r0 = blockIdx.x * kEvictR, r1 = min(Sk, r0 + kEvictR);
   // the w best keys are never beaten by w others: kept to the end
-  for (int r = r0 + (int)threadIdx.x; r < min(r1, w); r += 256) E[dma::index_of(K[r])] = Sk;
+  for (int r = r0 + tid; r < min(r1, w); r += kEvictThreads) E[dma::index_of(K[r])] = Sk;
   const int rs = max(r0, w);
   if (rs >= r1) return;
 
   // Bitmap of { j : rank[j] < rs }: the nearest checkpoint below rs, then
-  // the keys of the ranks in between, then the w-th smallest set bit from
-  // per-thread popcounts and one block scan.
+  // the keys of the ranks in between.
   const int c = rs / chk;
+  const int ri0 = c * chk;  // first rank inserted on top of the checkpoint
   const uint32_t* cp = ckpt + ((int64_t)seg * n_chk + c) * nwr;
-  for (int k = threadIdx.x; k < nwr; k += 256) bm[k] = c > 0 ? cp[k] : 0u;
-  __syncthreads();
-  for (int r = c * chk + (int)threadIdx.x; r < rs; r += 256) {
-    const uint32_t x = dma::index_of(K[r]);
-    atomicOr(&bm[x >> 5], 1u << (x & 31));
+  const uint64_t kw = (wave == 0 && rs + lane < r1) ? K[rs + lane] : 0ull;
+  uint64_t iv[kEvictInsPer];
+#pragma unroll
+  for (int u = 0; u < kEvictInsPer; ++u) {
+    const int r = ri0 + u * kEvictThreads + tid;
+    iv[u] = r < rs ? K[r] : 0ull;
+  }
+  if (tid < 64) s_m[tid] = -1;  // entries past the w-th (w < 64)
+  for (int k0 = 0; k0 < nwr; k0 += kEvictThreads * kEvictWordsPer) {
+    uint32_t wv[kEvictWordsPer];
+#pragma unroll
+    for (int u = 0; u < kEvictWordsPer; ++u) {
+      const int k = k0 + u * kEvictThreads + tid;
+      wv[u] = (c > 0 && k < nwr) ? cp[k] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kEvictWordsPer; ++u) {
+      const int k = k0 + u * kEvictThreads + tid;
+      if (k < nwr) bm[k] = wv[u];
+    }
+  }
+  __syncthreads();  // every word is written before the first insertion
+  for (int i0 = ri0; i0 < rs; i0 += kEvictThreads * kEvictInsPer) {
+    if (i0 != ri0) {
+#pragma unroll
+      for (int u = 0; u < kEvictInsPer; ++u) {
+        const int r = i0 + u * kEvictThreads + tid;
+        iv[u] = r < rs ? K[r] : 0ull;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kEvictInsPer; ++u) {
+      const int r = i0 + u * kEvictThreads + tid;
+      if (r < rs) {
+        const uint32_t x = dma::index_of(iv[u]);
+        atomicOr(&bm[x >> 5], 1u << (x & 31));
+      }
+    }
   }
   __syncthreads();
+
+  // M: set bits of ascending positions w-64 .. w-1 (0-based), from
+  // per-thread popcounts and one block scan; M[i] is position w-1-i.
   const int nw = (Sk + 31) >> 5;
-  const int per = (nw + 255) / 256;
-  const int wlo = min(nw, (int)threadIdx.x * per), whi = min(nw, wlo + per);
+  const int per = (nw + kEvictThreads - 1) / kEvictThreads;
+  const int wlo = min(nw, tid * per), whi = min(nw, wlo + per);
   int cnt = 0;
   for (int k = wlo; k < whi; ++k) cnt += __popc(bm[k]);
   int total;
-  const int before = block_excl_scan<256>(cnt, s_w, total);
-  if (threadIdx.x == 0 && total < w) s_f = -1;  // unreachable: rs >= w ranks are set
-  if (before < w && before + cnt >= w) {
-    int need = w - before;
-    for (int k = wlo; k < whi; ++k) {
+  const int before = block_excl_scan<kEvictThreads>(cnt, s_w, total);
+  const int plo = max(0, w - 64);
+  if (before < w && before + cnt > plo) {
+    int p = before;
+    for (int k = wlo; k < whi && p < w; ++k) {
       uint32_t x = bm[k];
       const int cc = __popc(x);
-      if (need <= cc) {
-        for (int q = 1; q < need; ++q) x &= x - 1;
-        s_f = k * 32 + __builtin_ctz(x);
-        break;
+      if (p + cc <= plo) {
+        p += cc;
+        continue;
       }
-      need -= cc;
+      for (; x && p < w; x &= x - 1u, ++p)
+        if (p >= plo) s_m[w - 1 - p] = k * 32 + __builtin_ctz(x);
     }
   }
   __syncthreads();
   if (wave != 0) return;
+  // total >= rs >= w set bits, so M[0] = f_0 is a real index
 
-  // Walk the block's ranks in order on one wave.  Everything the walk carries
-  // is wave-uniform (scalar registers): f, the 64-bit bitmap word holding f
-  // and the word below it (both with this walk's own insertions), and f's
-  // word index.  Insertions further down go to LDS, which is read again only
-  // when f gets there; f only ever moves down.  Per 64 keys, a ballot of
-  // x < f picks the keys that can move f (f only decreases, so no other key
-  // can); they are visited in order and the others keep e = x.
-  // 64-bit bitmap words are read as two 32-bit halves, so nothing depends on
-  // where dynamic LDS starts (an 8-byte access needs 8-byte alignment, and a
-  // 64-bit LDS atomic at an address 4 mod 8 faults the GPU); the only LDS
-  // atomics on the bitmap are 32-bit
-  auto bm64 = [&](int wi) -> uint64_t {
-    return ((uint64_t)bm[2 * wi + 1] << 32) | bm[2 * wi];
-  };
-  int f = s_f;
-  if (f < 0) return;  // unreachable (see above)
-  int cwi = f >> 6;
-  uint64_t cw = bm64(cwi);
-  uint64_t pw = cwi > 0 ? bm64(cwi - 1) : 0ull;
-  for (int g0 = rs; g0 < r1; g0 += 64) {
-    const int steps = min(64, r1 - g0);
-    const int xl = lane < steps ? (int)dma::index_of(K[g0 + lane]) : INT_MAX;  // one key per lane
-    int el = xl;  // e = x unless the key moves f
-    uint64_t cand = dma::ballot(xl < f);
-    while (cand) {
-      const int sl = __builtin_ctzll(cand);
-      cand &= cand - 1ull;
-      const int x = __builtin_amdgcn_readlane(xl, sl);
-      if (x < f) {
-        el = lane == sl ? f : el;  // e = f for this key
-        const int xw = x >> 6;
-        const uint64_t bit = 1ull << (x & 63);
-        if (xw == cwi) {
-          cw |= bit;
-        } else if (xw == cwi - 1) {
-          pw |= bit;
-        } else if (lane == 0) {
-          atomicOr(&bm[x >> 5], 1u << (x & 31));  // ds_or_b32: no return, no wait
-        }
-        // f <- largest set index below f (x itself qualifies)
-        uint64_t m = cw & ((1ull << (f & 63)) - 1ull);
-        if (m == 0ull) {
-          cw = pw;
-          --cwi;
-          m = cw;
-          while (m == 0ull && cwi > 0) {
-            --cwi;
-            cw = bm64(cwi);
-            m = cw;
-          }
-          pw = cwi > 0 ? bm64(cwi - 1) : 0ull;
-        }
-        f = m ? (cwi << 6) + 63 - __builtin_clzll(m) : -1;  // -1: unreachable (w bits below f)
-      }
+  int m = s_m[lane];                              // M, one entry per lane
+  const int f0 = __builtin_amdgcn_readfirstlane(__shfl(m, 0));
+  const int m63 = __shfl(m, 63);                  // -1 when w < 64
+  const int steps = r1 - rs;                      // 1..64 keys
+  const int xl = lane < steps ? (int)dma::index_of(kw) : INT_MAX;
+  const uint64_t sure = dma::ballot(xl < m63);                // movers whatever came before
+  const uint64_t open = dma::ballot(xl >= m63 && xl < f0);    // decided in order
+  uint64_t movers = sure;
+  for (uint64_t o = open; o; o &= o - 1ull) {
+    const int u = __builtin_ctzll(o);
+    const uint64_t below = (1ull << u) - 1ull;
+    const int t = __popcll(movers & below);  // moves before key u
+    const int f = __shfl(m, t);
+    const int xu = __shfl(xl, u);
+    if (xu < f) {  // wave-uniform
+      movers |= 1ull << u;
+      // insert xu below entry t: entries below xu move down one lane
+      const int up = __shfl_up(m, 1);
+      m = m > xu ? m : ((lane == 0 || up > xu) ? xu : up);
     }
-    if (lane < steps) E[xl] = el;
   }
+  const bool mv = (movers >> lane) & 1ull;
+  const int tk = dma::rank_below(movers);
+  const int fk = __shfl(m, tk);  // f when key k arrives (used by movers only)
+  if (lane < steps) E[xl] = mv ? fk : xl;
 }
 
 // ---------------------------------------------------------------- T3: tile lists
@@ -726,6 +810,236 @@ __global__ __launch_bounds__(kGroupWaves * 64) void group_lists_kernel(
   }
 }
 
+// L1 + L2 in one workgroup per group, with the group's candidates held in
+// LDS (when they fit: cap <= kFusedCap) instead of a round trip through
+// global memory: 16 waves scan keys 0..P_hi as L1 does, then build the tile
+// lists from LDS as L2 does.
+constexpr int kFusedWaves = 16;
+constexpr int kFusedCap = 8192;
+
+__global__ __launch_bounds__(kFusedWaves * 64) void lists_kernel(
+    const float* __restrict__ delta, const int32_t* __restrict__ evict, int Sk, int Sq, int q0,
+    int n_super, int n_tiles, int cap, int u_stride, int kt_stride, int32_t* __restrict__ u_idx,
+    int32_t* __restrict__ u_cnt, int32_t* __restrict__ u_nfull, float* __restrict__ u_dmax,
+    float* __restrict__ u_dlo, int32_t* __restrict__ kt_idx, int32_t* __restrict__ kt_cnt) {
+  extern __shared__ __align__(16) int32_t s_dyn[];
+  int32_t* s_cj = s_dyn;        // [cap] candidate keys, ascending
+  int32_t* s_ce = s_dyn + cap;  // [cap] their eviction rows
+  uint32_t* s_kt = reinterpret_cast<uint32_t*>(s_dyn + 2 * cap);  // per tile: key-tile bitmap
+  __shared__ int s_cw[kFusedWaves];
+  __shared__ int s_c[kFusedWaves][kSuperTiles][2];
+  // order codes of the largest delta per bucket: bucket i holds the keys of
+  // tile t0+i's own rows, bucket kSuperTiles every key before the group
+  __shared__ uint32_t s_b[kSuperTiles + 1];
+  const int tid = threadIdx.x;
+  const int seg = blockIdx.y, T = blockIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int t0 = T * kSuperTiles;
+  const int ng = min(kSuperTiles, n_tiles - t0);  // tiles in this group
+  const int P_lo = q0 + t0 * kListRows;
+  const int P_hi = q0 + min(Sq, (T + 1) * kSuperTiles * kListRows) - 1;
+  const int Pend = q0 + Sq - 1;  // last position
+  const int kw = kt_idx ? (kt_stride + 31) / 32 : 0;
+  if (tid <= kSuperTiles) s_b[tid] = 0u;  // 0: below every code
+  for (int k = tid; k < ng * kw; k += kFusedWaves * 64) s_kt[k] = 0u;
+
+  // ---- L1: the candidates C = { j <= P_hi : e_j > max(j, P_lo) }
+  {
+    const int32_t* E = evict + (int64_t)seg * Sk;
+    const float* Dl = delta + (int64_t)seg * Sk;
+    const int n = P_hi + 1;
+    const int L = ((n + 64 * kFusedWaves - 1) / (64 * kFusedWaves)) * 64;
+    const int j0 = min(n, wave * L), j1 = min(n, j0 + L);
+    int nc = 0;
+    for (int jb = j0; jb < j1; jb += 64 * kListUnroll) {
+      int e[kListUnroll];
+#pragma unroll
+      for (int u = 0; u < kListUnroll; ++u) {
+        const int j = jb + u * 64 + lane;
+        e[u] = j < j1 ? E[j] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < kListUnroll; ++u) {
+        const int j = jb + u * 64 + lane;
+        nc += __popcll(dma::ballot(j < j1 && e[u] > max(j, P_lo)));
+      }
+    }
+    if (lane == 0) s_cw[wave] = nc;
+    __syncthreads();
+    int oc = 0;
+#pragma unroll
+    for (int k = 0; k < kFusedWaves; ++k)
+      if (k < wave) oc += s_cw[k];
+    uint32_t m0 = 0u;  // this lane's largest code before the group
+    for (int jb = j0; jb < j1; jb += 64 * kListUnroll) {
+      int e[kListUnroll];
+      float d[kListUnroll];
+#pragma unroll
+      for (int u = 0; u < kListUnroll; ++u) {
+        const int j = jb + u * 64 + lane;
+        e[u] = j < j1 ? E[j] : 0;
+        d[u] = j < j1 ? Dl[j] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < kListUnroll; ++u) {
+        const int j = jb + u * 64 + lane;
+        const bool member = j < j1 && e[u] > max(j, P_lo);
+        const uint64_t bm = dma::ballot(member);
+        if (member) {
+          const int pos = oc + dma::rank_below(bm);
+          if (pos < cap) {
+            s_cj[pos] = j;
+            s_ce[pos] = e[u];
+          }
+        }
+        if (j < j1) {
+          if (j < P_lo)
+            m0 = max(m0, dma::ord32(d[u]));
+          else
+            atomicMax(&s_b[(j - P_lo) >> 6], dma::ord32(d[u]));
+        }
+        oc += __popcll(bm);
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m0 = max(m0, (uint32_t)__shfl_xor((int)m0, o));
+    if (lane == 0) atomicMax(&s_b[kSuperTiles], m0);
+  }
+  __syncthreads();
+  int nc = 0;
+#pragma unroll
+  for (int k = 0; k < kFusedWaves; ++k) nc += s_cw[k];
+  nc = min(nc, cap);
+  // tile t0+i: the largest delta over keys 0..p_hi (the keys before the
+  // group and buckets 0..i), and over the keys before its first row (before
+  // the group and buckets 0..i-1; minus infinity when there are none: code 0)
+  if (tid < ng) {
+    const int i = tid;
+    uint32_t mlo = s_b[kSuperTiles];
+    for (int k = 0; k < i; ++k) mlo = max(mlo, s_b[k]);
+    const uint32_t m = max(mlo, s_b[i]);
+    auto value = [](uint32_t c) {  // inverse of ord32
+      return c == 0u ? -INFINITY
+                     : __uint_as_float((c & 0x80000000u) ? (c & 0x7fffffffu) : ~c);
+    };
+    u_dmax[(int64_t)seg * n_tiles + t0 + i] = value(m);
+    if (u_dlo) u_dlo[(int64_t)seg * n_tiles + t0 + i] = value(mlo);
+  }
+
+  // ---- L2: each candidate against every tile of the group (see L2 above)
+  auto span = [](int a, int b) -> uint32_t {  // bits a..b
+    return (a > b || b < 0) ? 0u : (uint32_t)((2ull << b) - (1ull << a));
+  };
+  auto masks = [&](int j, int e, bool valid, uint32_t& mm, uint32_t& mf) {
+    const int r = j - P_lo;
+    const bool any = valid && e > j && j <= Pend;
+    mm = any ? span(r < 0 ? 0 : r >> 6, min((e - 1 - P_lo) >> 6, ng - 1)) : 0u;
+    const int fb = e > Pend ? ng - 1 : min((e - 64 - P_lo) >> 6, ng - 1);
+    mf = mm & span(r <= 0 ? 0 : (r + 63) >> 6, fb);
+  };
+  auto run_mask = [&](int j, uint64_t& runm) -> bool {
+    const int kt = j >> 6;
+    const int ktp = __shfl_up(kt, 1);
+    const bool start = lane == 0 || ktp != kt;
+    const uint64_t rs = dma::ballot(start);
+    const uint64_t above = lane == 63 ? 0ull : rs & (~0ull << (lane + 1));
+    const uint64_t upto = above ? (above & (0ull - above)) - 1ull : ~0ull;  // bits below next start
+    runm = upto & (~0ull << lane);
+    return start;
+  };
+  const int L2 = ((nc + 64 * kFusedWaves - 1) / (64 * kFusedWaves)) * 64;
+  const int k0 = min(nc, wave * L2), k1 = min(nc, k0 + L2);
+  int nfv = 0, npv = 0;  // per-tile counts live in lane i of the wave (tile t0 + i)
+  for (int kb = k0; kb < k1; kb += 64) {
+    const int kc = min(kb + lane, k1 - 1);  // clamped: validity applied by masks()
+    const int j = s_cj[kc], e = s_ce[kc];
+    uint32_t mm, mf;
+    masks(j, e, kb + lane < k1, mm, mf);
+    uint64_t runm = 0ull;
+    const bool rstart = kw ? run_mask(j, runm) : false;
+#pragma unroll
+    for (int i = 0; i < kSuperTiles; ++i) {
+      const bool member = (mm >> i) & 1u, full = (mf >> i) & 1u;
+      const uint64_t bf = dma::ballot(full), bp = dma::ballot(member && !full);
+      nfv += lane == i ? (int)__popcll(bf) : 0;
+      npv += lane == i ? (int)__popcll(bp) : 0;
+      if (rstart && ((bf | bp) & runm)) atomicOr(&s_kt[i * kw + (j >> 11)], 1u << ((j >> 6) & 31));
+    }
+  }
+  if (lane < kSuperTiles) {
+    s_c[wave][lane][0] = nfv;
+    s_c[wave][lane][1] = npv;
+  }
+  __syncthreads();
+  // lane i: this wave's offsets in tile i's two runs
+  int ofv = 0, opv = 0;
+  if (lane < kSuperTiles) {
+    int a = 0, bsum = 0, tf = 0, tp = 0;
+    for (int w2 = 0; w2 < kFusedWaves; ++w2) {
+      const int cf = s_c[w2][lane][0], cp = s_c[w2][lane][1];
+      if (w2 < wave) {
+        a += cf;
+        bsum += cp;
+      }
+      tf += cf;
+      tp += cp;
+    }
+    ofv = a;
+    opv = tf + bsum;  // the partial run follows the full run
+    if (wave == 0 && lane < ng) {
+      const int64_t g = (int64_t)seg * n_tiles + t0 + lane;
+      u_cnt[g] = min(tf + tp, u_stride);
+      u_nfull[g] = min(tf, u_stride);
+    }
+  }
+  int32_t* out0 = u_idx + ((int64_t)seg * n_tiles + t0) * u_stride;
+  for (int kb = k0; kb < k1; kb += 64) {
+    const int kc = min(kb + lane, k1 - 1);
+    const int j = s_cj[kc], e = s_ce[kc];
+    uint32_t mm, mf;
+    masks(j, e, kb + lane < k1, mm, mf);
+#pragma unroll
+    for (int i = 0; i < kSuperTiles; ++i) {
+      const bool member = (mm >> i) & 1u, full = (mf >> i) & 1u;
+      const uint64_t bf = dma::ballot(full), bp = dma::ballot(member && !full);
+      const int of_i = __builtin_amdgcn_readlane(ofv, i), op_i = __builtin_amdgcn_readlane(opv, i);
+      const int pos = full ? of_i + dma::rank_below(bf) : op_i + dma::rank_below(bp);
+      if (member && pos < u_stride) out0[(int64_t)i * u_stride + pos] = j;
+      ofv += lane == i ? (int)__popcll(bf) : 0;
+      opv += lane == i ? (int)__popcll(bp) : 0;
+    }
+  }
+  if (kw) {
+    __syncthreads();
+    // one wave per tile: ordered compaction of its key-tile bitmap
+    for (int i = wave; i < ng; i += kFusedWaves) {
+      const uint32_t* bm = s_kt + i * kw;
+      int32_t* kout = kt_idx + ((int64_t)seg * n_tiles + t0 + i) * kt_stride;
+      int at = 0;
+      for (int k = 0; k < kw; k += 64) {
+        const uint32_t x = k + lane < kw ? bm[k + lane] : 0u;
+        const int c = __popc(x);
+        int incl = c;  // inclusive prefix over the wave
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int y = __shfl_up(incl, o);
+          if (lane >= o) incl += y;
+        }
+        int pos = at + incl - c;
+        uint32_t y = x;
+        while (y) {
+          const int b = __builtin_ctz(y);
+          y &= y - 1;
+          if (pos < kt_stride) kout[pos] = (k + lane) * 32 + b;
+          ++pos;
+        }
+        at += __shfl(incl, 63);
+      }
+      if (lane == 0) kt_cnt[(int64_t)seg * n_tiles + t0 + i] = min(at, kt_stride);
+    }
+  }
+}
+
 // ---------------------------------------------------------------- decode: one row
 // Keys 0..p of one sequence; keeps the w best (Hugging Face blog "Trainable
 // Dynamic Mask Sparse Attention", section "Mask Combination with Causal
@@ -995,10 +1309,11 @@ static int64_t cand_cap(int64_t Sk, int64_t w) {
   return (c + 3) & ~int64_t(3);
 }
 
-// eviction checkpoints: every chk ranks, at most 64 per sequence
+// eviction checkpoints: every chk ranks (a multiple of 256), at most 64 per
+// sequence
 static int64_t ckpt_every(int64_t Sk) {
-  const int64_t c = std::max<int64_t>(1024, (Sk + 63) / 64);
-  return (c + 1023) & ~int64_t(1023);
+  const int64_t c = std::max<int64_t>(256, (Sk + 63) / 64);
+  return (c + 255) & ~int64_t(255);
 }
 static int64_t ckpt_words(int64_t Sk) { return (((Sk + 31) >> 5) + 3) & ~int64_t(3); }
 
@@ -1047,31 +1362,20 @@ hipError_t dma_launch_topk_prefill(const DmaTopkArgs& a, hipStream_t st) {
   uint64_t* kB = kA + n;
   int32_t* rank = reinterpret_cast<int32_t*>(kB + n);
 
-  const int nch = (Sk + kSortChunk - 1) / kSortChunk;
-  hipLaunchKernelGGL(sort_chunk_kernel, dim3(nch, BH), dim3(kSortThreads), 0, st, a.delta, Sk,
-                     kA);
+  // up to kRankRunsMax small runs: ranks by binary search; beyond that,
+  // large runs and merges
+  const bool by_search = Sk > kSortChunkSmall && Sk <= kRankRunsMax * kSortChunkSmall;
+  const int chunk = by_search || Sk <= kSortChunkSmall ? kSortChunkSmall : kSortChunkLarge;
+  const int nch = (Sk + chunk - 1) / chunk;
+  if (chunk == kSortChunkSmall)
+    hipLaunchKernelGGL(sort_chunk_kernel<kSortChunkSmall>, dim3(nch, BH),
+                       dim3(kSortChunkSmall / kSortPer), 0, st, a.delta, Sk, kA);
+  else
+    hipLaunchKernelGGL(sort_chunk_kernel<kSortChunkLarge>, dim3(nch, BH),
+                       dim3(kSortChunkLarge / kSortPer), 0, st, a.delta, Sk, kA);
   uint64_t* src = kA;
   uint64_t* dst = kB;
   const int rs = (int)rank_stride(Sk);
-  if (nch > 1 && nch <= kRankRunsMax) {
-    const size_t lds = (size_t)Sk * sizeof(uint64_t);
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&rank_runs_kernel),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    hipLaunchKernelGGL(rank_runs_kernel, dim3(nch * (kSortChunk / kRankRunsKeys), BH),
-                       dim3(kRankRunsThreads), lds, st, src, Sk, rs, rank, dst);
-    src = dst;
-  } else {
-    for (int L = kSortChunk; L < Sk; L <<= 1) {
-      const int nthr = (Sk + kMergeItems - 1) / kMergeItems;
-      hipLaunchKernelGGL(merge_kernel, dim3((nthr + 255) / 256, BH), dim3(256), 0, st, src, dst,
-                         Sk, L);
-      uint64_t* t = src;
-      src = dst;
-      dst = t;
-    }
-    hipLaunchKernelGGL(rank_kernel, dim3((Sk + 255) / 256, BH), dim3(256), 0, st, src, Sk, rs,
-                       rank);
-  }
   const int n_super = (int)n_super_of(a.Sq);
   const int cap = (int)cand_cap(a.Sk, a.w);
   int32_t* cj = rank + BH * rs;
@@ -1082,27 +1386,53 @@ hipError_t dma_launch_topk_prefill(const DmaTopkArgs& a, hipStream_t st) {
   const int n_chk = (Sk + chk - 1) / chk;
   const int nwr = (int)ckpt_words(Sk);
   const size_t bm_bytes = (size_t)nwr * sizeof(uint32_t);
-  if (n_chk > 1) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&ckpt_kernel),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)bm_bytes);
-    hipLaunchKernelGGL(ckpt_kernel, dim3(n_chk - 1, BH), dim3(256), bm_bytes, st, rank, Sk, rs,
-                       chk, n_chk, nwr, ckpt);
+  if (by_search) {
+    const dim3 grid(nch * (kSortChunkSmall / kRankRunsKeys), BH);
+    auto launch = [&](auto kern, int nr) {
+      const size_t lds = (size_t)nr * kSortChunkSmall * (sizeof(uint32_t) + sizeof(uint16_t));
+      (void)dma_func_max_lds(reinterpret_cast<const void*>(kern), lds);
+      hipLaunchKernelGGL(kern, grid, dim3(kRankRunsThreads), lds, st, src, Sk, rs, rank, dst);
+    };
+    if (nch <= 4) launch(rank_runs_kernel<4>, 4);
+    else if (nch <= 8) launch(rank_runs_kernel<8>, 8);
+    else launch(rank_runs_kernel<16>, 16);
+    src = dst;
+  } else {
+    for (int L = chunk; L < Sk; L <<= 1) {
+      const int nthr = (Sk + kMergeItems - 1) / kMergeItems;
+      hipLaunchKernelGGL(merge_kernel, dim3((nthr + 255) / 256, BH), dim3(256), 0, st, src, dst,
+                         Sk, L);
+      uint64_t* t = src;
+      src = dst;
+      dst = t;
+    }
+    hipLaunchKernelGGL(rank_kernel, dim3((Sk + 255) / 256, BH), dim3(256), 0, st, src, Sk, rs,
+                       rank);
   }
-  const int R = 64;
-  const size_t ev_lds = bm_bytes + 8 * sizeof(int);  // bitmap, then s_w[4], s_f (padded)
-  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&evict_kernel),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)ev_lds);
-  hipLaunchKernelGGL(evict_kernel, dim3((Sk + R - 1) / R, BH), dim3(256), ev_lds, st, src, Sk,
-                     (int)a.w, R, chk, n_chk, nwr, ckpt, a.evict);
+  if (n_chk > 1)
+    hipLaunchKernelGGL(ckpt_kernel, dim3((nwr * 32 + 255) / 256, BH), dim3(256), 0, st, rank, Sk,
+                       rs, chk, n_chk, nwr, ckpt);
+  const size_t ev_lds = bm_bytes + (8 + 64) * sizeof(int);  // bitmap, s_w[8], s_m[64]
+  (void)dma_func_max_lds(reinterpret_cast<const void*>(&evict_kernel), ev_lds);
+  hipLaunchKernelGGL(evict_kernel, dim3((Sk + kEvictR - 1) / kEvictR, BH), dim3(kEvictThreads),
+                     ev_lds, st, src, Sk, (int)a.w, chk, n_chk, nwr, ckpt, a.evict);
+  const int kwords = a.kt_idx ? (int)((a.kt_stride + 31) / 32) : 0;
+  if (kwords > kMaxKtWords) return hipErrorInvalidValue;
+  if (cap <= kFusedCap) {
+    const size_t lds = (size_t)2 * cap * sizeof(int32_t) + (size_t)kSuperTiles * kwords * 4;
+    (void)dma_func_max_lds(reinterpret_cast<const void*>(&lists_kernel), lds);
+    hipLaunchKernelGGL(lists_kernel, dim3(n_super, BH), dim3(kFusedWaves * 64), lds, st, a.delta,
+                       a.evict, Sk, (int)a.Sq, (int)a.q0, n_super, (int)a.n_tiles, cap,
+                       (int)a.u_stride, (int)a.kt_stride, a.u_idx, a.u_cnt, a.u_nfull, a.u_dmax,
+                       a.u_dlo, a.kt_idx, a.kt_cnt);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(cand_kernel, dim3(n_super, BH), dim3(kListWaves * 64), 0, st, a.delta,
                      a.evict, Sk, (int)a.Sq, (int)a.q0, n_super, (int)a.n_tiles, cap, cj, ce, ccnt,
                      a.u_dmax, a.u_dlo);
-  const size_t kt_lds =
-      a.kt_idx ? (size_t)kSuperTiles * ((a.kt_stride + 31) / 32) * sizeof(uint32_t) : 0;
-  if (kt_lds > (size_t)kSuperTiles * kMaxKtWords * sizeof(uint32_t)) return hipErrorInvalidValue;
+  const size_t kt_lds = (size_t)kSuperTiles * kwords * sizeof(uint32_t);
   if (kt_lds > 0)
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&group_lists_kernel),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kt_lds);
+    (void)dma_func_max_lds(reinterpret_cast<const void*>(&group_lists_kernel), kt_lds);
   hipLaunchKernelGGL(group_lists_kernel, dim3(n_super, BH), dim3(kGroupWaves * 64), kt_lds, st,
                      cj, ce, ccnt, (int)a.Sq, (int)a.q0, (int)a.n_tiles, n_super, cap,
                      (int)a.u_stride, (int)a.kt_stride, a.u_idx, a.u_cnt, a.u_nfull, a.kt_idx,
@@ -1131,8 +1461,7 @@ hipError_t dma_launch_decode_append(const float* delta, int64_t BH, int64_t Sk, 
                                    int32_t* u_idx, int32_t* u_cnt, int32_t* u_nfull,
                                    float* u_dmax, hipStream_t st) {
   const size_t lds = (size_t)w * sizeof(int32_t);
-  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_append_kernel),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  (void)dma_func_max_lds(reinterpret_cast<const void*>(&decode_append_kernel), lds);
   hipLaunchKernelGGL(decode_append_kernel, dim3((unsigned)BH), dim3(kAppThreads), lds, st, delta,
                      (int)Sk, (int)w, u_idx, u_cnt, u_nfull, u_dmax);
   return hipGetLastError();

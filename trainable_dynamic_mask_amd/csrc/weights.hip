@@ -400,8 +400,7 @@ hipError_t launch_mfma(const __bf16* V, int64_t B, int64_t Sk, int64_t Hkv, int6
   const int64_t ntiles = B * ((Sk + kKeysPerTile - 1) / kKeysPerTile);
   const int per_cu = std::max<int>(1, (int)((160 * 1024) / lds));
   const int64_t grid = std::min<int64_t>(ntiles, (int64_t)cu_count() * per_cu);
-  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&weights_mfma_kernel<W, NS, BWD>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  (void)dma_func_max_lds(reinterpret_cast<const void*>(&weights_mfma_kernel<W, NS, BWD>), lds);
   for (int h0 = 0; h0 < Hkv; h0 += 8)
     hipLaunchKernelGGL((weights_mfma_kernel<W, NS, BWD>), dim3((unsigned)grid), dim3(64 * W), lds,
                        st, V, sb, ss, (int)Sk, (int)B, C, (int)Hkv, h0, Delta, A, delta, ddelta,
