@@ -101,9 +101,12 @@ __device__ __forceinline__ uint64_t lane_xor64(uint64_t v, int lm) {
 // (lane_xor64), and only pairs that differ in bits 8 and up cross waves,
 // through LDS (two buffers, one barrier each).  Every element is updated by
 // its owner, which takes the larger or the smaller of itself and its partner.
+// It also writes, per 64-key block of indices, the largest delta code (0 for
+// none) for the tile lists' largest deltas.
 template <int CHUNK>
 __global__ __launch_bounds__(CHUNK / kSortPer) void sort_chunk_kernel(
-    const float* __restrict__ delta, int Sk, uint64_t* __restrict__ out) {
+    const float* __restrict__ delta, int Sk, uint64_t* __restrict__ out,
+    uint32_t* __restrict__ blk_code) {
   constexpr int kBits = __builtin_ctz(CHUNK);
   static_assert((1 << kBits) == CHUNK && kBits > kSortRegBits + 6, "chunk spans waves");
   __shared__ uint64_t s[2][CHUNK];
@@ -117,6 +120,16 @@ __global__ __launch_bounds__(CHUNK / kSortPer) void sort_chunk_kernel(
   for (int r = 0; r < kSortPer; ++r) {
     const int j = c0 + base + r;
     a[r] = (j < Sk) ? dma::key_of(d[j], (uint32_t)j) : 0ull;  // 0 sorts after every real key
+  }
+  {
+    // 16 lanes (one DPP row) hold a 64-key block
+    uint32_t bc = 0u;
+#pragma unroll
+    for (int r = 0; r < kSortPer; ++r) bc = max(bc, (uint32_t)(a[r] >> 32));
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) bc = max(bc, (uint32_t)__shfl_xor((int)bc, o));
+    const int nblk = (Sk + 63) >> 6;
+    if ((lane & 15) == 0 && c0 + base < Sk) blk_code[(int64_t)seg * nblk + ((c0 + base) >> 6)] = bc;
   }
   int lds_stage = 0;  // LDS stages alternate buffers, so a buffer is rewritten
                       // only after the barrier of the stage in between
@@ -365,10 +378,7 @@ __global__ __launch_bounds__(256) void ckpt_kernel(const int32_t* __restrict__ r
         mine;
 }
 
-// T2b: eviction rows of the keys of ranks [r0, r0 + 64), one wave per block.
-// Every global load of the block (its keys, the checkpoint words, the keys of
-// the ranks between the checkpoint and the block) is issued before the first
-// is used.
+// T2b: eviction rows, one block of 64 consecutive ranks per wave.
 //
 // The block's keys are taken in rank order, k = 0..63, key k with index x_k.
 // Let f_k be the w-th smallest index among the keys of rank < rs + k (the
@@ -383,6 +393,146 @@ __global__ __launch_bounds__(256) void ckpt_kernel(const int32_t* __restrict__ r
 // with M[63] <= x < f_0 are decided one at a time in rank order against
 // M[t], and the movers among them are inserted into M (a lane-parallel
 // shift).  Then mover k gets e_k = M[t_k], with t_k the movers before it.
+//
+// m: M, one entry per lane (-1 past the w-th set bit); xl: the block's key
+// indices, INT_MAX past the block.  Returns e for this lane's key.
+__device__ __forceinline__ int evict_walk(int m, int xl) {
+  const int lane = dma::lane_id();
+  const int f0 = __builtin_amdgcn_readfirstlane(__shfl(m, 0));
+  const int m63 = __shfl(m, 63);                             // -1 when w < 64
+  const uint64_t sure = dma::ballot(xl < m63);               // movers whatever came before
+  const uint64_t open = dma::ballot(xl >= m63 && xl < f0);   // decided in order
+  uint64_t movers = sure;
+  for (uint64_t o = open; o; o &= o - 1ull) {
+    const int u = __builtin_ctzll(o);
+    const int t = __popcll(movers & ((1ull << u) - 1ull));  // moves before key u
+    const int f = __shfl(m, t);
+    const int xu = __shfl(xl, u);
+    if (xu < f) {  // wave-uniform
+      movers |= 1ull << u;
+      // insert xu below entry t: entries below xu move down one lane
+      const int up = __shfl_up(m, 1);
+      m = m > xu ? m : ((lane == 0 || up > xu) ? xu : up);
+    }
+  }
+  const bool mv = (movers >> lane) & 1ull;
+  const int fk = __shfl(m, dma::rank_below(movers));  // f when key k arrives
+  return mv ? fk : xl;
+}
+
+// Orders one wave's LDS accesses across its lanes (no instruction: the
+// compiler keeps them in program order; the wave executes LDS in order).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+}
+
+// M from one wave's bitmap of nw words in LDS (at least w set bits): lane i
+// gets the set bit of ascending position w-1-i (0-based), -1 where there is
+// none (w < 64).  Per-word exclusive prefix counts go to s_pre (nw ints of
+// LDS); each lane then finds its word by a binary search over them (the last
+// word whose prefix is at most its position) and its bit by halving selects.
+__device__ __forceinline__ int wave_top_m(const uint32_t* bm, int nw, int w, int* s_pre) {
+  const int lane = dma::lane_id();
+  const int per = (nw + 63) >> 6;
+  const int wlo = min(nw, lane * per), whi = min(nw, wlo + per);
+  int cnt = 0;
+  for (int k = wlo; k < whi; ++k) cnt += __popc(bm[k]);
+  int incl = cnt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  int run = incl - cnt;
+  for (int k = wlo; k < whi; ++k) {
+    s_pre[k] = run;
+    run += __popc(bm[k]);
+  }
+  wave_lds_sync();
+  const int P = w - 1 - lane;
+  if (P < 0) return -1;
+  int lo = 0, hi = nw - 1;  // s_pre[lo] <= P
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (s_pre[mid] <= P) lo = mid;
+    else hi = mid - 1;
+  }
+  uint32_t x = bm[lo];
+  int r = P - s_pre[lo];  // r-th set bit of word lo (0-based)
+  int b = 0;
+#pragma unroll
+  for (int h = 16; h >= 1; h >>= 1) {
+    const int c = __popc(x & ((1u << h) - 1u));
+    if (r >= c) {
+      r -= c;
+      x >>= h;
+      b += h;
+    }
+  }
+  return lo * 32 + b;
+}
+
+// Eviction rows of the ranks [R0, R0 + 256), four blocks of 64, one per
+// wave.  The workgroup builds the bitmap of the ranks below R0 once (the
+// checkpoint below R0 plus the ranks in between; none when the checkpoints
+// are 256 ranks apart), then each wave copies it, adds the workgroup's ranks
+// below its own block, and walks its block with no further barrier.
+constexpr int kEvictWG = 4;  // blocks (waves) per workgroup
+constexpr int kEvictRanks = 64 * kEvictWG;
+
+__global__ __launch_bounds__(kEvictRanks) void evict_wg_kernel(
+    const uint64_t* __restrict__ sorted, int Sk, int w, int chk, int n_chk, int nwr,
+    const uint32_t* __restrict__ ckpt, int32_t* __restrict__ evict) {
+  extern __shared__ __align__(16) uint32_t s_lds[];
+  uint32_t* s_base = s_lds;                                    // [nwr] ranks < R0
+  uint32_t* s_bm = s_lds + nwr;                                // [kEvictWG][nwr] bitmaps
+  int* s_pre = reinterpret_cast<int*>(s_bm + kEvictWG * nwr);  // [kEvictWG][nwr] prefixes
+  int* s_x = s_pre + kEvictWG * nwr;                           // [kEvictRanks] indices
+  const int seg = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint64_t* K = sorted + (int64_t)seg * Sk;
+  int32_t* E = evict + (int64_t)seg * Sk;
+  const int R0 = blockIdx.x * kEvictRanks;
+  const int r = R0 + tid;  // this thread's rank
+  const int x = r < Sk ? (int)dma::index_of(K[r]) : INT_MAX;
+  const int c = R0 / chk;
+  const uint32_t* cp = ckpt + ((int64_t)seg * n_chk + c) * nwr;
+  for (int k = tid; k < nwr; k += kEvictRanks) s_base[k] = c > 0 ? cp[k] : 0u;
+  s_x[tid] = x;
+  if (r < min(Sk, w)) E[x] = Sk;  // the w best keys are kept to the end
+  __syncthreads();
+  if (c * chk < R0) {  // block-uniform
+    for (int q = c * chk + tid; q < R0; q += kEvictRanks) {
+      const uint32_t xi = dma::index_of(K[q]);
+      atomicOr(&s_base[xi >> 5], 1u << (xi & 31));
+    }
+    __syncthreads();
+  }
+  // ---- per wave: its block of ranks [b0, b1), walked from rs
+  const int b0 = R0 + 64 * wave, b1 = min(Sk, b0 + 64);
+  const int rsw = max(b0, w);
+  if (rsw >= b1) return;  // wave-uniform; no block barrier follows
+  uint32_t* bm = s_bm + wave * nwr;
+  for (int k = lane; k < nwr; k += 64) bm[k] = s_base[k];
+  wave_lds_sync();
+  for (int q = lane; q < rsw - R0; q += 64) {  // ranks R0 .. rsw-1
+    const int xi = s_x[q];
+    atomicOr(&bm[xi >> 5], 1u << (xi & 31));
+  }
+  wave_lds_sync();
+  const int m = wave_top_m(bm, (Sk + 31) >> 5, w, s_pre + wave * nwr);
+  const int xl = rsw + lane < b1 ? s_x[rsw - R0 + lane] : INT_MAX;
+  const int e = evict_walk(m, xl);
+  if (rsw + lane < b1) E[xl] = e;
+}
+
+// Eviction rows of the keys of ranks [r0, r0 + 64), one block per
+// workgroup, for large Sk (the per-wave bitmap copies of evict_wg_kernel
+// would not fit LDS).  Every global load of the block (its keys, the
+// checkpoint words, the keys of the ranks between the checkpoint and the
+// block) is issued before the first is used.
 constexpr int kEvictR = 64;  // ranks per block: one wave's keys
 constexpr int kEvictThreads = 256;
 constexpr int kEvictWordsPer = 8;  // checkpoint words per thread and load batch
@@ -479,32 +629,10 @@ __global__ __launch_bounds__(kEvictThreads) void evict_kernel(
   __syncthreads();
   if (wave != 0) return;
   // total >= rs >= w set bits, so M[0] = f_0 is a real index
-
-  int m = s_m[lane];                              // M, one entry per lane
-  const int f0 = __builtin_amdgcn_readfirstlane(__shfl(m, 0));
-  const int m63 = __shfl(m, 63);                  // -1 when w < 64
-  const int steps = r1 - rs;                      // 1..64 keys
+  const int steps = r1 - rs;  // 1..64 keys
   const int xl = lane < steps ? (int)dma::index_of(kw) : INT_MAX;
-  const uint64_t sure = dma::ballot(xl < m63);                // movers whatever came before
-  const uint64_t open = dma::ballot(xl >= m63 && xl < f0);    // decided in order
-  uint64_t movers = sure;
-  for (uint64_t o = open; o; o &= o - 1ull) {
-    const int u = __builtin_ctzll(o);
-    const uint64_t below = (1ull << u) - 1ull;
-    const int t = __popcll(movers & below);  // moves before key u
-    const int f = __shfl(m, t);
-    const int xu = __shfl(xl, u);
-    if (xu < f) {  // wave-uniform
-      movers |= 1ull << u;
-      // insert xu below entry t: entries below xu move down one lane
-      const int up = __shfl_up(m, 1);
-      m = m > xu ? m : ((lane == 0 || up > xu) ? xu : up);
-    }
-  }
-  const bool mv = (movers >> lane) & 1ull;
-  const int tk = dma::rank_below(movers);
-  const int fk = __shfl(m, tk);  // f when key k arrives (used by movers only)
-  if (lane < steps) E[xl] = mv ? fk : xl;
+  const int e = evict_walk(s_m[lane], xl);
+  if (lane < steps) E[xl] = e;
 }
 
 // ---------------------------------------------------------------- T3: tile lists
@@ -812,25 +940,34 @@ __global__ __launch_bounds__(kGroupWaves * 64) void group_lists_kernel(
 
 // L1 + L2 in one workgroup per group, with the group's candidates held in
 // LDS (when they fit: cap <= kFusedCap) instead of a round trip through
-// global memory: 16 waves scan keys 0..P_hi as L1 does, then build the tile
-// lists from LDS as L2 does.
+// global memory.  16 waves scan keys 0..P_hi for the candidates as L1 does,
+// then build the tile lists from LDS as L2 does, each wave for a slice of
+// the candidates and all tiles of the group: a counting pass (the tile
+// masks stay in registers), one barrier for the offsets, a writing pass.
+// Tile offsets are wave-uniform (scalar registers); list entries go out
+// through a raw buffer view of the group's lists, lanes with nothing to
+// store taking an offset past its end, so the stores need no branch; most
+// members are full, so partial members are written only by the batches
+// that hold any.  The largest deltas come from the sort's per-block maxima
+// below the group and one 64-key segment per tile, one wave each.
 constexpr int kFusedWaves = 16;
 constexpr int kFusedCap = 8192;
+constexpr int kFusedBatches = kFusedCap / (64 * kFusedWaves);  // 64-candidate batches per wave
+constexpr uint32_t kBufferDrop = 0x40000000u;  // a store offset past any list region
 
 __global__ __launch_bounds__(kFusedWaves * 64) void lists_kernel(
-    const float* __restrict__ delta, const int32_t* __restrict__ evict, int Sk, int Sq, int q0,
-    int n_super, int n_tiles, int cap, int u_stride, int kt_stride, int32_t* __restrict__ u_idx,
-    int32_t* __restrict__ u_cnt, int32_t* __restrict__ u_nfull, float* __restrict__ u_dmax,
-    float* __restrict__ u_dlo, int32_t* __restrict__ kt_idx, int32_t* __restrict__ kt_cnt) {
+    const float* __restrict__ delta, const uint32_t* __restrict__ blk_code,
+    const int32_t* __restrict__ evict, int Sk, int Sq, int q0, int n_super, int n_tiles, int cap,
+    int u_stride, int kt_stride, int32_t* __restrict__ u_idx, int32_t* __restrict__ u_cnt,
+    int32_t* __restrict__ u_nfull, float* __restrict__ u_dmax, float* __restrict__ u_dlo,
+    int32_t* __restrict__ kt_idx, int32_t* __restrict__ kt_cnt) {
   extern __shared__ __align__(16) int32_t s_dyn[];
-  int32_t* s_cj = s_dyn;        // [cap] candidate keys, ascending
-  int32_t* s_ce = s_dyn + cap;  // [cap] their eviction rows
-  uint32_t* s_kt = reinterpret_cast<uint32_t*>(s_dyn + 2 * cap);  // per tile: key-tile bitmap
+  int32_t* s_cj = s_dyn;             // [cap + 64] candidate keys, ascending (64 spill slots)
+  int32_t* s_ce = s_dyn + cap + 64;  // [cap + 64] their eviction rows
+  uint32_t* s_kt = reinterpret_cast<uint32_t*>(s_ce + cap + 64);  // per tile: key-tile bitmap
   __shared__ int s_cw[kFusedWaves];
   __shared__ int s_c[kFusedWaves][kSuperTiles][2];
-  // order codes of the largest delta per bucket: bucket i holds the keys of
-  // tile t0+i's own rows, bucket kSuperTiles every key before the group
-  __shared__ uint32_t s_b[kSuperTiles + 1];
+  __shared__ uint32_t s_seg[kSuperTiles + 1];  // largest codes: below the group, per tile
   const int tid = threadIdx.x;
   const int seg = blockIdx.y, T = blockIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -840,24 +977,44 @@ __global__ __launch_bounds__(kFusedWaves * 64) void lists_kernel(
   const int P_hi = q0 + min(Sq, (T + 1) * kSuperTiles * kListRows) - 1;
   const int Pend = q0 + Sq - 1;  // last position
   const int kw = kt_idx ? (kt_stride + 31) / 32 : 0;
-  if (tid <= kSuperTiles) s_b[tid] = 0u;  // 0: below every code
   for (int k = tid; k < ng * kw; k += kFusedWaves * 64) s_kt[k] = 0u;
+  const float* Dl = delta + (int64_t)seg * Sk;
+
+  // largest delta codes, loads issued first: wave i < ng the keys of tile
+  // t0+i's own rows, the last wave the keys below P_lo (block maxima, then
+  // the keys of the block holding P_lo)
+  uint32_t dmx = 0u;
+  if (wave < ng) {
+    const int j = P_lo + 64 * wave + lane;
+    dmx = j <= Pend ? dma::ord32(Dl[j]) : 0u;
+  } else if (wave == kFusedWaves - 1) {
+    const uint32_t* bc = blk_code + (int64_t)seg * ((Sk + 63) >> 6);
+    const int nb0 = P_lo >> 6;
+    for (int b = lane; b < nb0; b += 64) dmx = max(dmx, bc[b]);
+    const int jp = (nb0 << 6) + lane;
+    if (jp < P_lo) dmx = max(dmx, dma::ord32(Dl[jp]));
+  }
 
   // ---- L1: the candidates C = { j <= P_hi : e_j > max(j, P_lo) }
   {
     const int32_t* E = evict + (int64_t)seg * Sk;
-    const float* Dl = delta + (int64_t)seg * Sk;
     const int n = P_hi + 1;
     const int L = ((n + 64 * kFusedWaves - 1) / (64 * kFusedWaves)) * 64;
     const int j0 = min(n, wave * L), j1 = min(n, j0 + L);
-    int nc = 0;
-    for (int jb = j0; jb < j1; jb += 64 * kListUnroll) {
-      int e[kListUnroll];
+    // one load batch per wave (n <= 16384): the rows stay in registers across
+    // the barrier; otherwise both passes load
+    const bool one = L <= 64 * kListUnroll;
+    int e[kListUnroll];
+    auto load = [&](int jb) {
 #pragma unroll
       for (int u = 0; u < kListUnroll; ++u) {
         const int j = jb + u * 64 + lane;
         e[u] = j < j1 ? E[j] : 0;
       }
+    };
+    int nc = 0;
+    for (int jb = j0; jb < j1; jb += 64 * kListUnroll) {
+      load(jb);
 #pragma unroll
       for (int u = 0; u < kListUnroll; ++u) {
         const int j = jb + u * 64 + lane;
@@ -865,160 +1022,177 @@ __global__ __launch_bounds__(kFusedWaves * 64) void lists_kernel(
       }
     }
     if (lane == 0) s_cw[wave] = nc;
+    if (wave < ng || wave == kFusedWaves - 1) {
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) dmx = max(dmx, (uint32_t)__shfl_xor((int)dmx, o));
+      if (lane == 0) s_seg[wave < ng ? wave + 1 : 0] = dmx;
+    }
     __syncthreads();
     int oc = 0;
 #pragma unroll
     for (int k = 0; k < kFusedWaves; ++k)
       if (k < wave) oc += s_cw[k];
-    uint32_t m0 = 0u;  // this lane's largest code before the group
     for (int jb = j0; jb < j1; jb += 64 * kListUnroll) {
-      int e[kListUnroll];
-      float d[kListUnroll];
-#pragma unroll
-      for (int u = 0; u < kListUnroll; ++u) {
-        const int j = jb + u * 64 + lane;
-        e[u] = j < j1 ? E[j] : 0;
-        d[u] = j < j1 ? Dl[j] : 0.f;
-      }
+      if (!one) load(jb);
 #pragma unroll
       for (int u = 0; u < kListUnroll; ++u) {
         const int j = jb + u * 64 + lane;
         const bool member = j < j1 && e[u] > max(j, P_lo);
         const uint64_t bm = dma::ballot(member);
-        if (member) {
-          const int pos = oc + dma::rank_below(bm);
-          if (pos < cap) {
-            s_cj[pos] = j;
-            s_ce[pos] = e[u];
-          }
-        }
-        if (j < j1) {
-          if (j < P_lo)
-            m0 = max(m0, dma::ord32(d[u]));
-          else
-            atomicMax(&s_b[(j - P_lo) >> 6], dma::ord32(d[u]));
-        }
+        // non-members (and any overflow) write their own spill slot
+        const int pos = oc + dma::rank_below(bm);
+        const int at = (member && pos < cap) ? pos : cap + lane;
+        s_cj[at] = j;
+        s_ce[at] = e[u];
         oc += __popcll(bm);
       }
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) m0 = max(m0, (uint32_t)__shfl_xor((int)m0, o));
-    if (lane == 0) atomicMax(&s_b[kSuperTiles], m0);
   }
   __syncthreads();
   int nc = 0;
 #pragma unroll
   for (int k = 0; k < kFusedWaves; ++k) nc += s_cw[k];
   nc = min(nc, cap);
-  // tile t0+i: the largest delta over keys 0..p_hi (the keys before the
-  // group and buckets 0..i), and over the keys before its first row (before
-  // the group and buckets 0..i-1; minus infinity when there are none: code 0)
+  // tile t0+i: the largest delta over keys 0..p_hi (below the group and
+  // tiles 0..i) and over the keys before its first row (below the group and
+  // tiles 0..i-1; minus infinity when there are none: code 0)
   if (tid < ng) {
-    const int i = tid;
-    uint32_t mlo = s_b[kSuperTiles];
-    for (int k = 0; k < i; ++k) mlo = max(mlo, s_b[k]);
-    const uint32_t m = max(mlo, s_b[i]);
     auto value = [](uint32_t c) {  // inverse of ord32
       return c == 0u ? -INFINITY
                      : __uint_as_float((c & 0x80000000u) ? (c & 0x7fffffffu) : ~c);
     };
-    u_dmax[(int64_t)seg * n_tiles + t0 + i] = value(m);
-    if (u_dlo) u_dlo[(int64_t)seg * n_tiles + t0 + i] = value(mlo);
+    uint32_t mlo = s_seg[0];
+    for (int k = 1; k <= tid; ++k) mlo = max(mlo, s_seg[k]);
+    u_dmax[(int64_t)seg * n_tiles + t0 + tid] = value(max(mlo, s_seg[tid + 1]));
+    if (u_dlo) u_dlo[(int64_t)seg * n_tiles + t0 + tid] = value(mlo);
   }
 
-  // ---- L2: each candidate against every tile of the group (see L2 above)
+  // ---- L2: member and full tile masks of a candidate (bit i: tile t0 + i),
+  // in closed form: with r = j - P_lo, key j is in U of tile i iff e > j,
+  // j <= Pend and floor(r/64) <= i <= floor((e-1-P_lo)/64); every row of
+  // tile i keeps it iff also ceil(r/64) <= i and (e > Pend or
+  // i <= floor((e-64-P_lo)/64)).  Packed: full bits, then partial bits << 8.
   auto span = [](int a, int b) -> uint32_t {  // bits a..b
     return (a > b || b < 0) ? 0u : (uint32_t)((2ull << b) - (1ull << a));
   };
-  auto masks = [&](int j, int e, bool valid, uint32_t& mm, uint32_t& mf) {
+  auto masks = [&](int j, int e, bool valid) -> uint32_t {
     const int r = j - P_lo;
     const bool any = valid && e > j && j <= Pend;
-    mm = any ? span(r < 0 ? 0 : r >> 6, min((e - 1 - P_lo) >> 6, ng - 1)) : 0u;
+    const uint32_t mm = any ? span(r < 0 ? 0 : r >> 6, min((e - 1 - P_lo) >> 6, ng - 1)) : 0u;
     const int fb = e > Pend ? ng - 1 : min((e - 64 - P_lo) >> 6, ng - 1);
-    mf = mm & span(r <= 0 ? 0 : (r + 63) >> 6, fb);
-  };
-  auto run_mask = [&](int j, uint64_t& runm) -> bool {
-    const int kt = j >> 6;
-    const int ktp = __shfl_up(kt, 1);
-    const bool start = lane == 0 || ktp != kt;
-    const uint64_t rs = dma::ballot(start);
-    const uint64_t above = lane == 63 ? 0ull : rs & (~0ull << (lane + 1));
-    const uint64_t upto = above ? (above & (0ull - above)) - 1ull : ~0ull;  // bits below next start
-    runm = upto & (~0ull << lane);
-    return start;
+    const uint32_t mf = mm & span(r <= 0 ? 0 : (r + 63) >> 6, fb);
+    return mf | ((mm & ~mf) << 8);
   };
   const int L2 = ((nc + 64 * kFusedWaves - 1) / (64 * kFusedWaves)) * 64;
   const int k0 = min(nc, wave * L2), k1 = min(nc, k0 + L2);
-  int nfv = 0, npv = 0;  // per-tile counts live in lane i of the wave (tile t0 + i)
-  for (int kb = k0; kb < k1; kb += 64) {
-    const int kc = min(kb + lane, k1 - 1);  // clamped: validity applied by masks()
-    const int j = s_cj[kc], e = s_ce[kc];
-    uint32_t mm, mf;
-    masks(j, e, kb + lane < k1, mm, mf);
-    uint64_t runm = 0ull;
-    const bool rstart = kw ? run_mask(j, runm) : false;
+  int cF[kSuperTiles], cP[kSuperTiles];  // wave-uniform counts, then offsets
+#pragma unroll
+  for (int i = 0; i < kSuperTiles; ++i) cF[i] = cP[i] = 0;
+  uint32_t pm[kFusedBatches];  // packed masks per batch
+  int pj[kFusedBatches];       // keys per batch
+#pragma unroll
+  for (int bt = 0; bt < kFusedBatches; ++bt) {
+    const int kb = k0 + 64 * bt;
+    if (kb >= k1) break;
+    const int kc = min(kb + lane, k1 - 1);
+    pj[bt] = s_cj[kc];
+    pm[bt] = masks(pj[bt], s_ce[kc], kb + lane < k1);
 #pragma unroll
     for (int i = 0; i < kSuperTiles; ++i) {
-      const bool member = (mm >> i) & 1u, full = (mf >> i) & 1u;
-      const uint64_t bf = dma::ballot(full), bp = dma::ballot(member && !full);
-      nfv += lane == i ? (int)__popcll(bf) : 0;
-      npv += lane == i ? (int)__popcll(bp) : 0;
-      if (rstart && ((bf | bp) & runm)) atomicOr(&s_kt[i * kw + (j >> 11)], 1u << ((j >> 6) & 31));
+      cF[i] += __popcll(dma::ballot((pm[bt] >> i) & 1u));
+      cP[i] += __popcll(dma::ballot((pm[bt] >> (8 + i)) & 1u));
     }
   }
-  if (lane < kSuperTiles) {
-    s_c[wave][lane][0] = nfv;
-    s_c[wave][lane][1] = npv;
+  if (lane == 0) {
+#pragma unroll
+    for (int i = 0; i < kSuperTiles; ++i) {
+      s_c[wave][i][0] = cF[i];
+      s_c[wave][i][1] = cP[i];
+    }
   }
   __syncthreads();
-  // lane i: this wave's offsets in tile i's two runs
-  int ofv = 0, opv = 0;
-  if (lane < kSuperTiles) {
-    int a = 0, bsum = 0, tf = 0, tp = 0;
-    for (int w2 = 0; w2 < kFusedWaves; ++w2) {
-      const int cf = s_c[w2][lane][0], cp = s_c[w2][lane][1];
-      if (w2 < wave) {
-        a += cf;
-        bsum += cp;
+  {
+    // lane i: tile i's offsets for this wave (full run, then partial run)
+    int of = 0, op = 0;
+    if (lane < kSuperTiles) {
+      int a = 0, bsum = 0, tf = 0, tp = 0;
+      for (int w2 = 0; w2 < kFusedWaves; ++w2) {
+        const int f = s_c[w2][lane][0], pc = s_c[w2][lane][1];
+        if (w2 < wave) {
+          a += f;
+          bsum += pc;
+        }
+        tf += f;
+        tp += pc;
       }
-      tf += cf;
-      tp += cp;
+      of = a;
+      op = tf + bsum;
+      if (wave == 0 && lane < ng) {
+        const int64_t g = (int64_t)seg * n_tiles + t0 + lane;
+        u_cnt[g] = min(tf + tp, u_stride);
+        u_nfull[g] = min(tf, u_stride);
+      }
     }
-    ofv = a;
-    opv = tf + bsum;  // the partial run follows the full run
-    if (wave == 0 && lane < ng) {
-      const int64_t g = (int64_t)seg * n_tiles + t0 + lane;
-      u_cnt[g] = min(tf + tp, u_stride);
-      u_nfull[g] = min(tf, u_stride);
-    }
-  }
-  int32_t* out0 = u_idx + ((int64_t)seg * n_tiles + t0) * u_stride;
-  for (int kb = k0; kb < k1; kb += 64) {
-    const int kc = min(kb + lane, k1 - 1);
-    const int j = s_cj[kc], e = s_ce[kc];
-    uint32_t mm, mf;
-    masks(j, e, kb + lane < k1, mm, mf);
 #pragma unroll
     for (int i = 0; i < kSuperTiles; ++i) {
-      const bool member = (mm >> i) & 1u, full = (mf >> i) & 1u;
-      const uint64_t bf = dma::ballot(full), bp = dma::ballot(member && !full);
-      const int of_i = __builtin_amdgcn_readlane(ofv, i), op_i = __builtin_amdgcn_readlane(opv, i);
-      const int pos = full ? of_i + dma::rank_below(bf) : op_i + dma::rank_below(bp);
-      if (member && pos < u_stride) out0[(int64_t)i * u_stride + pos] = j;
-      ofv += lane == i ? (int)__popcll(bf) : 0;
-      opv += lane == i ? (int)__popcll(bp) : 0;
+      cF[i] = __builtin_amdgcn_readlane(of, i);
+      cP[i] = __builtin_amdgcn_readlane(op, i);
+    }
+  }
+  // the group's lists: ng rows of u_stride entries
+  const __amdgpu_buffer_rsrc_t lists = __builtin_amdgcn_make_buffer_rsrc(
+      u_idx + ((int64_t)seg * n_tiles + t0) * u_stride, (short)0,
+      (int)((uint32_t)ng * (uint32_t)u_stride * 4u), 0x00020000);
+#pragma unroll
+  for (int bt = 0; bt < kFusedBatches; ++bt) {
+    const int kb = k0 + 64 * bt;
+    if (kb >= k1) break;
+    const int j = pj[bt];
+    const uint32_t m = pm[bt];
+#pragma unroll
+    for (int i = 0; i < kSuperTiles; ++i) {
+      const bool full = (m >> i) & 1u;
+      const uint64_t bF = dma::ballot(full), bP = dma::ballot((m >> (8 + i)) & 1u);
+      const int pf = __builtin_amdgcn_mbcnt_hi((uint32_t)(bF >> 32),
+                                               __builtin_amdgcn_mbcnt_lo((uint32_t)bF, cF[i]));
+      const bool okf = full && pf < u_stride;
+      __builtin_amdgcn_raw_buffer_store_b32(
+          (uint32_t)j, lists, okf ? (uint32_t)(i * u_stride + pf) * 4u : kBufferDrop, 0, 0);
+      if (bP) {  // wave-uniform: batches with partial members are rare
+        const bool part = (m >> (8 + i)) & 1u;
+        const int pp = __builtin_amdgcn_mbcnt_hi((uint32_t)(bP >> 32),
+                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)bP, cP[i]));
+        const bool okp = part && pp < u_stride;
+        __builtin_amdgcn_raw_buffer_store_b32(
+            (uint32_t)j, lists, okp ? (uint32_t)(i * u_stride + pp) * 4u : kBufferDrop, 0, 0);
+      }
+      cF[i] += __popcll(bF);
+      cP[i] += __popcll(bP);
+    }
+    if (kw) {
+      // key tiles of the members: a lane marks its key tile for the tiles it
+      // is a member of, unless the lane below (candidates ascend) is a member
+      // of the same tile in the same key tile
+      const uint32_t mm = (m | (m >> 8)) & 0xffu;
+      const int ktl = j >> 6;
+      const int vb = __shfl_up((ktl << 8) | (int)mm, 1);
+      const uint32_t below = (lane > 0 && (vb >> 8) == ktl) ? (uint32_t)(vb & 0xff) : 0u;
+      for (uint32_t mk = mm & ~below; mk; mk &= mk - 1u)
+        atomicOr(&s_kt[__builtin_ctz(mk) * kw + (ktl >> 5)], 1u << (ktl & 31));
     }
   }
   if (kw) {
     __syncthreads();
-    // one wave per tile: ordered compaction of its key-tile bitmap
-    for (int i = wave; i < ng; i += kFusedWaves) {
-      const uint32_t* bm = s_kt + i * kw;
-      int32_t* kout = kt_idx + ((int64_t)seg * n_tiles + t0 + i) * kt_stride;
+    // one wave per tile: ordered compaction of its key-tile bitmap, four
+    // bits per lane per round of 256 key tiles
+    for (int t = wave; t < ng; t += kFusedWaves) {
+      const uint32_t* bm = s_kt + t * kw;
+      int32_t* kout = kt_idx + ((int64_t)seg * n_tiles + t0 + t) * kt_stride;
       int at = 0;
-      for (int k = 0; k < kw; k += 64) {
-        const uint32_t x = k + lane < kw ? bm[k + lane] : 0u;
-        const int c = __popc(x);
+      for (int k = 0; k < kw; k += 8) {
+        const int wi = k + (lane >> 3);
+        const uint32_t nib = wi < kw ? (bm[wi] >> (4 * (lane & 7))) & 0xfu : 0u;
+        const int c = __popc(nib);
         int incl = c;  // inclusive prefix over the wave
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
@@ -1026,16 +1200,15 @@ __global__ __launch_bounds__(kFusedWaves * 64) void lists_kernel(
           if (lane >= o) incl += y;
         }
         int pos = at + incl - c;
-        uint32_t y = x;
-        while (y) {
-          const int b = __builtin_ctz(y);
-          y &= y - 1;
-          if (pos < kt_stride) kout[pos] = (k + lane) * 32 + b;
-          ++pos;
+        const int base = wi * 32 + 4 * (lane & 7);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (((nib >> q) & 1u) && pos < kt_stride) kout[pos] = base + q;
+          pos += (nib >> q) & 1u;
         }
         at += __shfl(incl, 63);
       }
-      if (lane == 0) kt_cnt[(int64_t)seg * n_tiles + t0 + i] = min(at, kt_stride);
+      if (lane == 0) kt_cnt[(int64_t)seg * n_tiles + t0 + t] = min(at, kt_stride);
     }
   }
 }
@@ -1318,14 +1491,15 @@ static int64_t ckpt_every(int64_t Sk) {
 static int64_t ckpt_words(int64_t Sk) { return (((Sk + 31) >> 5) + 3) & ~int64_t(3); }
 
 size_t dma_topk_ws_bytes(int64_t BH, int64_t Sq, int64_t Sk, int64_t w) {
-  // two key buffers (ping-pong merges), ranks, the candidate lists, then the
-  // eviction checkpoints
+  // two key buffers (ping-pong merges), ranks, the candidate lists, the
+  // eviction checkpoints, then the largest delta code per 64-key block
   const size_t n = (size_t)BH * (size_t)Sk;
   const size_t ns = (size_t)BH * (size_t)n_super_of(Sq);
   const size_t nck = (size_t)BH * (size_t)((Sk + ckpt_every(Sk) - 1) / ckpt_every(Sk));
   return n * 2 * sizeof(uint64_t) + (size_t)BH * rank_stride(Sk) * sizeof(int32_t) +
          ns * (size_t)cand_cap(Sk, w) * 8 + ns * sizeof(int32_t) +
-         nck * (size_t)ckpt_words(Sk) * sizeof(uint32_t) + 256;
+         nck * (size_t)ckpt_words(Sk) * sizeof(uint32_t) +
+         (size_t)BH * (size_t)((Sk + 63) / 64) * sizeof(uint32_t) + 256;
 }
 
 // Scratch for callers that cannot allocate (dma_topk_mask_noalloc): the
@@ -1361,20 +1535,6 @@ hipError_t dma_launch_topk_prefill(const DmaTopkArgs& a, hipStream_t st) {
   uint64_t* kA = static_cast<uint64_t*>(a.ws);
   uint64_t* kB = kA + n;
   int32_t* rank = reinterpret_cast<int32_t*>(kB + n);
-
-  // up to kRankRunsMax small runs: ranks by binary search; beyond that,
-  // large runs and merges
-  const bool by_search = Sk > kSortChunkSmall && Sk <= kRankRunsMax * kSortChunkSmall;
-  const int chunk = by_search || Sk <= kSortChunkSmall ? kSortChunkSmall : kSortChunkLarge;
-  const int nch = (Sk + chunk - 1) / chunk;
-  if (chunk == kSortChunkSmall)
-    hipLaunchKernelGGL(sort_chunk_kernel<kSortChunkSmall>, dim3(nch, BH),
-                       dim3(kSortChunkSmall / kSortPer), 0, st, a.delta, Sk, kA);
-  else
-    hipLaunchKernelGGL(sort_chunk_kernel<kSortChunkLarge>, dim3(nch, BH),
-                       dim3(kSortChunkLarge / kSortPer), 0, st, a.delta, Sk, kA);
-  uint64_t* src = kA;
-  uint64_t* dst = kB;
   const int rs = (int)rank_stride(Sk);
   const int n_super = (int)n_super_of(a.Sq);
   const int cap = (int)cand_cap(a.Sk, a.w);
@@ -1386,6 +1546,21 @@ hipError_t dma_launch_topk_prefill(const DmaTopkArgs& a, hipStream_t st) {
   const int n_chk = (Sk + chk - 1) / chk;
   const int nwr = (int)ckpt_words(Sk);
   const size_t bm_bytes = (size_t)nwr * sizeof(uint32_t);
+  uint32_t* blk = ckpt + (size_t)BH * n_chk * nwr;
+
+  // up to kRankRunsMax small runs: ranks by binary search; beyond that,
+  // large runs and merges
+  const bool by_search = Sk > kSortChunkSmall && Sk <= kRankRunsMax * kSortChunkSmall;
+  const int chunk = by_search || Sk <= kSortChunkSmall ? kSortChunkSmall : kSortChunkLarge;
+  const int nch = (Sk + chunk - 1) / chunk;
+  if (chunk == kSortChunkSmall)
+    hipLaunchKernelGGL(sort_chunk_kernel<kSortChunkSmall>, dim3(nch, BH),
+                       dim3(kSortChunkSmall / kSortPer), 0, st, a.delta, Sk, kA, blk);
+  else
+    hipLaunchKernelGGL(sort_chunk_kernel<kSortChunkLarge>, dim3(nch, BH),
+                       dim3(kSortChunkLarge / kSortPer), 0, st, a.delta, Sk, kA, blk);
+  uint64_t* src = kA;
+  uint64_t* dst = kB;
   if (by_search) {
     const dim3 grid(nch * (kSortChunkSmall / kRankRunsKeys), BH);
     auto launch = [&](auto kern, int nr) {
@@ -1409,20 +1584,32 @@ hipError_t dma_launch_topk_prefill(const DmaTopkArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(rank_kernel, dim3((Sk + 255) / 256, BH), dim3(256), 0, st, src, Sk, rs,
                        rank);
   }
+  // eviction rows: 256-rank workgroups up to 16384 keys (checkpoints every
+  // 256 ranks: the base bitmap is one checkpoint; per wave a bitmap and its
+  // word prefixes in LDS), else 64-rank workgroups
+  const size_t wg_lds = (size_t)(1 + 2 * kEvictWG) * bm_bytes + (size_t)kEvictRanks * sizeof(int);
   if (n_chk > 1)
     hipLaunchKernelGGL(ckpt_kernel, dim3((nwr * 32 + 255) / 256, BH), dim3(256), 0, st, rank, Sk,
                        rs, chk, n_chk, nwr, ckpt);
-  const size_t ev_lds = bm_bytes + (8 + 64) * sizeof(int);  // bitmap, s_w[8], s_m[64]
-  (void)dma_func_max_lds(reinterpret_cast<const void*>(&evict_kernel), ev_lds);
-  hipLaunchKernelGGL(evict_kernel, dim3((Sk + kEvictR - 1) / kEvictR, BH), dim3(kEvictThreads),
-                     ev_lds, st, src, Sk, (int)a.w, chk, n_chk, nwr, ckpt, a.evict);
+  if (chk == kEvictRanks) {
+    (void)dma_func_max_lds(reinterpret_cast<const void*>(&evict_wg_kernel), wg_lds);
+    hipLaunchKernelGGL(evict_wg_kernel, dim3((Sk + kEvictRanks - 1) / kEvictRanks, BH),
+                       dim3(kEvictRanks), wg_lds, st, src, Sk, (int)a.w, chk, n_chk, nwr, ckpt,
+                       a.evict);
+  } else {
+    const size_t ev_lds = bm_bytes + (8 + 64) * sizeof(int);  // bitmap, s_w[8], s_m[64]
+    (void)dma_func_max_lds(reinterpret_cast<const void*>(&evict_kernel), ev_lds);
+    hipLaunchKernelGGL(evict_kernel, dim3((Sk + kEvictR - 1) / kEvictR, BH), dim3(kEvictThreads),
+                       ev_lds, st, src, Sk, (int)a.w, chk, n_chk, nwr, ckpt, a.evict);
+  }
   const int kwords = a.kt_idx ? (int)((a.kt_stride + 31) / 32) : 0;
   if (kwords > kMaxKtWords) return hipErrorInvalidValue;
   if (cap <= kFusedCap) {
-    const size_t lds = (size_t)2 * cap * sizeof(int32_t) + (size_t)kSuperTiles * kwords * 4;
+    const size_t lds = (size_t)2 * (cap + 64) * sizeof(int32_t) +
+                       (size_t)kSuperTiles * kwords * sizeof(uint32_t);
     (void)dma_func_max_lds(reinterpret_cast<const void*>(&lists_kernel), lds);
     hipLaunchKernelGGL(lists_kernel, dim3(n_super, BH), dim3(kFusedWaves * 64), lds, st, a.delta,
-                       a.evict, Sk, (int)a.Sq, (int)a.q0, n_super, (int)a.n_tiles, cap,
+                       blk, a.evict, Sk, (int)a.Sq, (int)a.q0, n_super, (int)a.n_tiles, cap,
                        (int)a.u_stride, (int)a.kt_stride, a.u_idx, a.u_cnt, a.u_nfull, a.u_dmax,
                        a.u_dlo, a.kt_idx, a.kt_cnt);
     return hipGetLastError();
