@@ -30,6 +30,7 @@
 // 32-bit codes and compacts the kept keys in index order.
 #include "../../include/dma.h"
 #include "common.h"
+#include "lds_dma.h"
 
 #include <algorithm>
 #include <climits>
@@ -102,10 +103,13 @@ __device__ __forceinline__ uint64_t lane_xor64(uint64_t v, int lm) {
 // through LDS (two buffers, one barrier each).  Every element is updated by
 // its owner, which takes the larger or the smaller of itself and its partner.
 // It also writes, per 64-key block of indices, the largest delta code (0 for
-// none) for the tile lists' largest deltas.
-template <int CHUNK>
+// none) for the tile lists' largest deltas.  SOA: the sorted chunks go out as
+// 32-bit codes and the low 16 bits of the reversed indices, rows of cstride
+// (a multiple of 8) entries, zero past Sk; otherwise as 64-bit keys.
+template <int CHUNK, bool SOA>
 __global__ __launch_bounds__(CHUNK / kSortPer) void sort_chunk_kernel(
     const float* __restrict__ delta, int Sk, uint64_t* __restrict__ out,
+    uint32_t* __restrict__ codes, uint16_t* __restrict__ revs, int cstride,
     uint32_t* __restrict__ blk_code) {
   constexpr int kBits = __builtin_ctz(CHUNK);
   static_assert((1 << kBits) == CHUNK && kBits > kSortRegBits + 6, "chunk spans waves");
@@ -173,10 +177,23 @@ __global__ __launch_bounds__(CHUNK / kSortPer) void sort_chunk_kernel(
       }
     }
   }
-  uint64_t* o = out + (int64_t)seg * Sk;
+  if (SOA) {
+    static_assert(kSortPer == 4, "one 16-byte and one 8-byte store per thread");
+    const int q = c0 + base;
+    if (q < cstride) {
+      *reinterpret_cast<uint4*>(codes + (int64_t)seg * cstride + q) =
+          make_uint4((uint32_t)(a[0] >> 32), (uint32_t)(a[1] >> 32), (uint32_t)(a[2] >> 32),
+                     (uint32_t)(a[3] >> 32));
+      *reinterpret_cast<uint2*>(revs + (int64_t)seg * cstride + q) =
+          make_uint2((a[0] & 0xffffu) | ((uint32_t)a[1] << 16),
+                     (a[2] & 0xffffu) | ((uint32_t)a[3] << 16));
+    }
+  } else {
+    uint64_t* o = out + (int64_t)seg * Sk;
 #pragma unroll
-  for (int r = 0; r < kSortPer; ++r)
-    if (c0 + base + r < Sk) o[c0 + base + r] = a[r];
+    for (int r = 0; r < kSortPer; ++r)
+      if (c0 + base + r < Sk) o[c0 + base + r] = a[r];
+  }
 }
 
 // ---------------------------------------------------------------- T1: merge
@@ -239,45 +256,61 @@ static_assert(kRankRunsMax * kSortChunkSmall <= 65536, "16-bit reversed indices"
 
 template <int NR>  // runs searched (>= the sequence's run count)
 __global__ __launch_bounds__(kRankRunsThreads) void rank_runs_kernel(
-    const uint64_t* __restrict__ runs, int Sk, int rstride, int32_t* __restrict__ rank,
-    uint64_t* __restrict__ merged) {
+    const uint32_t* __restrict__ codes, const uint16_t* __restrict__ revs, int cstride, int Sk,
+    int rstride, int32_t* __restrict__ rank, uint64_t* __restrict__ merged, int nseg) {
   constexpr int kRun = kSortChunkSmall;
   constexpr int kN = NR * kRun;
   extern __shared__ __align__(16) uint32_t s_code[];            // [kN] delta codes
   uint16_t* s_rev = reinterpret_cast<uint16_t*>(s_code + kN);  // [kN] reversed index, low 16 bits
-  const int seg = blockIdx.y;
-  const int tid = threadIdx.x;
-  const uint64_t* src = runs + (int64_t)seg * Sk;
-  // a sequence starts 8-byte aligned only (odd Sk), so 8-byte loads, all of
-  // a thread's in flight at once
-  constexpr int kFill = kN / kRankRunsThreads;
+  // workgroup i runs on XCD i % 8: with the sequence as the fast index, the
+  // workgroups of a sequence share one XCD's L2, which then holds its runs
+  const int id = blockIdx.x;
+  const int seg = id % nseg, bx = id / nseg;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int kWaves = kRankRunsThreads / 64;
   {
-    uint64_t v[kFill];
+    // the runs into LDS by direct 16-byte loads (1 KB per wave and load):
+    // codes, then reversed indices; loads past the row read its start, and
+    // those LDS words are cleared once the loads have landed
+    const uint32_t* cg = codes + (int64_t)seg * cstride;
+    const uint16_t* rg = revs + (int64_t)seg * cstride;
+    constexpr int kCodeLoads = kN * 4 / 1024 / kWaves, kRevLoads = kN * 2 / 1024 / kWaves;
+    const int uw = __builtin_amdgcn_readfirstlane(wave);  // m0 takes a scalar address
 #pragma unroll
-    for (int u = 0; u < kFill; ++u) v[u] = src[min(tid + u * kRankRunsThreads, Sk - 1)];
-#pragma unroll
-    for (int u = 0; u < kFill; ++u) {
-      const int i = tid + u * kRankRunsThreads;
-      const uint64_t k = i < Sk ? v[u] : 0ull;
-      s_code[i] = (uint32_t)(k >> 32);
-      s_rev[i] = (uint16_t)k;
+    for (int t = 0; t < kCodeLoads; ++t) {
+      const int blk = uw + kWaves * t;  // 256 codes each
+      const int g = 256 * blk + 4 * lane;
+      dma::dma_b128(cg + (g + 4 <= cstride ? g : 0), dma::lds_addr(s_code + 256 * blk));
     }
+#pragma unroll
+    for (int t = 0; t < kRevLoads; ++t) {
+      const int blk = uw + kWaves * t;  // 512 reversed indices each
+      const int g = 512 * blk + 8 * lane;
+      dma::dma_b128(rg + (g + 8 <= cstride ? g : 0), dma::lds_addr(s_rev + 512 * blk));
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int i = cstride + tid; i < kN; i += kRankRunsThreads) {
+      s_code[i] = 0u;
+      s_rev[i] = 0;
+    }
+    __syncthreads();
   }
-  __syncthreads();
 
-  const int r = blockIdx.x / (kRun / kRankRunsKeys);
-  const int q0 = r * kRun + (blockIdx.x % (kRun / kRankRunsKeys)) * kRankRunsKeys + tid;
+  const int r = bx / (kRun / kRankRunsKeys);
+  const int q0 = r * kRun + (bx % (kRun / kRankRunsKeys)) * kRankRunsKeys + tid;
   uint32_t c[kRankRunsU];
   uint16_t rv[kRankRunsU];
-  int cnt[kRankRunsU][NR];  // LDS position: run base plus the count so far
+  uint32_t off[kRankRunsU][NR];  // LDS byte offset: run base plus 4 x the count so far
 #pragma unroll
   for (int u = 0; u < kRankRunsU; ++u) {
     const int q = min(q0 + u * kRankRunsThreads, Sk - 1);
     c[u] = s_code[q];
     rv[u] = s_rev[q];
 #pragma unroll
-    for (int o = 0; o < NR; ++o) cnt[u][o] = o * kRun;
+    for (int o = 0; o < NR; ++o) off[u][o] = 4u * (uint32_t)(o * kRun);
   }
+  const char* sc = reinterpret_cast<const char*>(s_code);
   // all kRankRunsU x NR searches of a thread advance together, one halving
   // step at a time; the first kRun - 1 keys of a run, then the last one
 #pragma unroll
@@ -286,9 +319,10 @@ __global__ __launch_bounds__(kRankRunsThreads) void rank_runs_kernel(
     for (int o = 0; o < NR; ++o) {
       uint32_t v[kRankRunsU];
 #pragma unroll
-      for (int u = 0; u < kRankRunsU; ++u) v[u] = s_code[cnt[u][o] + step - 1];
+      for (int u = 0; u < kRankRunsU; ++u)
+        v[u] = *reinterpret_cast<const uint32_t*>(sc + off[u][o] + 4 * (step - 1));
 #pragma unroll
-      for (int u = 0; u < kRankRunsU; ++u) cnt[u][o] += v[u] > c[u] ? step : 0;
+      for (int u = 0; u < kRankRunsU; ++u) off[u][o] |= v[u] > c[u] ? 4u * step : 0u;
     }
   }
   uint32_t tie[kRankRunsU];  // bit o: the search stopped on a key of equal code
@@ -297,8 +331,8 @@ __global__ __launch_bounds__(kRankRunsThreads) void rank_runs_kernel(
     tie[u] = 0u;
 #pragma unroll
     for (int o = 0; o < NR; ++o) {
-      const uint32_t v = s_code[cnt[u][o]];
-      cnt[u][o] += v > c[u] ? 1 : 0;
+      const uint32_t v = *reinterpret_cast<const uint32_t*>(sc + off[u][o]);
+      off[u][o] += v > c[u] ? 4u : 0u;
       tie[u] |= (v == c[u] ? 1u : 0u) << o;
     }
   }
@@ -306,25 +340,27 @@ __global__ __launch_bounds__(kRankRunsThreads) void rank_runs_kernel(
   for (int u = 0; u < kRankRunsU; ++u) {
     int pos = 0;
 #pragma unroll
-    for (int o = 0; o < NR; ++o) pos += cnt[u][o] - o * kRun;
-    // equal codes: the keys of run o from cnt on with that code and a lower
-    // index (larger reversed index) also beat the key
+    for (int o = 0; o < NR; ++o) pos += (int)(off[u][o] >> 2) - o * kRun;
+    // equal codes: the keys of run o from the count on with that code and a
+    // lower index (larger reversed index) also beat the key
     for (uint32_t t = tie[u]; t; t &= t - 1u) {
       const int o = __builtin_ctz(t);
       const int n_o = min(kRun, Sk - o * kRun);
-      int lo = cnt[u][o], hi = o * kRun + n_o;  // first position that does not beat
+      const int c0 = (int)(off[u][o] >> 2);
+      int lo = c0, hi = o * kRun + n_o;  // first position that does not beat
       while (lo < hi) {
         const int mid = (lo + hi) >> 1;
         if (s_code[mid] == c[u] && s_rev[mid] > rv[u]) lo = mid + 1;
         else hi = mid;
       }
-      pos += lo - cnt[u][o];
+      pos += lo - c0;
     }
     const int q = q0 + u * kRankRunsThreads;
     if (q < Sk) {
-      const uint64_t x = src[q];
-      rank[(int64_t)seg * rstride + dma::index_of(x)] = pos;
-      merged[(int64_t)seg * Sk + pos] = x;
+      // the key itself, rebuilt from its code and index (which fits 16 bits)
+      const uint32_t j = 0xffffu - (uint32_t)rv[u];
+      rank[(int64_t)seg * rstride + j] = pos;
+      merged[(int64_t)seg * Sk + pos] = ((uint64_t)c[u] << 32) | (uint64_t)(0xffffffffu - j);
     }
   }
 }
@@ -1553,20 +1589,33 @@ hipError_t dma_launch_topk_prefill(const DmaTopkArgs& a, hipStream_t st) {
   const bool by_search = Sk > kSortChunkSmall && Sk <= kRankRunsMax * kSortChunkSmall;
   const int chunk = by_search || Sk <= kSortChunkSmall ? kSortChunkSmall : kSortChunkLarge;
   const int nch = (Sk + chunk - 1) / chunk;
-  if (chunk == kSortChunkSmall)
-    hipLaunchKernelGGL(sort_chunk_kernel<kSortChunkSmall>, dim3(nch, BH),
-                       dim3(kSortChunkSmall / kSortPer), 0, st, a.delta, Sk, kA, blk);
+  // runs for the binary searches: codes and reversed-index bits, rows of
+  // cstride entries, in the first key buffer
+  const int cstride = (Sk + 7) & ~7;
+  uint32_t* rcodes = reinterpret_cast<uint32_t*>(kA);
+  uint16_t* rrevs = reinterpret_cast<uint16_t*>(rcodes + (size_t)BH * cstride);
+  if (by_search)
+    hipLaunchKernelGGL((sort_chunk_kernel<kSortChunkSmall, true>), dim3(nch, BH),
+                       dim3(kSortChunkSmall / kSortPer), 0, st, a.delta, Sk, kA, rcodes, rrevs,
+                       cstride, blk);
+  else if (chunk == kSortChunkSmall)
+    hipLaunchKernelGGL((sort_chunk_kernel<kSortChunkSmall, false>), dim3(nch, BH),
+                       dim3(kSortChunkSmall / kSortPer), 0, st, a.delta, Sk, kA, rcodes, rrevs,
+                       cstride, blk);
   else
-    hipLaunchKernelGGL(sort_chunk_kernel<kSortChunkLarge>, dim3(nch, BH),
-                       dim3(kSortChunkLarge / kSortPer), 0, st, a.delta, Sk, kA, blk);
+    hipLaunchKernelGGL((sort_chunk_kernel<kSortChunkLarge, false>), dim3(nch, BH),
+                       dim3(kSortChunkLarge / kSortPer), 0, st, a.delta, Sk, kA, rcodes, rrevs,
+                       cstride, blk);
   uint64_t* src = kA;
   uint64_t* dst = kB;
   if (by_search) {
-    const dim3 grid(nch * (kSortChunkSmall / kRankRunsKeys), BH);
+    // one dimension, sequence fastest
+    const dim3 grid(nch * (kSortChunkSmall / kRankRunsKeys) * BH);
     auto launch = [&](auto kern, int nr) {
       const size_t lds = (size_t)nr * kSortChunkSmall * (sizeof(uint32_t) + sizeof(uint16_t));
       (void)dma_func_max_lds(reinterpret_cast<const void*>(kern), lds);
-      hipLaunchKernelGGL(kern, grid, dim3(kRankRunsThreads), lds, st, src, Sk, rs, rank, dst);
+      hipLaunchKernelGGL(kern, grid, dim3(kRankRunsThreads), lds, st, rcodes, rrevs, cstride, Sk,
+                         rs, rank, dst, (int)BH);
     };
     if (nch <= 4) launch(rank_runs_kernel<4>, 4);
     else if (nch <= 8) launch(rank_runs_kernel<8>, 8);
