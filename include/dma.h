@@ -183,7 +183,7 @@ dma_status dma_topk_mask_noalloc(const float* delta, int64_t B, int64_t Hkv, int
  *        identical to what dma_topk_mask(delta, B, Hkv, 1, Sk, Sk-1, w) writes.
  *        u_idx [B*Hkv, w], u_cnt, u_nfull, u_dmax [B*Hkv]; kt_idx and kt_cnt
  *        must be NULL (key-tile lists are not maintained).
- * Requires Sk-1 >= w (the list is full, stride w) and Sk <= 32768; sequences
+ * Requires Sk-1 >= w (the list is full, stride w) and w <= 32768; sequences
  * whose list does not hold w keys are left unchanged.  Updated in place on
  * the stream; O(w) work per sequence instead of a selection over all Sk keys.
  */

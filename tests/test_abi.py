@@ -63,7 +63,7 @@ def test_mask_dims(lib):
     assert _dims(lib, 1, 1, 10, 10, 0, 0)[0] == INVALID    # w < 1
     assert _dims(lib, 1, 0, 10, 10, 0, 3)[0] == INVALID    # no heads
     assert _dims(lib, 1, 1, 2, (1 << 20) + 1, 0, 3)[0] == UNSUPPORTED
-    assert _dims(lib, 1, 1, 1, 40000, 39999, 3)[0] == UNSUPPORTED  # decode row past 32768 keys
+    assert _dims(lib, 1, 1, 1, 40000, 39999, 3)[0] == OK  # decode rows of any length
     assert _dims(lib, 70000, 1, 2, 2, 0, 1)[0] == UNSUPPORTED
 
 
@@ -133,7 +133,7 @@ def test_decode_append_validation(lib):
     assert _append(lib, kt=True) == INVALID                  # key-tile lists are not kept
     assert _append(lib, mask=False) == INVALID
     assert _append(lib, delta=None) == INVALID
-    assert _append(lib, Sk=40000, w=16) == UNSUPPORTED       # beyond the one-row limit
+    assert _append(lib, Sk=70000, w=40000) == UNSUPPORTED    # a list larger than LDS holds
     assert _append(lib, B=0) == OK                           # empty: nothing launched
 
 

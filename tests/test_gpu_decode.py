@@ -24,7 +24,8 @@ def _decode(x, wl):
 @pytest.mark.parametrize("B,Hq,Hkv,Sk,w,dtype,D", [
     (2, 8, 2, 300, 37, "bf16", 128), (3, 4, 4, 1000, 1000, "bf16", 128),
     (1, 16, 2, 5000, 700, "bf16", 128), (2, 4, 2, 600, 257, "f32", 64),
-    (1, 8, 8, 100, 1, "bf16", 64), (1, 2, 1, 1, 5, "f32", 128)])
+    (1, 8, 8, 100, 1, "bf16", 64), (1, 2, 1, 1, 5, "f32", 128),
+    (1, 8, 2, 50000, 2048, "bf16", 128)])  # a cache past 32768 keys
 def test_decode_small(gpu_lib, B, Hq, Hkv, Sk, w, dtype, D):
     wl, x = make_small(B, Hq, Hkv, 1, Sk, D, w, dtype=dtype, q_offset=Sk - 1, seed=Sk + w,
                        device="cuda")

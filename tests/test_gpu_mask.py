@@ -118,6 +118,20 @@ def test_decode_select(gpu_lib, kind, p, w):
     check_mask(gm, d)
 
 
+@pytest.mark.parametrize("kind", ["random", "ties", "allequal", "signed_zeros"])
+@pytest.mark.parametrize("p,w", [(32768, 2048), (40000, 1), (40000, 5000), (70000, 2048),
+                                 (131071, 40000)])
+def test_decode_select_long_rows(gpu_lib, kind, p, w):
+    # rows past 32768 keys take the radix-pass selection; ties and equal
+    # weights exercise its equal-code handling, the last case a list larger
+    # than one key tile per thread
+    Sk = p + 1 + 5
+    d = _delta(kind, 2, 2, Sk, seed=p + w)
+    gm = dma.topk_mask(d, 1, p, w)
+    torch.cuda.synchronize()
+    check_mask(gm, d)
+
+
 def test_decode_workload(gpu_lib):
     wl = WORKLOADS["decode_32k"]
     x = make_inputs(wl, device="cuda")

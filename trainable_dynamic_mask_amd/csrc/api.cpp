@@ -30,7 +30,6 @@ dma_status check_mask_shape(int64_t B, int64_t Hkv, int64_t Sq, int64_t Sk, int6
   if (B < 0 || Hkv < 1 || Sq < 0 || Sk < 0 || q0 < 0 || w < 1) return DMA_ERR_INVALID_ARG;
   if (q0 + Sq > Sk) return DMA_ERR_INVALID_ARG;
   if (Sk > DMA_MAX_SK) return DMA_ERR_UNSUPPORTED;
-  if (Sq == 1 && q0 + 1 > 32768) return DMA_ERR_UNSUPPORTED;  // one-row select keeps keys in registers
   if (B * Hkv > 65535) return DMA_ERR_UNSUPPORTED;  // (batch, kv head) is a grid dimension
   return DMA_OK;
 }
@@ -187,7 +186,7 @@ dma_status dma_decode_keep_append(const float* delta, int64_t B, int64_t Hkv, in
   if (B < 0 || Hkv < 1 || w < 1 || Sk < 0) return DMA_ERR_INVALID_ARG;
   if (!mask) return DMA_ERR_INVALID_ARG;
   if (Sk - 1 < w) return DMA_ERR_INVALID_ARG;  // keep(Sk-2) must hold w keys
-  if (Sk > 32768) return DMA_ERR_UNSUPPORTED;    // the one-row limit of dma_topk_mask
+  if (w > 32768) return DMA_ERR_UNSUPPORTED;     // the list is staged in LDS
   if (B * Hkv > 65535) return DMA_ERR_UNSUPPORTED;
   if (mask->kt_idx || mask->kt_cnt) return DMA_ERR_INVALID_ARG;  // key-tile lists are not kept
   if (B == 0) return DMA_OK;

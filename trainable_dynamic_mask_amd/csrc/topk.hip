@@ -1430,6 +1430,180 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_select_kernel(
   }
 }
 
+// One row with more keys than decode_select_kernel holds in registers (the
+// same selection: the w best of keys 0..p, ties to the lower index).  One
+// workgroup of 1024 threads per sequence.  The threshold T, the w-th largest
+// code, comes from four 8-bit radix passes over delta: each pass builds the
+// histogram of the next digit among the keys whose leading digits match T's
+// so far (per-wave LDS histograms; a wave whose matching lanes share one
+// digit adds their count once), and a suffix scan picks the digit where the
+// count of larger keys reaches w.  The output then takes the keys in index
+// order in contiguous per-thread ranges of whole 64-key tiles: one pass
+// counts the keys above T and equal to T per range, block scans give each
+// range its share of the equal keys (lowest indices first) and its output
+// offset, and a second pass writes the kept keys and the touched key tiles.
+constexpr int kDecLThreads = 1024;
+constexpr int kDecLWaves = kDecLThreads / 64;
+
+// Exclusive prefix sum of v over the 1024 threads (two barriers); total out.
+__device__ __forceinline__ int dec_block_scan(int v, int* s_w, int& total) {
+  return block_excl_scan<kDecLThreads>(v, s_w, total);
+}
+
+__global__ __launch_bounds__(kDecLThreads) void decode_select_large_kernel(
+    const float* __restrict__ delta, int Sk, int p, int w, int u_stride, int kt_stride,
+    int32_t* __restrict__ u_idx, int32_t* __restrict__ u_cnt, int32_t* __restrict__ u_nfull,
+    float* __restrict__ u_dmax, int32_t* __restrict__ kt_idx, int32_t* __restrict__ kt_cnt) {
+  __shared__ uint32_t s_hist[kDecLWaves][256];
+  __shared__ int s_suf[257];
+  __shared__ int s_w[kDecLWaves];
+  __shared__ int s_sel[2];
+  __shared__ float s_m[kDecLWaves];
+  const int seg = blockIdx.x;
+  const int n = p + 1;
+  const float* Dl = delta + (int64_t)seg * Sk;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  uint32_t prefix = 0u, dmask = 0u;
+  int above = 0;  // keys whose code exceeds every code with T's leading digits
+  float mx = -INFINITY;
+  const bool all = n <= w;
+  for (int pass = 0; pass < 4 && !all; ++pass) {
+    const int shift = 24 - 8 * pass;
+    for (int k = lane; k < 256; k += 64) s_hist[wave][k] = 0u;
+    __syncthreads();
+    for (int j0 = 0; j0 < n; j0 += kDecLThreads) {
+      const int j = j0 + tid;
+      const float v = j < n ? Dl[j] : 0.f;
+      if (pass == 0 && j < n) mx = fmaxf(mx, v);
+      const uint32_t c = dma::ord32(v);
+      const bool m = j < n && (c & dmask) == prefix;
+      const uint32_t dg = (c >> shift) & 255u;
+      const uint64_t bm = dma::ballot(m);
+      if (bm) {
+        const int first = __builtin_ctzll(bm);
+        const uint32_t d0 = (uint32_t)__shfl((int)dg, first);
+        if (dma::ballot(m && dg == d0) == bm) {  // one digit for the whole wave
+          if (lane == first) atomicAdd(&s_hist[wave][d0], (uint32_t)__popcll(bm));
+        } else if (m) {
+          atomicAdd(&s_hist[wave][dg], 1u);
+        }
+      }
+    }
+    __syncthreads();
+    // suffix sums over the digits: s_suf[d] = keys with digit >= d
+    if (tid < 256) {
+      uint32_t t = 0u;
+      for (int k = 0; k < kDecLWaves; ++k) t += s_hist[k][tid];
+      s_suf[tid] = (int)t;
+    }
+    if (tid == 256) s_suf[256] = 0;
+    __syncthreads();
+    if (wave == 0) {
+      // lane l: digits 4l..4l+3, then a suffix scan over the lanes
+      int v4[4], tsum = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v4[q] = s_suf[4 * lane + q];
+        tsum += v4[q];
+      }
+      int incl = tsum;  // inclusive suffix over lanes l..63
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_down(incl, o);
+        if (lane + o < 64) incl += y;
+      }
+      int suf = incl - tsum;  // keys in digits above 4l+3
+#pragma unroll
+      for (int q = 3; q >= 0; --q) {
+        const int hi = suf;  // digits above 4l+q
+        suf += v4[q];
+        if (above + suf >= w && above + hi < w) {
+          s_sel[0] = 4 * lane + q;
+          s_sel[1] = above + hi;
+        }
+      }
+    }
+    __syncthreads();
+    prefix |= (uint32_t)s_sel[0] << shift;
+    dmask |= 255u << shift;
+    above = s_sel[1];
+    __syncthreads();  // s_sel and the histograms are rewritten next pass
+  }
+  if (all) {
+    for (int j0 = 0; j0 < n; j0 += kDecLThreads)
+      if (j0 + tid < n) mx = fmaxf(mx, Dl[j0 + tid]);
+  }
+  const uint32_t T = prefix;
+  const int need_eq = all ? 0 : w - above;  // keys equal to T that are kept, lowest index first
+
+  // ranges of whole 64-key tiles, one per thread
+  const int ntile = (n + 63) >> 6;
+  const int tper = (ntile + kDecLThreads - 1) / kDecLThreads;
+  const int k_lo = min(n, tid * tper * 64), k_hi = min(n, k_lo + tper * 64);
+  int ng = 0, ne = 0;
+  for (int j = k_lo; j < k_hi; ++j) {
+    const uint32_t c = dma::ord32(Dl[j]);
+    ng += (all || c > T) ? 1 : 0;
+    ne += (!all && c == T) ? 1 : 0;
+  }
+  int tot;
+  const int eb = dec_block_scan(ne, s_w, tot);  // equal keys before this range
+  const int take = min(ne, max(0, need_eq - eb));
+  int pos = dec_block_scan(ng + take, s_w, tot);
+  int32_t* out = u_idx + (int64_t)seg * u_stride;
+  int kt_here = 0;
+  {
+    int eq_left = take;
+    int last_tile = -1;
+    for (int j = k_lo; j < k_hi; ++j) {
+      const uint32_t c = dma::ord32(Dl[j]);
+      bool kept = all || c > T;
+      if (!kept && c == T && eq_left > 0) {
+        kept = true;
+        --eq_left;
+      }
+      if (kept) {
+        if (pos < u_stride) out[pos] = j;
+        ++pos;
+        if ((j >> 6) != last_tile) {
+          last_tile = j >> 6;
+          ++kt_here;
+        }
+      }
+    }
+  }
+  int ktot;
+  int kpos = dec_block_scan(kt_here, s_w, ktot);
+  if (kt_idx && kt_here) {
+    int last_tile = -1, eq_left = take;
+    for (int j = k_lo; j < k_hi; ++j) {
+      const uint32_t c = dma::ord32(Dl[j]);
+      bool kept = all || c > T;
+      if (!kept && c == T && eq_left > 0) {
+        kept = true;
+        --eq_left;
+      }
+      if (kept && (j >> 6) != last_tile) {
+        last_tile = j >> 6;
+        if (kpos < kt_stride) kt_idx[(int64_t)seg * kt_stride + kpos] = last_tile;
+        ++kpos;
+      }
+    }
+  }
+  mx = dma::wave_max(mx);
+  if (lane == 0) s_m[wave] = mx;
+  __syncthreads();
+  if (tid == 0) {
+    float m = s_m[0];
+    for (int k = 1; k < kDecLWaves; ++k) m = fmaxf(m, s_m[k]);
+    u_cnt[seg] = min(tot, u_stride);
+    u_nfull[seg] = min(tot, u_stride);
+    u_dmax[seg] = m;
+    if (kt_idx) kt_cnt[seg] = min(ktot, kt_stride);
+  }
+}
+
 // One decode step of the keep set (Hugging Face blog "Trainable Dynamic Mask
 // Sparse Attention", section "Mask Combination with Causal Constraints": the
 // keep set of position p is the top w of keys 0..p).  Because the sets nest,
@@ -1705,8 +1879,13 @@ hipError_t dma_launch_decode_append(const float* delta, int64_t BH, int64_t Sk, 
 
 hipError_t dma_launch_topk_decode(const DmaTopkArgs& a, hipStream_t st) {
   const int64_t BH = a.B * a.Hkv;
-  hipLaunchKernelGGL(decode_select_kernel, dim3(BH), dim3(kDecThreads), 0, st, a.delta, (int)a.Sk,
-                     (int)a.q0, (int)a.w, (int)a.u_stride, (int)a.kt_stride, a.u_idx, a.u_cnt,
-                     a.u_nfull, a.u_dmax, a.kt_idx, a.kt_cnt);
+  if (a.q0 + 1 <= kDecThreads * kDecKPT)
+    hipLaunchKernelGGL(decode_select_kernel, dim3(BH), dim3(kDecThreads), 0, st, a.delta,
+                       (int)a.Sk, (int)a.q0, (int)a.w, (int)a.u_stride, (int)a.kt_stride, a.u_idx,
+                       a.u_cnt, a.u_nfull, a.u_dmax, a.kt_idx, a.kt_cnt);
+  else
+    hipLaunchKernelGGL(decode_select_large_kernel, dim3(BH), dim3(kDecLThreads), 0, st, a.delta,
+                       (int)a.Sk, (int)a.q0, (int)a.w, (int)a.u_stride, (int)a.kt_stride, a.u_idx,
+                       a.u_cnt, a.u_nfull, a.u_dmax, a.kt_idx, a.kt_cnt);
   return hipGetLastError();
 }
