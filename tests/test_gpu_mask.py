@@ -28,6 +28,16 @@ def _delta(kind, B, H, S, seed):
     elif kind == "signed_zeros":  # -0 and +0 are equal: they tie, the lower index wins
         vals = torch.tensor([-0.0, 0.0, -0.0, 0.0, -1.0, 1.0])
         d = vals[torch.randint(0, 6, (B, H, S), generator=g)]
+    elif kind == "periodic":  # depends on j mod 512 only: a spaced sample sees few values
+        d = ((torch.arange(S) * 37) % 512 + 1).float().expand(B, H, S).contiguous()
+    elif kind == "clusters":  # two far-apart groups with a spread inside each
+        hi = torch.rand(B, H, S, generator=g) < 0.5
+        d = torch.exp(torch.randn(B, H, S, generator=g)) * torch.where(hi, 1e3, 1e-3)
+    elif kind == "narrow":  # every weight within a few hundred ulps of 1
+        d = 1.0 + torch.randint(0, 300, (B, H, S), generator=g).float() * 2.0 ** -23
+    elif kind == "negative":  # all below zero, some -inf
+        d = -torch.exp(torch.randn(B, H, S, generator=g))
+        d[torch.rand(B, H, S, generator=g) < 0.01] = float("-inf")
     else:
         d = torch.exp(torch.randn(B, H, S, generator=g))
     return d.cuda()
@@ -113,6 +123,21 @@ def test_mask_deterministic(gpu_lib):
 def test_decode_select(gpu_lib, kind, p, w):
     Sk = p + 1 + 3  # cache longer than the row's prefix
     d = _delta(kind, 3, 2, Sk, seed=p + w)
+    gm = dma.topk_mask(d, 1, p, w)
+    torch.cuda.synchronize()
+    check_mask(gm, d)
+
+
+@pytest.mark.parametrize("kind", ["random", "increasing", "decreasing", "periodic", "clusters",
+                                  "narrow", "negative", "ties"])
+@pytest.mark.parametrize("p,w", [(300, 100), (1000, 999), (8191, 2048), (25000, 3000),
+                                 (32767, 1), (32767, 2048), (32767, 16384), (32767, 31000)])
+def test_decode_select_bracket(gpu_lib, kind, p, w):
+    # rows of at most 32768 keys: the sampled bracket with radix passes, and
+    # the full bit search when the bracket misses (structured rows, ties,
+    # half the row kept)
+    Sk = p + 1 + 2
+    d = _delta(kind, 2, 2, Sk, seed=p * 5 + w)
     gm = dma.topk_mask(d, 1, p, w)
     torch.cuda.synchronize()
     check_mask(gm, d)

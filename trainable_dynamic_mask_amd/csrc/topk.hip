@@ -1253,28 +1253,160 @@ __global__ __launch_bounds__(kFusedWaves * 64) void lists_kernel(
 // Keys 0..p of one sequence; keeps the w best (Hugging Face blog "Trainable
 // Dynamic Mask Sparse Attention", section "Mask Combination with Causal
 // Constraints": the top w of the causally visible keys by delta, ties to the
-// lower index).  Thread t holds the codes of
-// keys k*512 + t (coalesced loads, 64 registers).  The threshold, the largest
-// code T with #{code >= T} >= w, is found bit by bit from the top.  The
-// leading bits run over every key; the keys that can still reach the
-// threshold (code >= the partial T, a few thousand for real rows) then move
-// through LDS into 16 registers per thread for the remaining bits, unless
-// there are more than kDecCand of them (ties), when the search stays on the
-// full set.  The ordered output comes from two LDS bitmaps (code > T, and
-// code == T for the ties, kept lowest index first), one 64-key tile per
-// thread, which also gives the key-tile list.
+// lower index).  One workgroup of 512 threads per sequence; thread t holds
+// the weights of keys k*512 + t (coalesced loads, 64 registers; NaN past the
+// row, which no comparison admits).  The kept set is every key above T, the
+// w-th largest weight, plus the lowest-index keys equal to T, w keys in all.
+//
+// T comes from a bracket.  A sample of 512 keys (32 strata spread over the
+// row, 16 keys from one 128-byte line in each, loaded ahead of the row so
+// that it is processed while the row is still in flight) goes into 256 bins
+// over its own range; the bins that hold the sample ranks a margin either
+// side of the w-th largest's expected rank give bounds lo and hi.  As the
+// row arrives, each thread counts its keys above hi and parks the weights in
+// [lo, hi] in its own LDS column.  When fewer than w keys lie above hi, at
+// least w at or above lo, and no column overflowed, T is found by 8-bit radix
+// passes over the order codes of the parked weights (LDS histograms; every
+// wave scans the bins itself, so one barrier per pass).  Otherwise (a row the
+// sample misjudged, or heavy ties) the search runs bit by bit over every key:
+// the leading kDecLead bits over all of them, the rest over the keys still in
+// reach when there are at most kDecCand, else over all.
+//
+// The output is in index order: ballots turn the verdicts into one 64-bit
+// word per 64-key tile (tile k*8 + wave from register k of wave `wave`), and
+// thread t then owns tile t, which also gives the key-tile list.
 constexpr int kDecThreads = 512;
 constexpr int kDecWaves = kDecThreads / 64;
 constexpr int kDecKPT = 64;          // rows up to 32768 keys
-constexpr int kDecLead = 12;         // bits fixed over the full set
-constexpr int kDecCand = 8192;       // candidates carried to the remaining bits
+constexpr int kDecSlots = 24;        // parked bracket weights per thread
+constexpr int kDecBins = 256;
+constexpr int kDecPasses = 4;        // 8-bit radix passes cover 32 bits
+constexpr int kDecLead = 12;         // bits fixed over the full set (fallback)
+constexpr int kDecCand = 8192;       // candidates carried to the remaining bits (fallback)
 constexpr int kDecCPT = kDecCand / kDecThreads;
+static_assert(kDecSlots * kDecThreads >= kDecCand, "the fallback shares the slot array");
+static_assert(kDecSlots * kDecThreads * 4 >= 2 * kDecThreads * 8, "the bitmaps reuse the slots");
 
-// Block total of per-thread counts in [0, 128): the wave sums its counts bit
-// plane by bit plane with ballots (no cross-lane chains), one LDS slot per
-// wave, one barrier.  Callers alternate two slot sets, which makes the one
-// barrier enough: a wave cannot write a set again before every wave has
-// passed the next call's barrier, i.e. finished reading it.
+// Barrier that waits for the wave's LDS accesses only: loads of the row that
+// are still in flight stay in flight.  The empty asm statements keep the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void dec_lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // lgkmcnt(0) only
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Order code of a non-NaN float, a bijection onto [0x00800000, 0xff800000]
+// with -0 and +0 one value: positive values map to u | 2^31, negative ones to
+// -u (mod 2^32); 0 stays free for keys past the row.
+__device__ __forceinline__ uint32_t dec_code(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u)) + (u >> 31);
+}
+constexpr uint32_t kCodeNegInf = 0x00800000u, kCodePosInf = 0xff800000u;
+// the float of a code; codes below -inf's give -inf, above +inf's NaN (which
+// no weight reaches)
+__device__ __forceinline__ float dec_value(uint32_t c) {
+  if (c <= kCodeNegInf) return -INFINITY;
+  return __uint_as_float(c >= 0x80000000u ? c & 0x7fffffffu : 0u - c);
+}
+
+// DPP row shift right by S lanes inside 16-lane rows; lanes with no source
+// get `fill`.
+template <int S>
+__device__ __forceinline__ int dec_shr(int x, int fill) {
+  return __builtin_amdgcn_update_dpp(fill, x, 0x110 + S, 0xf, 0xf, false);
+}
+// Inclusive prefix sum over the wave: within rows by DPP shifts, then the
+// row totals by readlane.
+__device__ __forceinline__ int dec_wave_scan(int x) {
+  x += dec_shr<1>(x, 0);
+  x += dec_shr<2>(x, 0);
+  x += dec_shr<4>(x, 0);
+  x += dec_shr<8>(x, 0);
+  const int t0 = __builtin_amdgcn_readlane(x, 15), t1 = __builtin_amdgcn_readlane(x, 31),
+            t2 = __builtin_amdgcn_readlane(x, 47);
+  const int row = (int)(threadIdx.x & 63) >> 4;
+  return x + (row == 0 ? 0 : row == 1 ? t0 : row == 2 ? t0 + t1 : t0 + t1 + t2);
+}
+__device__ __forceinline__ uint32_t dec_wave_max(uint32_t x) {
+  x = max(x, (uint32_t)dec_shr<1>((int)x, (int)x));
+  x = max(x, (uint32_t)dec_shr<2>((int)x, (int)x));
+  x = max(x, (uint32_t)dec_shr<4>((int)x, (int)x));
+  x = max(x, (uint32_t)dec_shr<8>((int)x, (int)x));
+  return max(max((uint32_t)__builtin_amdgcn_readlane((int)x, 15),
+                 (uint32_t)__builtin_amdgcn_readlane((int)x, 31)),
+             max((uint32_t)__builtin_amdgcn_readlane((int)x, 47),
+                 (uint32_t)__builtin_amdgcn_readlane((int)x, 63)));
+}
+__device__ __forceinline__ uint32_t dec_wave_min(uint32_t x) {
+  x = min(x, (uint32_t)dec_shr<1>((int)x, (int)x));
+  x = min(x, (uint32_t)dec_shr<2>((int)x, (int)x));
+  x = min(x, (uint32_t)dec_shr<4>((int)x, (int)x));
+  x = min(x, (uint32_t)dec_shr<8>((int)x, (int)x));
+  return min(min((uint32_t)__builtin_amdgcn_readlane((int)x, 15),
+                 (uint32_t)__builtin_amdgcn_readlane((int)x, 31)),
+             min((uint32_t)__builtin_amdgcn_readlane((int)x, 47),
+                 (uint32_t)__builtin_amdgcn_readlane((int)x, 63)));
+}
+
+// Exclusive prefix sum over the 512 threads, total out; one barrier, so each
+// call site needs its own s_w.
+__device__ __forceinline__ int dec_scan512(int v, int* s_w, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int incl = dec_wave_scan(v);
+  if (lane == 63) s_w[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  total = 0;
+#pragma unroll
+  for (int k = 0; k < kDecWaves; ++k) {
+    const int t = s_w[k];
+    if (k < wave) before += t;
+    total += t;
+  }
+  return before + incl - v;
+}
+
+// Bins of an LDS histogram, larger values in higher bins: the bin b holding
+// descending rank r (0-based), i.e. above(b) <= r < above(b) + h[b], where
+// above(b) counts the entries of the bins past b.  Every wave computes it on
+// its own from the same bins (lane l takes bins 252-4l .. 255-4l).  Returns
+// -1 when r is past the total.
+__device__ __forceinline__ int dec_find_bin(const uint32_t* hist, int r, int& above, int& inbin) {
+  const int lane = threadIdx.x & 63;
+  const uint4 h = reinterpret_cast<const uint4*>(hist)[63 - lane];
+  const int s4 = (int)(h.x + h.y + h.z + h.w);
+  int a = dec_wave_scan(s4) - s4;  // entries in the bins above this lane's
+  int b = -1, ab = 0, hb = 0;
+  const int hv[4] = {(int)h.w, (int)h.z, (int)h.y, (int)h.x};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (a <= r && r < a + hv[i]) {
+      b = 255 - 4 * lane - i;
+      ab = a;
+      hb = hv[i];
+    }
+    a += hv[i];
+  }
+  const uint64_t m = dma::ballot(b >= 0);
+  if (m == 0ull) {
+    above = 0;
+    inbin = 0;
+    return -1;
+  }
+  const int src = __builtin_ctzll(m);
+  above = __builtin_amdgcn_readlane(ab, src);
+  inbin = __builtin_amdgcn_readlane(hb, src);
+  return __builtin_amdgcn_readlane(b, src);
+}
+
+// Block total of per-thread counts in [0, 128) (fallback search): the wave
+// sums its counts bit plane by bit plane with ballots (no cross-lane chains),
+// one LDS slot per wave, one barrier.  Callers alternate two slot sets, which
+// makes the one barrier enough: a wave cannot write a set again before every
+// wave has passed the next call's barrier, i.e. finished reading it.
 __device__ __forceinline__ int dec_block_count(int c, int* s_slots) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int tw = 0;
@@ -1288,18 +1420,24 @@ __device__ __forceinline__ int dec_block_count(int c, int* s_slots) {
   return tot;
 }
 
-// One bit per round, hi down to lo: T | bit is taken when at least w codes
-// reach it.  Padding codes are 0 and never reach a candidate (all >= 1).
+// One bit per round, hi down to lo: T | bit is taken when at least w keys
+// reach it.  Over codes (0 for no key, below every candidate) or over the
+// weights themselves (compared with the candidate's float; NaN past the row).
 // cge tracks #{code >= T}.
-template <int K>
-__device__ __forceinline__ uint32_t dec_bit_search(const uint32_t (&x)[K], uint32_t T, int hi,
-                                                   int lo, int w, int* s_cnt, int& round,
-                                                   int& cge) {
+__device__ __forceinline__ bool dec_reaches(uint32_t x, uint32_t cand, float) { return x >= cand; }
+__device__ __forceinline__ bool dec_reaches(float x, uint32_t, float fc) { return x >= fc; }
+__device__ __forceinline__ bool dec_above(uint32_t x, uint32_t T, float) { return x > T; }
+__device__ __forceinline__ bool dec_above(float x, uint32_t, float fT) { return x > fT; }
+
+template <typename X, int K>
+__device__ __forceinline__ uint32_t dec_bit_search(const X (&x)[K], uint32_t T, int hi, int lo,
+                                                   int w, int* s_cnt, int& round, int& cge) {
   for (int bit = hi; bit >= lo; --bit) {
     const uint32_t cand = T | (1u << bit);
+    const float fc = dec_value(cand);
     int c = 0;
 #pragma unroll
-    for (int k = 0; k < K; ++k) c += x[k] >= cand ? 1 : 0;
+    for (int k = 0; k < K; ++k) c += dec_reaches(x[k], cand, fc) ? 1 : 0;
     const int tot = dec_block_count(c, s_cnt + (round & 1) * kDecWaves);
     ++round;
     if (tot >= w) {
@@ -1310,105 +1448,269 @@ __device__ __forceinline__ uint32_t dec_bit_search(const uint32_t (&x)[K], uint3
   return T;
 }
 
-template <int K>
-__device__ __forceinline__ int dec_count_above(const uint32_t (&x)[K], uint32_t T, int* s_cnt,
+template <typename X, int K>
+__device__ __forceinline__ int dec_count_above(const X (&x)[K], uint32_t T, int* s_cnt,
                                                int& round) {
+  const float fT = dec_value(T);
   int c = 0;
 #pragma unroll
-  for (int k = 0; k < K; ++k) c += x[k] > T ? 1 : 0;
+  for (int k = 0; k < K; ++k) c += dec_above(x[k], T, fT) ? 1 : 0;
   const int tot = dec_block_count(c, s_cnt + (round & 1) * kDecWaves);
   ++round;
   return tot;
 }
 
-__global__ __launch_bounds__(kDecThreads, 2) void decode_select_kernel(
+__global__ __launch_bounds__(kDecThreads, 4) void decode_select_kernel(
     const float* __restrict__ delta, int Sk, int p, int w, int u_stride, int kt_stride,
     int32_t* __restrict__ u_idx, int32_t* __restrict__ u_cnt, int32_t* __restrict__ u_nfull,
     float* __restrict__ u_dmax, int32_t* __restrict__ kt_idx, int32_t* __restrict__ kt_cnt) {
-  __shared__ int s_w[kDecWaves];
+  __shared__ int s_w1[kDecWaves], s_w2[kDecWaves], s_w3[kDecWaves];
   __shared__ int s_cnt[2 * kDecWaves];
   __shared__ float s_m[kDecWaves];
-  // read and written as 64-bit words: static arrays of 8-byte alignment
-  __shared__ __align__(8) uint32_t s_gt[kDecThreads * kDecKPT / 32];  // code > T (or all, n <= w)
-  __shared__ __align__(8) uint32_t s_eq[kDecThreads * kDecKPT / 32];  // code == T
-  static_assert(__alignof__(s_gt) >= 8 && __alignof__(s_eq) >= 8,
-                "64-bit LDS words need 8-byte alignment");
-  __shared__ uint32_t s_cand[kDecCand];
+  __shared__ uint32_t s_smin[kDecWaves], s_smax[kDecWaves];
+  __shared__ int s_red[kDecWaves], s_ovf[kDecWaves];
+  __shared__ __align__(16) uint32_t s_hist[kDecPasses + 1][kDecBins];
+  // parked weights (thread t's column: entries t, t + 512, ...), then their
+  // codes less lo; afterwards the tile bitmaps (weight >= T, or weight > T and
+  // weight == T when ties are split)
+  __shared__ __align__(16) uint32_t s_slots[kDecSlots * kDecThreads];
+  uint32_t* const s_cand = s_slots;
+  uint64_t* const s_gt = reinterpret_cast<uint64_t*>(s_slots);
+  uint64_t* const s_eq = reinterpret_cast<uint64_t*>(s_slots) + kDecThreads;
   const int seg = blockIdx.x;
   const int n = p + 1;
   const float* Dl = delta + (int64_t)seg * Sk;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint32_t code[kDecKPT];
-  float mx = -INFINITY;
+  const bool sel = n > w;
+
+  for (int i = tid; i < (kDecPasses + 1) * kDecBins; i += kDecThreads) (&s_hist[0][0])[i] = 0u;
+  // The sample first, then the row.  Sample key of thread t: stratum t/16 of
+  // 32 starts at a multiple of 32 keys near (t/16)*n/32, and takes every other
+  // key of that 32-key line.  A relaxed atomic load is ordered, so it is
+  // issued here rather than moved down to its use.
+  const uint32_t skey =
+      min((((uint32_t)(tid >> 4) * (uint32_t)n) >> 5 & ~31u) + 2u * (uint32_t)(tid & 15),
+          (uint32_t)(n - 1));
+  const float vs = __hip_atomic_load(Dl + skey, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  // register k: key k*512 + tid (past the row, a key of the last 512-key
+  // block, loaded and then replaced by NaN); a wave-uniform block start plus
+  // an offset below 512
+  const int last = (n - 1) & ~(kDecThreads - 1);
+  float v[kDecKPT];
 #pragma unroll
   for (int k = 0; k < kDecKPT; ++k) {
-    const int j = k * kDecThreads + tid;
-    const float v = Dl[min(j, n - 1)];  // every load issues before the first use
-    code[k] = (j < n) ? dma::ord32(v) : 0u;
-    mx = fmaxf(mx, v);  // the clamped key is a real one
+    const int base = min(k * kDecThreads, last);
+    v[k] = (Dl + base)[min((uint32_t)tid, (uint32_t)(n - 1 - base))];
   }
-  mx = dma::wave_max(mx);
+  const uint32_t sc = dec_code(vs);  // used here, so the load is not sunk into the branch
+
+  // the bracket [lo, hi] as codes and as floats; with nothing to select it
+  // admits no weight (NaN bounds)
+  uint32_t lo = kCodeNegInf, hi = kCodePosInf;
+  float flo = __uint_as_float(0x7fc00000u), fhi = flo;
+  if (sel) {
+    const uint32_t mn = dec_wave_min(sc), mxc = dec_wave_max(sc);
+    if (lane == 0) {
+      s_smin[wave] = mn;
+      s_smax[wave] = mxc;
+    }
+    dec_lds_barrier();
+    uint32_t gmin = s_smin[0], gmax = s_smax[0];
+#pragma unroll
+    for (int k = 1; k < kDecWaves; ++k) {
+      gmin = min(gmin, s_smin[k]);
+      gmax = max(gmax, s_smax[k]);
+    }
+    const uint32_t R = gmax - gmin;
+    const int sh = R < (uint32_t)kDecBins ? 0 : 24 - __builtin_clz(R);
+    const uint32_t dg = (sc - gmin) >> sh;  // < 256
+    // a wave whose samples share one bin (a flat row) adds them at once
+    const uint32_t d0 = __builtin_amdgcn_readfirstlane(dg);
+    if (dma::ballot(dg != d0) == 0ull) {
+      if (lane == 0) atomicAdd(&s_hist[0][d0], 64u);
+    } else {
+      atomicAdd(&s_hist[0][dg], 1u);
+    }
+    dec_lds_barrier();
+    // expected descending sample rank of the w-th largest, and a margin of
+    // about 4.5 binomial standard deviations either side
+    const float q = (float)w / (float)n;
+    const int margin = 4 + (int)(4.5f * sqrtf((float)kDecThreads * q * (1.f - q)));
+    const int r = (int)(((int64_t)(2 * w - 1) * kDecThreads) / (2 * (int64_t)n));
+    int ab, hb;
+    if (r - margin >= 0) {
+      const int b = dec_find_bin(s_hist[0], r - margin, ab, hb);
+      if (b >= 0) {  // bin b's last code
+        const uint64_t top = (uint64_t)gmin + ((uint64_t)(b + 1) << sh) - 1u;
+        hi = (uint32_t)min(top, (uint64_t)kCodePosInf);
+      }
+    }
+    if (r + margin < kDecThreads) {
+      const int b = dec_find_bin(s_hist[0], r + margin, ab, hb);
+      if (b >= 0) lo = max(gmin + ((uint32_t)b << sh), kCodeNegInf);  // bin b's first code
+    }
+    flo = dec_value(lo);
+    fhi = dec_value(hi);
+  }
+
+  // the row: NaN past it, the largest weight, and the bracket pass
+  float mx = -INFINITY;
+  int c_gt = 0, c_in = 0;
+#pragma unroll
+  for (int k = 0; k < kDecKPT; ++k) {
+    const float x = tid < n - k * kDecThreads ? v[k] : __uint_as_float(0x7fc00000u);
+    v[k] = x;
+    mx = fmaxf(mx, x);
+    c_gt += x > fhi ? 1 : 0;
+    if (x >= flo && x <= fhi) {
+      if (c_in < kDecSlots) s_cand[c_in * kDecThreads + tid] = __float_as_uint(x);
+      ++c_in;
+    }
+  }
+  mx = dec_value(dec_wave_max(dec_code(mx)));  // max over codes: -0 and +0 as one
   if (lane == 0) s_m[wave] = mx;
 
-  uint32_t T = 0;
-  int need_eq = 0;
-  if (n > w) {
-    int round = 0, cge = n;
-    T = dec_bit_search(code, T, 31, 32 - kDecLead, w, s_cnt, round, cge);
-    int gt_tot;
-    if (cge <= kDecCand) {
-      // order-free compaction of the keys with code >= T
-      int sc = 0;
-#pragma unroll
-      for (int k = 0; k < kDecKPT; ++k) sc += (k * kDecThreads + tid < n && code[k] >= T) ? 1 : 0;
-      int stot;
-      int at = block_excl_scan<kDecThreads>(sc, s_w, stot);
-#pragma unroll
-      for (int k = 0; k < kDecKPT; ++k)
-        if (k * kDecThreads + tid < n && code[k] >= T && at < kDecCand) s_cand[at++] = code[k];
-      __syncthreads();
-      uint32_t cr[kDecCPT];
-#pragma unroll
-      for (int i = 0; i < kDecCPT; ++i) {
-        const int q = i * kDecThreads + tid;
-        cr[i] = q < stot ? s_cand[q] : 0u;
-      }
-      T = dec_bit_search(cr, T, 31 - kDecLead, 0, w, s_cnt, round, cge);
-      gt_tot = dec_count_above(cr, T, s_cnt, round);
-    } else {
-      T = dec_bit_search(code, T, 31 - kDecLead, 0, w, s_cnt, round, cge);
-      gt_tot = dec_count_above(code, T, s_cnt, round);
-    }
-    need_eq = w - gt_tot;  // keys with code == T that are kept, lowest index first
-  }
-  // bitmaps of the verdicts: key k*512 + 64*wave + lane is bit lane of the
-  // 64-bit word k*8 + wave
-#pragma unroll
-  for (int k = 0; k < kDecKPT; ++k) {
-    const bool in = k * kDecThreads + tid < n;
-    const uint64_t g = __ballot(in && (n <= w || code[k] > T));
-    const uint64_t e = __ballot(in && n > w && code[k] == T);
+  uint32_t T = kCodeNegInf;  // nothing to select: every key of the row
+  int need_eq = 0;           // keys equal to T that are kept, lowest index first
+  bool split = false;        // some keys equal to T are kept and some are not
+  if (sel) {
+    // block totals of c_gt and c_in (packed: each wave total is below 2^13)
+    const int pk = __builtin_amdgcn_readlane(dec_wave_scan(c_gt | (c_in << 16)), 63);
+    const bool ovf_w = dma::ballot(c_in > kDecSlots) != 0ull;
     if (lane == 0) {
-      reinterpret_cast<uint64_t*>(s_gt)[k * kDecWaves + wave] = g;
-      reinterpret_cast<uint64_t*>(s_eq)[k * kDecWaves + wave] = e;
+      s_red[wave] = pk;
+      s_ovf[wave] = ovf_w ? 1 : 0;
+    }
+    dec_lds_barrier();  // also publishes the parked weights
+    int gt_hi = 0, n_in = 0, ovf = 0;
+#pragma unroll
+    for (int k = 0; k < kDecWaves; ++k) {
+      const int x = s_red[k];
+      gt_hi += x & 0xffff;
+      n_in += x >> 16;
+      ovf |= s_ovf[k];
+    }
+    if (!ovf && gt_hi < w && gt_hi + n_in >= w) {
+      // radix passes over y = code - lo of the parked weights, 8 bits at a
+      // time from the top bit of hi - lo down; need = the rank of T - lo
+      // among them, from the top
+      const uint32_t span = hi - lo;
+      const int mine = min(c_in, kDecSlots);
+      const int wmine = (int)dec_wave_max((uint32_t)mine);  // the wave's longest column
+      uint32_t y[kDecSlots];
+#pragma unroll
+      for (int i = 0; i < kDecSlots; ++i) {
+        if (i >= wmine) break;
+        y[i] = i < mine ? dec_code(__uint_as_float(s_cand[i * kDecThreads + tid])) - lo : 0u;
+      }
+      int need = w - gt_hi, inb = n_in;
+      int hbit = span == 0u ? 0 : 32 - __builtin_clz(span);
+      uint32_t ypre = 0u;  // the bits of T - lo at and above hbit
+      for (int pass = 0; pass < kDecPasses && hbit > 0; ++pass) {
+        const int s = max(hbit - 8, 0);
+        const uint32_t dmask = (1u << (hbit - s)) - 1u;
+        // y matches the digits found so far: (y & hmask) == yfix
+        const uint32_t hmask = hbit >= 32 ? 0u : ~0u << hbit;
+        const uint32_t yfix = hbit >= 32 ? 0u : ypre << hbit;
+        uint32_t* const hist = s_hist[1 + pass];
+#pragma unroll
+        for (int i = 0; i < kDecSlots; ++i) {
+          if (i >= wmine) break;
+          if (i < mine && (y[i] & hmask) == yfix) atomicAdd(&hist[(y[i] >> s) & dmask], 1u);
+        }
+        dec_lds_barrier();
+        int above, inbin;
+        const int d = dec_find_bin(hist, need - 1, above, inbin);
+        need -= above;
+        inb = inbin;
+        ypre = (ypre << (hbit - s)) | (uint32_t)d;
+        hbit = s;
+      }
+      T = lo + ypre;
+      need_eq = need;
+      split = need < inb;
+    } else {
+      int round = 0, cge = n;
+      T = dec_bit_search(v, 0u, 31, 32 - kDecLead, w, s_cnt, round, cge);
+      int gt_tot;
+      if (cge <= kDecCand) {
+        // order-free compaction of the codes of the keys at or above T
+        const float fT = dec_value(T);
+        int sc2 = 0;
+#pragma unroll
+        for (int k = 0; k < kDecKPT; ++k) sc2 += v[k] >= fT ? 1 : 0;
+        int stot;
+        int at = dec_scan512(sc2, s_w1, stot);
+#pragma unroll
+        for (int k = 0; k < kDecKPT; ++k)
+          if (v[k] >= fT && at < kDecCand) s_cand[at++] = dec_code(v[k]);
+        __syncthreads();
+        uint32_t cr[kDecCPT];
+#pragma unroll
+        for (int i = 0; i < kDecCPT; ++i) {
+          const int q = i * kDecThreads + tid;
+          cr[i] = q < stot ? s_cand[q] : 0u;
+        }
+        T = dec_bit_search(cr, T, 31 - kDecLead, 0, w, s_cnt, round, cge);
+        gt_tot = dec_count_above(cr, T, s_cnt, round);
+      } else {
+        T = dec_bit_search(v, T, 31 - kDecLead, 0, w, s_cnt, round, cge);
+        gt_tot = dec_count_above(v, T, s_cnt, round);
+      }
+      need_eq = w - gt_tot;
+      split = true;
+    }
+  }
+  // tile bitmaps: the ballot of register k in wave `wave` is the word of key
+  // tile k*8 + wave, stored at wave*64 + k (four registers per store group).
+  // Every read of the parked weights is behind a barrier already passed.
+  const float fT = dec_value(T);
+  ulonglong2* const g2 = reinterpret_cast<ulonglong2*>(s_gt + wave * kDecKPT);
+  ulonglong2* const e2 = reinterpret_cast<ulonglong2*>(s_eq + wave * kDecKPT);
+  if (!split) {
+#pragma unroll
+    for (int k = 0; k < kDecKPT; k += 4) {
+      const uint64_t a = dma::ballot(v[k] >= fT), b = dma::ballot(v[k + 1] >= fT);
+      const uint64_t c = dma::ballot(v[k + 2] >= fT), d = dma::ballot(v[k + 3] >= fT);
+      if (lane == 0) {
+        g2[k / 2] = make_ulonglong2(a, b);
+        g2[k / 2 + 1] = make_ulonglong2(c, d);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < kDecKPT; k += 2) {
+      const uint64_t a = dma::ballot(v[k] > fT), b = dma::ballot(v[k + 1] > fT);
+      const uint64_t c = dma::ballot(v[k] == fT), d = dma::ballot(v[k + 1] == fT);
+      if (lane == 0) {
+        g2[k / 2] = make_ulonglong2(a, b);
+        e2[k / 2] = make_ulonglong2(c, d);
+      }
     }
   }
   __syncthreads();
   // thread t: keys [64t, 64t + 64), i.e. key tile t
-  const uint64_t gt64 = reinterpret_cast<const uint64_t*>(s_gt)[tid];
-  const uint64_t eq64 = reinterpret_cast<const uint64_t*>(s_eq)[tid];
-  const int ne = __popcll(eq64);
-  int etot;
-  const int eb = block_excl_scan<kDecThreads>(ne, s_w, etot);
-  const int allow = min(ne, max(0, need_eq - eb));
-  uint64_t kept = gt64, x = eq64;
-  for (int r = 0; r < allow; ++r) {
-    kept |= x & (~x + 1ull);
-    x &= x - 1ull;
+  const int tw = (tid & (kDecWaves - 1)) * kDecKPT + (tid >> 3);
+  uint64_t kept = s_gt[tw];
+  if (split) {
+    uint64_t x = s_eq[tw];
+    const int ne = __popcll(x);
+    int etot;
+    const int eb = dec_scan512(ne, s_w2, etot);
+    const int allow = min(ne, max(0, need_eq - eb));
+    for (int r = 0; r < allow; ++r) {
+      kept |= x & (~x + 1ull);
+      x &= x - 1ull;
+    }
   }
+  // one scan for both the output offsets and the key-tile list (packed:
+  // at most 32768 kept keys, 512 tiles)
   const int nk = __popcll(kept);
-  int tot;
-  int pos = block_excl_scan<kDecThreads>(nk, s_w, tot);
+  const int f = kept != 0ull ? 1 : 0;
+  int tot2;
+  const int pre = dec_scan512(nk | (f << 16), s_w3, tot2);
+  const int tot = tot2 & 0xffff, ktot = tot2 >> 16;
+  int pos = pre & 0xffff;
   int32_t* out = u_idx + (int64_t)seg * u_stride;
   for (uint64_t y = kept; y; y &= y - 1ull) {
     if (pos < u_stride) out[pos] = 64 * tid + __builtin_ctzll(y);
@@ -1422,9 +1724,7 @@ __global__ __launch_bounds__(kDecThreads, 2) void decode_select_kernel(
     u_dmax[seg] = m;
   }
   if (kt_idx) {
-    const int f = kept != 0ull ? 1 : 0;
-    int ktot;
-    const int at = block_excl_scan<kDecThreads>(f, s_w, ktot);
+    const int at = pre >> 16;
     if (f && at < kt_stride) kt_idx[(int64_t)seg * kt_stride + at] = tid;
     if (tid == 0) kt_cnt[seg] = min(ktot, kt_stride);
   }
