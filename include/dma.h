@@ -90,8 +90,14 @@ void dma_tile_sizes(int32_t* Bq, int32_t* Bk);
  *          (a row always keeps its best key); the attention derives it from
  *          u_dlo and the tile's own keys.  May be NULL for dma_topk_mask
  *          (then not written); the bf16 prefill attention requires it.
+ *   u_dval float [n_tiles_total * u_stride]   with Sq == 1 only: delta of each
+ *          key of u_idx, at the same positions.  May be NULL (not written).
+ *          When set, the one-row mask calls write it and the one-row attention
+ *          reads it instead of gathering delta at the listed keys (one
+ *          contiguous read of w values instead of one scattered read per key,
+ *          which touches nearly every line of the delta row).
  * With Sq == 1 (one decode row) evict and u_dlo are not read or written and
- * may be NULL.
+ * may be NULL.  With Sq > 1 u_dval is not read or written.
  */
 typedef struct {
   int32_t* evict;
@@ -102,6 +108,7 @@ typedef struct {
   int32_t* kt_idx;
   int32_t* kt_cnt;
   float* u_dlo;
+  float* u_dval;
 } dma_mask;
 
 typedef struct {

@@ -58,6 +58,15 @@ def check_mask(gm, delta_gpu, om=None):
     u_dmax = gm.u_dmax[: B * Hkv * nT].cpu().numpy().reshape(B, Hkv, nT)
     d32 = delta_gpu.detach().cpu().numpy()
     np.testing.assert_array_equal(u_cnt, om["u_cnt"])
+    if Sq == 1 and getattr(gm, "u_dval", None) is not None:
+        # the listed keys' delta, copied bit for bit
+        u_dval = gm.u_dval[: B * Hkv * us].cpu().numpy().reshape(B, Hkv, us)
+        for b in range(B):
+            for h in range(Hkv):
+                c = u_cnt[b, h, 0]
+                got = u_dval[b, h, :c].view(np.uint32)
+                want = d32[b, h, u_idx[b, h, 0, :c]].view(np.uint32)
+                np.testing.assert_array_equal(got, want, err_msg=f"u_dval {(b, h)}")
     if Sq > 1 and gm.u_dlo is not None:
         # largest delta over the keys before each tile's first row (-inf for none)
         u_dlo = gm.u_dlo[: B * Hkv * nT].cpu().numpy().reshape(B, Hkv, nT)

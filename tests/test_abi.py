@@ -38,7 +38,7 @@ def test_exports_every_declared_function(lib):
 def test_status_strings_and_versions(lib):
     assert lib.dma_status_string(0) == b"ok"
     assert lib.dma_status_string(3) == b"workspace too small"
-    assert lib.dma_abi_version() == 4
+    assert lib.dma_abi_version() == 5
     bq, bk = ctypes.c_int32(), ctypes.c_int32()
     lib.dma_tile_sizes(ctypes.byref(bq), ctypes.byref(bk))
     assert (bq.value, bk.value) == (64, 64)

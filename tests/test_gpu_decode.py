@@ -35,6 +35,20 @@ def test_decode_small(gpu_lib, B, Hq, Hkv, Sk, w, dtype, D):
     compare_rows(O, lse, Or, Lr, rows, dtype, "decode small")
 
 
+@pytest.mark.parametrize("Sk,w", [(5000, 700), (40000, 2048)])
+def test_decode_kept_delta_copy(gpu_lib, Sk, w):
+    # the attention reads the mask's copy of delta at the listed keys; without
+    # the copy it gathers delta itself: the outputs must be bit-identical
+    wl, x = make_small(2, 8, 2, 1, Sk, 128, w, dtype="bf16", q_offset=Sk - 1, seed=Sk,
+                       device="cuda")
+    d = dma.weights(x["V"], x["Delta"], x["A"])
+    gm = dma.topk_mask(d, 1, wl.q_offset, w)
+    O1, L1 = dma.attn_fwd(x["Q"], x["K"], x["V"], d, gm, return_lse=True)
+    gm.u_dval = None
+    O2, L2 = dma.attn_fwd(x["Q"], x["K"], x["V"], d, gm, return_lse=True)
+    assert torch.equal(O1, O2) and torch.equal(L1, L2)
+
+
 def test_decode_equals_last_prefill_row(gpu_lib):
     # the same sequence as a 4096-row prefill: its last row must match decode
     wl, x = make_small(1, 8, 2, 4096, 4096, 128, 512, dtype="bf16", seed=9, device="cuda")

@@ -18,7 +18,8 @@ def _lists(m, w):
     BH = m.B * m.Hkv
     cnt = m.u_cnt[:BH].cpu().numpy()
     idx = m.u_idx[:BH * w].view(BH, w).cpu().numpy()
-    return cnt, idx, m.u_nfull[:BH].cpu().numpy(), m.u_dmax[:BH].cpu().numpy()
+    dval = m.u_dval[:BH * w].view(BH, w).cpu().numpy().view(np.uint32)  # bits: -0 != +0 here
+    return cnt, idx, m.u_nfull[:BH].cpu().numpy(), m.u_dmax[:BH].cpu().numpy(), dval
 
 
 def _delta(kind, B, Hkv, S, seed):
@@ -52,7 +53,7 @@ def test_append_matches_selection(gpu_lib, kind, B, Hkv, w, steps):
         dma.decode_keep_append(d, m)
         ref = dma.topk_mask(d, 1, Sk - 1, w, kt_lists=False)
         got, want = _lists(m, w), _lists(ref, w)
-        for a, b, name in zip(got, want, ("u_cnt", "u_idx", "u_nfull", "u_dmax")):
+        for a, b, name in zip(got, want, ("u_cnt", "u_idx", "u_nfull", "u_dmax", "u_dval")):
             assert np.array_equal(a, b), f"{name} differs after key {Sk - 1}"
         if Sk in (S0 + 1, S0 + steps):
             dd = to64(d)

@@ -67,6 +67,8 @@ def _check_mask(mask: "Mask", B: int, Hkv: int, Sq: int, Sk: int):
                           ("u_dlo", mask.u_dlo, n if Sq > 1 else 0)):
         if need and (t is None or t.numel() < need):
             raise ValueError(f"mask array {name} holds fewer than {need} entries")
+    if Sq == 1 and mask.u_dval is not None and mask.u_dval.numel() < d["u_elems"]:
+        raise ValueError(f"mask array u_dval holds fewer than {d['u_elems']} entries")
 
 
 def _check_qkv(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor):
@@ -111,10 +113,12 @@ class Mask:
     kt_idx: Optional[torch.Tensor]
     kt_cnt: Optional[torch.Tensor]
     u_dlo: Optional[torch.Tensor] = None
+    u_dval: Optional[torch.Tensor] = None
 
     def cstruct(self):
         return DmaMask(_ptr(self.evict), _ptr(self.u_idx), _ptr(self.u_cnt), _ptr(self.u_nfull),
-                       _ptr(self.u_dmax), _ptr(self.kt_idx), _ptr(self.kt_cnt), _ptr(self.u_dlo))
+                       _ptr(self.u_dmax), _ptr(self.kt_idx), _ptr(self.kt_cnt), _ptr(self.u_dlo),
+                       _ptr(self.u_dval))
 
 
 def alloc_mask(B, Hkv, Sq, Sk, q_offset, w, device, kt_lists=True) -> Mask:
@@ -130,7 +134,9 @@ def alloc_mask(B, Hkv, Sq, Sk, q_offset, w, device, kt_lists=True) -> Mask:
                 kt_idx=torch.empty(max(1, d["kt_elems"]), **i32) if kt_lists else None,
                 kt_cnt=torch.empty(max(1, n), **i32) if kt_lists else None,
                 u_dlo=torch.empty(max(1, n), dtype=torch.float32, device=device)
-                if Sq > 1 else None)
+                if Sq > 1 else None,
+                u_dval=torch.empty(max(1, d["u_elems"]), dtype=torch.float32, device=device)
+                if Sq == 1 else None)
 
 
 def weights(V: torch.Tensor, Delta: torch.Tensor, A: torch.Tensor,

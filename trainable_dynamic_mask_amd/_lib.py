@@ -23,7 +23,7 @@ _SZ = ctypes.c_size_t
 
 class DmaMask(ctypes.Structure):
     _fields_ = [("evict", _P), ("u_idx", _P), ("u_cnt", _P), ("u_nfull", _P), ("u_dmax", _P),
-                ("kt_idx", _P), ("kt_cnt", _P), ("u_dlo", _P)]
+                ("kt_idx", _P), ("kt_cnt", _P), ("u_dlo", _P), ("u_dval", _P)]
 
 
 class DmaMaskDims(ctypes.Structure):

@@ -3,6 +3,7 @@
 // enqueued unless every argument checks out.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <map>
@@ -14,7 +15,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 4;
+constexpr int kAbiVersion = 5;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -60,6 +61,20 @@ hipError_t dma_func_max_lds(const void* fn, size_t bytes) {
   e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
   if (e == hipSuccess) cur = bytes;
   return e;
+}
+
+int dma_cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
 }
 
 extern "C" {
@@ -159,6 +174,7 @@ dma_status dma_topk_mask(const float* delta, int64_t B, int64_t Hkv, int64_t Sq,
   a.kt_cnt = out->kt_cnt;
   a.ws = ws;
   a.u_dlo = Sq > 1 ? out->u_dlo : nullptr;
+  a.u_dval = Sq == 1 ? out->u_dval : nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (Sq == 1) return hip_status(dma_launch_topk_decode(a, s));
   const size_t need = dma_topk_workspace_bytes(B, Hkv, Sq, Sk, w);
@@ -193,7 +209,7 @@ dma_status dma_decode_keep_append(const float* delta, int64_t B, int64_t Hkv, in
   if (!delta || !mask->u_idx || !mask->u_cnt || !mask->u_nfull || !mask->u_dmax)
     return DMA_ERR_INVALID_ARG;
   return hip_status(dma_launch_decode_append(delta, B * Hkv, Sk, w, mask->u_idx, mask->u_cnt,
-                                             mask->u_nfull, mask->u_dmax,
+                                             mask->u_nfull, mask->u_dmax, mask->u_dval,
                                              static_cast<hipStream_t>(stream)));
 }
 
@@ -254,6 +270,7 @@ dma_status attn_fwd_impl(const void* Q, const void* K, const void* V, dma_dtype 
   a.u_nfull = mask->u_nfull;
   a.u_dmax = mask->u_dmax;
   a.u_dlo = mask->u_dlo;
+  a.u_dval = Sq == 1 ? mask->u_dval : nullptr;
   a.n_tiles = d.n_tiles;
   a.u_stride = d.u_stride;
   a.scale = scale > 0.f ? scale : 1.f / std::sqrt((float)D);

@@ -13,14 +13,16 @@
 //            coalesced, partial sums are reduced through LDS.
 // A second kernel merges the splits' (max, sum, o) triples per query head.
 //
-// bf16 with D = 128 runs decode_mfma_kernel instead: each wave takes 64 list
-// entries and gathers their K and V rows into LDS with direct 16-byte loads
-// (every load instruction covers 4 whole rows), then S^T = K Q^T and
-// O^T += V^T P^T run on v_mfma_f32_32x32x16_bf16 with the kv head's G query
-// heads as the 32 columns.  Each wave writes its own (max, sum, o) triple.
+// bf16 with D = 128 runs decode_mfma_kernel instead: each wave takes up to
+// 512 list entries in 32-key stages, two stages of K and V rows in flight
+// into LDS (direct 16-byte loads, every instruction 4 whole rows) while the
+// previous one is computed; S^T = K Q^T and O^T += V^T P^T run on
+// v_mfma_f32_32x32x16_bf16 with the kv head's G query heads as the 32
+// columns.  Each wave writes one (max, sum, o) triple per query head.
 #include "lds_dma.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace {
 
@@ -100,7 +102,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DmaAttnArgs a, i
 #pragma unroll
         for (int e = 0; e < E; ++e) dot[gq] = fmaf(qs[gq][d0 + e], kv[e], dot[gq]);
     }
-    const float bias = dl[j] - dmax;
+    const float bias = (a.u_dval ? a.u_dval[seg * a.u_stride + k0 + tid] : dl[j]) - dmax;
 #pragma unroll
     for (int gq = 0; gq < GB; ++gq) sc[gq][tid] = fmaf(dot[gq], a.scale, bias);
   }
@@ -164,158 +166,218 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DmaAttnArgs a, i
 }
 
 // ---------------------------------------------------------------- bf16, D = 128
-constexpr int kWaveKeys = 64;   // list entries per wave
-constexpr int kMfmaWaves = 1;   // waves per workgroup (32 KB of LDS: five workgroups per CU)
-constexpr int kDRowB = 256;     // bytes per K/V row
+constexpr int kStageKeys = 32;                 // list entries per pipeline stage
+constexpr int kDRowB = 256;                    // bytes per K/V row
+constexpr int kStageBytes = kStageKeys * kDRowB;
+constexpr int kMaxStages = 16;                 // list entries per wave: at most 512
+constexpr int kMinRange = 64;                  // and at least 64 (the workspace's split count)
+constexpr int kPipeWavesPerCU = 5;             // 32 KB of LDS per wave
 
 // chunk c of row r at c ^ (((r & 3) << 2) | ((r >> 2) & 3)): conflict-free for
 // both the 16-byte row reads (S^T) and the transposing reads (O^T)
 __device__ __forceinline__ int dswz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 
-__global__ __launch_bounds__(kMfmaWaves * 64) void decode_mfma_kernel(DmaAttnArgs a,
-                                                                          int nsplit) {
-  __shared__ __align__(16) unsigned char sk[kMfmaWaves][kWaveKeys * kDRowB];
-  __shared__ __align__(16) unsigned char sv[kMfmaWaves][kWaveKeys * kDRowB];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+// One wave per workgroup takes `range` consecutive list entries of one
+// (batch, kv head) in stages of 32 keys, two stages in flight: the K and V
+// rows of stage s+2 are gathered into LDS (direct 16-byte loads, 4 whole rows
+// per instruction) while stage s+1's are still arriving and stage s is
+// computed, so every wave keeps loads in flight from its first stage to its
+// last.  S^T = K Q^T and O^T += V^T P^T run on v_mfma_f32_32x32x16_bf16 with
+// the kv head's G query heads as the 32 columns; the softmax is online over
+// the stages (running max per column, sums and output rescaled when it grows).
+// Each wave ends with one (max, sum, o) triple per query head.  FUSED: the
+// workgroup holds all nsplit waves of one (batch, kv head), which merge their
+// triples through LDS and write O; otherwise one wave per workgroup writes
+// its triples to the workspace for decode_combine_kernel.
+template <bool FUSED>
+__global__ __launch_bounds__(FUSED ? kPipeWavesPerCU * 64 : 64, 2) void decode_mfma_kernel(
+    DmaAttnArgs a, int nsplit, int range) {
+  extern __shared__ __align__(16) unsigned char s_dyn[];  // per wave: K[2], V[2] stages
+  const int lane = threadIdx.x & 63;
   const int l32 = lane & 31, hi = lane >> 5;
   const int G = (int)(a.Hq / a.Hkv);
-  const int h = blockIdx.y, b = blockIdx.z;
-  const int split = blockIdx.x * kMfmaWaves + wave;
+  const int wave = FUSED ? __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) : 0;
+  unsigned char* const s_wave = s_dyn + wave * 4 * kStageBytes;
+  unsigned char (*const sk)[kStageBytes] = reinterpret_cast<unsigned char (*)[kStageBytes]>(s_wave);
+  unsigned char (*const sv)[kStageBytes] =
+      reinterpret_cast<unsigned char (*)[kStageBytes]>(s_wave + 2 * kStageBytes);
+  const int split = FUSED ? wave : (int)blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int64_t seg = (int64_t)b * a.Hkv + h;
   const int cnt = a.u_cnt[seg];
   const float dmax = a.u_dmax[seg];
   const int32_t* list = a.u_idx + seg * a.u_stride;
-  const int k0 = split * kWaveKeys;
-  const int nk = max(0, min(kWaveKeys, cnt - k0));
+  const int k0 = split * range;
+  const int nk = max(0, min(range, cnt - k0));
   const int n = l32;  // query head column: hq = h*G + n for n < G
-  float* part = static_cast<float*>(a.ws) + (((int64_t)b * a.Hq + h * G + min(n, G - 1)) * nsplit + split) * 130;
-  if (nk == 0) {
-    if (n < G) {
-      if (hi == 0) {
-        part[0] = -INFINITY;
-        part[1] = 0.f;
-      }
-#pragma unroll
-      for (int d = 0; d < 64; ++d) part[2 + hi * 64 + d] = 0.f;
-    }
-    return;
-  }
-  // list entry of this lane's key (clamped: positions past the list repeat its
-  // last key and are masked)
-  const int jk = list[k0 + min(lane, nk - 1)];
-  const float bias = a.delta[seg * a.Sk + jk] - dmax;
-  const unsigned char* Kg = static_cast<const unsigned char*>(a.K) + (b * a.ksb + h * a.ksh) * 2;
-  const unsigned char* Vg = static_cast<const unsigned char*>(a.V) + (b * a.ksb + h * a.ksh) * 2;
-  const uint32_t rowb = (uint32_t)(a.kss * 2);
-  const uint32_t lk = dma::lds_addr(&sk[wave][0]), lv = dma::lds_addr(&sv[wave][0]);
-  // 16 pieces of 4 rows: lane L fills row 4p + L/16, chunk slot L%16
-#pragma unroll
-  for (int p = 0; p < 16; ++p) {
-    const int row = p * 4 + (lane >> 4);
-    const int lc = (lane & 15) ^ dswz(row);
-    const uint32_t j = (uint32_t)__shfl(jk, row);
-    dma::dma_b128(Kg + j * rowb + lc * 16, lk + p * 1024);
-    dma::dma_b128(Vg + j * rowb + lc * 16, lv + p * 1024);
-  }
-  // Q^T operands: column n (query head h*G + n; zero past G), d = kk*16 + 8*hi + [0, 8)
-  dma::bf16x8 qf[8];
-  {
-    const uint16_t* qrow = static_cast<const uint16_t*>(a.Q) + b * a.qsb +
-                           (int64_t)(h * G + min(n, G - 1)) * a.qsh;
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      dma::u32x4 v = *reinterpret_cast<const dma::u32x4*>(qrow + kk * 16 + hi * 8);
-      if (n >= G) v = dma::u32x4{0u, 0u, 0u, 0u};
-      qf[kk] = __builtin_bit_cast(dma::bf16x8, v);
-    }
-  }
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0);  // this wave's rows have landed in its own LDS
-  asm volatile("" ::: "memory");
-  const unsigned char* KT = sk[wave];
-  const unsigned char* VT = sv[wave];
-  // S^T = K Q^T: register i of block mb is key mb*32 + 8(i/4) + 4hi + i%4
-  dma::f32x16 s[2];
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) s[mb][i] = 0.f;
-#pragma unroll
-  for (int kk = 0; kk < 8; ++kk)
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      const int row = mb * 32 + l32;
-      const dma::bf16x8 kop = *reinterpret_cast<const dma::bf16x8*>(
-          KT + row * kDRowB + (((2 * kk + hi) ^ dswz(row)) << 4));
-      s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qf[kk], s[mb], 0, 0, 0);
-    }
-  // logits with the keys' bias; the lane's column is one query head
-  float mx = -INFINITY;
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = mb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-      const float bk = __shfl(bias, key);
-      const float v = key < nk ? fmaf(s[mb][i], a.scale, bk) : -INFINITY;
-      s[mb][i] = v;
-      mx = fmaxf(mx, v);
-    }
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  // l sums the weights (the log-sum-exp); lr sums them as rounded to bf16 for
-  // the PV product, which normalises this split's output, so a row dominated
-  // by one key returns that key's value row unaffected by the weight's rounding
-  float l = 0.f, lr = 0.f;
-  dma::bf16x8 pb[2][2];
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      float p[8];
-#pragma unroll
-      for (int t8 = 0; t8 < 8; ++t8) {
-        p[t8] = __expf(s[mb][hf * 8 + t8] - mx);
-        l += p[t8];
-      }
-      pb[mb][hf] = dma::to_bf16x8(p);
-#pragma unroll
-      for (int t8 = 0; t8 < 8; ++t8) lr += (float)pb[mb][hf][t8];
-    }
-  l += __shfl_xor(l, 32);
-  lr += __shfl_xor(lr, 32);
-  // O^T += V^T P^T over four 16-key steps; V read with the transposing load
+  // running max of the lane's column, sums of the weights (l) and of the
+  // weights as rounded to bf16 for the PV product (lr), both over this lane's
+  // half of each stage's keys; o = O^T for the column (all empty: no keys)
+  float m = -INFINITY, l = 0.f, lr = 0.f;
   dma::f32x16 o[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
-  const int g = lane >> 4, r = lane & 15;
+  if (nk > 0) {
+    const int nst = (nk + kStageKeys - 1) / kStageKeys;
+    // list entries (and their logit biases) of the range, entry k0 + 64i + lane
+    // in register i; positions past the range repeat its last entry and are
+    // masked (loaded unconditionally: no branch between the loads and their use)
+    int jk[kMaxStages / 2];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+    for (int i = 0; i < kMaxStages / 2; ++i) jk[i] = list[k0 + min(64 * i + lane, nk - 1)];
+    float bias[kMaxStages / 2];
+    if (a.u_dval) {  // the mask's copy of delta at the listed keys: one contiguous read
+      const float* dv = a.u_dval + seg * a.u_stride + k0;
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      const int k0r = mb * 32 + 16 * hf + 4 * (g >> 1) + (r >> 2);
+      for (int i = 0; i < kMaxStages / 2; ++i) bias[i] = dv[min(64 * i + lane, nk - 1)] - dmax;
+    } else {
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const int d0 = db * 32 + 16 * (g & 1) + 4 * (r & 3);
-        const int lc = d0 >> 3, byte = (d0 & 7) * 2;
-        typedef __attribute__((address_space(3))) unsigned char lds_u8;
-        const lds_u8* base = (const lds_u8*)VT;
-        const dma::i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (dma::lds_i16x4*)(base + k0r * kDRowB + ((lc ^ dswz(k0r)) << 4) + byte));
-        const dma::i16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (dma::lds_i16x4*)(base + (k0r + 8) * kDRowB + ((lc ^ dswz(k0r + 8)) << 4) + byte));
-        const dma::u32x2 lo2 = __builtin_bit_cast(dma::u32x2, lo);
-        const dma::u32x2 up2 = __builtin_bit_cast(dma::u32x2, up);
-        const dma::u32x4 vv = {lo2[0], lo2[1], up2[0], up2[1]};
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(dma::bf16x8, vv),
-                                                        pb[mb][hf], o[db], 0, 0, 0);
+      for (int i = 0; i < kMaxStages / 2; ++i) bias[i] = a.delta[seg * a.Sk + jk[i]] - dmax;
+    }
+    const unsigned char* Kg = static_cast<const unsigned char*>(a.K) + (b * a.ksb + h * a.ksh) * 2;
+    const unsigned char* Vg = static_cast<const unsigned char*>(a.V) + (b * a.ksb + h * a.ksh) * 2;
+    const uint32_t rowb = (uint32_t)(a.kss * 2);
+    const uint32_t lk = dma::lds_addr(&sk[0][0]), lv = dma::lds_addr(&sv[0][0]);
+    // a stage of parity P (its rows in lanes 32P.. of a jk register) into
+    // buffer P: 8 pieces of 4 rows for K and for V; lane L fills row 4p + L/16,
+    // chunk slot L%16
+    auto issue = [&](const int jr, auto P) {
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        const int row = p * 4 + (lane >> 4);
+        const int lc = (lane & 15) ^ dswz(row);
+        const uint32_t j = (uint32_t)__shfl(jr, 32 * P() + row);
+        dma::dma_b128_u(Kg + j * rowb + lc * 16, lk + P() * kStageBytes + p * 1024);
+        dma::dma_b128_u(Vg + j * rowb + lc * 16, lv + P() * kStageBytes + p * 1024);
+      }
+    };
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    issue(jk[0], P0{});
+    if (nst > 1) issue(jk[0], P1{});
+    // Q^T operands: column n (query head h*G + n; zero past G), d = kk*16 + 8*hi + [0, 8)
+    dma::bf16x8 qf[8];
+    {
+      const uint16_t* qrow = static_cast<const uint16_t*>(a.Q) + b * a.qsb +
+                             (int64_t)(h * G + min(n, G - 1)) * a.qsh;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        dma::u32x4 v = *reinterpret_cast<const dma::u32x4*>(qrow + kk * 16 + hi * 8);
+        if (n >= G) v = dma::u32x4{0u, 0u, 0u, 0u};
+        qf[kk] = __builtin_bit_cast(dma::bf16x8, v);
       }
     }
+    const int g = lane >> 4, r = lane & 15;
+    // stage s (parity P): its list entries in jk[0] / bias[0], those of stage
+    // s + 2 in jk[1]
+    auto stage = [&](const int s, auto P) {
+      // stage s has landed once at most the next stage's 16 loads are pending
+      asm volatile("" ::: "memory");
+      if (s + 1 < nst)
+        __builtin_amdgcn_s_waitcnt((1 << 14) | (7 << 4) | (15 << 8));  // vmcnt(16)
+      else
+        __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
+      asm volatile("" ::: "memory");
+      const unsigned char* KT = sk[P()];
+      const unsigned char* VT = sv[P()];
+      // S^T = K Q^T: register i is key 8(i/4) + 4hi + i%4 of the stage
+      dma::f32x16 sc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sc[i] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const dma::bf16x8 kop = *reinterpret_cast<const dma::bf16x8*>(
+            KT + l32 * kDRowB + (((2 * kk + hi) ^ dswz(l32)) << 4));
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qf[kk], sc, 0, 0, 0);
+      }
+      // logits with the keys' bias, the stage's max and the new running max
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = 8 * (i >> 2) + 4 * hi + (i & 3);
+        const float bk = __shfl(bias[0], 32 * P() + key);
+        const float v = s * kStageKeys + key < nk ? fmaf(sc[i], a.scale, bk) : -INFINITY;
+        sc[i] = v;
+        mx = fmaxf(mx, v);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mn = fmaxf(m, mx);
+      const float alpha = m == mn ? 1.f : __expf(m - mn);
+      m = mn;
+      dma::bf16x8 pb[2];
+      float ls = 0.f, lrs = 0.f;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        float p[8];
+#pragma unroll
+        for (int t8 = 0; t8 < 8; ++t8) {
+          p[t8] = __expf(sc[hf * 8 + t8] - mn);
+          ls += p[t8];
+        }
+        pb[hf] = dma::to_bf16x8(p);
+#pragma unroll
+        for (int t8 = 0; t8 < 8; ++t8) lrs += (float)pb[hf][t8];
+      }
+      l = fmaf(l, alpha, ls);
+      lr = fmaf(lr, alpha, lrs);
+      if (dma::ballot(alpha != 1.f)) {  // some column's max grew
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+      }
+      // O^T += V^T P^T over two 16-key steps; V read with the transposing load
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int k0r = 16 * hf + 4 * (g >> 1) + (r >> 2);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const int d0 = db * 32 + 16 * (g & 1) + 4 * (r & 3);
+          const int lc = d0 >> 3, byte = (d0 & 7) * 2;
+          typedef __attribute__((address_space(3))) unsigned char lds_u8;
+          const lds_u8* base = (const lds_u8*)VT;
+          const dma::i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (dma::lds_i16x4*)(base + k0r * kDRowB + ((lc ^ dswz(k0r)) << 4) + byte));
+          const dma::i16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (dma::lds_i16x4*)(base + (k0r + 8) * kDRowB + ((lc ^ dswz(k0r + 8)) << 4) + byte));
+          const dma::u32x2 lo2 = __builtin_bit_cast(dma::u32x2, lo);
+          const dma::u32x2 up2 = __builtin_bit_cast(dma::u32x2, up);
+          const dma::u32x4 vv = {lo2[0], lo2[1], up2[0], up2[1]};
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(dma::bf16x8, vv),
+                                                          pb[hf], o[db], 0, 0, 0);
+        }
+      }
+      // buffer P is free once its reads have returned: stage s+2 goes there
+      if (s + 2 < nst) {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // lgkmcnt(0)
+        asm volatile("" ::: "memory");
+        issue(jk[1], P);
+      }
+    };
+#pragma unroll 1
+    for (int s = 0; s < nst; s += 2) {
+      stage(s, P0{});
+      if (s + 1 < nst) stage(s + 1, P1{});
+      // the next pair's entries move to register 0
+#pragma unroll
+      for (int i = 0; i + 1 < kMaxStages / 2; ++i) {
+        jk[i] = jk[i + 1];
+        bias[i] = bias[i + 1];
+      }
+    }
+    l += __shfl_xor(l, 32);
+    lr += __shfl_xor(lr, 32);
+  }
   // this wave's (max, sum, o) for query head n: register i of block db is
   // d = db*32 + 8(i/4) + 4hi + i%4.  o is stored as l/lr times the product, so
-  // that o / l, what the merge divides by, is the product over lr
+  // that o / l, what the merge divides by, is the product over lr.  FUSED: in
+  // the wave's own LDS (its loads have all landed and been read), else in the
+  // workspace
+  float* part = FUSED ? reinterpret_cast<float*>(s_wave) + min(n, G - 1) * 130
+                      : static_cast<float*>(a.ws) +
+                            (((int64_t)b * a.Hq + h * G + min(n, G - 1)) * nsplit + split) * 130;
   if (n < G) {
     const float f = lr > 0.f ? l / lr : 0.f;
 #pragma unroll
@@ -323,7 +385,7 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void decode_mfma_kernel(DmaAttnArg
 #pragma unroll
       for (int i = 0; i < 16; ++i) o[db][i] *= f;
     if (hi == 0) {
-      part[0] = mx;
+      part[0] = m;
       part[1] = l;
     }
 #pragma unroll
@@ -332,6 +394,30 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void decode_mfma_kernel(DmaAttnArg
       for (int q4 = 0; q4 < 4; ++q4)
 #pragma unroll
         for (int k = 0; k < 4; ++k) part[2 + db * 32 + 8 * q4 + 4 * hi + k] = o[db][4 * q4 + k];
+  }
+  if constexpr (FUSED) {
+    // the merge of decode_combine_kernel over the workgroup's waves, in the
+    // same order and arithmetic; one (query head, d) per thread
+    __syncthreads();
+    for (int t = threadIdx.x; t < G * 128; t += blockDim.x) {
+      const int nn = t >> 7, d = t & 127;
+      float M = -INFINITY;
+      for (int sp = 0; sp < nsplit; ++sp)
+        M = fmaxf(M, reinterpret_cast<const float*>(s_dyn + sp * 4 * kStageBytes)[nn * 130]);
+      float L = 0.f, ov = 0.f;
+      if (M != -INFINITY) {
+        for (int sp = 0; sp < nsplit; ++sp) {
+          const float* pp = reinterpret_cast<const float*>(s_dyn + sp * 4 * kStageBytes) + nn * 130;
+          const float fs = expf(pp[0] - M);
+          L = fmaf(pp[1], fs, L);
+          ov = fmaf(pp[2 + d], fs, ov);
+        }
+      }
+      const float res = L > 0.f ? ov / L : 0.f;
+      const int hq = h * G + nn;
+      static_cast<__bf16*>(a.O)[((int64_t)b * a.Sq * a.Hq + hq) * 128 + d] = (__bf16)res;
+      if (a.lse && d == 0) a.lse[(int64_t)b * a.Hq + hq] = M + logf(L) + dmax;
+    }
   }
 }
 
@@ -389,12 +475,36 @@ hipError_t launch(const DmaAttnArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Entries per wave: enough waves for whole rounds of the LDS-bound five per
+// CU, at most 512 entries (16 stages) and at least 64 per wave.
+int pipe_range(int64_t BH, int64_t u_stride) {
+  const int64_t slots = (int64_t)dma_cu_count() * kPipeWavesPerCU;
+  int64_t per = std::max<int64_t>((u_stride + kMaxStages * kStageKeys - 1) /
+                                      (kMaxStages * kStageKeys),
+                                  (slots + BH - 1) / BH);
+  const int64_t rounds = (BH * per + slots - 1) / slots;
+  per = std::max<int64_t>(per, rounds * slots / BH);
+  per = std::min<int64_t>(per, (u_stride + kMinRange - 1) / kMinRange);
+  int64_t range = (u_stride + per - 1) / per;
+  range = (range + kStageKeys - 1) / kStageKeys * kStageKeys;
+  return (int)std::max<int64_t>(range, kMinRange);
+}
+
 hipError_t launch_mfma(const DmaAttnArgs& a, hipStream_t st) {
-  const int nw = (int)((a.u_stride + kWaveKeys - 1) / kWaveKeys);  // splits: one per wave
-  const int nwg = (nw + kMfmaWaves - 1) / kMfmaWaves;
-  const int nsplit = nwg * kMfmaWaves;
-  hipLaunchKernelGGL(decode_mfma_kernel, dim3((unsigned)nwg, (unsigned)a.Hkv, (unsigned)a.B),
-                     dim3(kMfmaWaves * 64), 0, st, a, nsplit);
+  const int range = pipe_range(a.B * a.Hkv, a.u_stride);
+  const int nsplit = (int)((a.u_stride + range - 1) / range);
+  const size_t wave_lds = 4 * kStageBytes;
+  if (nsplit == kPipeWavesPerCU) {
+    // one workgroup per (batch, kv head) fills a CU's LDS: merge in place
+    const void* fn = reinterpret_cast<const void*>(&decode_mfma_kernel<true>);
+    (void)dma_func_max_lds(fn, nsplit * wave_lds);
+    hipLaunchKernelGGL(decode_mfma_kernel<true>, dim3(1, (unsigned)a.Hkv, (unsigned)a.B),
+                       dim3(64 * nsplit), nsplit * wave_lds, st, a, nsplit, range);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(decode_mfma_kernel<false>,
+                     dim3((unsigned)nsplit, (unsigned)a.Hkv, (unsigned)a.B), dim3(64), wave_lds,
+                     st, a, nsplit, range);
   hipLaunchKernelGGL((decode_combine_kernel<__bf16, 128>), dim3((unsigned)a.Hq, (unsigned)a.B),
                      dim3(128), 0, st, a, nsplit);
   return hipGetLastError();
@@ -412,9 +522,8 @@ hipError_t launch_g(const DmaAttnArgs& a, hipStream_t st) {
 }  // namespace
 
 size_t dma_attn_decode_ws_bytes(int64_t B, int64_t Hq, int64_t D, int64_t u_stride) {
-  // enough for either path: one split per 64-entry wave (bf16, D = 128) or per 256 entries
-  const int64_t nw = (u_stride + kWaveKeys - 1) / kWaveKeys;
-  const int64_t nsplit = std::max<int64_t>((nw + kMfmaWaves - 1) / kMfmaWaves * kMfmaWaves,
+  // enough for either path: at least 64 entries per split (bf16, D = 128) or 256
+  const int64_t nsplit = std::max<int64_t>((u_stride + kMinRange - 1) / kMinRange,
                                            (u_stride + kSplit - 1) / kSplit);
   return (size_t)(B * Hq * nsplit * (D + 2)) * sizeof(float);
 }

@@ -72,6 +72,8 @@ __device__ __forceinline__ int rank_below(uint64_t m) {
 // least `bytes`.  The runtime call is made only when the limit has to grow:
 // it costs host time that a chain of short launches shows as idle GPU time.
 hipError_t dma_func_max_lds(const void* fn, size_t bytes);
+// compute units of the current device (cached per device)
+int dma_cu_count();
 hipError_t dma_launch_fill_zero(float* p, int64_t n, hipStream_t st);
 hipError_t dma_launch_weights_bwd(const void* V, int64_t B, int64_t Sk, int64_t Hkv, int64_t D,
                                   int64_t sb, int64_t ss, const float* Delta, const float* A,
@@ -94,12 +96,13 @@ struct DmaTopkArgs {
   int32_t* kt_cnt;
   void* ws;
   float* u_dlo = nullptr;  // prefill: largest delta before each tile's first row, or null
+  float* u_dval = nullptr; // one row: delta of each listed key, or null
 };
 hipError_t dma_launch_topk_prefill(const DmaTopkArgs& a, hipStream_t st);
 hipError_t dma_launch_topk_decode(const DmaTopkArgs& a, hipStream_t st);
 hipError_t dma_launch_decode_append(const float* delta, int64_t BH, int64_t Sk, int64_t w,
                                    int32_t* u_idx, int32_t* u_cnt, int32_t* u_nfull,
-                                   float* u_dmax, hipStream_t st);
+                                   float* u_dmax, float* u_dval, hipStream_t st);
 size_t dma_topk_ws_bytes(int64_t BH, int64_t Sq, int64_t Sk, int64_t w);
 // this device's copy of the static mask scratch (DMA_TOPK_SCRATCH_BYTES)
 hipError_t dma_topk_scratch(void** ptr);
@@ -119,6 +122,7 @@ struct DmaAttnArgs {
   const int32_t* u_nfull;
   const float* u_dmax;
   const float* u_dlo = nullptr;  // bf16 prefill: largest delta before each tile's first row
+  const float* u_dval = nullptr; // one row: delta of each listed key, or null
   int64_t n_tiles, u_stride;
   float scale;
   void* O;

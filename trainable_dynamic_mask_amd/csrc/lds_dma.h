@@ -33,6 +33,12 @@ __device__ __forceinline__ void dma_b128(const void* src, uint32_t lds) {
       : "v"(src), "s"(lds)
       : "m0");
 }
+// The same with the LDS address read from lane 0 just before the m0 write,
+// for callers whose uniform address the compiler may keep in a vector
+// register.
+__device__ __forceinline__ void dma_b128_u(const void* src, uint32_t lds) {
+  dma_b128(src, (uint32_t)__builtin_amdgcn_readfirstlane((int)lds));
+}
 __device__ __forceinline__ void dma_b32(const void* src, uint32_t lds) {
   asm volatile(
       "s_mov_b32 m0, %1\n\t"

@@ -1351,13 +1351,13 @@ __device__ __forceinline__ uint32_t dec_wave_min(uint32_t x) {
                  (uint32_t)__builtin_amdgcn_readlane((int)x, 63)));
 }
 
-// Exclusive prefix sum over the 512 threads, total out; one barrier, so each
-// call site needs its own s_w.
+// Exclusive prefix sum over the 512 threads, total out; one barrier (LDS
+// only: loads in flight stay in flight), so each call site needs its own s_w.
 __device__ __forceinline__ int dec_scan512(int v, int* s_w, int& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int incl = dec_wave_scan(v);
   if (lane == 63) s_w[wave] = incl;
-  __syncthreads();
+  dec_lds_barrier();
   int before = 0;
   total = 0;
 #pragma unroll
@@ -1463,7 +1463,8 @@ __device__ __forceinline__ int dec_count_above(const X (&x)[K], uint32_t T, int*
 __global__ __launch_bounds__(kDecThreads, 4) void decode_select_kernel(
     const float* __restrict__ delta, int Sk, int p, int w, int u_stride, int kt_stride,
     int32_t* __restrict__ u_idx, int32_t* __restrict__ u_cnt, int32_t* __restrict__ u_nfull,
-    float* __restrict__ u_dmax, int32_t* __restrict__ kt_idx, int32_t* __restrict__ kt_cnt) {
+    float* __restrict__ u_dmax, float* __restrict__ u_dval, int32_t* __restrict__ kt_idx,
+    int32_t* __restrict__ kt_cnt) {
   __shared__ int s_w1[kDecWaves], s_w2[kDecWaves], s_w3[kDecWaves];
   __shared__ int s_cnt[2 * kDecWaves];
   __shared__ float s_m[kDecWaves];
@@ -1703,6 +1704,23 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_select_kernel(
       x &= x - 1ull;
     }
   }
+  int32_t* out = u_idx + (int64_t)seg * u_stride;
+  float* dout = u_dval ? u_dval + (int64_t)seg * u_stride : nullptr;
+  // the first kDecPre kept keys of the tile and their delta (cache hits: the
+  // row was just read), loaded before the scan so that it hides the latency
+  constexpr int kDecPre = 8;
+  int pk[kDecPre];
+  float pv[kDecPre];
+  uint64_t rest = kept;
+#pragma unroll
+  for (int i = 0; i < kDecPre; ++i) {
+    pk[i] = 64 * tid + (rest ? __builtin_ctzll(rest) : 0);  // key 64*tid: a real key
+    rest &= rest - 1ull;
+  }
+  if (dout) {
+#pragma unroll
+    for (int i = 0; i < kDecPre; ++i) pv[i] = Dl[pk[i]];
+  }
   // one scan for both the output offsets and the key-tile list (packed:
   // at most 32768 kept keys, 512 tiles)
   const int nk = __popcll(kept);
@@ -1711,9 +1729,20 @@ __global__ __launch_bounds__(kDecThreads, 4) void decode_select_kernel(
   const int pre = dec_scan512(nk | (f << 16), s_w3, tot2);
   const int tot = tot2 & 0xffff, ktot = tot2 >> 16;
   int pos = pre & 0xffff;
-  int32_t* out = u_idx + (int64_t)seg * u_stride;
-  for (uint64_t y = kept; y; y &= y - 1ull) {
-    if (pos < u_stride) out[pos] = 64 * tid + __builtin_ctzll(y);
+#pragma unroll
+  for (int i = 0; i < kDecPre; ++i) {
+    if (i < nk && pos + i < u_stride) {
+      out[pos + i] = pk[i];
+      if (dout) dout[pos + i] = pv[i];
+    }
+  }
+  pos += min(nk, kDecPre);
+  for (uint64_t y = rest; y; y &= y - 1ull) {  // tiles with more kept keys
+    if (pos < u_stride) {
+      const int key = 64 * tid + __builtin_ctzll(y);
+      out[pos] = key;
+      if (dout) dout[pos] = Dl[key];
+    }
     ++pos;
   }
   if (tid == 0) {
@@ -1753,7 +1782,8 @@ __device__ __forceinline__ int dec_block_scan(int v, int* s_w, int& total) {
 __global__ __launch_bounds__(kDecLThreads) void decode_select_large_kernel(
     const float* __restrict__ delta, int Sk, int p, int w, int u_stride, int kt_stride,
     int32_t* __restrict__ u_idx, int32_t* __restrict__ u_cnt, int32_t* __restrict__ u_nfull,
-    float* __restrict__ u_dmax, int32_t* __restrict__ kt_idx, int32_t* __restrict__ kt_cnt) {
+    float* __restrict__ u_dmax, float* __restrict__ u_dval, int32_t* __restrict__ kt_idx,
+    int32_t* __restrict__ kt_cnt) {
   __shared__ uint32_t s_hist[kDecLWaves][256];
   __shared__ int s_suf[257];
   __shared__ int s_w[kDecLWaves];
@@ -1852,19 +1882,24 @@ __global__ __launch_bounds__(kDecLThreads) void decode_select_large_kernel(
   const int take = min(ne, max(0, need_eq - eb));
   int pos = dec_block_scan(ng + take, s_w, tot);
   int32_t* out = u_idx + (int64_t)seg * u_stride;
+  float* dout = u_dval ? u_dval + (int64_t)seg * u_stride : nullptr;
   int kt_here = 0;
   {
     int eq_left = take;
     int last_tile = -1;
     for (int j = k_lo; j < k_hi; ++j) {
-      const uint32_t c = dma::ord32(Dl[j]);
+      const float dj = Dl[j];
+      const uint32_t c = dma::ord32(dj);
       bool kept = all || c > T;
       if (!kept && c == T && eq_left > 0) {
         kept = true;
         --eq_left;
       }
       if (kept) {
-        if (pos < u_stride) out[pos] = j;
+        if (pos < u_stride) {
+          out[pos] = j;
+          if (dout) dout[pos] = dj;
+        }
         ++pos;
         if ((j >> 6) != last_tile) {
           last_tile = j >> 6;
@@ -1917,7 +1952,8 @@ constexpr int kAppThreads = 256;
 
 __global__ __launch_bounds__(kAppThreads) void decode_append_kernel(
     const float* __restrict__ delta, int Sk, int w, int32_t* __restrict__ u_idx,
-    int32_t* __restrict__ u_cnt, int32_t* __restrict__ u_nfull, float* __restrict__ u_dmax) {
+    int32_t* __restrict__ u_cnt, int32_t* __restrict__ u_nfull, float* __restrict__ u_dmax,
+    float* __restrict__ u_dval) {
   extern __shared__ __align__(16) int32_t s_list[];  // [w]
   __shared__ uint64_t s_k[kAppThreads / 64];
   __shared__ float s_m[kAppThreads / 64];
@@ -1970,6 +2006,12 @@ __global__ __launch_bounds__(kAppThreads) void decode_append_kernel(
   if (enters) {
     const int pm = s_pos;
     for (int i = pm + tid; i < w; i += kAppThreads) list[i] = i + 1 < w ? s_list[i + 1] : p;
+  }
+  if (u_dval) {  // every entry's delta, so no earlier state is assumed
+    float* dl = u_dval + (int64_t)seg * w;
+    const int pm = enters ? s_pos : w;
+    for (int i = tid; i < w; i += kAppThreads)
+      dl[i] = i < pm ? Dl[s_list[i]] : (i + 1 < w ? Dl[s_list[i + 1]] : dp);
   }
   if (tid == 0) {
     u_nfull[seg] = w;
@@ -2169,11 +2211,11 @@ hipError_t dma_launch_cand(const float* delta, const int32_t* evict, int64_t BH,
 
 hipError_t dma_launch_decode_append(const float* delta, int64_t BH, int64_t Sk, int64_t w,
                                    int32_t* u_idx, int32_t* u_cnt, int32_t* u_nfull,
-                                   float* u_dmax, hipStream_t st) {
+                                   float* u_dmax, float* u_dval, hipStream_t st) {
   const size_t lds = (size_t)w * sizeof(int32_t);
   (void)dma_func_max_lds(reinterpret_cast<const void*>(&decode_append_kernel), lds);
   hipLaunchKernelGGL(decode_append_kernel, dim3((unsigned)BH), dim3(kAppThreads), lds, st, delta,
-                     (int)Sk, (int)w, u_idx, u_cnt, u_nfull, u_dmax);
+                     (int)Sk, (int)w, u_idx, u_cnt, u_nfull, u_dmax, u_dval);
   return hipGetLastError();
 }
 
@@ -2182,10 +2224,10 @@ hipError_t dma_launch_topk_decode(const DmaTopkArgs& a, hipStream_t st) {
   if (a.q0 + 1 <= kDecThreads * kDecKPT)
     hipLaunchKernelGGL(decode_select_kernel, dim3(BH), dim3(kDecThreads), 0, st, a.delta,
                        (int)a.Sk, (int)a.q0, (int)a.w, (int)a.u_stride, (int)a.kt_stride, a.u_idx,
-                       a.u_cnt, a.u_nfull, a.u_dmax, a.kt_idx, a.kt_cnt);
+                       a.u_cnt, a.u_nfull, a.u_dmax, a.u_dval, a.kt_idx, a.kt_cnt);
   else
     hipLaunchKernelGGL(decode_select_large_kernel, dim3(BH), dim3(kDecLThreads), 0, st, a.delta,
                        (int)a.Sk, (int)a.q0, (int)a.w, (int)a.u_stride, (int)a.kt_stride, a.u_idx,
-                       a.u_cnt, a.u_nfull, a.u_dmax, a.kt_idx, a.kt_cnt);
+                       a.u_cnt, a.u_nfull, a.u_dmax, a.u_dval, a.kt_idx, a.kt_cnt);
   return hipGetLastError();
 }

@@ -376,20 +376,6 @@ __global__ void fill_zero_kernel(float* __restrict__ p, int64_t n) {
     p[i] = 0.f;
 }
 
-int cu_count() {
-  static int cached[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        n <= 0)
-      n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
-
 template <int W, int NS, bool BWD = false>
 hipError_t launch_mfma(const __bf16* V, int64_t B, int64_t Sk, int64_t Hkv, int64_t D, int64_t sb,
                        int64_t ss, const float* Delta, const float* A, float* delta,
@@ -399,7 +385,7 @@ hipError_t launch_mfma(const __bf16* V, int64_t B, int64_t Sk, int64_t Hkv, int6
   const size_t lds = (size_t)C / 8 * kSplitRows * 16 + (size_t)2 * W * kRedRows * 64 * 4;
   const int64_t ntiles = B * ((Sk + kKeysPerTile - 1) / kKeysPerTile);
   const int per_cu = std::max<int>(1, (int)((160 * 1024) / lds));
-  const int64_t grid = std::min<int64_t>(ntiles, (int64_t)cu_count() * per_cu);
+  const int64_t grid = std::min<int64_t>(ntiles, (int64_t)dma_cu_count() * per_cu);
   (void)dma_func_max_lds(reinterpret_cast<const void*>(&weights_mfma_kernel<W, NS, BWD>), lds);
   for (int h0 = 0; h0 < Hkv; h0 += 8)
     hipLaunchKernelGGL((weights_mfma_kernel<W, NS, BWD>), dim3((unsigned)grid), dim3(64 * W), lds,
