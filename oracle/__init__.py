@@ -7,6 +7,7 @@ states each definition it follows.  This wrapper only marshals numpy arrays.
 
 Functions (all inputs are copied to contiguous numpy arrays first):
   weights(V, Delta, A)                      -> delta [B, Hkv, Sk] float64
+  vproj(X, Wv)                              -> V = X Wv [..., N] float64 (X [..., Cin])
   keep_row(delta_row, p, w)                 -> ascending int32 key list
   mask(delta, q0, Sq, w, Bq, Bk)            -> dict(evict, row_cnt, u_cnt, u_idx, kt_cnt, kt_idx)
   attn_rows(Q, K, V, delta, q0, w, rows, scale=None) -> (O [n, D], lse [n])
@@ -38,6 +39,8 @@ def _load():
     lib.orc_num_threads.restype = ctypes.c_int
     lib.orc_weights.argtypes = [_P, _P, _P, _I64, _I64, _I64, _I64, _P]
     lib.orc_weights.restype = None
+    lib.orc_vproj.argtypes = [_P, _P, _I64, _I64, _I64, _P]
+    lib.orc_vproj.restype = None
     lib.orc_keep_row.argtypes = [_P, _I64, _I64, _P]
     lib.orc_keep_row.restype = _I64
     lib.orc_mask.argtypes = [_P, _I64, _I64, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P,
@@ -90,6 +93,20 @@ def weights(V, Delta, A):
     out = np.empty((B, Hkv, Sk), np.float64)
     lib.orc_weights(_ptr(V), _ptr(Dl), _ptr(Av), B, Sk, Hkv, D, _ptr(out))
     return out
+
+
+def vproj(X, Wv):
+    """V[..., n] = sum_k X[..., k] Wv[k, n] in fp64 (the value projection)."""
+    lib = _load()
+    X = _np(X, np.float32)
+    W = _np(Wv, np.float32)
+    lead, Cin = X.shape[:-1], X.shape[-1]
+    assert W.ndim == 2 and W.shape[0] == Cin
+    N = W.shape[1]
+    M = int(np.prod(lead)) if lead else 1
+    out = np.empty((M, N), np.float64)
+    lib.orc_vproj(_ptr(X), _ptr(W), M, Cin, N, _ptr(out))
+    return out.reshape(*lead, N)
 
 
 def keep_row(d, p, w):

@@ -89,6 +89,23 @@ void orc_weights(const float* V, const float* Delta, const float* A, int64_t B, 
     }
 }
 
+// Value projection, the linear map whose output is the value matrix the
+// delta equation starts from (DMA blog, section "Dynamic Sparse Mask
+// Generation"):  V[m, n] = sum_k X[m, k] * Wv[k, n]  over the M = B*Sk rows,
+// each sum taken in order of k.
+void orc_vproj(const float* X, const float* Wv, int64_t M, int64_t Cin, int64_t N, double* V) {
+#pragma omp parallel for schedule(static)
+  for (int64_t m = 0; m < M; ++m) {
+    double* out = V + m * N;
+    for (int64_t n = 0; n < N; ++n) out[n] = 0.0;
+    for (int64_t k = 0; k < Cin; ++k) {
+      const double x = (double)X[m * Cin + k];
+      const float* wrow = Wv + k * N;
+      for (int64_t n = 0; n < N; ++n) out[n] += x * (double)wrow[n];
+    }
+  }
+}
+
 // Keep set of one query position p (keys 0..p of one delta row), ascending.
 int64_t orc_keep_row(const double* d, int64_t p, int64_t w, int32_t* out) {
   std::vector<int32_t> scratch;
