@@ -60,6 +60,9 @@ def parse():
                          "repetition after a 512 MiB flush of the caches, and print their "
                          "achieved GB/s against the algorithmic bytes (own JSON line)")
     ap.add_argument("--reps", type=int, default=20, help="repetitions per stage (--hbm-stages)")
+    ap.add_argument("--vproj", action="store_true",
+                    help="the value projection with delta fused into its epilogue, against "
+                         "the projection alone followed by the weights call (hidden = Hq*D)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (the reference "
                          "reading of the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -215,6 +218,67 @@ def backward_bench(args, wl, x, dev):
     print(json.dumps(out), flush=True)
 
 
+def vproj_bench(args, wl, x, dev):
+    """Fused value projection + weights (dma_vproj_weights with Delta) against the
+    same projection without the epilogue followed by dma_weights, which re-reads V.
+    X [B, Sk, Hq*D] and Wv [Hq*D, Hkv*D] are seeded bf16 normals (Wv scaled by
+    1/sqrt(Cin)), Delta and A the workload's."""
+    import statistics
+    import torch
+    import trainable_dynamic_mask_amd as dma
+    B, Sk, Hkv, D = wl.B, wl.Sk, wl.Hkv, wl.D
+    Cin = wl.Hq * wl.D
+    g = torch.Generator(device=dev).manual_seed(wl.seed + 31)
+    X = torch.randn(B, Sk, Cin, generator=g, device=dev).to(torch.bfloat16)
+    Wv = (torch.randn(Cin, Hkv * D, generator=g, device=dev) / Cin ** 0.5).to(torch.bfloat16)
+    V = torch.empty(B, Sk, Hkv, D, dtype=torch.bfloat16, device=dev)
+    delta = torch.empty(B, Hkv, Sk, dtype=torch.float32, device=dev)
+    lib = dma.load()
+    ws = torch.empty(max(16, lib.dma_vproj_workspace_bytes(B, Sk, Hkv, D)), dtype=torch.uint8,
+                     device=dev)
+
+    def fused():
+        dma.vproj_weights(X, Wv, Hkv, x["Delta"], x["A"], V=V, delta=delta, workspace=ws)
+
+    def proj():
+        dma.vproj_weights(X, Wv, Hkv, V=V)
+
+    def wts():
+        dma.weights(V, x["Delta"], x["A"], out=delta)
+
+    def separate():
+        proj()
+        wts()
+
+    def timed(f):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.reps)]
+        for a, b in ev:
+            a.record()
+            f()
+            b.record()
+        torch.cuda.synchronize()
+        return statistics.median(a.elapsed_time(b) for a, b in ev)
+
+    clock_ramp(separate, args.clock_ramp_ms)
+    res = {}
+    for _ in range(2):  # interleaved twice: the median of each over both passes
+        for name, f in (("fused", fused), ("separate", separate), ("projection", proj),
+                        ("weights", wts)):
+            for _ in range(3):
+                f()
+            res.setdefault(name, []).append(timed(f))
+    ms = {k: round(statistics.median(v), 4) for k, v in res.items()}
+    flop = 2.0 * B * Sk * Cin * Hkv * D
+    out = {"mode": "vproj", "workload": wl.name, "B": B, "Sk": Sk, "Cin": Cin, "N": Hkv * D,
+           "reps": args.reps, "ms": ms,
+           "tflops_fused": round(flop / (ms["fused"] * 1e-3) / 1e12, 1),
+           "tflops_projection": round(flop / (ms["projection"] * 1e-3) / 1e12, 1),
+           "saved_ms": round(ms["separate"] - ms["fused"], 4),
+           "v_bytes_not_reread": B * Sk * Hkv * D * 2}
+    print(json.dumps(out), flush=True)
+
+
 def hbm_stages(args, wl, x, dev):
     """The HBM-bound stages one at a time.  Before every repetition a 512 MiB
     buffer is read and written, which evicts the 256 MB Infinity Cache and the
@@ -317,6 +381,9 @@ def main():
         return
     if args.hbm_stages:
         hbm_stages(args, wl, x, dev)
+        return
+    if args.vproj:
+        vproj_bench(args, wl, x, dev)
         return
     delta = torch.empty(wl.B, wl.Hkv, wl.Sk, dtype=torch.float32, device=dev)
     mask = dma.alloc_mask(wl.B, wl.Hkv, wl.Sq, wl.Sk, wl.q_offset, wl.w, dev)

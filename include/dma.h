@@ -297,6 +297,35 @@ dma_status dma_attn_bwd(const void* Q, const void* K, const void* V, dma_dtype t
                         float* dQ, float* dK, float* dV, float* ddelta, void* ws,
                         size_t ws_bytes, void* stream);
 
+/*
+ * Steps 0 and 1 fused (DMA blog, section "Dynamic Sparse Mask Generation":
+ * delta is computed from the value matrix): the value projection with the
+ * dynamic weights formed in its epilogue.
+ *   V[b,j,n]     = sum_{k < Cin} X[b,j,k] * Wv[k,n],  n < Hkv*D   (fp32 sums,
+ *                  stored as bf16)
+ *   delta[b,h,j] = exp(softplus(sum_n V[b,j,n] * Delta[n,h]) * A[h]) over the
+ *                  stored bf16 V, i.e. dma_weights on the V written here (the
+ *                  products are exact as there; the fp32 sums run in another
+ *                  order).
+ * X      bf16 [B, Sk, Cin], element (b,j,k) at b*x_stride_b + j*x_stride_s + k.
+ * Wv     bf16 [Cin, Hkv*D] row-major (the projection's weight, input-major).
+ * V      bf16 [B, Sk, Hkv, D] (output), element (b,j,n) at b*v_stride_b +
+ *        j*v_stride_s + n.
+ * Delta, A, delta as in dma_weights.  delta NULL: the projection alone
+ *        (Delta and A are not read, no workspace is needed).
+ * ws     dma_vproj_workspace_bytes(B, Sk, Hkv, D) bytes (16-byte aligned),
+ *        contents undefined afterwards.
+ * Limits: Cin a positive multiple of 64; Hkv*D a multiple of 256 and at most
+ * 2048; Hkv <= 8 when delta is computed; B*Sk < 2^31; bases and strides
+ * 16-byte aligned.  Otherwise DMA_ERR_UNSUPPORTED / DMA_ERR_INVALID_ARG.
+ */
+size_t dma_vproj_workspace_bytes(int64_t B, int64_t Sk, int64_t Hkv, int64_t D);
+dma_status dma_vproj_weights(const void* X, int64_t B, int64_t Sk, int64_t Cin,
+                             int64_t x_stride_b, int64_t x_stride_s, const void* Wv, int64_t Hkv,
+                             int64_t D, void* V, int64_t v_stride_b, int64_t v_stride_s,
+                             const float* Delta, const float* A, float* delta, void* ws,
+                             size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

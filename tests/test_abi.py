@@ -38,7 +38,7 @@ def test_exports_every_declared_function(lib):
 def test_status_strings_and_versions(lib):
     assert lib.dma_status_string(0) == b"ok"
     assert lib.dma_status_string(3) == b"workspace too small"
-    assert lib.dma_abi_version() == 5
+    assert lib.dma_abi_version() == 6
     bq, bk = ctypes.c_int32(), ctypes.c_int32()
     lib.dma_tile_sizes(ctypes.byref(bq), ctypes.byref(bk))
     assert (bq.value, bk.value) == (64, 64)
@@ -98,6 +98,37 @@ def test_weights_validation(lib):
     assert _weights(lib, ss=132) == INVALID                  # 264-byte rows: not 16-aligned
     assert _weights(lib, B=0, V=None) == OK                  # empty: nothing launched
     assert _weights(lib, Sk=0, V=None) == OK
+
+
+def _vproj(lib, B=1, Sk=16, Cin=128, xsb=None, xss=None, X=FAKE, Wv=FAKE, Hkv=2, D=128, V=FAKE,
+           vsb=None, vss=None, Delta=FAKE, A=FAKE, delta=FAKE, ws=FAKE, ws_bytes=1 << 30):
+    xss = Cin if xss is None else xss
+    xsb = xss * Sk if xsb is None else xsb
+    vss = Hkv * D if vss is None else vss
+    vsb = vss * Sk if vsb is None else vsb
+    return lib.dma_vproj_weights(X, B, Sk, Cin, xsb, xss, Wv, Hkv, D, V, vsb, vss, Delta, A,
+                                 delta, ws, ws_bytes, None)
+
+
+def test_vproj_validation(lib):
+    assert _vproj(lib, Cin=96) == UNSUPPORTED                # K steps of 64
+    assert _vproj(lib, Hkv=1, D=128) == UNSUPPORTED          # 128 columns: tiles of 256
+    assert _vproj(lib, Hkv=32, D=128) == UNSUPPORTED         # over 2048 columns
+    assert _vproj(lib, Hkv=16, D=64) == UNSUPPORTED          # delta for more than 8 heads
+    assert _vproj(lib, Hkv=16, D=64, delta=None, ws=None, ws_bytes=0, B=0) == OK
+    assert _vproj(lib, Cin=0) == INVALID
+    assert _vproj(lib, X=None) == INVALID
+    assert _vproj(lib, Wv=None) == INVALID
+    assert _vproj(lib, A=None) == INVALID                    # delta asked without A
+    assert _vproj(lib, X=MISALIGNED) == INVALID
+    assert _vproj(lib, xss=100) == INVALID                   # row stride below Cin
+    assert _vproj(lib, xss=132) == INVALID                   # 264-byte rows: not 16-aligned
+    assert _vproj(lib, vss=200) == INVALID                   # row stride below Hkv*D
+    assert _vproj(lib, ws=None) == WORKSPACE
+    need = lib.dma_vproj_workspace_bytes(1, 16, 2, 128)
+    assert need > 0 and _vproj(lib, ws_bytes=need - 1) == WORKSPACE
+    assert _vproj(lib, B=0, X=None) == OK                    # empty: nothing launched
+    assert lib.dma_vproj_workspace_bytes(0, 16, 2, 128) == 0
 
 
 def _topk(lib, B=1, Hkv=2, Sq=16, Sk=16, q0=0, w=4, mask=True, ws=FAKE, ws_bytes=1 << 30):

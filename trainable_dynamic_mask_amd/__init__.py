@@ -158,6 +158,46 @@ def weights(V: torch.Tensor, Delta: torch.Tensor, A: torch.Tensor,
     return out
 
 
+def vproj_weights(X: torch.Tensor, Wv: torch.Tensor, Hkv: int, Delta: Optional[torch.Tensor] = None,
+                  A: Optional[torch.Tensor] = None, V: Optional[torch.Tensor] = None,
+                  delta: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Value projection V = X Wv (X [B,Sk,Cin] bf16, Wv [Cin, Hkv*D] bf16) with the
+    dynamic weights formed in its epilogue when Delta and A are given:
+    returns (V [B,Sk,Hkv,D] bf16, delta [B,Hkv,Sk] float32), or V alone."""
+    _need_cuda(X, Wv)
+    if X.dim() != 3 or X.dtype != torch.bfloat16 or X.stride(2) != 1:
+        raise ValueError("X must be bf16 [B, Sk, Cin] with contiguous rows")
+    B, Sk, Cin = X.shape
+    if Wv.dim() != 2 or Wv.dtype != torch.bfloat16 or Wv.shape[0] != Cin or Wv.shape[1] % Hkv:
+        raise ValueError("Wv must be bf16 [Cin, Hkv*D]")
+    Wv = Wv.contiguous()
+    D = Wv.shape[1] // Hkv
+    if V is None:
+        V = torch.empty(B, Sk, Hkv, D, dtype=torch.bfloat16, device=X.device)
+    elif V.dtype != torch.bfloat16 or tuple(V.shape) != (B, Sk, Hkv, D) or V.stride(3) != 1 \
+            or V.stride(2) != D:
+        raise ValueError("V must be bf16 [B, Sk, Hkv, D] with contiguous rows")
+    lib = load()
+    fused = Delta is not None
+    if fused:
+        _need_cuda(Delta, A)
+        Delta = Delta.contiguous().float()
+        A = A.contiguous().float()
+        if delta is None:
+            delta = torch.empty(B, Hkv, Sk, dtype=torch.float32, device=X.device)
+        elif delta.dtype != torch.float32 or tuple(delta.shape) != (B, Hkv, Sk) \
+                or not delta.is_contiguous():
+            raise ValueError("delta must be contiguous float32 [B, Hkv, Sk]")
+    nbytes = lib.dma_vproj_workspace_bytes(B, Sk, Hkv, D) if fused else 0
+    if nbytes and (workspace is None or workspace.numel() < nbytes):
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=X.device)
+    check("dma_vproj_weights", lib.dma_vproj_weights(
+        _ptr(X), B, Sk, Cin, X.stride(0), X.stride(1), _ptr(Wv), Hkv, D, _ptr(V), V.stride(0),
+        V.stride(1), _ptr(Delta), _ptr(A), _ptr(delta) if fused else ctypes.c_void_p(0),
+        _ptr(workspace) if nbytes else ctypes.c_void_p(0), nbytes, _stream(X.device)))
+    return (V, delta) if fused else V
+
+
 def topk_mask(delta: torch.Tensor, Sq: int, q_offset: int, w: int, kt_lists: bool = True,
               mask: Optional[Mask] = None, workspace: Optional[torch.Tensor] = None,
               noalloc: bool = False) -> Mask:

@@ -36,7 +36,8 @@ EXPORTS = ["dma_status_string", "dma_abi_version", "dma_tile_sizes", "dma_mask_d
            "dma_topk_workspace_bytes", "dma_attn_workspace_bytes", "dma_weights",
            "dma_topk_mask", "dma_topk_mask_noalloc", "dma_decode_keep_append", "dma_attn_fwd",
            "dma_attn_fwd_train", "dma_attn_bwd_workspace_bytes", "dma_attn_bwd",
-           "dma_weights_bwd_workspace_bytes", "dma_weights_bwd"]
+           "dma_weights_bwd_workspace_bytes", "dma_weights_bwd", "dma_vproj_workspace_bytes",
+           "dma_vproj_weights"]
 
 _lib = None
 _lib_safe = None
@@ -115,6 +116,11 @@ def _open(path):
     lib.dma_weights_bwd.argtypes = [_P, ctypes.c_int, _I64, _I64, _I64, _I64, _I64, _I64, _P, _P,
                                     _P, _P, _P, _P, _P, _SZ, _P]
     lib.dma_weights_bwd.restype = ctypes.c_int
+    lib.dma_vproj_workspace_bytes.argtypes = [_I64, _I64, _I64, _I64]
+    lib.dma_vproj_workspace_bytes.restype = _SZ
+    lib.dma_vproj_weights.argtypes = [_P, _I64, _I64, _I64, _I64, _I64, _P, _I64, _I64, _P, _I64,
+                                      _I64, _P, _P, _P, _P, _SZ, _P]
+    lib.dma_vproj_weights.restype = ctypes.c_int
     return lib
 
 

@@ -15,7 +15,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 5;
+constexpr int kAbiVersion = 6;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -140,6 +140,40 @@ dma_status dma_weights(const void* V, dma_dtype vt, int64_t B, int64_t Sk, int64
     return DMA_ERR_INVALID_ARG;
   return hip_status(dma_launch_weights(V, vt == DMA_BF16, B, Sk, Hkv, D, v_stride_b, v_stride_s,
                                        Delta, A, delta, static_cast<hipStream_t>(stream)));
+}
+
+size_t dma_vproj_workspace_bytes(int64_t B, int64_t Sk, int64_t Hkv, int64_t D) {
+  if (B < 1 || Sk < 1 || Hkv < 1 || D < 1) return 0;
+  return dma_vproj_ws_bytes(B * Sk, Hkv * D);
+}
+
+dma_status dma_vproj_weights(const void* X, int64_t B, int64_t Sk, int64_t Cin,
+                             int64_t x_stride_b, int64_t x_stride_s, const void* Wv, int64_t Hkv,
+                             int64_t D, void* V, int64_t v_stride_b, int64_t v_stride_s,
+                             const float* Delta, const float* A, float* delta, void* ws,
+                             size_t ws_bytes, void* stream) {
+  if (B < 0 || Sk < 0 || Cin < 1 || Hkv < 1 || D < 1) return DMA_ERR_INVALID_ARG;
+  const int64_t N = Hkv * D;
+  if (Cin % 64 != 0 || N % 256 != 0 || N > 2048) return DMA_ERR_UNSUPPORTED;
+  if (delta && Hkv > 8) return DMA_ERR_UNSUPPORTED;
+  if (B * Sk >= ((int64_t)1 << 31) || B > 65535) return DMA_ERR_UNSUPPORTED;
+  if (B == 0 || Sk == 0) return DMA_OK;
+  if (!X || !Wv || !V) return DMA_ERR_INVALID_ARG;
+  if (delta && (!Delta || !A)) return DMA_ERR_INVALID_ARG;
+  if (x_stride_s < Cin || x_stride_b < 0 || (B > 1 && x_stride_b < x_stride_s * Sk))
+    return DMA_ERR_INVALID_ARG;
+  if (v_stride_s < N || v_stride_b < 0 || (B > 1 && v_stride_b < v_stride_s * Sk))
+    return DMA_ERR_INVALID_ARG;
+  if (!aligned16(X) || !aligned16(Wv) || !aligned16(V) || (x_stride_s * 2) % 16 != 0 ||
+      (x_stride_b * 2) % 16 != 0 || (v_stride_s * 2) % 16 != 0 || (v_stride_b * 2) % 16 != 0)
+    return DMA_ERR_INVALID_ARG;
+  if (delta) {
+    if (!ws || ws_bytes < dma_vproj_workspace_bytes(B, Sk, Hkv, D)) return DMA_ERR_WORKSPACE;
+    if (!aligned16(ws)) return DMA_ERR_INVALID_ARG;
+  }
+  return hip_status(dma_launch_vproj(X, x_stride_b, x_stride_s, Wv, V, v_stride_b, v_stride_s, B,
+                                     Sk, Cin, N, Hkv, Delta, A, delta, ws,
+                                     static_cast<hipStream_t>(stream)));
 }
 
 dma_status dma_topk_mask(const float* delta, int64_t B, int64_t Hkv, int64_t Sq, int64_t Sk,

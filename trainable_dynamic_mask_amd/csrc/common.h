@@ -74,6 +74,11 @@ __device__ __forceinline__ int rank_below(uint64_t m) {
 hipError_t dma_func_max_lds(const void* fn, size_t bytes);
 // compute units of the current device (cached per device)
 int dma_cu_count();
+size_t dma_vproj_ws_bytes(int64_t M, int64_t N);
+hipError_t dma_launch_vproj(const void* X, int64_t x_sb, int64_t x_ss, const void* Wv, void* V,
+                            int64_t v_sb, int64_t v_ss, int64_t B, int64_t Sk, int64_t Cin,
+                            int64_t N, int64_t Hkv, const float* Delta, const float* A,
+                            float* delta, void* ws, hipStream_t st);
 hipError_t dma_launch_fill_zero(float* p, int64_t n, hipStream_t st);
 hipError_t dma_launch_weights_bwd(const void* V, int64_t B, int64_t Sk, int64_t Hkv, int64_t D,
                                   int64_t sb, int64_t ss, const float* Delta, const float* A,
