@@ -218,8 +218,9 @@ dma_status dma_decode_keep_append(const float* delta, int64_t B, int64_t Hkv, in
  * Arithmetic: BF16 inputs use bf16 MFMA products with fp32 accumulation and
  * an fp32 online softmax; F32 inputs are computed in fp32 throughout.
  * BF16 with Sq > 1 reads mask->u_dlo (required).
- * Limits: BF16 with Sq > 1 needs D == 128 and the rows of one (batch, kv
- * head) within 4 GiB: (Sk-1)*kv_strides[1]*2 + 256 <= 2^32; otherwise
+ * Limits: BF16 with Sq > 1 needs D == 128, the rows of one (batch, kv
+ * head) within 4 GiB: (Sk-1)*kv_strides[1]*2 + 256 <= 2^32, a key row
+ * stride under 16 MiB (kv_strides[1]*2 < 2^24) and Sk <= 2^24; otherwise
  * DMA_ERR_UNSUPPORTED.  With Sq == 1 any strides are accepted: key rows
  * further apart than that are gathered with 64-bit offsets by the (slower)
  * vector kernel instead of the matrix-core one.

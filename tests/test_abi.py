@@ -189,6 +189,10 @@ def test_attn_validation(lib):
     assert _attn(lib, ks=(16 * 2 * 128, 2 * 128 + 3, 128)) == INVALID  # odd row stride
     assert _attn(lib, Sq=1, Sk=16, q0=15) == WORKSPACE       # decode row needs split partials
     assert _attn(lib, dlo=None) == INVALID                   # bf16 prefill reads u_dlo
+    # bf16 prefill gathers: 32-bit row offsets, 24-bit index and stride products
+    assert _attn(lib, Sk=70000, q0=69984, ks=(70000 << 16, 1 << 16, 128)) == UNSUPPORTED
+    assert _attn(lib, ks=(16 << 23, 1 << 23, 128)) == UNSUPPORTED
+    assert _attn(lib, Sk=(1 << 24) + 1, q0=(1 << 24) - 15, ks=(0, 0, 128)) == UNSUPPORTED
     assert _attn(lib, Sq=0, q0=16) == OK
     assert _attn(lib, B=0) == OK
 

@@ -273,9 +273,11 @@ dma_status attn_fwd_impl(const void* Q, const void* K, const void* V, dma_dtype 
         (kv_strides[i] * esz) % 16 != 0)
       return DMA_ERR_INVALID_ARG;
   if ((Hq > 1 && q_strides[2] < D) || (Hkv > 1 && kv_strides[2] < D)) return DMA_ERR_INVALID_ARG;
-  // the bf16 prefill gathers key rows by 32-bit byte offsets from the (b, h) base
+  // the bf16 prefill gathers key rows by 32-bit byte offsets from the (b, h)
+  // base, formed by 24-bit products of key index and row stride
   if (t == DMA_BF16 && Sq > 1 && Sk > 0 &&
-      (Sk - 1) * kv_strides[1] * 2 + 256 > ((int64_t)1 << 32))
+      ((Sk - 1) * kv_strides[1] * 2 + 256 > ((int64_t)1 << 32) ||
+       kv_strides[1] * 2 >= ((int64_t)1 << 24) || Sk > ((int64_t)1 << 24)))
     return DMA_ERR_UNSUPPORTED;
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O)) return DMA_ERR_INVALID_ARG;
   const Dims d = dims_of(Sq, Sk, w);

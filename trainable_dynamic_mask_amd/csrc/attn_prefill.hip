@@ -75,6 +75,7 @@ constexpr float kLazy = 8.f;  // base-2 headroom before O is rescaled (weights s
 constexpr float kRefSpan = 64.f;
 
 using dma::dma_b128;
+using dma::dma_b128_s;
 using dma::dma_b32;
 using dma::i16x4;
 using dma::lds_addr;
@@ -122,7 +123,7 @@ __device__ __forceinline__ void gather_tile(uint32_t tile, const int (&idx)[16 /
     const int piece = wave + t * NW;
     const int row = piece * 4 + rsub;
     const int lc = pc ^ (IS_V ? ((row & 3) << 2) : (row & 15));
-    dma_b128(g + (uint32_t)idx[t] * rowb + lc * 16, tile + piece * 1024);
+    dma_b128_s(g, __umul24((uint32_t)idx[t], rowb) + lc * 16, tile + piece * 1024);
   }
 }
 
@@ -139,8 +140,8 @@ __device__ __forceinline__ void gather_piece(int i, uint32_t ktile, uint32_t vti
   const int row = piece * 4 + (lane >> 4);
   const int lc = (lane & 15) ^ (is_v ? ((row & 3) << 2) : (row & 15));
   const int idx = is_v ? vidx[t] : kidx[t];
-  dma_b128((is_v ? vg : kg) + (uint32_t)idx * rowb + lc * 16,
-           (is_v ? vtile : ktile) + piece * 1024);
+  dma_b128_s(is_v ? vg : kg, __umul24((uint32_t)idx, rowb) + lc * 16,
+             (is_v ? vtile : ktile) + piece * 1024);
 }
 
 // Key indices of the rows this lane gathers for chunk ch (see gather_tile):
@@ -231,9 +232,9 @@ __device__ __forceinline__ void g_phase(Acc& acc, const dma::bf16x8 (&pb)[2][2],
                                         const float* bias_row, const float* dval_row,
                                         float rref, float bias_div, int lane, F&& dma_issue) {
   const int l32 = lane & 31, hi = lane >> 5;
-  // the wave in its MFMA phase issues first on its SIMD, ahead of the
-  // softmax wave sharing it (measured: slightly faster; the reverse, slower)
-  __builtin_amdgcn_s_setprio(1);
+  // Both waves of a SIMD keep the same issue priority: with one barrier per
+  // step, raising this phase's wave measured 1.9% slower at 16K (it delays
+  // the softmax wave sharing the SIMD, which then ends the step late).
   // the scores start from the keys' bias divided by the score scale, so the
   // MFMAs add q.k to it (register i of block mb holds key mb*32 + 8*(i/4) +
   // 4*hi + i%4; the rows point at key 4*hi of the chunk).  Waves whose rows
@@ -314,7 +315,6 @@ __device__ __forceinline__ void g_phase(Acc& acc, const dma::bf16x8 (&pb)[2][2],
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
   }
   __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-  __builtin_amdgcn_s_setprio(0);
 }
 
 // Softmax of one chunk: logits in the base-2 domain, lazy rescale of O, and
@@ -460,7 +460,10 @@ __global__ __launch_bounds__(NH * 128, 1) void attn_prefill_bf16_kernel(DmaAttnA
       static_cast<const unsigned char*>(a.K) + (b * a.ksb + h * a.ksh) * 2;
   const unsigned char* Vg =
       static_cast<const unsigned char*>(a.V) + (b * a.ksb + h * a.ksh) * 2;
-  const uint32_t rowb = (uint32_t)(a.kss * 2);  // row stride in bytes; offsets fit 32 bits
+  // row stride in bytes; the host checks that offsets fit 32 bits and that
+  // key indices and the stride fit 24 (the row offsets use the full-rate
+  // 24-bit multiply)
+  const uint32_t rowb = (uint32_t)(a.kss * 2);
   const float scale2 = a.scale * kLog2e;
   const float bias_div = kLog2e / scale2;  // bias enters the scores before the scale
   const uint32_t lds_k = lds_addr(&sm.k[0][0]), lds_v = lds_addr(&sm.v[0][0]);
@@ -541,9 +544,14 @@ __global__ __launch_bounds__(NH * 128, 1) void attn_prefill_bf16_kernel(DmaAttnA
     }
   }
   phase_barrier<-1>();  // the list entries are visible; delta is still in flight
+  // K(0) -> buffer 0, and already K(1) -> 1 and V(0) -> 0, all in flight together
   int kr[16 / NW], vr[16 / NW];
   gather_rows<NW>(kr, sm, 0, wave, lane);
   gather_tile<NW, false>(lds_k, kr, Kg, rowb, wave, lane);
+  gather_rows<NW>(kr, sm, 1, wave, lane);
+  gather_rows<NW>(vr, sm, 0, wave, lane);
+  gather_tile<NW, false>(lds_k + 1 * kTileB, kr, Kg, rowb, wave, lane);
+  gather_tile<NW, true>(lds_v + 0 * kTileB, vr, Vg, rowb, wave, lane);
   __builtin_amdgcn_s_waitcnt(7 << 4);  // vmcnt(0)
   asm volatile("" ::: "memory");
   if (wave == 0) DMA_PREPARE(0);
@@ -567,41 +575,45 @@ __global__ __launch_bounds__(NH * 128, 1) void attn_prefill_bf16_kernel(DmaAttnA
 #pragma unroll
       for (int t8 = 0; t8 < 8; ++t8) pb[mb][hf][t8] = (__bf16)0.f;
 
-  // Step c is G_c, barrier, S_c, barrier; group A runs G_c in interval 2c,
-  // group B in interval 2c+1.  G_c reads K(c) from buffer c%3 and V(c-1)
-  // from buffer (c+2)%3.  Each K/V tile is gathered half by each group, in
-  // batches, four intervals before it is read:
-  //   group A, batch c (start of G_c):   K(c+2) -> c+2, V(c+1) -> c+1
-  //   group B, batch c (start of S_c):   K(c+3) -> c,   V(c+2) -> c+2
-  // (buffer numbers mod 3), each into a buffer whose last reader ran in the
-  // interval before.  A wave's barrier after its S (group A) or G (group B)
-  // phase waits for all but its latest batch, so batch c has landed by the
-  // end of interval 2c+3 (A) or 2c+5 (B), before K(c+2)/K(c+3) are read.
-  // Wave 0 adds three metadata loads to each group-A batch.  G_0 and G_nch
-  // run both MFMA halves: G_0's PV multiplies zeros, G_nch's scores
+  // One workgroup barrier per step.  In step c group A runs G_c then S_c,
+  // group B runs S_{c-1} then G_c, so while one wave of a SIMD multiplies the
+  // other mostly exponentiates, and within the step the two halves may slide
+  // against each other (a barrier between the two phases as well cost 16% in
+  // a replica of the loop).  G_c reads K(c) from buffer c%3 and V(c-1) from
+  // buffer (c+2)%3.  In step c every wave gathers its pieces of K(c+2) into
+  // buffer (c+2)%3 and of V(c+1) into buffer (c+1)%3, both last read in step
+  // c-1 (group A during G_c, group B during S_{c-1}); at the barrier ending
+  // step c each wave waits for all its loads but those of step c, so the
+  // tiles read in step c+1 have landed.  Wave 0 adds three metadata loads
+  // per step (list entries five steps ahead, delta and eviction rows three
+  // ahead) and prepares the mask and bias of chunk c+1, into a slot that no
+  // one reads in step c.  Both groups pass nch + 1 barriers in the loop;
+  // step nch of group A and step 0 of group B have no softmax, G_0
+  // multiplies the zero P(-1) by the zeroed V(-1), and the scores of G_nch
   // (padding keys) are unused.
 #define DMA_TILES(c_)                                                 \
   const int b0_ = (c_) % kBufs;                                       \
   const int b2_ = b0_ == 0 ? 2 : b0_ - 1; /* (c+2) % 3 */              \
-  const int b1_ = b0_ == 2 ? 0 : b0_ + 1; /* (c+1) % 3 */              \
   const unsigned char* KC = sm.k[b0_];                                \
   const unsigned char* VP = sm.v[b2_]
 #define DMA_STEP_A(MASKED, RR)                                                          \
   do {                                                                                  \
     DMA_TILES(c);                                                                       \
+    const int b1_ = b0_ == 2 ? 0 : b0_ + 1; /* (c+1) % 3 */                             \
+    const uint32_t kt_ = lds_k + b2_ * kTileB, vt_ = lds_v + b1_ * kTileB;              \
     int jd = 0;                                                                         \
     if (wave == 0) jd = sm.jraw[(c + 3) % kRaw][lane];                                  \
-    const uint32_t kt_ = lds_k + b2_ * kTileB, vt_ = lds_v + b1_ * kTileB;              \
     g_phase<NG, RR>(acc, pb, s, qf, KC, VP, &sm.bias[c % kFin][4 * hi],                 \
                     &sm.dval[c % kFin][4 * hi], rref, bias_div, lane, [&](int i_) {       \
       gather_piece<NW>(i_, kt_, vt_, kr, vr, Kg, Vg, rowb, wave, lane);                 \
     });                                                                                 \
+    asm volatile("" ::: "memory"); __builtin_amdgcn_sched_barrier(0);                    \
     if (wave == 0) {                                                                    \
       DMA_LIST(c + 5);                                                                  \
       DMA_DELTA(c + 3, jd);                                                             \
+      DMA_PREPARE(c + 1);                                                               \
     }                                                                                   \
-    phase_barrier<-1>();                                                                \
-    if (wave == 0) DMA_PREPARE(c + 1);                                                  \
+    asm volatile("" ::: "memory"); __builtin_amdgcn_sched_barrier(0);                    \
     if (c < nch)                                                                        \
       softmax_phase<MASKED, ROUNDED, 0>(acc, s, pb, sm, c % kFin, hi, pos, scale2, [](int) {});  \
     gather_rows<NW>(kr, sm, c + 3, wave, lane);                                         \
@@ -619,32 +631,24 @@ __global__ __launch_bounds__(NH * 128, 1) void attn_prefill_bf16_kernel(DmaAttnA
     gather_rows<NW>(kr, sm, c + 3, wave, lane);                                         \
     gather_rows<NW>(vr, sm, c + 2, wave, lane);                                         \
     phase_barrier<NG>();                                                                \
-    {                                                                                   \
-      const uint32_t kt_ = lds_k + b0_ * kTileB, vt_ = lds_v + b2_ * kTileB;            \
-      auto issue_ = [&](int i_) {                                                       \
-        gather_piece<NW>(i_, kt_, vt_, kr, vr, Kg, Vg, rowb, wave, lane);               \
-      };                                                                                \
-      if (c < nch)                                                                      \
-        softmax_phase<MASKED, ROUNDED, NG>(acc, s, pb, sm, c % kFin, hi, pos, scale2, issue_);   \
-      else                                                                              \
-        for (int i_ = 0; i_ < NG; ++i_) issue_(i_);                                     \
+    if (c < nch) {                                                                      \
+      const uint32_t kn_ = lds_k + b0_ * kTileB, vn_ = lds_v + b2_ * kTileB;            \
+      softmax_phase<MASKED, ROUNDED, NG>(acc, s, pb, sm, c % kFin, hi, pos, scale2,     \
+                                         [&](int i_) {                                  \
+        gather_piece<NW>(i_, kn_, vn_, kr, vr, Kg, Vg, rowb, wave, lane);               \
+      });                                                                               \
     }                                                                                   \
-    phase_barrier<-1>();                                                                \
   } while (0)
 
   // Chunks [0, nplain) hold only keys every row keeps; the rest need the
-  // per-element mask; separate loops keep the two bodies' registers apart,
-  // and each group runs its own loops.  The last step (c == nch) only
-  // finishes the PV product of chunk nch-1.
+  // per-element mask; separate loops keep the two bodies' registers apart.
+  // Group B's loop body is its step's second half (G_c) followed by the
+  // first half of the next step (S_c, which gathers K(c+3) and V(c+2)); its
+  // step-0 gathers go out before the loop.
+  gather_rows<NW>(kr, sm, 2, wave, lane);
+  gather_rows<NW>(vr, sm, 1, wave, lane);
+  int c = 0;
   if (grp_a) {
-    // batch -1: K(1) -> 1, V(0) -> 0
-    gather_rows<NW>(kr, sm, 1, wave, lane);
-    gather_rows<NW>(vr, sm, 0, wave, lane);
-    gather_tile<NW, false>(lds_k + 1 * kTileB, kr, Kg, rowb, wave, lane);
-    gather_tile<NW, true>(lds_v + 0 * kTileB, vr, Vg, rowb, wave, lane);
-    gather_rows<NW>(kr, sm, 2, wave, lane);
-    gather_rows<NW>(vr, sm, 1, wave, lane);
-    int c = 0;
     if (rowref) {  // a separate copy of the loops keeps the common one unchanged
       for (; c < nplain; ++c) DMA_STEP_A(false, true);
       for (; c <= nch; ++c) DMA_STEP_A(true, true);
@@ -652,21 +656,9 @@ __global__ __launch_bounds__(NH * 128, 1) void attn_prefill_bf16_kernel(DmaAttnA
       for (; c < nplain; ++c) DMA_STEP_A(false, false);
       for (; c <= nch; ++c) DMA_STEP_A(true, false);
     }
-    // one more barrier so both groups meet equally often
-    phase_barrier<-1>();
   } else {
-    // group B idles through interval 0, issuing batches -2 (K(1) -> 1,
-    // V(0) -> 0) and -1 (K(2) -> 2, V(1) -> 1)
-    gather_rows<NW>(kr, sm, 1, wave, lane);
-    gather_rows<NW>(vr, sm, 0, wave, lane);
-    gather_tile<NW, false>(lds_k + 1 * kTileB, kr, Kg, rowb, wave, lane);
-    gather_tile<NW, true>(lds_v + 0 * kTileB, vr, Vg, rowb, wave, lane);
-    gather_rows<NW>(kr, sm, 2, wave, lane);
-    gather_rows<NW>(vr, sm, 1, wave, lane);
     gather_tile<NW, false>(lds_k + 2 * kTileB, kr, Kg, rowb, wave, lane);
     gather_tile<NW, true>(lds_v + 1 * kTileB, vr, Vg, rowb, wave, lane);
-    phase_barrier<-1>();
-    int c = 0;
     if (rowref) {
       for (; c < nplain; ++c) DMA_STEP_B(false, true);
       for (; c <= nch; ++c) DMA_STEP_B(true, true);

@@ -33,6 +33,18 @@ __device__ __forceinline__ void dma_b128(const void* src, uint32_t lds) {
       : "v"(src), "s"(lds)
       : "m0");
 }
+// The same with the global address split into a uniform base (scalar
+// registers) and a 32-bit per-lane byte offset: one vector register per load
+// instead of a 64-bit pair.
+__device__ __forceinline__ void dma_b128_s(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(off), "s"(base), "s"(lds)
+      : "m0");
+}
 // The same with the LDS address read from lane 0 just before the m0 write,
 // for callers whose uniform address the compiler may keep in a vector
 // register.
