@@ -415,6 +415,12 @@ template <int NH, bool ROUNDED>
 __global__ __launch_bounds__(NH * 128, 1) void attn_prefill_bf16_kernel(DmaAttnArgs a) {
   constexpr int NW = NH * 2;
   constexpr int NG = 2 * (16 / NW);  // direct loads per wave for one K and one V tile
+  // In the chunk loop one group-A wave issues the key metadata loads and
+  // another prepares the mask and bias: with four waves per group these are
+  // waves 1 and 3, whose softmax phase ends earliest (wave 0 and 2 had ~900
+  // cycles per step less slack when measured).
+  constexpr int kLoadWave = NW >= 4 ? 1 : 0;
+  constexpr int kPrepWave = NW >= 8 ? 3 : 0;
   __shared__ __align__(16) Smem sm;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -502,12 +508,12 @@ __global__ __launch_bounds__(NH * 128, 1) void attn_prefill_bf16_kernel(DmaAttnA
     }
   }
 
-  // Key metadata, all by wave 0: the list entries of chunk x are loaded
-  // straight into slot x % 8 of jraw five steps before chunk x is first
-  // multiplied, delta and the eviction rows of those keys three steps
-  // before (addressed by the landed list entries), and in the softmax phase
-  // of the step before, wave 0 turns them into the mask and bias of slot
-  // x % 4, padding the positions past the list.
+  // Key metadata (wave 0 in the prologue, kLoadWave and kPrepWave in the
+  // loop): the list entries of chunk x are loaded straight into slot x % 8
+  // of jraw five steps before chunk x is first multiplied, delta and the
+  // eviction rows of those keys three steps before (addressed by the landed
+  // list entries), and in the step before, they become the mask and bias of
+  // slot x % 4, with the positions past the list padded.
 #define DMA_LIST(x_) dma_b32(list + min((x_) * kBk + lane, clast), lds_j + ((x_) % kRaw) * 256)
 #define DMA_DELTA(x_, j_)                                   \
   do {                                                      \
@@ -584,13 +590,14 @@ __global__ __launch_bounds__(NH * 128, 1) void attn_prefill_bf16_kernel(DmaAttnA
   // buffer (c+2)%3 and of V(c+1) into buffer (c+1)%3, both last read in step
   // c-1 (group A during G_c, group B during S_{c-1}); at the barrier ending
   // step c each wave waits for all its loads but those of step c, so the
-  // tiles read in step c+1 have landed.  Wave 0 adds three metadata loads
+  // tiles read in step c+1 have landed.  kLoadWave adds three metadata loads
   // per step (list entries five steps ahead, delta and eviction rows three
-  // ahead) and prepares the mask and bias of chunk c+1, into a slot that no
-  // one reads in step c.  Both groups pass nch + 1 barriers in the loop;
-  // step nch of group A and step 0 of group B have no softmax, G_0
-  // multiplies the zero P(-1) by the zeroed V(-1), and the scores of G_nch
-  // (padding keys) are unused.
+  // ahead); kPrepWave prepares the mask and bias of chunk c+1, into a slot
+  // that no one reads in step c, from raw metadata whose loads its issuer
+  // waited for before the barrier that ended step c-1.  Both groups pass
+  // nch + 1 barriers in the loop; step nch of group A and step 0 of group B
+  // have no softmax, G_0 multiplies the zero P(-1) by the zeroed V(-1), and
+  // the scores of G_nch (padding keys) are unused.
 #define DMA_TILES(c_)                                                 \
   const int b0_ = (c_) % kBufs;                                       \
   const int b2_ = b0_ == 0 ? 2 : b0_ - 1; /* (c+2) % 3 */              \
@@ -602,23 +609,23 @@ __global__ __launch_bounds__(NH * 128, 1) void attn_prefill_bf16_kernel(DmaAttnA
     const int b1_ = b0_ == 2 ? 0 : b0_ + 1; /* (c+1) % 3 */                             \
     const uint32_t kt_ = lds_k + b2_ * kTileB, vt_ = lds_v + b1_ * kTileB;              \
     int jd = 0;                                                                         \
-    if (wave == 0) jd = sm.jraw[(c + 3) % kRaw][lane];                                  \
+    if (wave == kLoadWave) jd = sm.jraw[(c + 3) % kRaw][lane];                          \
     g_phase<NG, RR>(acc, pb, s, qf, KC, VP, &sm.bias[c % kFin][4 * hi],                 \
                     &sm.dval[c % kFin][4 * hi], rref, bias_div, lane, [&](int i_) {       \
       gather_piece<NW>(i_, kt_, vt_, kr, vr, Kg, Vg, rowb, wave, lane);                 \
     });                                                                                 \
     asm volatile("" ::: "memory"); __builtin_amdgcn_sched_barrier(0);                    \
-    if (wave == 0) {                                                                    \
+    if (wave == kLoadWave) {                                                            \
       DMA_LIST(c + 5);                                                                  \
       DMA_DELTA(c + 3, jd);                                                             \
-      DMA_PREPARE(c + 1);                                                               \
     }                                                                                   \
+    if (wave == kPrepWave) DMA_PREPARE(c + 1);                                          \
     asm volatile("" ::: "memory"); __builtin_amdgcn_sched_barrier(0);                    \
     if (c < nch)                                                                        \
       softmax_phase<MASKED, ROUNDED, 0>(acc, s, pb, sm, c % kFin, hi, pos, scale2, [](int) {});  \
     gather_rows<NW>(kr, sm, c + 3, wave, lane);                                         \
     gather_rows<NW>(vr, sm, c + 2, wave, lane);                                         \
-    if (wave == 0)                                                                      \
+    if (wave == kLoadWave)                                                              \
       phase_barrier<NG + 3>();                                                          \
     else                                                                                \
       phase_barrier<NG>();                                                              \
