@@ -21,15 +21,15 @@
 // one wave of each per SIMD.  Each wave alternates an MFMA phase
 //   G_c = { O += V(c-1) P(c-1)^T ;  S(c) = K(c) Q^T }
 // and a VALU phase
-//   S_c = { softmax of S(c) -> P(c) },
-// with a workgroup barrier after every phase.  Group B starts one phase late,
-// so between two barriers one wave of every SIMD runs MFMAs while the other
-// runs the softmax.
+//   S_c = { softmax of S(c) -> P(c) }.
+// Step c ends with a workgroup barrier; in it group A runs G_c then S_c and
+// group B runs S_{c-1} then G_c, so one wave of every SIMD mostly runs MFMAs
+// while the other runs the softmax.
 //
 // Memory pipeline: K/V tiles are triple-buffered and gathered straight from
-// HBM into LDS (direct loads, no registers), half by each group, four
-// phases before they are read; the loads of one batch are spread over the
-// issuing phase so that the address unit is never flooded.  The key
+// HBM into LDS (direct loads, no registers) by the group-A waves, two steps
+// before they are read; a step's loads are spread over the issuing phase so
+// that the address unit is never flooded.  The key
 // metadata (list entries, delta, eviction rows) moves the same way, five
 // and three steps ahead, and is turned into the mask and bias of a chunk one
 // step ahead.  The direct loads are inline asm, invisible to the compiler:
@@ -551,13 +551,16 @@ __global__ __launch_bounds__(NH * 128, 1) void attn_prefill_bf16_kernel(DmaAttnA
   }
   phase_barrier<-1>();  // the list entries are visible; delta is still in flight
   // K(0) -> buffer 0, and already K(1) -> 1 and V(0) -> 0, all in flight together
-  int kr[16 / NW], vr[16 / NW];
-  gather_rows<NW>(kr, sm, 0, wave, lane);
-  gather_tile<NW, false>(lds_k, kr, Kg, rowb, wave, lane);
-  gather_rows<NW>(kr, sm, 1, wave, lane);
-  gather_rows<NW>(vr, sm, 0, wave, lane);
-  gather_tile<NW, false>(lds_k + 1 * kTileB, kr, Kg, rowb, wave, lane);
-  gather_tile<NW, true>(lds_v + 0 * kTileB, vr, Vg, rowb, wave, lane);
+  {
+    int pk[16 / NW], pv[16 / NW];
+    gather_rows<NW>(pk, sm, 0, wave, lane);
+    gather_tile<NW, false>(lds_k, pk, Kg, rowb, wave, lane);
+    gather_rows<NW>(pk, sm, 1, wave, lane);
+    gather_rows<NW>(pv, sm, 0, wave, lane);
+    gather_tile<NW, false>(lds_k + 1 * kTileB, pk, Kg, rowb, wave, lane);
+    gather_tile<NW, true>(lds_v + 0 * kTileB, pv, Vg, rowb, wave, lane);
+  }
+  int kr[16 / (NW / 2)], vr[16 / (NW / 2)];
   __builtin_amdgcn_s_waitcnt(7 << 4);  // vmcnt(0)
   asm volatile("" ::: "memory");
   if (wave == 0) DMA_PREPARE(0);
@@ -586,11 +589,13 @@ __global__ __launch_bounds__(NH * 128, 1) void attn_prefill_bf16_kernel(DmaAttnA
   // other mostly exponentiates, and within the step the two halves may slide
   // against each other (a barrier between the two phases as well cost 16% in
   // a replica of the loop).  G_c reads K(c) from buffer c%3 and V(c-1) from
-  // buffer (c+2)%3.  In step c every wave gathers its pieces of K(c+2) into
-  // buffer (c+2)%3 and of V(c+1) into buffer (c+1)%3, both last read in step
-  // c-1 (group A during G_c, group B during S_{c-1}); at the barrier ending
-  // step c each wave waits for all its loads but those of step c, so the
-  // tiles read in step c+1 have landed.  kLoadWave adds three metadata loads
+  // buffer (c+2)%3.  In step c the group-A waves gather K(c+2) into buffer
+  // (c+2)%3 and V(c+1) into buffer (c+1)%3, both last read in step c-1,
+  // spread over their softmax phase S_c (group B's softmax, which overlaps
+  // group A's MFMA phase, ends the step; group A's has slack, and moving the
+  // loads there measured 1.5% faster than half of them in each group).  At
+  // the barrier ending step c a group-A wave waits for all its loads but
+  // those of step c, so the tiles read in step c+1 have landed.  kLoadWave adds three metadata loads
   // per step (list entries five steps ahead, delta and eviction rows three
   // ahead); kPrepWave prepares the mask and bias of chunk c+1, into a slot
   // that no one reads in step c, from raw metadata whose loads its issuer
@@ -610,10 +615,8 @@ __global__ __launch_bounds__(NH * 128, 1) void attn_prefill_bf16_kernel(DmaAttnA
     const uint32_t kt_ = lds_k + b2_ * kTileB, vt_ = lds_v + b1_ * kTileB;              \
     int jd = 0;                                                                         \
     if (wave == kLoadWave) jd = sm.jraw[(c + 3) % kRaw][lane];                          \
-    g_phase<NG, RR>(acc, pb, s, qf, KC, VP, &sm.bias[c % kFin][4 * hi],                 \
-                    &sm.dval[c % kFin][4 * hi], rref, bias_div, lane, [&](int i_) {       \
-      gather_piece<NW>(i_, kt_, vt_, kr, vr, Kg, Vg, rowb, wave, lane);                 \
-    });                                                                                 \
+    g_phase<0, RR>(acc, pb, s, qf, KC, VP, &sm.bias[c % kFin][4 * hi],                  \
+                   &sm.dval[c % kFin][4 * hi], rref, bias_div, lane, [](int) {});           \
     asm volatile("" ::: "memory"); __builtin_amdgcn_sched_barrier(0);                    \
     if (wave == kLoadWave) {                                                            \
       DMA_LIST(c + 5);                                                                  \
@@ -622,40 +625,35 @@ __global__ __launch_bounds__(NH * 128, 1) void attn_prefill_bf16_kernel(DmaAttnA
     if (wave == kPrepWave) DMA_PREPARE(c + 1);                                          \
     asm volatile("" ::: "memory"); __builtin_amdgcn_sched_barrier(0);                    \
     if (c < nch)                                                                        \
-      softmax_phase<MASKED, ROUNDED, 0>(acc, s, pb, sm, c % kFin, hi, pos, scale2, [](int) {});  \
-    gather_rows<NW>(kr, sm, c + 3, wave, lane);                                         \
-    gather_rows<NW>(vr, sm, c + 2, wave, lane);                                         \
+      softmax_phase<MASKED, ROUNDED, 2 * NG>(acc, s, pb, sm, c % kFin, hi, pos, scale2,  \
+                                             [&](int i_) {                              \
+        gather_piece<NW / 2>(i_, kt_, vt_, kr, vr, Kg, Vg, rowb, wave, lane);           \
+      });                                                                               \
+    gather_rows<NW / 2>(kr, sm, c + 3, wave, lane);                                     \
+    gather_rows<NW / 2>(vr, sm, c + 2, wave, lane);                                     \
     if (wave == kLoadWave)                                                              \
-      phase_barrier<NG + 3>();                                                          \
+      phase_barrier<2 * NG + 3>();                                                      \
     else                                                                                \
-      phase_barrier<NG>();                                                              \
+      phase_barrier<2 * NG>();                                                          \
   } while (0)
 #define DMA_STEP_B(MASKED, RR)                                                          \
   do {                                                                                  \
     DMA_TILES(c);                                                                       \
     g_phase<0, RR>(acc, pb, s, qf, KC, VP, &sm.bias[c % kFin][4 * hi],                  \
                    &sm.dval[c % kFin][4 * hi], rref, bias_div, lane, [](int) {});           \
-    gather_rows<NW>(kr, sm, c + 3, wave, lane);                                         \
-    gather_rows<NW>(vr, sm, c + 2, wave, lane);                                         \
-    phase_barrier<NG>();                                                                \
-    if (c < nch) {                                                                      \
-      const uint32_t kn_ = lds_k + b0_ * kTileB, vn_ = lds_v + b2_ * kTileB;            \
-      softmax_phase<MASKED, ROUNDED, NG>(acc, s, pb, sm, c % kFin, hi, pos, scale2,     \
-                                         [&](int i_) {                                  \
-        gather_piece<NW>(i_, kn_, vn_, kr, vr, Kg, Vg, rowb, wave, lane);               \
-      });                                                                               \
-    }                                                                                   \
+    phase_barrier<-1>();                                                                \
+    if (c < nch)                                                                        \
+      softmax_phase<MASKED, ROUNDED, 0>(acc, s, pb, sm, c % kFin, hi, pos, scale2, [](int) {});  \
   } while (0)
 
   // Chunks [0, nplain) hold only keys every row keeps; the rest need the
   // per-element mask; separate loops keep the two bodies' registers apart.
   // Group B's loop body is its step's second half (G_c) followed by the
-  // first half of the next step (S_c, which gathers K(c+3) and V(c+2)); its
-  // step-0 gathers go out before the loop.
-  gather_rows<NW>(kr, sm, 2, wave, lane);
-  gather_rows<NW>(vr, sm, 1, wave, lane);
+  // first half of the next step (S_c).
   int c = 0;
   if (grp_a) {
+    gather_rows<NW / 2>(kr, sm, 2, wave, lane);
+    gather_rows<NW / 2>(vr, sm, 1, wave, lane);
     if (rowref) {  // a separate copy of the loops keeps the common one unchanged
       for (; c < nplain; ++c) DMA_STEP_A(false, true);
       for (; c <= nch; ++c) DMA_STEP_A(true, true);
@@ -664,8 +662,6 @@ __global__ __launch_bounds__(NH * 128, 1) void attn_prefill_bf16_kernel(DmaAttnA
       for (; c <= nch; ++c) DMA_STEP_A(true, false);
     }
   } else {
-    gather_tile<NW, false>(lds_k + 2 * kTileB, kr, Kg, rowb, wave, lane);
-    gather_tile<NW, true>(lds_v + 1 * kTileB, vr, Vg, rowb, wave, lane);
     if (rowref) {
       for (; c < nplain; ++c) DMA_STEP_B(false, true);
       for (; c <= nch; ++c) DMA_STEP_B(true, true);
