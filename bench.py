@@ -63,6 +63,9 @@ def parse():
     ap.add_argument("--vproj", action="store_true",
                     help="the value projection with delta fused into its epilogue, against "
                          "the projection alone followed by the weights call (hidden = Hq*D)")
+    ap.add_argument("--natural-ab", action="store_true",
+                    help="time the attention on the gathered keep lists against natural-order "
+                         "block skipping (the mask's key-tile lists, per-element keep test)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (the reference "
                          "reading of the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -279,6 +282,58 @@ def vproj_bench(args, wl, x, dev):
     print(json.dumps(out), flush=True)
 
 
+def natural_ab(args, wl, x, dev):
+    """The gathered-list attention against natural-order block skipping on the
+    same kernel: the natural-order lists hold every key of each query tile's
+    active 64-key tiles (the mask step's block-skip list) under the per-element
+    keep test, so both compute the same outputs; the ratio of their times is
+    what gathering the kept keys saves."""
+    import statistics
+    import torch
+    import trainable_dynamic_mask_amd as dma
+    from trainable_dynamic_mask_amd.blockskip import chunk_counts, natural_order_mask
+    delta = dma.weights(x["V"], x["Delta"], x["A"])
+    mask = dma.topk_mask(delta, wl.Sq, wl.q_offset, wl.w, kt_lists=True)
+    nat = natural_order_mask(mask)
+    O_g = torch.empty_like(x["Q"])
+    O_n = torch.empty_like(x["Q"])
+
+    def gathered():
+        dma.attn_fwd(x["Q"], x["K"], x["V"], delta, mask, out=O_g)
+
+    def natural():
+        dma.attn_fwd(x["Q"], x["K"], x["V"], delta, nat, out=O_n)
+
+    def timed(f):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.reps)]
+        for a, b in ev:
+            a.record()
+            f()
+            b.record()
+        torch.cuda.synchronize()
+        return statistics.median(a.elapsed_time(b) for a, b in ev)
+
+    clock_ramp(gathered, args.clock_ramp_ms)
+    res = {}
+    for _ in range(2):  # interleaved twice: the median of each over both passes
+        for name, f in (("gathered", gathered), ("natural", natural)):
+            for _ in range(3):
+                f()
+            res.setdefault(name, []).append(timed(f))
+    ms = {k: round(statistics.median(v), 4) for k, v in res.items()}
+    torch.cuda.synchronize()
+    diff = (O_g.float() - O_n.float()).abs().max().item()
+    cg, cn = chunk_counts(mask, nat)
+    flop = wl.effective_flops()
+    out = {"mode": "natural_ab", "workload": wl.name, "reps": args.reps, "ms": ms,
+           "speedup": round(ms["natural"] / ms["gathered"], 3),
+           "chunks": {"gathered": cg, "natural": cn}, "work_ratio": round(cn / cg, 3),
+           "effective_tflops": {k: round(flop / (v * 1e-3) / 1e12, 1) for k, v in ms.items()},
+           "max_abs_diff_outputs": diff}
+    print(json.dumps(out), flush=True)
+
+
 def hbm_stages(args, wl, x, dev):
     """The HBM-bound stages one at a time.  Before every repetition a 512 MiB
     buffer is read and written, which evicts the 256 MB Infinity Cache and the
@@ -384,6 +439,9 @@ def main():
         return
     if args.vproj:
         vproj_bench(args, wl, x, dev)
+        return
+    if args.natural_ab:
+        natural_ab(args, wl, x, dev)
         return
     delta = torch.empty(wl.B, wl.Hkv, wl.Sk, dtype=torch.float32, device=dev)
     mask = dma.alloc_mask(wl.B, wl.Hkv, wl.Sq, wl.Sk, wl.q_offset, wl.w, dev)

@@ -245,3 +245,30 @@ def test_large_delta_born_inside_a_tile(gpu_lib, q0):
     print(f"large births q0={q0}: max abs {m:.2e}, lse err over {small.sum()} small-delta rows "
           f"{err.max():.2e}")
     assert small.sum() > 100 and err.max() <= 2e-4
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,S,w,seed", [
+    (1, 8, 2, 1024, 128, 1),   # 16 query tiles, lists much shorter than the prefix
+    (2, 4, 1, 640, 300, 2),    # G = 4, a partial last query tile
+    (1, 4, 2, 256, 256, 3),    # w >= S: every key kept
+])
+def test_natural_order_lists(gpu_lib, B, Hq, Hkv, S, w, seed):
+    """Natural-order block skipping (every key of each query tile's active
+    64-key tiles, per-element keep test) is the comparison schedule of the
+    bench's --natural-ab mode; on the same kernel it must give the oracle's
+    outputs on every row, as the gathered lists do."""
+    from trainable_dynamic_mask_amd.blockskip import chunk_counts, natural_order_mask
+    wl, x = make_small(B, Hq, Hkv, S, S, 128, w, dtype="bf16", delta_std=0.05, seed=seed,
+                       device="cuda")
+    d = dma.weights(x["V"], x["Delta"], x["A"])
+    gm = dma.topk_mask(d, wl.Sq, wl.q_offset, wl.w, kt_lists=True)
+    nat = natural_order_mask(gm)
+    On, lse_n = dma.attn_fwd(x["Q"], x["K"], x["V"], d, nat, return_lse=True)
+    torch.cuda.synchronize()
+    rows = _all_rows(wl)
+    Or, Lr = _oracle_rows(x, d, wl, rows)
+    compare_rows(On, lse_n, Or, Lr, rows, "bf16", f"natural {(B, Hq, Hkv, S, w)}")
+    cg, cn = chunk_counts(gm, nat)
+    # every active key tile is visited whole, so the natural schedule does at
+    # least the gathered lists' work
+    assert cn >= cg
