@@ -126,6 +126,23 @@ def test_heavy_tailed_delta(gpu_lib):
     compare_rows(Oi, None, Or, Lr, rows, "bf16", "heavy tail (no lse)")
 
 
+@pytest.mark.parametrize("scale,delta_std,q0,seed", [(1.0, 0.02, 0, 31), (3.0, 0.05, 0, 32),
+                                                     (3.0, 0.02, 150, 33)])
+def test_large_score_terms(gpu_lib, scale, delta_std, q0, seed):
+    # Score scales far above 1/sqrt(D): q.k*scale reaches +-100 and beyond, so
+    # rows meet keys far above and far below their running reference (the
+    # rescale path, and weights that overflow before it) in every tile.
+    S = 700
+    wl, x = make_small(1, 8, 2, S - q0, S, 128, 300, dtype="bf16", delta_std=delta_std,
+                       q_offset=q0, seed=seed, device="cuda")
+    d, gm, O, lse, Oi = _run(x, wl, scale=scale)
+    rows = _all_rows(wl)
+    Or, Lr = _oracle_rows(x, d, wl, rows, scale=scale)
+    assert float(np.abs(Lr).max()) > 20.0 * scale  # the logits really are large
+    compare_rows(O, lse, Or, Lr, rows, "bf16", f"scale {scale}")
+    compare_rows(Oi, None, Or, Lr, rows, "bf16", f"scale {scale} (no lse)")
+
+
 def test_f32_heavy_tail_every_row(gpu_lib):
     # delta std 0.1 (delta up to ~1e8, fp32 spacing ~8 there): rows that do not
     # see their tile's largest delta keep full precision because the fp32 path

@@ -69,6 +69,11 @@ constexpr int kXcds = 8;        // accelerator complex dies, each with its own L
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.f;  // base-2 headroom before O is rescaled (weights stay <= 2^8)
+// reference of a row that has met no kept key yet: finite, so that the
+// exponents of its masked (-inf) logits stay -inf
+constexpr float kNoRef = -3.402823466e38f;
+// largest base-2 gap from a row's first largest logit up to its reference
+constexpr float kFloor = 64.f;
 // largest gap between the tile's largest delta and a wave's first row's own
 // largest delta that the shared tile offset serves (scores up to kRefSpan /
 // scale ~ 724 in magnitude keep ~2^-14 absolute precision)
@@ -185,6 +190,7 @@ struct Acc {
   float m;           // base-2 reference
   float l;           // this lane's partial row sum of the weights (the log-sum-exp)
   float lr;          // the same sum of the weights as rounded to bf16 for the PV product
+  float mbest;       // base-2 bias of the row's largest kept delta (its best key's bias)
 };
 
 // V^T operands of PV k-step ks = (mb, hf) = (ks/2, ks%2) for the four d
@@ -317,72 +323,20 @@ __device__ __forceinline__ void g_phase(Acc& acc, const dma::bf16x8 (&pb)[2][2],
   __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 }
 
-// Softmax of one chunk: logits in the base-2 domain, lazy rescale of O, and
-// P = exp2(s - m) as the bf16 B operands of the PV product.  MASKED chunks
-// hold keys that only some rows of the tile keep and apply j <= p < e_j per
-// element; the others hold keys every row keeps.  Lane (l32, hi) holds
-// key(mb, i) = mb*32 + 8*(i/4) + 4*hi + i%4 of query l32; the other 32 keys
-// of the same query sit in lane ^ 32.
-template <bool MASKED, bool ROUNDED, int NDMA, typename F>
-__device__ __forceinline__ void softmax_phase(Acc& acc, dma::f32x16 (&s)[2],
-                                              dma::bf16x8 (&pb)[2][2], const Smem& sm, int slot,
-                                              int hi, int pos, float scale2, F&& dma_issue) {
-  const int* pjp = &sm.pj[slot][4 * hi];
-  const int* pep = &sm.e[slot][4 * hi];
-  // four partial maxima and four partial sums keep the dependency chains
-  // short: a wave runs this phase alone on its SIMD's vector unit
-  float mxp[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int kb = mb * 32 + 8 * q4;
-      int4 jv = {0, 0, 0, 0}, evv = {0, 0, 0, 0};
-      if constexpr (MASKED) {
-        jv = *reinterpret_cast<const int4*>(pjp + kb);
-        evv = *reinterpret_cast<const int4*>(pep + kb);
-      }
-      const int pj[4] = {jv.x, jv.y, jv.z, jv.w};
-      const int pe[4] = {evv.x, evv.y, evv.z, evv.w};
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = q4 * 4 + r;
-        // the logit is scale2 * v with v = q.k + bias / scale2.  ROUNDED rounds
-        // it first, as the backward recomputes it; otherwise the factor goes
-        // into the exponent below (scale2 > 0 keeps the maximum)
-        float v = ROUNDED ? s[mb][i] * scale2 : s[mb][i];
-        // kept iff pj <= pos < pe, one unsigned compare (pe <= pj: never)
-        if constexpr (MASKED)
-          v = ((uint32_t)(pos - pj[r]) < (uint32_t)(pe[r] - pj[r])) ? v : -INFINITY;
-        s[mb][i] = v;
-        mxp[q4] = fmaxf(mxp[q4], v);
-      }
-    }
-  // Each lane tests its own 32 keys against the query's shared reference m;
-  // only when some lane needs a new reference does the wave combine the two
-  // halves of each query (lane l and l ^ 32), so the common path has no
-  // cross-lane exchange.
-  float mx = fmaxf(fmaxf(mxp[0], mxp[1]), fmaxf(mxp[2], mxp[3]));
-  if constexpr (!ROUNDED) mx *= scale2;
-  if (__ballot(mx > acc.m + kLazy) != 0ull) {
-    // rare: a logit above the reference by more than the headroom
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(acc.m, mx);
-    const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(acc.m - m_new);
-    acc.l *= alpha;
-    acc.lr *= alpha;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc.o[db][i] *= alpha;
-    acc.m = m_new;
-  }
-  const float m_use = (acc.m == -INFINITY) ? 0.f : acc.m;
-  // O is normalised by the sum of the weights exactly as the PV product sees
-  // them (rounded to bf16): then a row dominated by one key returns that
-  // key's value row with no error from the weight's rounding.  The sum of
-  // rounded pairs is one bf16 dot product with (1, 1) per two weights.  The
-  // log-sum-exp (ROUNDED: asked for) uses the unrounded weights.
+// Weights of one chunk as the bf16 B operands of the PV product, and their
+// sums.  FIRST: the scores s become the exponents x = scale2*s - m in place
+// (x = s - m when ROUNDED: s is the rounded logit) and P = exp2(x); otherwise
+// s already holds exponents and P = exp2(s - m).  O is normalised by the sum
+// of the weights exactly as the PV product sees them (rounded to bf16): then
+// a row dominated by one key returns that key's value row with no error from
+// the weight's rounding.  The sum of rounded pairs is one bf16 dot product
+// with (1, 1) per two weights.  The log-sum-exp (ROUNDED: asked for) uses the
+// unrounded weights.  Four partial sums keep the dependency chains short.
+// The group's direct loads (NDMA per phase) go out evenly over the pass.
+template <bool ROUNDED, bool FIRST, int NDMA, typename F>
+__device__ __forceinline__ void weights_pass(dma::f32x16 (&s)[2], dma::bf16x8 (&pb)[2][2],
+                                             float m_use, float scale2, float& sum_p,
+                                             float& sum_r, F&& dma_issue) {
   float rsp[4] = {0.f, 0.f, 0.f, 0.f};
   float rsr[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -396,8 +350,13 @@ __device__ __forceinline__ void softmax_phase(Acc& acc, dma::f32x16 (&s)[2],
       float p[8];
 #pragma unroll
       for (int t8 = 0; t8 < 8; ++t8) {
-        p[t8] = __builtin_amdgcn_exp2f(ROUNDED ? s[mb][hf * 8 + t8] - m_use
-                                               : fmaf(s[mb][hf * 8 + t8], scale2, -m_use));
+        const int i = hf * 8 + t8;
+        if constexpr (FIRST) {
+          s[mb][i] = ROUNDED ? s[mb][i] - m_use : fmaf(s[mb][i], scale2, -m_use);
+          p[t8] = __builtin_amdgcn_exp2f(s[mb][i]);
+        } else {
+          p[t8] = __builtin_amdgcn_exp2f(s[mb][i] - m_use);
+        }
         if constexpr (ROUNDED) rsp[t8 & 3] += p[t8];
       }
       pb[mb][hf] = to_bf16x8(p);
@@ -407,8 +366,121 @@ __device__ __forceinline__ void softmax_phase(Acc& acc, dma::f32x16 (&s)[2],
         rsr[k] = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes2, rsr[k], false);
       }
     }
-  if constexpr (ROUNDED) acc.l += (rsp[0] + rsp[1]) + (rsp[2] + rsp[3]);
-  acc.lr += (rsr[0] + rsr[1]) + (rsr[2] + rsr[3]);
+  if constexpr (ROUNDED) sum_p = (rsp[0] + rsp[1]) + (rsp[2] + rsp[3]);
+  sum_r = (rsr[0] + rsr[1]) + (rsr[2] + rsr[3]);
+}
+
+// Rescale of O and the sums when a row's reference m grows by d >= 0.
+__device__ __forceinline__ void rescale(Acc& acc, float d) {
+  const float alpha = __builtin_amdgcn_exp2f(-d);
+  acc.l *= alpha;
+  acc.lr *= alpha;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc.o[db][i] *= alpha;
+  acc.m += d;
+}
+
+// Largest of x over the two lanes of one query (lane and lane ^ 32), by the
+// gfx950 lane swap between the wave's halves (no LDS round trip).
+__device__ __forceinline__ float row_max2(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                   false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+
+// Largest of the lane's 32 values.
+__device__ __forceinline__ float lane_max(const dma::f32x16 (&s)[2]) {
+  float mxp[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mxp[i & 3] = fmaxf(mxp[i & 3], s[mb][i]);
+  return fmaxf(fmaxf(mxp[0], mxp[1]), fmaxf(mxp[2], mxp[3]));
+}
+
+// Softmax of one chunk: logits in the base-2 domain, lazy rescale of O, and
+// the weights P.  MASKED chunks hold keys that only some rows of the tile
+// keep and apply j <= p < e_j per element; the others hold keys every row
+// keeps.  Lane (l32, hi) holds key(mb, i) = mb*32 + 8*(i/4) + 4*hi + i%4 of
+// query l32; the other 32 keys of the same query sit in lane ^ 32.
+//
+// The lazy rule: a row's reference m moves only when one of its logits
+// exceeds it by more than kLazy, and then every lane of the wave moves m to
+// the largest logit of its query (both halves) and rescales O.  Such a logit
+// has a weight above 2^kLazy, which rounds to at least 2^kLazy in bf16, so
+// the lane's sum of the rounded weights (needed anyway) reaches 2^kLazy.
+// Hence, once every row of the wave has a reference, the common path takes
+// no maximum: the weights are computed against the current m, and only when
+// some lane's sum reaches 2^kLazy (a NaN sum counts) does the wave take the
+// maximum of the exponents, apply the rule and, if it fired, recompute the
+// weights from the exponents kept in place.  A row's first reference comes
+// from its first kept keys and the bias of its best key (below), so that the
+// rule fires only on unusually large score terms (or where delta is heavy-
+// tailed and a row's first keys lie far below its best one).
+template <bool MASKED, bool ROUNDED, int NDMA, typename F>
+__device__ __forceinline__ void softmax_phase(Acc& acc, dma::f32x16 (&s)[2],
+                                              dma::bf16x8 (&pb)[2][2], const Smem& sm, int slot,
+                                              int hi, int pos, float scale2, F&& dma_issue) {
+  if constexpr (MASKED || ROUNDED) {
+    const int* pjp = &sm.pj[slot][4 * hi];
+    const int* pep = &sm.e[slot][4 * hi];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int kb = mb * 32 + 8 * q4;
+        int4 jv = {0, 0, 0, 0}, evv = {0, 0, 0, 0};
+        if constexpr (MASKED) {
+          jv = *reinterpret_cast<const int4*>(pjp + kb);
+          evv = *reinterpret_cast<const int4*>(pep + kb);
+        }
+        const int pj[4] = {jv.x, jv.y, jv.z, jv.w};
+        const int pe[4] = {evv.x, evv.y, evv.z, evv.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = q4 * 4 + r;
+          // the logit is scale2 * v with v = q.k + bias / scale2.  ROUNDED
+          // rounds it first, as the backward recomputes it; otherwise the
+          // factor goes into the exponent
+          float v = ROUNDED ? s[mb][i] * scale2 : s[mb][i];
+          // kept iff pj <= pos < pe, one unsigned compare (pe <= pj: never)
+          if constexpr (MASKED)
+            v = ((uint32_t)(pos - pj[r]) < (uint32_t)(pe[r] - pj[r])) ? v : -INFINITY;
+          s[mb][i] = v;
+        }
+      }
+  }
+  constexpr float kLazyW = 256.f;  // 2^kLazy
+  static_assert(kLazy == 8.f, "kLazyW is 2^kLazy");
+  if (__ballot(acc.m == kNoRef) != 0ull) {
+    // A row with no reference yet (O and the sums still 0) that has kept
+    // keys in this chunk takes the larger of their largest logit c and the
+    // bias mbest of its best key, but at most c + kFloor: later keys then only
+    // exceed the reference by more than kLazy when their score term
+    // (q.k)*scale*log2(e) does, and the row's largest weight stays at least
+    // 2^-kFloor.  Rows that have a reference keep it.
+    float mx = lane_max(s);
+    if constexpr (!ROUNDED) mx *= scale2;  // scale2 > 0 keeps the maximum
+    mx = row_max2(mx);
+    if (acc.m == kNoRef && mx > -INFINITY) acc.m = fminf(fmaxf(mx, acc.mbest), mx + kFloor);
+  }
+  float sum_p = 0.f, sum_r;
+  // rows still without a reference have every logit at -inf: weights 0
+  weights_pass<ROUNDED, true, NDMA>(s, pb, acc.m, scale2, sum_p, sum_r, dma_issue);
+  if (__ballot(!(sum_r < kLazyW)) != 0ull) {
+    // s holds the exponents x = logit - m now; the row's largest logit so far
+    // is m + (largest x of both halves)
+    const float mx = lane_max(s);
+    if (__ballot(mx > kLazy) != 0ull) {
+      const float d = fmaxf(row_max2(mx), 0.f);
+      rescale(acc, d);
+      weights_pass<ROUNDED, false, 0>(s, pb, d, scale2, sum_p, sum_r, [](int) {});
+    }
+  }
+  if constexpr (ROUNDED) acc.l += sum_p;
+  acc.lr += sum_r;
 }
 
 template <int NH, bool ROUNDED>
@@ -571,7 +643,11 @@ __global__ __launch_bounds__(NH * 128, 1) void attn_prefill_bf16_kernel(DmaAttnA
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc.o[db][i] = 0.f;
-  acc.m = -INFINITY;
+  acc.m = kNoRef;
+  // Every kept delta of row p is at most r(p), which one kept key reaches,
+  // so the row's logits lie below mbest + (q.k)*scale*log2(e), and one of
+  // them is at least mbest - |q.k|*scale*log2(e).
+  acc.mbest = rowref ? 0.f : (rref - dmax) * kLog2e;
   acc.l = 0.f;
   acc.lr = 0.f;
   dma::f32x16 s[2];
