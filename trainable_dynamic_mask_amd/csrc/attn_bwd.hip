@@ -526,7 +526,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(DmaBwdArgs a) {
 
 // ---------------------------------------------------------------- reduce
 // One wave per key: lane L sums d = 2L, 2L+1 over the key's groups; the
-// groups' partial rows are independent loads, four in flight.
+// groups' partial rows are independent loads, up to kRedBatch groups in
+// flight (a key is kept on ~w rows, so most keys take one batch).
+constexpr int kRedBatch = 8;
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(DmaBwdArgs a) {
   const DmaAttnArgs& f = a.f;
   const int64_t seg = blockIdx.y;
@@ -542,27 +544,33 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(DmaBwdArgs a) {
   float sd = 0.f;
   if (r0 < r1) {
     const int g0 = r0 / kGroupRows, g1 = (r1 - 1) / kGroupRows;
-    for (int gb = g0; gb <= g1; gb += 4) {
-      int64_t o[4];
+    for (int gb = g0; gb <= g1; gb += kRedBatch) {
+      int64_t o[kRedBatch];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < kRedBatch; ++u) {
         const int64_t gi = seg * a.n_super + min(gb + u, g1);
         // a kept key is a candidate of each of these groups; the clamp only keeps
         // the read inside the group's rows whatever the map holds
         o[u] = gi * a.cap + min(max(a.pmap[gi * f.Sk + j], 0), (int)a.cap - 1);
       }
+      // every load is issued before any is used (past g1 they reread group
+      // g1's row and are dropped), so the batch's loads are all in flight
+      float2 x[kRedBatch], y[kRedBatch];
+      float z[kRedBatch];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float2 x = reinterpret_cast<const float2*>(a.pk + o[u] * kD)[lane];
-        const float2 y = reinterpret_cast<const float2*>(a.pv + o[u] * kD)[lane];
-        const float z = a.pd[o[u]];
-        if (gb + u <= g1) {
-          sk.x += x.x;
-          sk.y += x.y;
-          sv.x += y.x;
-          sv.y += y.y;
-          sd += z;
-        }
+      for (int u = 0; u < kRedBatch; ++u) {
+        x[u] = reinterpret_cast<const float2*>(a.pk + o[u] * kD)[lane];
+        y[u] = reinterpret_cast<const float2*>(a.pv + o[u] * kD)[lane];
+        z[u] = a.pd[o[u]];
+      }
+#pragma unroll
+      for (int u = 0; u < kRedBatch; ++u) {
+        const bool in = gb + u <= g1;
+        sk.x += in ? x[u].x : 0.f;
+        sk.y += in ? x[u].y : 0.f;
+        sv.x += in ? y[u].x : 0.f;
+        sv.y += in ? y[u].y : 0.f;
+        sd += in ? z[u] : 0.f;
       }
     }
   }
