@@ -106,35 +106,6 @@ __device__ __forceinline__ dma::f32x16 mfma(dma::bf16x8 a, dma::bf16x8 b, dma::f
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// ---------------------------------------------------------------- dot
-// One row (b, i, hq) of 128 values per 16 lanes.
-// O + O_res (when given) restores the forward's fp32 O.
-__global__ __launch_bounds__(256) void bwd_dot_kernel(const uint16_t* __restrict__ O,
-                                                      const uint16_t* __restrict__ Ores,
-                                                      const uint16_t* __restrict__ dO,
-                                                      int64_t nrows, int Sq, int Hq,
-                                                      float* __restrict__ Dv) {
-  const int64_t r = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int l = threadIdx.x & 15;
-  float acc = 0.f;
-  if (r < nrows) {
-    const u32x4 a = reinterpret_cast<const u32x4*>(O + r * kD)[l];
-    const u32x4 b = reinterpret_cast<const u32x4*>(dO + r * kD)[l];
-    u32x4 c = {0u, 0u, 0u, 0u};
-    if (Ores) c = reinterpret_cast<const u32x4*>(Ores + r * kD)[l];
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      acc += (dma::bf16_lo(a[e]) + dma::bf16_lo(c[e])) * dma::bf16_lo(b[e]) +
-             (dma::bf16_hi(a[e]) + dma::bf16_hi(c[e])) * dma::bf16_hi(b[e]);
-  }
-#pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
-  if (l == 0 && r < nrows) {
-    const int64_t hq = r % Hq, bi = r / Hq, i = bi % Sq, b = bi / Sq;
-    Dv[(b * Hq + hq) * Sq + i] = acc;
-  }
-}
-
 // ---------------------------------------------------------------- dq
 struct DqSmem {
   unsigned char k[2][kTileB];  // K chunk tiles (gathered rows)
@@ -194,7 +165,34 @@ __global__ __launch_bounds__(NH * 128, 2) void bwd_dq_kernel(DmaBwdArgs a) {
   // first, exact for every key near the row's maximum whatever the range of
   // delta, so the logits carried stay small
   const float lse_q = f.lse[((int64_t)b * f.Hq + hq) * f.Sq + nr];
-  const float dv_q = a.Dv[((int64_t)b * f.Hq + hq) * f.Sq + nr];
+  // D_i = dO_i . O_i: this lane's 64 of the row's 128 values against the dO^T
+  // operand it holds, then the other half from lane ^ 32.  O + O_res (when
+  // given) restores the forward's fp32 O.  Every (row, query head) belongs to
+  // exactly one wave, which stores D_i for the key-major passes.
+  float dv_q;
+  {
+    const int64_t ro = ((b * f.Sq + nr) * f.Hq + hq) * kD + hi * 8;
+    const uint16_t* orow = static_cast<const uint16_t*>(f.O) + ro;
+    const uint16_t* rrow = static_cast<const uint16_t*>(f.ores) + ro;
+    u32x4 ov[8], rv[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      ov[kk] = *reinterpret_cast<const u32x4*>(orow + kk * 16);
+      rv[kk] = f.ores ? *reinterpret_cast<const u32x4*>(rrow + kk * 16) : u32x4{0u, 0u, 0u, 0u};
+    }
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const u32x4 gv = __builtin_bit_cast(u32x4, gf[kk]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        acc[e] += (dma::bf16_lo(ov[kk][e]) + dma::bf16_lo(rv[kk][e])) * dma::bf16_lo(gv[e]) +
+                  (dma::bf16_hi(ov[kk][e]) + dma::bf16_hi(rv[kk][e])) * dma::bf16_hi(gv[e]);
+    }
+    const float part = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    dv_q = part + __shfl_xor(part, 32);
+    if (hi == 0 && n < rows) a.Dv[((int64_t)b * f.Hq + hq) * f.Sq + r_lo + n] = dv_q;
+  }
 
   const uint32_t lds_k = lds_addr(&sm.k[0][0]), lds_v = lds_addr(&sm.v[0][0]);
   const uint32_t lds_j = lds_addr(&sm.jl[0][0]), lds_d = lds_addr(&sm.dl[0][0]),
@@ -629,11 +627,6 @@ hipError_t dma_launch_attn_bwd(DmaBwdArgs& a, hipStream_t st) {
   p += al256(nc * 4);
   a.pmap = reinterpret_cast<int32_t*>(p);
 
-  const int64_t nrows = f.B * f.Sq * f.Hq;
-  hipLaunchKernelGGL(bwd_dot_kernel, dim3((unsigned)((nrows + 15) / 16)), dim3(256), 0, st,
-                     static_cast<const uint16_t*>(f.O), static_cast<const uint16_t*>(f.ores),
-                     static_cast<const uint16_t*>(a.dO), nrows,
-                     (int)f.Sq, (int)f.Hq, a.Dv);
   hipError_t e = dma_launch_cand(f.delta, f.evict, BH, f.Sk, f.Sq, f.q0, f.w, a.cj, a.ce, a.ccnt,
                                  a.cdmax, st);
   if (e != hipSuccess) return e;
