@@ -6,8 +6,9 @@ a hand-counted vmcnt at a later phase barrier.  libdma_hip_safe.so is the
 same source built with DMA_SAFE_SYNC, where every barrier waits for all
 loads in flight.  Any read of LDS before its data landed would make the two
 differ, so their outputs must be bit-identical (O and the log-sum-exp, both
-forwards).  The backward kernels wait for all loads at every barrier, so
-there is no separate variant of them.
+forwards).  The backward's dq kernel (four query heads per workgroup) runs
+the same ping-pong with loads in flight across a barrier; its gradients are
+compared the same way.
 """
 import pytest
 import torch
@@ -66,3 +67,27 @@ def test_fast_and_safe_sync_agree_small(gpu_lib, B, Hq, Hkv, S, w):
     for lse in (False, True):
         fast, slow = _both(x, d, gm, lse)
         _equal(fast, slow, f"{(B, Hq, Hkv, S, w)} (lse={lse})")
+
+
+@pytest.mark.parametrize("name,shape", [("prefill_16k", None),
+                                        ("adhoc", (1, 8, 2, 700, 300, 150))])
+def test_backward_fast_and_safe_sync_agree_bitwise(gpu_lib, name, shape):
+    from trainable_dynamic_mask_amd.inputs import make_grad
+    if shape is None:
+        wl = WORKLOADS[name]
+        x = make_inputs(wl, device="cuda")
+    else:
+        B, Hq, Hkv, S, w, q0 = shape
+        wl, x = make_small(B, Hq, Hkv, S - q0, S, 128, w, dtype="bf16", q_offset=q0,
+                           seed=41, device="cuda")
+    print(f"backward race cross-check {name} Sq {wl.Sq}", flush=True)
+    d = dma.weights(x["V"], x["Delta"], x["A"])
+    gm = dma.topk_mask(d, wl.Sq, wl.q_offset, wl.w)
+    O, lse, Ores = dma.attn_fwd_train(x["Q"], x["K"], x["V"], d, gm)
+    dO = make_grad(wl, device="cuda")
+    fast = dma.attn_bwd(x["Q"], x["K"], x["V"], d, gm, O, lse, dO, O_res=Ores)
+    slow = dma.attn_bwd(x["Q"], x["K"], x["V"], d, gm, O, lse, dO, O_res=Ores,
+                        lib=_lib.load_safe())
+    torch.cuda.synchronize()
+    for u, v, n in zip(fast, slow, ("dQ", "dK", "dV", "ddelta")):
+        _equal(u, v, f"{name} backward {n}")

@@ -313,10 +313,12 @@ def attn_fwd_train(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, delta: tor
 def attn_bwd(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, delta: torch.Tensor, mask: Mask,
              O: torch.Tensor, lse: torch.Tensor, dO: torch.Tensor,
              O_res: Optional[torch.Tensor] = None,
-             scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None):
+             scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None,
+             lib=None):
     """Gradients of sum(dO * O) of attn_fwd (keep sets fixed): float32 dQ
     [B,Sq,Hq,D], dK and dV [B,Sk,Hkv,D], ddelta [B,Hkv,Sk].  O and lse are
-    the forward's outputs; O_res (from attn_fwd_train) makes dO . O exact."""
+    the forward's outputs; O_res (from attn_fwd_train) makes dO . O exact.
+    lib: the loaded library to call (default load(); the tests pass load_safe())."""
     _check_qkv(Q, K, V)
     B, Sq, Hq, D = Q.shape
     _, Sk, Hkv, _ = K.shape
@@ -333,7 +335,7 @@ def attn_bwd(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, delta: torch.Ten
     # (a temporary freed at once could hand its memory to the next copy)
     delta_c, O_c, lse_c, dO_c = (t.contiguous() for t in (delta, O, lse, dO))
     Ores_c = O_res.contiguous() if O_res is not None else None
-    lib = load()
+    lib = lib or load()
     dev = Q.device
     dQ = torch.empty(B, Sq, Hq, D, dtype=torch.float32, device=dev)
     dK = torch.empty(B, Sk, Hkv, D, dtype=torch.float32, device=dev)

@@ -11,12 +11,13 @@
 // (i over the rows and the G query heads of the key's kv head).
 //
 // Kernels:
-//   dot     Dv_i = dO_i . O_i.
 //   dq      query-major with the forward's work split: a workgroup walks the
-//           compacted key list of its 64-row tile, 64 keys per chunk, one
-//           wave per (query head, 32-row half).  S^T = K Q^T and dP^T = V dO^T
-//           read K and V rows; dQ^T += K^T dS^T reads K transposed.  Q^T and
-//           dO^T stay in registers.
+//           compacted key list of its 64-row tile, one wave per (query head,
+//           32-row half).  S^T = K Q^T and dP^T = V dO^T read K and V rows;
+//           dQ^T += K^T dS^T reads K transposed.  Q^T and dO^T stay in
+//           registers.  Its prologue also forms Dv_i = dO_i . O_i.  With four
+//           query heads per workgroup the waves run the forward's ping-pong
+//           (bwd_dq_pp_kernel), else one 64-key chunk per step.
 //   dkv     key-major over groups of 512 rows (8 query tiles), in two passes
 //           (dV, then dK and ddelta) so that two waves fit per SIMD.  The keys some
 //           row of a group keeps (at most w + 511: the candidate lists of the
@@ -319,6 +320,278 @@ __global__ __launch_bounds__(NH * 128, 2) void bwd_dq_kernel(DmaBwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- dq, ping-pong
+// The same gradient, for four query heads per workgroup (8 waves, one of each
+// group per SIMD), with the forward's ping-pong.  A step is one 32-key block
+// b (chunk b/2, half b%2).  Per block a wave runs an MFMA phase
+//   M_b = { dQ^T += K^T dS^T of block b-1 ;  S^T, dP^T of block b }
+// and a VALU phase
+//   V_b = { dS^T of block b from S^T and dP^T }.
+// In step b group A (waves 0-3) runs M_b then V_b; group B (waves 4-7) runs
+// V_{b-1} then M_b, so one wave of every SIMD mostly multiplies while the
+// other mostly exponentiates.  One workgroup barrier ends each step.
+//
+// Memory: K of chunk c sits in buffer c % 3 (read by the S products of its
+// two blocks and by their dQ products one step later), V of chunk c in
+// c % 2, list entries in slot c % 4, delta and eviction rows in c % 3.  At
+// the start of step 2c the waves gather chunk c+1 (K, V rows, delta and
+// eviction rows) and wave 0 loads the list entries of chunk c+2; the barrier
+// ending step 2c+1 waits for them (two steps in flight), and every buffer a
+// step writes was last read two steps or more before it.
+struct DqPpSmem {
+  unsigned char k[3][kTileB];  // K of chunk c in buffer c % 3
+  unsigned char v[2][kTileB];  // V of chunk c in buffer c % 2
+  int jl[4][kBk];              // list entries of chunk c in slot c % 4
+  float dl[3][kBk];            // delta of chunk c's keys in slot c % 3
+  int ev[3][kBk];              // their eviction rows
+};
+
+// End of a ping-pong step: the LDS reads of this wave are done, and at the
+// steps that close a load window (LOADS) its direct loads have landed too.
+template <bool LOADS>
+__device__ __forceinline__ void pp_barrier() {
+  asm volatile("" ::: "memory");
+#ifdef DMA_SAFE_SYNC
+  __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) expcnt(0) lgkmcnt(0)
+#else
+  if constexpr (LOADS)
+    __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) expcnt(0) lgkmcnt(0)
+  else
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // lgkmcnt(0) only
+#endif
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__global__ __launch_bounds__(512, 2) void bwd_dq_pp_kernel(DmaBwdArgs a) {
+  constexpr int NH = 4, NW = 8;
+  __shared__ __align__(16) DqPpSmem sm;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hi = lane >> 5;
+  const DmaAttnArgs& f = a.f;
+  const int G = (int)(f.Hq / f.Hkv);
+  const int ngrp = G / NH;
+  const int t = blockIdx.x, h = blockIdx.y;
+  const int b = blockIdx.z / ngrp, hgrp = blockIdx.z % ngrp;
+  const int hq = h * G + hgrp * NH + (wave >> 1);
+  const int half = wave & 1;
+  const bool grp_a = wave < NW / 2;
+  const int64_t seg = (int64_t)b * f.Hkv + h;
+  const int64_t g = seg * f.n_tiles + t;
+  const int r_lo = t * kBq;
+  const int rows = min(kBq, (int)f.Sq - r_lo);
+  const int cnt = f.u_cnt[g];
+  const int32_t* list = f.u_idx + g * f.u_stride;
+  const float* dlg = f.delta + seg * f.Sk;
+  const int32_t* evg = f.evict + seg * f.Sk;
+  const int nch = (cnt + kBk - 1) / kBk;
+  const int nb = 2 * nch;  // 32-key blocks
+  const int clast = max(cnt - 1, 0);
+  const unsigned char* Kg = static_cast<const unsigned char*>(f.K) + (b * f.ksb + h * f.ksh) * 2;
+  const unsigned char* Vg = static_cast<const unsigned char*>(f.V) + (b * f.ksb + h * f.ksh) * 2;
+  const uint32_t rowb = (uint32_t)(f.kss * 2);
+  const float scale2 = f.scale * kLog2e;
+
+  // this lane's query column n, its Q^T and dO^T operands, lse and D_i
+  const int n = half * 32 + l32;
+  const int nr = r_lo + (n < rows ? n : 0);  // rows past the tile repeat its first row
+  const int pos = (int)f.q0 + r_lo + n;
+  dma::bf16x8 qf[8], gf[8];
+  {
+    const uint16_t* qrow =
+        static_cast<const uint16_t*>(f.Q) + b * f.qsb + hq * f.qsh + (int64_t)nr * f.qss;
+    const uint16_t* grow = static_cast<const uint16_t*>(a.dO) + ((b * f.Sq + nr) * f.Hq + hq) * kD;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      qf[kk] = __builtin_bit_cast(dma::bf16x8,
+                                  *reinterpret_cast<const u32x4*>(qrow + kk * 16 + hi * 8));
+      gf[kk] = __builtin_bit_cast(dma::bf16x8,
+                                  *reinterpret_cast<const u32x4*>(grow + kk * 16 + hi * 8));
+    }
+  }
+  const float lse_q = f.lse[((int64_t)b * f.Hq + hq) * f.Sq + nr];
+  // D_i = dO_i . O_i, as in bwd_dq_kernel
+  float dv_q;
+  {
+    const int64_t ro = ((b * f.Sq + nr) * f.Hq + hq) * kD + hi * 8;
+    const uint16_t* orow = static_cast<const uint16_t*>(f.O) + ro;
+    const uint16_t* rrow = static_cast<const uint16_t*>(f.ores) + ro;
+    u32x4 ov[8], rv[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      ov[kk] = *reinterpret_cast<const u32x4*>(orow + kk * 16);
+      rv[kk] = f.ores ? *reinterpret_cast<const u32x4*>(rrow + kk * 16) : u32x4{0u, 0u, 0u, 0u};
+    }
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const u32x4 gv = __builtin_bit_cast(u32x4, gf[kk]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        acc[e] += (dma::bf16_lo(ov[kk][e]) + dma::bf16_lo(rv[kk][e])) * dma::bf16_lo(gv[e]) +
+                  (dma::bf16_hi(ov[kk][e]) + dma::bf16_hi(rv[kk][e])) * dma::bf16_hi(gv[e]);
+    }
+    const float part = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    dv_q = part + __shfl_xor(part, 32);
+    if (hi == 0 && n < rows) a.Dv[((int64_t)b * f.Hq + hq) * f.Sq + r_lo + n] = dv_q;
+  }
+
+  const uint32_t lds_k = lds_addr(&sm.k[0][0]), lds_v = lds_addr(&sm.v[0][0]);
+  const uint32_t lds_j = lds_addr(&sm.jl[0][0]), lds_d = lds_addr(&sm.dl[0][0]),
+                 lds_e = lds_addr(&sm.ev[0][0]);
+  // chunk x's K and V rows (16 pieces of 4 rows per tile, piece p by wave
+  // p % NW; lane L fills row 4p + L/16, chunk slot L%16), and wave 0 its
+  // delta and eviction rows
+  auto gather = [&](int x) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int kb = x % 3, vb = x & 1, js = x & 3, ds_ = x % 3;
+#pragma unroll
+    for (int u = 0; u < 16 / NW; ++u) {
+      const int piece = wave + u * NW;
+      const int row = piece * 4 + (ln >> 4);
+      const int lc = (ln & 15) ^ swz(row);
+      const uint32_t j = (uint32_t)sm.jl[js][row];
+      dma_b128(Kg + j * rowb + lc * 16, lds_k + kb * kTileB + piece * 1024);
+      dma_b128(Vg + j * rowb + lc * 16, lds_v + vb * kTileB + piece * 1024);
+    }
+    if (wave == 0) {
+      const int j = sm.jl[js][lane];
+      dma_b32(dlg + j, lds_d + ds_ * 256);
+      dma_b32(evg + j, lds_e + ds_ * 256);
+    }
+  };
+  // the loads of step b (even steps only): list entries of chunk b/2 + 2, chunk b/2 + 1
+  auto issue = [&](int bb) {
+    if ((bb & 1) == 0) {
+      const int c = bb >> 1;
+      if (c < nch) {
+        if (wave == 0) dma_b32(list + min((c + 2) * kBk + lane, clast), lds_j + ((c + 2) & 3) * 256);
+        if (c + 1 < nch) gather(c + 1);
+      }
+    }
+  };
+
+  // prologue: list entries of chunks 0 and 1, then chunk 0's rows
+  if (wave == 0) {
+    dma_b32(list + min(lane, clast), lds_j);
+    dma_b32(list + min(kBk + lane, clast), lds_j + 256);
+  }
+  wait_all_barrier();
+  gather(0);
+  wait_all_barrier();
+
+  dma::f32x16 dq[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dq[db][i] = 0.f;
+  dma::f32x16 s, dp;
+  dma::bf16x8 dsb[2];
+
+  // M_bb: dQ of block bb-1 (from dsb), then S^T and dP^T of block bb (lane
+  // (l32, hi) reads key row mb*32 + l32; register i is key mb*32 + 8(i/4) +
+  // 4hi + i%4)
+  auto mphase = [&](int bb) {
+    if (bb >= 1) {
+      const int pbk = bb - 1;
+      const unsigned char* KP = sm.k[(pbk >> 1) % 3];
+      const int pmb = pbk & 1;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+          dq[db] = mfma(tr_operand(KP, pmb * 32 + 16 * hf, db * 32, lane), dsb[hf], dq[db]);
+    }
+    if (bb < nb) {
+      const int cb = bb >> 1, mb = bb & 1;
+      const unsigned char* KT = sm.k[cb % 3];
+      const unsigned char* VT = sm.v[cb & 1];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        s[i] = 0.f;
+        dp[i] = 0.f;
+      }
+      const int row = mb * 32 + l32;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        s = mfma(row_operand(KT, row, 2 * kk + hi), qf[kk], s);
+        dp = mfma(row_operand(VT, row, 2 * kk + hi), gf[kk], dp);
+      }
+    }
+  };
+  // V_bb: dS^T = P^T (dP^T - D) of block bb as bf16 B operands
+  auto vphase = [&](int bb) {
+    const int cb = bb >> 1, mb = bb & 1;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      float ds[8];
+#pragma unroll
+      for (int h4 = 0; h4 < 2; ++h4) {
+        const int q4 = 2 * hf + h4;
+        const int kb = mb * 32 + 8 * q4 + 4 * hi;
+        const int4 j4 = *reinterpret_cast<const int4*>(&sm.jl[cb & 3][kb]);
+        const int4 e4 = *reinterpret_cast<const int4*>(&sm.ev[cb % 3][kb]);
+        const float4 d4 = *reinterpret_cast<const float4*>(&sm.dl[cb % 3][kb]);
+        const int jv[4] = {j4.x, j4.y, j4.z, j4.w};
+        const int ev[4] = {e4.x, e4.y, e4.z, e4.w};
+        const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 4 * q4 + r;
+          // list padding (positions past cnt) and rows outside [j, e) get weight 0
+          const bool kept = (cb * kBk + kb + r < cnt) &
+                            ((uint32_t)(pos - jv[r]) < (uint32_t)(ev[r] - jv[r]));
+          const float v = fmaf(s[i], scale2, (dv[r] - lse_q) * kLog2e);
+          const float p = __builtin_amdgcn_exp2f(kept ? v : -INFINITY);
+          ds[4 * h4 + r] = p * (dp[i] - dv_q);
+        }
+      }
+      dsb[hf] = to_bf16x8(ds);
+    }
+  };
+
+  if (grp_a) {
+    for (int bb = 0; bb <= nb; ++bb) {
+      issue(bb);
+      mphase(bb);
+      if (bb < nb) vphase(bb);
+      if (bb & 1)
+        pp_barrier<true>();
+      else
+        pp_barrier<false>();
+    }
+  } else {
+    for (int bb = 0; bb <= nb; ++bb) {
+      issue(bb);
+      if (bb >= 1) vphase(bb - 1);
+      mphase(bb);
+      if (bb & 1)
+        pp_barrier<true>();
+      else
+        pp_barrier<false>();
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+
+  if (n < rows) {
+    float* orow = a.dQ + (((int64_t)b * f.Sq + r_lo + n) * f.Hq + hq) * kD;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d = db * 32 + 8 * q4 + 4 * hi;
+        float4 o;
+        o.x = f.scale * dq[db][4 * q4 + 0];
+        o.y = f.scale * dq[db][4 * q4 + 1];
+        o.z = f.scale * dq[db][4 * q4 + 2];
+        o.w = f.scale * dq[db][4 * q4 + 3];
+        *reinterpret_cast<float4*>(orow + d) = o;
+      }
+  }
+}
+
 // ---------------------------------------------------------------- dkv
 struct DkvSmem {
   unsigned char q[2][kTileB];   // Q rows of one (row tile, query head)
@@ -582,7 +855,10 @@ template <int NH>
 hipError_t launch_dq(DmaBwdArgs& a, hipStream_t st) {
   const int G = (int)(a.f.Hq / a.f.Hkv);
   dim3 grid((unsigned)a.f.n_tiles, (unsigned)a.f.Hkv, (unsigned)(a.f.B * (G / NH)));
-  hipLaunchKernelGGL(bwd_dq_kernel<NH>, grid, dim3(NH * 128), 0, st, a);
+  if constexpr (NH == 4)
+    hipLaunchKernelGGL(bwd_dq_pp_kernel, grid, dim3(NH * 128), 0, st, a);
+  else
+    hipLaunchKernelGGL(bwd_dq_kernel<NH>, grid, dim3(NH * 128), 0, st, a);
   return hipGetLastError();
 }
 
