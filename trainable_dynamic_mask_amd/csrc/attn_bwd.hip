@@ -521,8 +521,14 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_pp_kernel(DmaBwdArgs a) {
       }
     }
   };
-  // V_bb: dS^T = P^T (dP^T - D) of block bb as bf16 B operands
-  auto vphase = [&](int bb) {
+  // V_bb: dS^T = P^T (dP^T - D) of block bb as bf16 B operands.  The
+  // exponent is scale2 * s + log2(e) * delta - log2(e) * lse: two FMAs per
+  // element.  MASKED blocks test j <= p < e_j and the list's end per element;
+  // the others (the leading chunks, whose keys every row of the tile keeps)
+  // need no test.
+  const float nl = -lse_q * kLog2e;
+  auto vphase = [&](int bb, auto masked) {
+    constexpr bool MASKED = decltype(masked)::value;
     const int cb = bb >> 1, mb = bb & 1;
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
@@ -531,41 +537,71 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_pp_kernel(DmaBwdArgs a) {
       for (int h4 = 0; h4 < 2; ++h4) {
         const int q4 = 2 * hf + h4;
         const int kb = mb * 32 + 8 * q4 + 4 * hi;
-        const int4 j4 = *reinterpret_cast<const int4*>(&sm.jl[cb & 3][kb]);
-        const int4 e4 = *reinterpret_cast<const int4*>(&sm.ev[cb % 3][kb]);
         const float4 d4 = *reinterpret_cast<const float4*>(&sm.dl[cb % 3][kb]);
-        const int jv[4] = {j4.x, j4.y, j4.z, j4.w};
-        const int ev[4] = {e4.x, e4.y, e4.z, e4.w};
         const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+        int jv[4] = {0, 0, 0, 0}, ev[4] = {0, 0, 0, 0};
+        if constexpr (MASKED) {
+          const int4 j4 = *reinterpret_cast<const int4*>(&sm.jl[cb & 3][kb]);
+          const int4 e4 = *reinterpret_cast<const int4*>(&sm.ev[cb % 3][kb]);
+          jv[0] = j4.x; jv[1] = j4.y; jv[2] = j4.z; jv[3] = j4.w;
+          ev[0] = e4.x; ev[1] = e4.y; ev[2] = e4.z; ev[3] = e4.w;
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int i = 4 * q4 + r;
-          // list padding (positions past cnt) and rows outside [j, e) get weight 0
-          const bool kept = (cb * kBk + kb + r < cnt) &
-                            ((uint32_t)(pos - jv[r]) < (uint32_t)(ev[r] - jv[r]));
-          const float v = fmaf(s[i], scale2, (dv[r] - lse_q) * kLog2e);
-          const float p = __builtin_amdgcn_exp2f(kept ? v : -INFINITY);
+          float v = fmaf(s[i], scale2, fmaf(dv[r], kLog2e, nl));
+          if constexpr (MASKED) {
+            // list padding (positions past cnt) and rows outside [j, e) get weight 0
+            const bool kept = (cb * kBk + kb + r < cnt) &
+                              ((uint32_t)(pos - jv[r]) < (uint32_t)(ev[r] - jv[r]));
+            v = kept ? v : -INFINITY;
+          }
+          const float p = __builtin_amdgcn_exp2f(v);
           ds[4 * h4 + r] = p * (dp[i] - dv_q);
         }
       }
       dsb[hf] = to_bf16x8(ds);
     }
   };
+  using Plain = std::integral_constant<bool, false>;
+  using Masked = std::integral_constant<bool, true>;
+  // blocks [0, pb) belong to chunks every row keeps
+  const int pb = 2 * min(f.u_nfull[g] / kBk, nch);
 
   if (grp_a) {
-    for (int bb = 0; bb <= nb; ++bb) {
+    int bb = 0;
+    for (; bb < pb; ++bb) {
       issue(bb);
       mphase(bb);
-      if (bb < nb) vphase(bb);
+      vphase(bb, Plain{});
+      if (bb & 1)
+        pp_barrier<true>();
+      else
+        pp_barrier<false>();
+    }
+    for (; bb <= nb; ++bb) {
+      issue(bb);
+      mphase(bb);
+      if (bb < nb) vphase(bb, Masked{});
       if (bb & 1)
         pp_barrier<true>();
       else
         pp_barrier<false>();
     }
   } else {
-    for (int bb = 0; bb <= nb; ++bb) {
+    int bb = 0;
+    for (; bb <= pb; ++bb) {
       issue(bb);
-      if (bb >= 1) vphase(bb - 1);
+      if (bb >= 1) vphase(bb - 1, Plain{});
+      mphase(bb);
+      if (bb & 1)
+        pp_barrier<true>();
+      else
+        pp_barrier<false>();
+    }
+    for (; bb <= nb; ++bb) {
+      issue(bb);
+      vphase(bb - 1, Masked{});
       mphase(bb);
       if (bb & 1)
         pp_barrier<true>();
