@@ -697,6 +697,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(DmaBwdArgs a) {
   const int nsteps = nt * G;
 
   const float scale2 = f.scale * kLog2e;
+  const float dltl = dlt * kLog2e;
+  const uint32_t span = (uint32_t)(e - j);
   const uint32_t lds_q = lds_addr(&sm.q[0][0]), lds_g = lds_addr(&sm.g[0][0]);
   const uint32_t lds_l = lds_addr(&sm.lse[0][0]), lds_dv = lds_addr(&sm.dv[0][0]);
   // step st = (k-th alive row tile, head st % G)
@@ -747,6 +749,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(DmaBwdArgs a) {
     const int buf = st & 1;
     const int rt = tile_of(st);
     const int p0 = (int)f.q0 + g_lo + rt * kBq;
+    const int pj0 = p0 - j;  // this lane's key against the tile's first row
     const unsigned char* QT = sm.q[buf];
     const unsigned char* GT = sm.g[buf];
 #pragma unroll
@@ -779,9 +782,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(DmaBwdArgs a) {
 #pragma unroll
           for (int r4 = 0; r4 < 4; ++r4) {
             const int i = kb * 8 + q4 * 4 + r4;
-            const int p = p0 + rb + r4;
-            const bool kept = (uint32_t)(p - j) < (uint32_t)(e - j);
-            const float v = fmaf(s[i], scale2, (dlt - lr[r4]) * kLog2e);
+            // kept iff j <= p < e: one unsigned compare of p - j against e - j
+            const bool kept = (uint32_t)(pj0 + rb + r4) < span;
+            // exponent scale2 * s + log2(e) * (delta - lse): two FMAs
+            const float v = fmaf(s[i], scale2, fmaf(lr[r4], -kLog2e, dltl));
             const float pp = __builtin_amdgcn_exp2f(kept ? v : -INFINITY);
             if constexpr (MODE == 0) {
               pv[q4 * 4 + r4] = pp;
