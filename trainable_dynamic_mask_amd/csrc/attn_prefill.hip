@@ -759,6 +759,37 @@ __global__ __launch_bounds__(NH * 128, 1) void attn_prefill_bf16_kernel(DmaAttnA
   const float lt = acc.l + __shfl_xor(acc.l, 32);
   const float ltr = acc.lr + __shfl_xor(acc.lr, 32);
   const float inv = ltr > 0.f ? 1.f / ltr : 0.f;
+  // O goes out through LDS so that each store instruction writes whole
+  // 256-byte rows: the wave's 32 x 128 bf16 tile is written to its own LDS
+  // region (rows padded to 272 bytes) in the accumulator layout, then read
+  // back and stored 16 bytes per lane, 16 lanes per row.  The K/V buffers
+  // are free once every wave's direct loads have landed.
+  __syncthreads();
+  constexpr int kOutRowB = kRowB + 16;
+  static_assert(8 * 32 * kOutRowB <= (int)(sizeof(sm.k) + sizeof(sm.v)), "O staging fits");
+  unsigned char* ow = &sm.k[0][0] + wave * (32 * kOutRowB);
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d = db * 32 + 8 * q4 + 4 * hi;
+      u32x2 u;
+      u[0] = pack_bf16x2(acc.o[db][q4 * 4 + 0] * inv, acc.o[db][q4 * 4 + 1] * inv);
+      u[1] = pack_bf16x2(acc.o[db][q4 * 4 + 2] * inv, acc.o[db][q4 * 4 + 3] * inv);
+      *reinterpret_cast<u32x2*>(ow + l32 * kOutRowB + d * 2) = u;
+    }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int r = it * 4 + (lane >> 4);  // the wave's row r: query half*32 + r
+    const u32x4 v = *reinterpret_cast<const u32x4*>(ow + r * kOutRowB + (lane & 15) * 16);
+    if (half * 32 + r < rows)
+      *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.O) +
+                                (((int64_t)b * a.Sq + r_lo + half * 32 + r) * a.Hq + hq) * kD +
+                                (lane & 15) * 8) = v;
+  }
   if (n < rows) {
     uint16_t* orow = static_cast<uint16_t*>(a.O) + (((int64_t)b * a.Sq + r_lo + n) * a.Hq + hq) * kD;
 #pragma unroll
@@ -766,14 +797,13 @@ __global__ __launch_bounds__(NH * 128, 1) void attn_prefill_bf16_kernel(DmaAttnA
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int d = db * 32 + 8 * q4 + 4 * hi;
-        float x[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) x[k] = acc.o[db][q4 * 4 + k] * inv;
-        u32x2 u;
-        u[0] = pack_bf16x2(x[0], x[1]);
-        u[1] = pack_bf16x2(x[2], x[3]);
-        *reinterpret_cast<u32x2*>(orow + d) = u;
         if (a.ores) {
+          float x[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) x[k] = acc.o[db][q4 * 4 + k] * inv;
+          u32x2 u;
+          u[0] = pack_bf16x2(x[0], x[1]);
+          u[1] = pack_bf16x2(x[2], x[3]);
           // x - bf16(x) is exact in fp32; stored in bf16 it carries x to ~2^-18
           u32x2 r;
           r[0] = pack_bf16x2(x[0] - dma::bf16_lo(u[0]), x[1] - dma::bf16_hi(u[0]));
