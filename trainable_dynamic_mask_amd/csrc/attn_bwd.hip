@@ -611,20 +611,42 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_pp_kernel(DmaBwdArgs a) {
   }
   __builtin_amdgcn_s_waitcnt(0);
 
-  if (n < rows) {
-    float* orow = a.dQ + (((int64_t)b * f.Sq + r_lo + n) * f.Hq + hq) * kD;
+  // dQ goes out through LDS (the K/V buffers, free after the last barrier)
+  // in two halves of 64 columns, so that each store instruction writes whole
+  // 256-byte row pieces (16 bytes per lane, 16 lanes per row) instead of 16
+  // bytes in each of 32 rows
+  __syncthreads();
+  constexpr int kOutRowB = 256 + 16;
+  static_assert(8 * 32 * kOutRowB <= (int)(sizeof(sm.k) + sizeof(sm.v)), "dQ staging fits");
+  unsigned char* ow = &sm.k[0][0] + wave * (32 * kOutRowB);
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+  for (int h2 = 0; h2 < 2; ++h2) {
+#pragma unroll
+    for (int db = 2 * h2; db < 2 * h2 + 2; ++db)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const int d = db * 32 + 8 * q4 + 4 * hi;
+        const int dl = (db - 2 * h2) * 32 + 8 * q4 + 4 * hi;
         float4 o;
         o.x = f.scale * dq[db][4 * q4 + 0];
         o.y = f.scale * dq[db][4 * q4 + 1];
         o.z = f.scale * dq[db][4 * q4 + 2];
         o.w = f.scale * dq[db][4 * q4 + 3];
-        *reinterpret_cast<float4*>(orow + d) = o;
+        *reinterpret_cast<float4*>(ow + l32 * kOutRowB + dl * 4) = o;
       }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int r = it * 4 + (lane >> 4);  // the wave's row r: query half*32 + r
+      const float4 v = *reinterpret_cast<const float4*>(ow + r * kOutRowB + (lane & 15) * 16);
+      if (half * 32 + r < rows)
+        *reinterpret_cast<float4*>(a.dQ + (((int64_t)b * f.Sq + r_lo + half * 32 + r) * f.Hq + hq) * kD +
+                                   h2 * 64 + (lane & 15) * 4) = v;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 }
 
@@ -812,22 +834,47 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(DmaBwdArgs a) {
   // partial sums of this group for the lane's key; register i of block db is
   // d = db*32 + 8(i/4) + 4hi + i%4
   dd += __shfl_xor(dd, 32);
-  if (real) {
-    const int64_t o = gi * a.cap + slot;
-    float* out = (MODE == 0 ? a.pv : a.pk) + o * kD;
+  // The wave's 32 partial rows are consecutive slots, i.e. 16 KB of
+  // contiguous memory: they go out through LDS (the Q/dO buffers, free after
+  // the last barrier) in two halves of 64 columns, 16 bytes per lane and 16
+  // lanes per 256-byte row piece, instead of 16 bytes in each of 32 rows
+  {
+    constexpr int kOutRowB = 256 + 16;
+    static_assert(4 * 32 * kOutRowB <= (int)(sizeof(sm.q) + sizeof(sm.g)), "partial staging fits");
+    unsigned char* ow = &sm.q[0][0] + wave * (32 * kOutRowB);
+    float* outw = (MODE == 0 ? a.pv : a.pk) + (gi * a.cap + slice * kSliceKeys + wave * 32) * kD;
     const float sc = MODE == 0 ? 1.f : f.scale;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int h2 = 0; h2 < 2; ++h2) {
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d = db * 32 + 8 * q4 + 4 * hi;
-        float4 x;
-        x.x = sc * acc[db][4 * q4 + 0];
-        x.y = sc * acc[db][4 * q4 + 1];
-        x.z = sc * acc[db][4 * q4 + 2];
-        x.w = sc * acc[db][4 * q4 + 3];
-        *reinterpret_cast<float4*>(out + d) = x;
+      for (int db = 2 * h2; db < 2 * h2 + 2; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int dl = (db - 2 * h2) * 32 + 8 * q4 + 4 * hi;
+          float4 x;
+          x.x = sc * acc[db][4 * q4 + 0];
+          x.y = sc * acc[db][4 * q4 + 1];
+          x.z = sc * acc[db][4 * q4 + 2];
+          x.w = sc * acc[db][4 * q4 + 3];
+          *reinterpret_cast<float4*>(ow + l32 * kOutRowB + dl * 4) = x;
+        }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int r = it * 4 + (lane >> 4);  // the wave's key r: slot slice*128 + wave*32 + r
+        const float4 v = *reinterpret_cast<const float4*>(ow + r * kOutRowB + (lane & 15) * 16);
+        if (slice * kSliceKeys + wave * 32 + r < count)
+          *reinterpret_cast<float4*>(outw + r * kD + h2 * 64 + (lane & 15) * 4) = v;
       }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+  }
+  if (real) {
+    const int64_t o = gi * a.cap + slot;
     if (MODE == 1 && hi == 0) {
       a.pd[o] = dd;
       a.pmap[gi * f.Sk + j] = slot;

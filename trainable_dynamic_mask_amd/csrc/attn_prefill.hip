@@ -768,6 +768,25 @@ __global__ __launch_bounds__(NH * 128, 1) void attn_prefill_bf16_kernel(DmaAttnA
   constexpr int kOutRowB = kRowB + 16;
   static_assert(8 * 32 * kOutRowB <= (int)(sizeof(sm.k) + sizeof(sm.v)), "O staging fits");
   unsigned char* ow = &sm.k[0][0] + wave * (32 * kOutRowB);
+  auto wave_sync = [] {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  // one bf16 [32 x 128] tile of the wave (O, then its rounding residual)
+  // from LDS to rows of dst
+  auto store_rows = [&](uint16_t* dst) {
+    wave_sync();
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int r = it * 4 + (lane >> 4);  // the wave's row r: query half*32 + r
+      const u32x4 v = *reinterpret_cast<const u32x4*>(ow + r * kOutRowB + (lane & 15) * 16);
+      if (half * 32 + r < rows)
+        *reinterpret_cast<u32x4*>(dst + (((int64_t)b * a.Sq + r_lo + half * 32 + r) * a.Hq + hq) * kD +
+                                  (lane & 15) * 8) = v;
+    }
+    wave_sync();
+  };
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -778,39 +797,26 @@ __global__ __launch_bounds__(NH * 128, 1) void attn_prefill_bf16_kernel(DmaAttnA
       u[1] = pack_bf16x2(acc.o[db][q4 * 4 + 2] * inv, acc.o[db][q4 * 4 + 3] * inv);
       *reinterpret_cast<u32x2*>(ow + l32 * kOutRowB + d * 2) = u;
     }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-  for (int it = 0; it < 8; ++it) {
-    const int r = it * 4 + (lane >> 4);  // the wave's row r: query half*32 + r
-    const u32x4 v = *reinterpret_cast<const u32x4*>(ow + r * kOutRowB + (lane & 15) * 16);
-    if (half * 32 + r < rows)
-      *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.O) +
-                                (((int64_t)b * a.Sq + r_lo + half * 32 + r) * a.Hq + hq) * kD +
-                                (lane & 15) * 8) = v;
-  }
-  if (n < rows) {
-    uint16_t* orow = static_cast<uint16_t*>(a.O) + (((int64_t)b * a.Sq + r_lo + n) * a.Hq + hq) * kD;
+  store_rows(static_cast<uint16_t*>(a.O));
+  if (a.ores) {
+    // x - bf16(x) is exact in fp32; stored in bf16 it carries x to ~2^-18
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int d = db * 32 + 8 * q4 + 4 * hi;
-        if (a.ores) {
-          float x[4];
+        float x[4];
 #pragma unroll
-          for (int k = 0; k < 4; ++k) x[k] = acc.o[db][q4 * 4 + k] * inv;
-          u32x2 u;
-          u[0] = pack_bf16x2(x[0], x[1]);
-          u[1] = pack_bf16x2(x[2], x[3]);
-          // x - bf16(x) is exact in fp32; stored in bf16 it carries x to ~2^-18
-          u32x2 r;
-          r[0] = pack_bf16x2(x[0] - dma::bf16_lo(u[0]), x[1] - dma::bf16_hi(u[0]));
-          r[1] = pack_bf16x2(x[2] - dma::bf16_lo(u[1]), x[3] - dma::bf16_hi(u[1]));
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.ores) + (orow - static_cast<uint16_t*>(a.O)) + d) = r;
-        }
+        for (int k = 0; k < 4; ++k) x[k] = acc.o[db][q4 * 4 + k] * inv;
+        const uint32_t u0 = pack_bf16x2(x[0], x[1]), u1 = pack_bf16x2(x[2], x[3]);
+        u32x2 r;
+        r[0] = pack_bf16x2(x[0] - dma::bf16_lo(u0), x[1] - dma::bf16_hi(u0));
+        r[1] = pack_bf16x2(x[2] - dma::bf16_lo(u1), x[3] - dma::bf16_hi(u1));
+        *reinterpret_cast<u32x2*>(ow + l32 * kOutRowB + d * 2) = r;
       }
+    store_rows(static_cast<uint16_t*>(a.ores));
+  }
+  if (n < rows) {
     if (a.lse && hi == 0)
       a.lse[((int64_t)b * a.Hq + hq) * a.Sq + r_lo + n] =
           (acc.m + __log2f(lt)) * kLn2 + (rowref ? rref : dmax);
